@@ -1,0 +1,242 @@
+"""CPU oracle for the ELSAA attention forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never links, loads or
+calls it, and it imports nothing from the GPU library.
+
+The arithmetic lives in ``elsaa_oracle.c`` (binary64, OpenMP over independent
+rows); this module compiles it with gcc, loads it with ctypes and composes the
+stages in the order the method applies them:
+
+  SRP codes -> stable sort by bucket -> chunked exact attention (o_s, lse)
+  -> RACE tables -> RACE gather (o_lr, Z_lr) -> gates -> alpha and fusion.
+
+Sources: "ELSAA: Efficient Low-Rank and Sparse Attention Approximation for
+Training Transformers" (arxivlens summary, first paragraph) and "Two Efficient
+Attentions, One Denominator Problem" (sections "Two efficient branches can
+still be mis-scaled" and "The ablation isolates the actual contribution").
+Each C function states the passage and the reading it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "elsaa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (binary64, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int, ctypes.c_long, ctypes.c_double
+        lib.oracle_num_threads.restype = i32
+        lib.oracle_set_num_threads.argtypes = [i32]
+        lib.oracle_exact_dot_sign.argtypes = [P, P, i32]
+        lib.oracle_exact_dot_sign.restype = i32
+        lib.oracle_srp_codes.argtypes = [P, i64, i32, P, i32, i32, P, i32, i32]
+        lib.oracle_stable_sort.argtypes = [P, i64, i32, i32, P]
+        lib.oracle_stable_sort.restype = i32
+        lib.oracle_chunk_attention.argtypes = [P, P, P, P, P, i64, i32, i32, i32, P, P]
+        lib.oracle_chunk_attention.restype = i64
+        lib.oracle_race_tables.argtypes = [P, P, i64, i32, i32, i32, i32, P, P]
+        lib.oracle_race_query.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P]
+        lib.oracle_gates.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
+        lib.oracle_fuse.argtypes = [P, P, P, P, P, P, f64, i64, i32, P, P]
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    _load().oracle_set_num_threads(int(n))
+
+
+# ---------------------------------------------------------------- stages ----
+
+def exact_dot_sign(x, r) -> int:
+    """Sign of the exact dot product of two vectors of <=24-bit floats."""
+    x = _f64(x); r = _f64(r)
+    assert x.shape == r.shape and x.ndim == 1
+    return _load().oracle_exact_dot_sign(_p(x), _p(r), x.shape[0])
+
+
+def srp_codes(x, planes, first: int, nbits: int) -> np.ndarray:
+    """Codes of rows x[..., d] under planes[first:first+nbits]; bit t <-> plane first+t."""
+    x = _f64(x); planes = _f64(planes)
+    d = x.shape[-1]
+    rows = x.size // d if d else 0
+    out = np.zeros(x.shape[:-1], dtype=np.int32)
+    if rows:
+        _load().oracle_srp_codes(_p(x), rows, d, _p(planes), first, nbits, _p(out), 1, 0)
+    return out
+
+
+def race_codes(x, planes, n_sort: int, L: int, P: int) -> np.ndarray:
+    """[..., L] codes: table l uses planes[n_sort + l*P : n_sort + (l+1)*P]."""
+    x = _f64(x); planes = _f64(planes)
+    d = x.shape[-1]
+    rows = x.size // d
+    out = np.zeros(x.shape[:-1] + (L,), dtype=np.int32)
+    lib = _load()
+    for l in range(L):
+        lib.oracle_srp_codes(_p(x), rows, d, _p(planes), n_sort + l * P, P, _p(out), L, l)
+    return out
+
+
+def stable_sort(codes, nbuckets: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.int32)
+    n = codes.shape[-1]
+    segs = codes.size // n if n else 0
+    perm = np.zeros(codes.shape, dtype=np.int32)
+    if segs and _load().oracle_stable_sort(_p(codes), segs, n, nbuckets, _p(perm)) != 0:
+        raise MemoryError("oracle_stable_sort: allocation failed")
+    return perm
+
+
+def chunk_attention(q, k, v, perm_q, perm_k, w: int):
+    """Returns (o_s [..., N, d], lse [..., N], pairs)."""
+    q = _f64(q); k = _f64(k); v = _f64(v)
+    perm_q = np.ascontiguousarray(perm_q, dtype=np.int32)
+    perm_k = np.ascontiguousarray(perm_k, dtype=np.int32)
+    n, d = q.shape[-2], q.shape[-1]
+    segs = q.size // (n * d)
+    o = np.zeros(q.shape, dtype=np.float64)
+    lse = np.zeros(q.shape[:-1], dtype=np.float64)
+    pairs = _load().oracle_chunk_attention(_p(q), _p(k), _p(v), _p(perm_q), _p(perm_k),
+                                           segs, n, d, w, _p(o), _p(lse))
+    return o, lse, int(pairs)
+
+
+def race_tables(v, kcodes, P: int):
+    """Returns (sums [..., L, 2^P, d], counts [..., L, 2^P])."""
+    v = _f64(v)
+    kcodes = np.ascontiguousarray(kcodes, dtype=np.int32)
+    n, d = v.shape[-2], v.shape[-1]
+    L = kcodes.shape[-1]
+    lead = v.shape[:-2]
+    segs = v.size // (n * d)
+    sums = np.zeros(lead + (L, 1 << P, d), dtype=np.float64)
+    counts = np.zeros(lead + (L, 1 << P), dtype=np.float64)
+    _load().oracle_race_tables(_p(v), _p(kcodes), segs, n, d, L, P, _p(sums), _p(counts))
+    return sums, counts
+
+
+def race_query(qcodes, sums, counts, P: int):
+    """Returns (o_lr [..., N, d], z_lr [..., N])."""
+    qcodes = np.ascontiguousarray(qcodes, dtype=np.int32)
+    sums = _f64(sums); counts = _f64(counts)
+    n, L = qcodes.shape[-2], qcodes.shape[-1]
+    d = sums.shape[-1]
+    segs = qcodes.size // (n * L)
+    o = np.zeros(qcodes.shape[:-1] + (d,), dtype=np.float64)
+    z = np.zeros(qcodes.shape[:-1], dtype=np.float64)
+    _load().oracle_race_query(_p(qcodes), _p(sums), _p(counts), segs, n, d, L, P, _p(o), _p(z))
+    return o, z
+
+
+def gates(x_gate, gate_w, gate_b, H: int):
+    """x_gate [B, N, dg], gate_w [2, H, dg], gate_b [2, H] -> (g_s, g_lr) [B, H, N]."""
+    x_gate = _f64(x_gate); gate_w = _f64(gate_w); gate_b = _f64(gate_b)
+    B, n, dg = x_gate.shape
+    g_s = np.zeros((B, H, n)); g_lr = np.zeros((B, H, n))
+    _load().oracle_gates(_p(x_gate), _p(gate_w), _p(gate_b), B, H, n, dg, _p(g_s), _p(g_lr))
+    return g_s, g_lr
+
+
+def fuse(o_s, lse, o_lr, z_lr, g_s, g_lr, lam: float):
+    """Returns (alpha [..., N], y [..., N, d])."""
+    o_s = _f64(o_s); lse = _f64(lse); o_lr = _f64(o_lr); z_lr = _f64(z_lr)
+    g_s = _f64(g_s); g_lr = _f64(g_lr)
+    d = o_s.shape[-1]
+    rows = o_s.size // d
+    alpha = np.zeros(o_s.shape[:-1]); y = np.zeros(o_s.shape)
+    _load().oracle_fuse(_p(o_s), _p(lse), _p(o_lr), _p(z_lr), _p(g_s), _p(g_lr),
+                        float(lam), rows, d, _p(alpha), _p(y))
+    return alpha, y
+
+
+# --------------------------------------------------------------- forward ----
+
+@dataclass
+class OracleResult:
+    sort_code_q: np.ndarray
+    sort_code_k: np.ndarray
+    race_code_q: np.ndarray
+    race_code_k: np.ndarray
+    perm_q: np.ndarray
+    perm_k: np.ndarray
+    o_s: np.ndarray
+    lse: np.ndarray
+    race_sum: np.ndarray
+    race_cnt: np.ndarray
+    o_lr: np.ndarray
+    z_lr: np.ndarray
+    g_s: np.ndarray
+    g_lr: np.ndarray
+    alpha: np.ndarray
+    y: np.ndarray
+    pairs: int
+    seconds: float
+
+
+def forward(q, k, v, x_gate, hyperplanes, gate_w, gate_b, *, sort_bits: int,
+            chunk: int, race_tables_n: int, race_bits: int, lam: float) -> OracleResult:
+    """The whole forward pass on binary64 copies of the stored inputs.
+
+    q, k, v: [B, H, N, d]; x_gate: [B, N, dg]; hyperplanes: [sort_bits + L*P, d]
+    (sort planes first, then table l's P planes); gate_w [2, H, dg]; gate_b [2, H].
+    """
+    t0 = time.perf_counter()
+    q = _f64(q); k = _f64(k); v = _f64(v); planes = _f64(hyperplanes)
+    B, H, N, d = q.shape
+    L, P = race_tables_n, race_bits
+    assert N % chunk == 0
+    cq = srp_codes(q, planes, 0, sort_bits)
+    ck = srp_codes(k, planes, 0, sort_bits)
+    rq = race_codes(q, planes, sort_bits, L, P)
+    rk = race_codes(k, planes, sort_bits, L, P)
+    pq = stable_sort(cq, 1 << sort_bits)
+    pk = stable_sort(ck, 1 << sort_bits)
+    o_s, lse, pairs = chunk_attention(q, k, v, pq, pk, chunk)
+    sums, counts = race_tables(v, rk, P)
+    o_lr, z_lr = race_query(rq, sums, counts, P)
+    g_s, g_lr = gates(x_gate, gate_w, gate_b, H)
+    alpha, y = fuse(o_s, lse, o_lr, z_lr, g_s, g_lr, lam)
+    return OracleResult(cq, ck, rq, rk, pq, pk, o_s, lse, sums, counts, o_lr, z_lr,
+                        g_s, g_lr, alpha, y, pairs, time.perf_counter() - t0)
