@@ -1,0 +1,95 @@
+// elsaa_internal.hpp -- shared definitions of the ELSAA gfx950 kernels and the
+// host library that launches them.  Not part of the public ABI (include/elsaa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "elsaa.h"
+
+namespace elsaa {
+
+// ----------------------------------------------------------------------------
+// Problem geometry derived from elsaa_params_t (host side).
+// ----------------------------------------------------------------------------
+struct Geometry {
+  int B, H, N, D, DG;
+  int ns;        // Sort-LSH bits
+  int w;         // chunk
+  int L, P;      // RACE tables, bits
+  int BH;
+  long long rows;  // BH * N (rows of q, and of k)
+  int R;         // hyperplane rows = ns + L * P
+  int nb_sort;   // 2^ns
+  int nb_race;   // 2^P
+  int rcb;       // bytes per RACE code: 1 if P <= 8 else 2
+  int sort_tiles;  // ceil(N / kSortTile)
+  int dc;        // RACE build column slice
+  bool bf16;
+  float lambda;
+};
+
+// Device buffers carved out of the caller's workspace.
+struct Buffers {
+  uint16_t *scode;  // [2][BH][N]     q codes then k codes
+  void *rcode;      // [2][BH][N][L]  uint8 or uint16
+  int32_t *perm;    // [2][BH][N]
+  uint32_t *hist;   // [2][BH][nb_sort][sort_tiles] -> exclusive offsets
+  float *tsum;      // [BH][L][nb_race][D]
+  float *tcnt;      // [BH][L][nb_race]
+  void *o_s;        // [BH][N][D] in dtype
+  float *lse;       // [BH][N]
+};
+
+constexpr int kSortTile = 2048;         // elements per sort tile (4 waves x 8 rounds x 64)
+constexpr int kRaceLdsBytes = 64 * 1024;  // LDS budget of one RACE-build table slice
+
+// Launchers (each enqueues on `stream`, returns hipError_t of the launch).
+hipError_t launch_hash(const Geometry &g, const void *q, const void *k, const void *planes,
+                       const Buffers &buf, hipStream_t stream);
+hipError_t launch_sort(const Geometry &g, const Buffers &buf, hipStream_t stream);
+hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *k,
+                                  const void *v, const Buffers &buf, hipStream_t stream);
+hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
+                             hipStream_t stream);
+hipError_t launch_fuse(const Geometry &g, const void *x_gate, const float *gate_w,
+                       const float *gate_b, const Buffers &buf, const elsaa_aux_t *aux,
+                       void *out, hipStream_t stream);
+
+// ----------------------------------------------------------------------------
+// Device helpers.
+// ----------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even binary32 -> bfloat16 bits (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float *p) { return *p; }
+  static __device__ __forceinline__ float store_val(float f) { return f; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t *p) { return bf16_bits_to_f32(*p); }
+  static __device__ __forceinline__ uint16_t store_val(float f) { return f32_to_bf16_bits(f); }
+};
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace elsaa

@@ -1,0 +1,84 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU oracle
+on the same seeded inputs.  Codes, permutations and RACE counts must match
+bit for bit; floating-point tensors must satisfy max|d| / max|ref| <= 1e-4
+(fp32 inputs) or <= 2e-2 (bf16 inputs), per tensor.
+
+Sizes here are ones the oracle finishes in seconds while still spanning many
+tiles of every kernel; each workload keeps its own hash settings, chunk,
+generator and head dimension, with B, H (and N where needed) reduced.
+Full-size runs with sampled checks live in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_common import compare_all, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (workload, overrides)
+    "tiny-fp32": ("tiny-fp32", {}),
+    "small-bf16": ("small-bf16", dict(B=1, H=2)),
+    "vision16k-bf16-1head": ("vision16k-bf16", dict(B=1, H=1)),
+    "text32k-bf16-1head": ("text32k-bf16", dict(B=1, H=1)),
+    "needle-bf16-N16k": ("needle256k-bf16", dict(H=1, N=16384)),
+    # edge cases
+    "fp32-d128": ("tiny-fp32", dict(d=128, H=2, N=2048, chunk=128)),
+    "bf16-ragged-sort-tile": ("small-bf16", dict(B=1, H=3, N=64 * 37, chunk=64)),
+    "bf16-single-chunk": ("small-bf16", dict(B=1, H=1, N=64, chunk=64)),
+    "bf16-L3-P5": ("small-bf16", dict(B=1, H=2, race_tables=3, race_bits=5)),
+    "bf16-P0": ("small-bf16", dict(B=1, H=1, race_bits=0)),
+    "bf16-sort12": ("small-bf16", dict(B=1, H=1, N=8192, sort_bits=12)),
+    "bf16-P12-L4": ("small-bf16", dict(B=1, H=1, race_tables=4, race_bits=12)),
+    "bf16-d128-w64": ("needle256k-bf16", dict(H=2, N=4096, chunk=64, sort_bits=7, race_tables=5, race_bits=9)),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_parity(case):
+    name, over = CASES[case]
+    wl = workloads.workload(name, **over)
+    inp = workloads.generate(wl, seed=11)
+    print(f"[parity] {case}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} {wl.dtype}", flush=True)
+    g = run_gpu(inp)
+    r = run_oracle(inp)
+    errs = compare_all(g, r, wl.dtype, case)
+    print(f"[parity] {case}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+
+
+def test_exact_attention_special_case():
+    """sort_bits = 0 and chunk = N: the sparse branch is dense softmax attention."""
+    wl = workloads.workload("small-bf16", B=1, H=2, N=1024, chunk=1024, sort_bits=0)
+    inp = workloads.generate(wl, seed=5)
+    g = run_gpu(inp)
+    np.testing.assert_array_equal(g["perm_q"], np.broadcast_to(np.arange(1024), (1, 2, 1024)))
+    for h in range(2):
+        q = inp.q[0, h].astype(np.float64); k = inp.k[0, h].astype(np.float64)
+        v = inp.v[0, h].astype(np.float64)
+        s = q @ k.T / np.sqrt(wl.d)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        o = p @ v / p.sum(axis=1, keepdims=True)
+        lse = (m[:, 0] + np.log(p.sum(axis=1)))
+        assert np.abs(g["o_sparse"][0, h] - o).max() / np.abs(o).max() <= 2e-2
+        assert np.abs(g["lse_s"][0, h] - lse).max() / np.abs(lse).max() <= 2e-2
+
+
+def test_lambda_zero_ablation():
+    """lambda = 0 fixes the sparse multiplier to one (the uncorrected hybrid)."""
+    wl = workloads.workload("small-bf16", B=1, H=2)
+    inp = workloads.generate(wl, seed=6)
+    g = run_gpu(inp, lam=0.0)
+    assert (g["alpha"] == 1.0).all()
+    r = run_oracle(inp, lam=0.0)
+    compare_all(g, r, wl.dtype, "lambda0")
+
+
+def test_deterministic():
+    wl = workloads.workload("text32k-bf16", B=1, H=2, N=8192)
+    inp = workloads.generate(wl, seed=7)
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    for key in ("y", "race_sum", "o_sparse", "lse_s", "perm_q", "perm_k"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
