@@ -43,7 +43,10 @@ class ElsaaParams(ctypes.Structure):
         ("gate_w", ctypes.c_void_p), ("gate_b", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p), ("aux", ctypes.POINTER(ElsaaAux)),
+        ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
     ]
+
+STAGES = ("hash", "sort", "race_build", "chunk_attention", "fuse")
 
 
 class ElsaaError(RuntimeError):
@@ -91,7 +94,7 @@ def last_error() -> str:
 
 def make_params(B, H, N, d, d_gate, *, sort_bits, chunk, race_tables, race_bits, lam,
                 dtype=DTYPE_BF16, gate_w_ptr=0, gate_b_ptr=0, workspace_ptr=0,
-                workspace_bytes=0, stream_ptr=0, aux=None) -> ElsaaParams:
+                workspace_bytes=0, stream_ptr=0, aux=None, stage_events=None) -> ElsaaParams:
     p = ElsaaParams()
     p.B, p.H, p.N, p.d, p.d_gate = B, H, N, d, d_gate
     p.sort_bits, p.chunk, p.race_tables, p.race_bits = sort_bits, chunk, race_tables, race_bits
@@ -101,6 +104,7 @@ def make_params(B, H, N, d, d_gate, *, sort_bits, chunk, race_tables, race_bits,
     p.workspace, p.workspace_bytes = workspace_ptr or None, workspace_bytes
     p.stream = stream_ptr or None
     p.aux = ctypes.pointer(aux) if aux is not None else None
+    p.stage_events = stage_events
     return p
 
 
@@ -183,7 +187,9 @@ class Forward:
             setattr(s, name, a[name].data_ptr())
         self._aux_struct = s
 
-    def __call__(self, q, k, v, x_gate, hyperplanes, gate_w, gate_b, stream=None):
+    def __call__(self, q, k, v, x_gate, hyperplanes, gate_w, gate_b, stream=None,
+                 stage_events=None):
+        """stage_events: optional ctypes array of 6 hipEvent_t handles (see elsaa.h)."""
         torch = self.torch
         B, H, N, d, dg = (self.shape[x] for x in ("B", "H", "N", "d", "d_gate"))
         R = self.cfg["sort_bits"] + self.cfg["race_tables"] * self.cfg["race_bits"]
@@ -200,7 +206,7 @@ class Forward:
         p = make_params(B, H, N, d, dg, dtype=self.dtype_code, gate_w_ptr=gate_w.data_ptr(),
                         gate_b_ptr=gate_b.data_ptr(), workspace_ptr=self.workspace.data_ptr(),
                         workspace_bytes=self.ws_bytes, stream_ptr=stream.cuda_stream,
-                        aux=self._aux_struct, **self.cfg)
+                        aux=self._aux_struct, stage_events=stage_events, **self.cfg)
         st = lib().elsaa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), x_gate.data_ptr(),
                                  hyperplanes.data_ptr() if R else None, ctypes.byref(p),
                                  self.out.data_ptr())

@@ -167,11 +167,21 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
   carve(g, static_cast<char *>(params->workspace), &buf);
   hipStream_t s = static_cast<hipStream_t>(params->stream);
 
-  hipError_t e = elsaa::launch_hash(g, q, k, hyperplanes, buf, s);
+  void *const *ev = params->stage_events;
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = elsaa::launch_hash(g, q, k, hyperplanes, buf, s);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = elsaa::launch_sort(g, buf, s);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = elsaa::launch_race_build(g, v, buf, s);
+  if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = elsaa::launch_chunk_attention(g, q, k, v, buf, s);
+  if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess) e = elsaa::launch_fuse(g, x_gate, params->gate_w, params->gate_b, buf, params->aux, out, s);
+  if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess && params->aux) e = copy_aux(g, buf, params->aux, s);
   if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';

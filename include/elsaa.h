@@ -101,6 +101,12 @@ typedef struct {
   size_t workspace_bytes;
   void *stream;        /* hipStream_t; NULL = default stream                      */
   elsaa_aux_t *aux;    /* host pointer to optional outputs; NULL = none           */
+  void *const *stage_events; /* host array of 6 hipEvent_t, or NULL.  Event i is
+                        recorded on `stream` just before stage i is enqueued
+                        (0 hash, 1 sort, 2 RACE build, 3 chunk attention,
+                        4 gather/gates/fusion) and event 5 after the last one,
+                        so elapsed(i, i+1) times stage i.  The caller creates
+                        and owns the events.                                     */
 } elsaa_params_t;
 
 /* Host-only check of every field of *p except the device pointers' targets.

@@ -101,6 +101,6 @@ def test_forward_rejects_before_launch():
 
 def test_struct_layout_matches_header():
     # elsaa_params_t: 9 int32, float, enum, then 8-byte aligned pointers
-    assert ctypes.sizeof(elsaa.ElsaaParams) == 48 + 8 * 2 + 8 + 8 + 8 + 8
+    assert ctypes.sizeof(elsaa.ElsaaParams) == 48 + 8 * 2 + 8 + 8 + 8 + 8 + 8
     assert elsaa.ElsaaParams.gate_w.offset == 48
     assert ctypes.sizeof(elsaa.ElsaaAux) == 15 * 8
