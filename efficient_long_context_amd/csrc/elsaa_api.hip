@@ -66,9 +66,6 @@ int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
   g->nb_race = 1 << p->race_bits;
   g->rcb = p->race_bits <= 8 ? 1 : 2;
   g->sort_tiles = (p->N + elsaa::kSortTile - 1) / elsaa::kSortTile;
-  int dc = p->d;
-  while (dc > 1 && static_cast<long long>(g->L) * g->nb_race * (dc + 1) * 4 > 80 * 1024) dc >>= 1;
-  g->dc = dc;
   g->bf16 = p->dtype == ELSAA_DTYPE_BF16;
   g->lambda = p->lambda;
   return ELSAA_OK;

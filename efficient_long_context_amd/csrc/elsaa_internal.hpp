@@ -25,7 +25,6 @@ struct Geometry {
   int nb_race;   // 2^P
   int rcb;       // bytes per RACE code: 1 if P <= 8 else 2
   int sort_tiles;  // ceil(N / kSortTile)
-  int dc;        // RACE build column slice
   bool bf16;
   float lambda;
 };
@@ -81,12 +80,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float *p) { return *p; }
+  // four consecutive values; p must be 16-byte aligned
+  static __device__ __forceinline__ void load4(const float *p, float *out) {
+    const float4 x = *reinterpret_cast<const float4 *>(p);
+    out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+  }
   static __device__ __forceinline__ float store_val(float f) { return f; }
 };
 template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ float load(const uint16_t *p) { return bf16_bits_to_f32(*p); }
+  // four consecutive values; p must be 8-byte aligned
+  static __device__ __forceinline__ void load4(const uint16_t *p, float *out) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    out[0] = __uint_as_float(x.x << 16); out[1] = __uint_as_float(x.x & 0xffff0000u);
+    out[2] = __uint_as_float(x.y << 16); out[3] = __uint_as_float(x.y & 0xffff0000u);
+  }
   static __device__ __forceinline__ uint16_t store_val(float f) { return f32_to_bf16_bits(f); }
 };
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits
+// for every outstanding global load of the wave (its release fence covers all
+// address spaces), which would drain register prefetches issued ahead of it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
