@@ -98,6 +98,15 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ uint16_t store_val(float f) { return f32_to_bf16_bits(f); }
 };
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Maps the hardware workgroup index of a 1-D grid of `grid` workgroups (a
+// multiple of 8) to a logical index such that consecutive logical workgroups
+// run on the same XCD and share its L2.
+constexpr int kXcdCount = 8;
+__device__ __forceinline__ long long xcd_logical_block(long long hw_block, long long grid) {
+  return (hw_block % kXcdCount) * (grid / kXcdCount) + hw_block / kXcdCount;
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits
 // for every outstanding global load of the wave (its release fence covers all
 // address spaces), which would drain register prefetches issued ahead of it.

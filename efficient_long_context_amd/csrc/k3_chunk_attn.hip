@@ -9,41 +9,61 @@
 // position: o_s = softmax-weighted sum of values, and lse = log sum exp(score),
 // the log of the sparse branch's softmax mass Z_s used by the fusion.
 //
-// bf16 kernel (d = 64 or 128): one workgroup of 4 waves per 64 sorted queries
-// (w is a multiple of 64, so a tile never straddles chunks).  Each wave owns 16
-// queries.  Key blocks of 64 gathered rows are staged in LDS: K row-major
-// (padded rows), V transposed (so the PV operand reads contiguous keys).
-// S^T = K Q^T and O^T = V^T P^T run on 16x16x32 bf16 MFMA with fp32
-// accumulation; the softmax is online (running max in the exp2 domain), with
-// P rounded to bf16 for the PV product and the row sum taken from the fp32 P.
+// bf16 kernel (d = 64 or 128): one workgroup per QT sorted queries (QT = 128
+// with 8 waves when w is a multiple of 128, else 64 with 4 waves; a tile never
+// straddles chunks).  Each wave owns 16 queries, whose Q^T fragments stay in
+// registers.  Key blocks of 64 gathered rows are staged in LDS -- K row-major
+// (padded rows), V transposed so the PV operand reads contiguous keys -- and
+// the next block's rows are loaded into registers while the current one is
+// used.  S^T = K Q^T and O^T = V^T P^T run on 16x16x32 bf16 MFMA with fp32
+// accumulation; the softmax is online in the exp2 domain (v_exp_f32 directly:
+// every argument is <= 0), P is rounded to bf16 for the PV product and the row
+// sum is taken from the fp32 P.  Workgroups of neighbouring tiles (which share
+// key blocks) are mapped to the same XCD.
 #include "elsaa_internal.hpp"
 
 namespace elsaa {
 namespace {
 
-constexpr int kQTile = 64;
 constexpr int kKBlock = 64;
 
-template <int D>
-__global__ __launch_bounds__(256) void elsaa_k3_chunk_attn_bf16(
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);  // v_cvt_pk_bf16_f32 (RNE)
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+template <int D, int QT>
+__global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N, int w,
-    float scale_log2, uint16_t *__restrict__ o_s, float *__restrict__ lse) {
-  constexpr int kKRow = D + 8;        // padded K row in LDS (bf16 elements)
-  constexpr int kVRow = kKBlock + 8;  // padded V^T row in LDS
+    int tiles_per_seg, int n_tiles, float scale_log2, uint16_t *__restrict__ o_s,
+    float *__restrict__ lse) {
+  constexpr int kThreads = QT * 4;      // 16 queries per wave
+  constexpr int kKRow = D + 8;          // padded K row in LDS (bf16 elements)
+  constexpr int kVRow = kKBlock + 8;    // padded V^T row in LDS
+  constexpr int kKChunks = kKBlock * (D / 8);              // 16-byte pieces of a K block
+  constexpr int kVPairs = (kKBlock / 2) * (D / 8);         // (key pair, 8-column) pieces of V
+  constexpr int kKPer = (kKChunks + kThreads - 1) / kThreads;
+  constexpr int kVPer = (kVPairs + kThreads - 1) / kThreads;
   __shared__ __align__(16) uint16_t Ks[kKBlock * kKRow];
   __shared__ __align__(16) uint16_t Vt[D * kVRow];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const long long bh = blockIdx.y;
-  const int r0 = blockIdx.x * kQTile;
+  const long long tile = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (tile >= n_tiles) return;  // padding workgroup (whole group exits)
+  const long long bh = tile / tiles_per_seg;
+  const int r0 = static_cast<int>(tile % tiles_per_seg) * QT;
   const int c = r0 / w;
   const int lo = c > 0 ? (c - 1) * w : 0;
   const int hi = (c + 1) * w;
   const long long seg = bh * N;
+  const int32_t *pk = perm_k + seg;
 
-  // Q^T operand: lane holds query (r16) of this wave, d-slice g*8 .. +7 of each 32.
+  // Q^T operand: lane holds query r16 of this wave, d-slice g*8 .. +7 of each 32.
   const int qidx = perm_q[seg + r0 + wave * 16 + r16];
   const uint16_t *qrow = q + (seg + qidx) * D;
   bf16x8 bq[D / 32];
@@ -51,34 +71,61 @@ __global__ __launch_bounds__(256) void elsaa_k3_chunk_attn_bf16(
   for (int kk = 0; kk < D / 32; ++kk)
     bq[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(qrow + kk * 32 + g * 8));
 
+  // Block loader: K piece i -> row i / (D/8), chunk i % (D/8); V piece i -> key
+  // pair i % 32, chunk i / 32.  Pieces past the count are clamped reloads.
+  u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer];
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int p = 0; p < kKPer; ++p) {
+      int i = tid + p * kThreads;
+      i = i < kKChunks ? i : kKChunks - 1;
+      const int j = i / (D / 8), ch = i % (D / 8);
+      kreg[p] = *reinterpret_cast<const u16x8 *>(k + (seg + pk[kb + j]) * D + ch * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < kVPer; ++p) {
+      int i = tid + p * kThreads;
+      i = i < kVPairs ? i : kVPairs - 1;
+      const int jp = i % (kKBlock / 2), ch = i / (kKBlock / 2);
+      vreg0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + pk[kb + 2 * jp]) * D + ch * 8);
+      vreg1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + pk[kb + 2 * jp + 1]) * D + ch * 8);
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int p = 0; p < kKPer; ++p) {
+      const int i = tid + p * kThreads;
+      if (i < kKChunks) {
+        const int j = i / (D / 8), ch = i % (D / 8);
+        *reinterpret_cast<u16x8 *>(Ks + j * kKRow + ch * 8) = kreg[p];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kVPer; ++p) {
+      const int i = tid + p * kThreads;
+      if (i < kVPairs) {
+        const int jp = i % (kKBlock / 2), ch = i / (kKBlock / 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = static_cast<uint32_t>(vreg0[p][e]) | (static_cast<uint32_t>(vreg1[p][e]) << 16);
+          *reinterpret_cast<uint32_t *>(Vt + (ch * 8 + e) * kVRow + 2 * jp) = word;
+        }
+      }
+    }
+  };
+
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   float m = -INFINITY;  // running max of score * log2(e) / sqrt(d)
   float l_part = 0.0f;  // this lane's share of the running sum
 
+  load_block(lo);
   for (int kb = lo; kb < hi; kb += kKBlock) {
     __syncthreads();  // previous block fully consumed
-    // K block: 64 rows x D/8 chunks of 16 bytes
-    for (int idx = tid; idx < kKBlock * (D / 8); idx += 256) {
-      const int j = idx / (D / 8), ch = idx % (D / 8);
-      const int kidx = perm_k[seg + kb + j];
-      *reinterpret_cast<u16x8 *>(Ks + j * kKRow + ch * 8) =
-          *reinterpret_cast<const u16x8 *>(k + (seg + kidx) * D + ch * 8);
-    }
-    // V block transposed: thread takes keys 2*jp, 2*jp+1 and an 8-wide d chunk
-    for (int idx = tid; idx < (kKBlock / 2) * (D / 8); idx += 256) {
-      const int jp = idx % (kKBlock / 2), ch = idx / (kKBlock / 2);
-      const int k0 = perm_k[seg + kb + 2 * jp], k1 = perm_k[seg + kb + 2 * jp + 1];
-      const u16x8 v0 = *reinterpret_cast<const u16x8 *>(v + (seg + k0) * D + ch * 8);
-      const u16x8 v1 = *reinterpret_cast<const u16x8 *>(v + (seg + k1) * D + ch * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t word = static_cast<uint32_t>(v0[e]) | (static_cast<uint32_t>(v1[e]) << 16);
-        *reinterpret_cast<uint32_t *>(Vt + (ch * 8 + e) * kVRow + 2 * jp) = word;
-      }
-    }
+    store_block();
     __syncthreads();
+    if (kb + kKBlock < hi) load_block(kb + kKBlock);  // next block in flight during the math
 
     // S^T tiles: lane holds keys kt*16 + g*4 + i for query r16
     f32x4 s[kKBlock / 16];
@@ -101,7 +148,7 @@ __global__ __launch_bounds__(256) void elsaa_k3_chunk_attn_bf16(
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     const float m_new = fmaxf(m, bmax * scale_log2);
-    const float corr = exp2f(m - m_new);  // 0 on the first block (m = -inf)
+    const float corr = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block (m = -inf)
     m = m_new;
     l_part *= corr;
 #pragma unroll
@@ -110,23 +157,25 @@ __global__ __launch_bounds__(256) void elsaa_k3_chunk_attn_bf16(
     // P = exp2(s * scale - m); PV over two 32-key steps
 #pragma unroll
     for (int m2 = 0; m2 < kKBlock / 32; ++m2) {
-      u16x8 pb;
+      uint32_t pw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = exp2f(__builtin_fmaf(s[2 * m2][i], scale_log2, -m));
-        const float p1 = exp2f(__builtin_fmaf(s[2 * m2 + 1][i], scale_log2, -m));
-        l_part += p0 + p1;
-        pb[i] = f32_to_bf16_bits(p0);
-        pb[4 + i] = f32_to_bf16_bits(p1);
+      for (int i = 0; i < 4; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2][i], scale_log2, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2][i + 1], scale_log2, -m));
+        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2 + 1][i], scale_log2, -m));
+        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2 + 1][i + 1], scale_log2, -m));
+        l_part += (p0 + p1) + (p2 + p3);
+        pw[i / 2] = pack_bf16x2(p0, p1);
+        pw[2 + i / 2] = pack_bf16x2(p2, p3);
       }
-      const bf16x8 bp = __builtin_bit_cast(bf16x8, pb);
+      const bf16x8 bp = __builtin_bit_cast(bf16x8, (uint4){pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         const uint16_t *vr = Vt + (dt * 16 + r16) * kVRow + m2 * 32 + g * 4;
-        const u16x4 lo4 = *reinterpret_cast<const u16x4 *>(vr);
-        const u16x4 hi4 = *reinterpret_cast<const u16x4 *>(vr + 16);
-        const u16x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        o[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, av), bp, o[dt]);
+        const uint2 lo4 = *reinterpret_cast<const uint2 *>(vr);
+        const uint2 hi4 = *reinterpret_cast<const uint2 *>(vr + 16);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, (uint4){lo4.x, lo4.y, hi4.x, hi4.y});
+        o[dt] = mfma16x16x32(av, bp, o[dt]);
       }
     }
   }
@@ -137,10 +186,9 @@ __global__ __launch_bounds__(256) void elsaa_k3_chunk_attn_bf16(
   uint16_t *orow = o_s + (seg + qidx) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
-    u16x4 outv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) outv[i] = f32_to_bf16_bits(o[dt][i] * inv);
-    *reinterpret_cast<u16x4 *>(orow + dt * 16 + g * 4) = outv;
+    const uint2 outv = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
+                        pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
+    *reinterpret_cast<uint2 *>(orow + dt * 16 + g * 4) = outv;
   }
   if (g == 0) lse[seg + qidx] = (m + log2f(l_tot)) * 0.69314718055994530942f;
 }
@@ -182,6 +230,20 @@ __global__ __launch_bounds__(128) void elsaa_k3_chunk_attn_f32(
   lse[seg + qidx] = (m + log2f(l)) * 0.69314718055994530942f;
 }
 
+template <int D, int QT>
+hipError_t launch_bf16(const Geometry &g, const void *q, const void *k, const void *v,
+                       const Buffers &buf, float scale_log2, hipStream_t stream) {
+  const int tiles_per_seg = g.N / QT;
+  const long long n_tiles = static_cast<long long>(tiles_per_seg) * g.BH;
+  const long long grid = (n_tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
+  hipLaunchKernelGGL((elsaa_k3_chunk_attn_bf16<D, QT>), dim3(static_cast<unsigned>(grid)),
+                     dim3(QT * 4), 0, stream, static_cast<const uint16_t *>(q),
+                     static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), buf.perm,
+                     buf.perm + g.rows, g.N, g.w, tiles_per_seg, static_cast<int>(n_tiles),
+                     scale_log2, static_cast<uint16_t *>(buf.o_s), buf.lse);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *k, const void *v,
@@ -190,30 +252,24 @@ hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *
   const int32_t *pq = buf.perm;
   const int32_t *pk = buf.perm + g.rows;
   if (g.bf16) {
-    const dim3 grid(g.N / kQTile, g.BH);
+    const bool wide = g.w % 128 == 0;
     if (g.D == 64)
-      hipLaunchKernelGGL(elsaa_k3_chunk_attn_bf16<64>, grid, dim3(256), 0, stream,
-                         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                         static_cast<const uint16_t *>(v), pq, pk, g.N, g.w, scale_log2,
-                         static_cast<uint16_t *>(buf.o_s), buf.lse);
-    else
-      hipLaunchKernelGGL(elsaa_k3_chunk_attn_bf16<128>, grid, dim3(256), 0, stream,
-                         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                         static_cast<const uint16_t *>(v), pq, pk, g.N, g.w, scale_log2,
-                         static_cast<uint16_t *>(buf.o_s), buf.lse);
-  } else {
-    const dim3 grid((g.N + 127) / 128, g.BH);
-    if (g.D == 64)
-      hipLaunchKernelGGL(elsaa_k3_chunk_attn_f32<64>, grid, dim3(128), 0, stream,
-                         static_cast<const float *>(q), static_cast<const float *>(k),
-                         static_cast<const float *>(v), pq, pk, g.N, g.w, scale_log2,
-                         static_cast<float *>(buf.o_s), buf.lse);
-    else
-      hipLaunchKernelGGL(elsaa_k3_chunk_attn_f32<128>, grid, dim3(128), 0, stream,
-                         static_cast<const float *>(q), static_cast<const float *>(k),
-                         static_cast<const float *>(v), pq, pk, g.N, g.w, scale_log2,
-                         static_cast<float *>(buf.o_s), buf.lse);
+      return wide ? launch_bf16<64, 128>(g, q, k, v, buf, scale_log2, stream)
+                  : launch_bf16<64, 64>(g, q, k, v, buf, scale_log2, stream);
+    return wide ? launch_bf16<128, 128>(g, q, k, v, buf, scale_log2, stream)
+                : launch_bf16<128, 64>(g, q, k, v, buf, scale_log2, stream);
   }
+  const dim3 grid((g.N + 127) / 128, g.BH);
+  if (g.D == 64)
+    hipLaunchKernelGGL(elsaa_k3_chunk_attn_f32<64>, grid, dim3(128), 0, stream,
+                       static_cast<const float *>(q), static_cast<const float *>(k),
+                       static_cast<const float *>(v), pq, pk, g.N, g.w, scale_log2,
+                       static_cast<float *>(buf.o_s), buf.lse);
+  else
+    hipLaunchKernelGGL(elsaa_k3_chunk_attn_f32<128>, grid, dim3(128), 0, stream,
+                       static_cast<const float *>(q), static_cast<const float *>(k),
+                       static_cast<const float *>(v), pq, pk, g.N, g.w, scale_log2,
+                       static_cast<float *>(buf.o_s), buf.lse);
   return hipGetLastError();
 }
 

@@ -33,7 +33,6 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTK = 64;       // keys per staged tile
 constexpr int kMaxRB = 32;    // buckets per wave
 constexpr int kRound = 8;     // keys added per straight-line round
-constexpr int kXcds = 8;
 
 // One thread's share of a tile: 8 consecutive values of one key row and 16
 // bytes of the tile's code block (the codes of 64 consecutive keys are one
@@ -55,13 +54,11 @@ __global__ __launch_bounds__(kThreads) void elsaa_k4_race_build(
   extern __shared__ __align__(16) float lds[];
   const int code_words = (kTK * L * static_cast<int>(sizeof(CT)) + 15) / 16;  // 16-byte words per tile
   float *tile = lds;                                         // [kTK + 1][64] fp32; row kTK is zero
-  CT *tcode = reinterpret_cast<CT *>(lds + (kTK + 1) * 64);  // [kTK][L]
+  CT *tcode = reinterpret_cast<CT *>(lds + (kTK + 1) * 64);  // [kTK][L], in kThreads x 16 bytes
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // XCD-aware order: consecutive logical workgroups share an XCD.
-  const int lin = blockIdx.x;
-  const int per_xcd = gridDim.x / kXcds;
-  const int logical = (lin % kXcds) * per_xcd + lin / kXcds;
+  const int logical = static_cast<int>(xcd_logical_block(blockIdx.x, gridDim.x));
   if (logical >= wg_real) return;  // whole workgroup exits together
   const long long bh = logical / wg_per_bh;
   const int wg = logical % wg_per_bh;
@@ -94,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void elsaa_k4_race_build(
       *reinterpret_cast<f32x4 *>(p.x) = *reinterpret_cast<const f32x4 *>(src);
       *reinterpret_cast<f32x4 *>(p.x + 4) = *reinterpret_cast<const f32x4 *>(src + 4);
     }
-    p.c = csrc[static_cast<long long>(tt) * code_words + (code_loader ? tid : 0)];
+    p.c = csrc[static_cast<long long>(tt) * code_words + (code_loader ? tid : 0)];  // all threads load
   };
 
   auto step = [&](TileRegs<VT> &p, int t) {
@@ -107,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void elsaa_k4_race_build(
     }
     *reinterpret_cast<f32x4 *>(tile + tk * 64 + tc) = lo;
     *reinterpret_cast<f32x4 *>(tile + tk * 64 + tc + 4) = hi;
-    if (code_loader) reinterpret_cast<uint4 *>(tcode)[tid] = p.c;
+    reinterpret_cast<uint4 *>(tcode)[tid] = p.c;  // unconditional: words past the block are unused
     lds_barrier();
     load(p, t + 4);  // refill this ring slot four tiles ahead
     if (!active || t >= n_tiles) return;  // steps past the end only keep the ring uniform
@@ -179,9 +176,8 @@ hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &bu
   const int wg_per_cs = (g.L * nr + kWaves - 1) / kWaves;
   const int wg_per_bh = wg_per_cs * ncs;
   const long long wg_real = static_cast<long long>(wg_per_bh) * g.BH;
-  const long long grid = (wg_real + kXcds - 1) / kXcds * kXcds;
-  const size_t code_bytes = (static_cast<size_t>(kTK) * g.L * g.rcb + 15) / 16 * 16;
-  const size_t lds = static_cast<size_t>(kTK + 1) * 64 * 4 + code_bytes;
+  const long long grid = (wg_real + kXcdCount - 1) / kXcdCount * kXcdCount;
+  const size_t lds = static_cast<size_t>(kTK + 1) * 64 * 4 + static_cast<size_t>(kThreads) * 16;
   const void *rk = static_cast<const char *>(buf.rcode) + static_cast<size_t>(g.rows) * g.L * g.rcb;
   const dim3 cgrid(g.L, g.BH);
   const size_t clds = static_cast<size_t>(g.nb_race) * 4;

@@ -18,6 +18,8 @@
 // Layout: d/4 lanes per query, 4 value columns per lane (16-byte table reads),
 // the gate dot products split over the same lanes and reduced with xor
 // shuffles inside the query's lane group.
+#include <type_traits>
+
 #include "elsaa_internal.hpp"
 
 namespace elsaa {
@@ -45,15 +47,70 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
   const long long b = bh / H;
   const int nb = 1 << P;
 
-  // gates
+  // Every independent load is issued before the first use: RACE rows (in
+  // groups of 16 tables), the sparse output, its LSE and the gate inputs.
+  // Summing as loads arrive would serialise their memory latencies.
+  const CT *qc = qcodes + qi * L;
+  const float *ts = tsum + bh * L * nb * static_cast<long long>(D) + sub * 4;
+  const float *tc = tcnt + bh * L * nb;
+  const VT *os = o_s + qi * D + sub * 4;
+  float osv[4];
+  Elem<VT>::load4(os, osv);
+  const float lse_i = lse[qi];
+
+  float z = 0.0f;
+  f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto gather = [&](auto group, int l0) {
+    constexpr int G = decltype(group)::value;
+    long long row[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int l = l0 + e < L ? l0 + e : L - 1;  // clamped: extra rows are loaded, not added
+      row[e] = static_cast<long long>(l) * nb + qc[l];
+    }
+    f32x4 t[G];
+    float c[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      t[e] = *reinterpret_cast<const f32x4 *>(ts + row[e] * D);
+      c[e] = tc[row[e]];
+    }
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      if (l0 + e < L) {
+        num += t[e];
+        z += c[e];
+      }
+    }
+  };
+  // no loop for L <= 16: keeps the compiler from draining loads at a loop header
+  if (L <= 4) gather(std::integral_constant<int, 4>(), 0);
+  else if (L <= 8) gather(std::integral_constant<int, 8>(), 0);
+  else if (L <= 16) gather(std::integral_constant<int, 16>(), 0);
+  else for (int l0 = 0; l0 < L; l0 += 16) gather(std::integral_constant<int, 16>(), l0);
+
+  // gates: with d_gate = 4 x (lanes per query) each lane takes 4 consecutive
+  // inputs in one load; any other width takes the strided loop
   const VT *xg = x_gate + (b * N + i) * DG;
   const float *w0 = gate_w + static_cast<long long>(h) * DG;
   const float *w1 = gate_w + static_cast<long long>(H + h) * DG;
   float a0 = 0.0f, a1 = 0.0f;
-  for (int e = sub; e < DG; e += kLanesPerQuery) {
-    const float xv = Elem<VT>::load(xg + e);
-    a0 = __builtin_fmaf(xv, w0[e], a0);
-    a1 = __builtin_fmaf(xv, w1[e], a1);
+  if (DG == 4 * kLanesPerQuery) {
+    float xv[4];
+    Elem<VT>::load4(xg + sub * 4, xv);
+    const f32x4 wa = *reinterpret_cast<const f32x4 *>(w0 + sub * 4);
+    const f32x4 wb = *reinterpret_cast<const f32x4 *>(w1 + sub * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a0 = __builtin_fmaf(xv[e], wa[e], a0);
+      a1 = __builtin_fmaf(xv[e], wb[e], a1);
+    }
+  } else {
+    for (int e = sub; e < DG; e += kLanesPerQuery) {
+      const float xv = Elem<VT>::load(xg + e);
+      a0 = __builtin_fmaf(xv, w0[e], a0);
+      a1 = __builtin_fmaf(xv, w1[e], a1);
+    }
   }
 #pragma unroll
   for (int off = kLanesPerQuery / 2; off > 0; off >>= 1) {
@@ -63,32 +120,18 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
   const float g_s = 1.0f / (1.0f + __expf(-(a0 + gate_b[h])));
   const float g_lr = 1.0f / (1.0f + __expf(-(a1 + gate_b[H + h])));
 
-  // RACE gather
-  const CT *qc = qcodes + qi * L;
-  const float *ts = tsum + bh * L * nb * static_cast<long long>(D);
-  const float *tc = tcnt + bh * L * nb;
-  float z = 0.0f;
-  f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int l = 0; l < L; ++l) {
-    const int bkt = qc[l];
-    const long long row = static_cast<long long>(l) * nb + bkt;
-    z += tc[row];
-    num += *reinterpret_cast<const f32x4 *>(ts + row * D + sub * 4);
-  }
   const float z_lr = z / static_cast<float>(L);
   f32x4 o_lr = {0.0f, 0.0f, 0.0f, 0.0f};
   if (z > 0.0f) o_lr = num * (1.0f / z);  // (num / L) / (z / L)
 
   const float mass_lr = lambda * z_lr;
-  const float alpha = mass_lr > 0.0f ? 1.0f / (1.0f + __expf(__logf(mass_lr) - lse[qi])) : 1.0f;
+  const float alpha = mass_lr > 0.0f ? 1.0f / (1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
 
-  const VT *os = o_s + qi * D + sub * 4;
   VT *dst = out + qi * D + sub * 4;
   const float ws = g_s * alpha;
   if (valid) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      dst[e] = Elem<VT>::store_val(__builtin_fmaf(ws, Elem<VT>::load(os + e), g_lr * o_lr[e]));
+    for (int e = 0; e < 4; ++e) dst[e] = Elem<VT>::store_val(__builtin_fmaf(ws, osv[e], g_lr * o_lr[e]));
     if (aux.o_lr) *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * 4) = o_lr;
     if (sub == 0) {
       if (aux.z_lr) aux.z_lr[qi] = z_lr;
