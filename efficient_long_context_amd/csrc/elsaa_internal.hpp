@@ -34,6 +34,7 @@ struct Buffers {
   uint16_t *scode;  // [2][BH][N]     q codes then k codes
   void *rcode;      // [2][BH][N][L]  uint8 or uint16
   int32_t *perm;    // [2][BH][N]
+  uint8_t *flags;   // [2][BH][N]     rows whose codes need the exact pass
   uint32_t *hist;   // [2][BH][nb_sort][sort_tiles] -> exclusive offsets
   float *tsum;      // [BH][L][nb_race][D]
   float *tcnt;      // [BH][L][nb_race]

@@ -19,8 +19,7 @@
 namespace elsaa {
 namespace {
 
-constexpr int kRowsPerTile = 16;
-constexpr int kTilesPerWg = 32;  // 512 rows per workgroup
+constexpr int kTilesPerWg = 64;  // 1024 rows per workgroup
 
 __device__ __forceinline__ bool in_safe_range(float a) {
   a = fabsf(a);
@@ -106,130 +105,177 @@ __device__ __forceinline__ uint32_t bit_field(GetWord get, int pos, int n) {
 }
 
 // ---------------------------------------------------------------- bf16 path --
-template <int D>
+// A workgroup of 4 waves hashes 64 rows per step (16 per wave).  The rows of
+// the next step are loaded into registers while the current step is hashed and
+// staged in LDS at the top of the next step.  NPT = R_pad / 16 plane tiles is a
+// compile-time count.
+//
+// Certification, per row: the row passes the range check when its largest
+// |element| lies in [2^-40, 2^40] (then |x|^2 is a normal binary32 and dropping
+// squares of elements below 2^-63 changes |x| by a relative 2^-40 at most).
+// tau_row = |x| * max_t(c |r_t|) + d 2^-124 bounds the error of every plane's
+// projection of that row (c = (d + 2) 2^-22, twice the worst-case relative
+// error of d fp32 additions; d 2^-124 covers flushed subnormal products and
+// partial sums).  Planes outside the range, or rows that fail the check, send
+// every projection to the exact path.
+template <int D, int NPT>
 __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
     const uint16_t *__restrict__ xq, const uint16_t *__restrict__ xk,
     const uint16_t *__restrict__ planes, int R, int ns, int L, int P, long long rows,
-    uint16_t *__restrict__ scode, void *__restrict__ rcode, int rcb) {
-  constexpr int kLdsRow = D + 8;  // padded plane row (bf16 elements)
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int R_pad = (R + 15) & ~15;
-  const int n_words = (R_pad + 31) >> 5;
-  uint16_t *sp = reinterpret_cast<uint16_t *>(smem);
-  float *spn = reinterpret_cast<float *>(smem + static_cast<size_t>(R_pad) * kLdsRow * 2);
-  int *ssafe = reinterpret_cast<int *>(spn + R_pad);
-  uint32_t *smask = reinterpret_cast<uint32_t *>(ssafe + R_pad);  // [4 waves][16 rows][8 words]
+    uint16_t *__restrict__ scode, void *__restrict__ rcode, int rcb, uint8_t *__restrict__ flags) {
+  constexpr int kLdsRow = D + 8;  // padded row (bf16 elements)
+  constexpr int kRPad = NPT * 16;
+  constexpr int kWords = (kRPad + 31) / 32;
+  constexpr int kStepRows = 64;
+  constexpr int kPieces = kStepRows * (D / 8) / 256;  // 16-byte pieces per thread per step
+  __shared__ __align__(16) uint16_t sp[kRPad * kLdsRow];
+  __shared__ __align__(16) uint16_t sx[kStepRows * kLdsRow];
+  __shared__ float s_red[2];  // max_t c|r_t| and "all planes in range"
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tensor = blockIdx.y;
   const uint16_t *x = tensor ? xk : xq;
 
-  // Stage the hyperplanes (zero rows beyond R) and their norms.
-  for (int idx = tid; idx < R_pad * (D / 8); idx += 256) {
+  // Stage the hyperplanes (zero rows beyond R).
+  for (int idx = tid; idx < kRPad * (D / 8); idx += 256) {
     const int t = idx / (D / 8), ch = idx % (D / 8);
     u16x8 val = (u16x8)0;
     if (t < R) val = *reinterpret_cast<const u16x8 *>(planes + static_cast<size_t>(t) * D + ch * 8);
     *reinterpret_cast<u16x8 *>(sp + t * kLdsRow + ch * 8) = val;
   }
   __syncthreads();
-  for (int t = tid; t < R_pad; t += 256) {
-    float ss = 0.0f;
-    int safe = 1;
-    for (int e = 0; e < D; ++e) {
-      const float f = bf16_bits_to_f32(sp[t * kLdsRow + e]);
-      ss += f * f;
-      safe &= in_safe_range(f) ? 1 : 0;
+  if (wave == 0) {  // plane norms: wave 0, lane t handles planes t, t+64, ...
+    float rmax = 0.0f;
+    int ok = 1;
+    for (int t = lane; t < R; t += 64) {
+      float ss = 0.0f, amax = 0.0f;
+      for (int e = 0; e < D; ++e) {
+        const float f = bf16_bits_to_f32(sp[t * kLdsRow + e]);
+        ss = __builtin_fmaf(f, f, ss);
+        amax = fmaxf(amax, fabsf(f));
+      }
+      ok &= (amax >= 0x1p-40f && amax <= 0x1p40f) ? 1 : 0;
+      rmax = fmaxf(rmax, sqrtf(ss));
     }
-    spn[t] = sqrtf(ss);
-    ssafe[t] = safe;
+    for (int off = 32; off > 0; off >>= 1) {
+      rmax = fmaxf(rmax, __shfl_xor(rmax, off));
+      ok &= __shfl_xor(ok, off);
+    }
+    if (lane == 0) {
+      s_red[0] = static_cast<float>(D + 2) * 0x1p-22f * rmax;
+      s_red[1] = ok ? 1.0f : 0.0f;
+    }
   }
   __syncthreads();
-
-  const int g = lane >> 4, r16 = lane & 15;
-  const long long n_tiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
-  uint32_t *wmask = smask + wave * 16 * 8;
-  const float c_rel = static_cast<float>(D + 2) * 0x1p-22f;
+  const float c_plane = s_red[0];
+  const bool planes_ok = s_red[1] != 0.0f;
   const float c_abs = static_cast<float>(D) * 0x1p-124f;
 
-  for (int it = wave; it < kTilesPerWg; it += 4) {
-    const long long tile = static_cast<long long>(blockIdx.x) * kTilesPerWg + it;
-    if (tile >= n_tiles) break;
-    const long long row = tile * kRowsPerTile + r16;
-    const bool valid = row < rows;
-    const uint16_t *xr = x + (valid ? row : 0) * D;
+  const int g = lane >> 4, r16 = lane & 15;
+  const long long row_begin = static_cast<long long>(blockIdx.x) * (kTilesPerWg * 16);
+  const long long row_end = row_begin + kTilesPerWg * 16 < rows ? row_begin + kTilesPerWg * 16 : rows;
 
+  u16x8 pre[kPieces];
+  auto load_step = [&](long long r0) {
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+      const int i = tid + p * 256;
+      const long long row = r0 + i / (D / 8);
+      const long long rr = row < rows ? row : rows - 1;  // clamped; results of clamped rows are discarded
+      pre[p] = *reinterpret_cast<const u16x8 *>(x + rr * D + (i % (D / 8)) * 8);
+    }
+  };
+
+  load_step(row_begin);
+  for (long long r0 = row_begin; r0 < row_end; r0 += kStepRows) {
+    __syncthreads();  // previous step's rows fully read
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+      const int i = tid + p * 256;
+      *reinterpret_cast<u16x8 *>(sx + (i / (D / 8)) * kLdsRow + (i % (D / 8)) * 8) = pre[p];
+    }
+    __syncthreads();
+    if (r0 + kStepRows < row_end) load_step(r0 + kStepRows);  // in flight while this step is hashed
+
+    const int lrow = wave * 16 + r16;
+    const long long row = r0 + lrow;
+    const bool valid = row < row_end;
+    const uint16_t *xr = sx + lrow * kLdsRow;
+
+    // |x| and max |x_i| of the row (lane group g holds a quarter of it)
+    float ss = 0.0f, amax = 0.0f;
     bf16x8 b[D / 32];
-    float ss = 0.0f;
-    int safe = 1;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      u16x8 raw = (u16x8)0;
-      if (valid) raw = *reinterpret_cast<const u16x8 *>(xr + kk * 32 + g * 8);
+      const u16x8 raw = *reinterpret_cast<const u16x8 *>(xr + kk * 32 + g * 8);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float f = bf16_bits_to_f32(raw[i]);
-        ss += f * f;
-        safe &= in_safe_range(f) ? 1 : 0;
+        ss = __builtin_fmaf(f, f, ss);
+        amax = fmaxf(amax, fabsf(f));
       }
       b[kk] = __builtin_bit_cast(bf16x8, raw);
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    safe &= __shfl_xor(safe, 16);
-    safe &= __shfl_xor(safe, 32);
-    const float xnorm = sqrtf(ss);
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const bool row_ok = planes_ok && amax >= 0x1p-40f && amax <= 0x1p40f;
+    // tau = +inf sends every projection of this row to the exact path
+    const float tau = row_ok ? __builtin_fmaf(sqrtf(ss), c_plane, c_abs) : INFINITY;
 
-    uint32_t cur = 0;
-    for (int pt = 0; pt < R_pad / 16; ++pt) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto project = [&](int pt) {
+      f32x4 a4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
         const bf16x8 a = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u16x8 *>(sp + (pt * 16 + r16) * kLdsRow + kk * 32 + g * 8));
-        acc = mfma16x16x32(a, b[kk], acc);
+        a4 = mfma16x16x32(a, b[kk], a4);
       }
-      // lane holds <plane pt*16 + g*4 + i, row r16>
-      uint32_t bits = 0;
+      return a4;  // lane holds <plane pt*16 + g*4 + i, row r16>
+    };
+    uint32_t words[kWords];
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) words[w] = 0u;
+    unsigned long long unsure = 0ull;
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt) {
+      const f32x4 a4 = project(pt);
+      // bit position before the per-lane shift by 4g is (pt & 1) * 16 + i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = pt * 16 + g * 4 + i;
-        if (t < R && valid) {
-          const float p = acc[i];
-          const float tau = c_rel * xnorm * spn[t] + c_abs;
-          int bit;
-          if (safe && ssafe[t] && fabsf(p) > tau) {
-            bit = p > 0.0f;
-          } else {
-            bit = exact_dot_sign<uint16_t>(xr, sp + t * kLdsRow, D) > 0;
-          }
-          bits |= static_cast<uint32_t>(bit) << ((pt & 1) * 16 + g * 4 + i);
-        }
-      }
-      bits |= __shfl_xor(bits, 16);
-      bits |= __shfl_xor(bits, 32);
-      cur = (pt & 1) ? (cur | bits) : bits;
-      if ((pt & 1) || pt == R_pad / 16 - 1) {
-        if (lane < 16) wmask[lane * 8 + (pt >> 1)] = cur;
+        words[pt >> 1] |= (a4[i] > 0.0f ? 1u : 0u) << ((pt & 1) * 16 + i);
+        unsure |= __ballot(!(fabsf(a4[i]) > tau) && pt * 16 + g * 4 + i < R);  // padding planes: bit 0
       }
     }
-    // wave-local LDS: make the mask words visible to the lanes that extract codes
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // Extract and store codes: lane (row r16, group g) writes table groups g, g+4, ...
-    const long long orow = tile * kRowsPerTile + r16;
-    if (orow < rows) {
-      auto get = [&](int wd) -> uint32_t { return wd < n_words ? wmask[r16 * 8 + wd] : 0u; };
-      const long long out_row = static_cast<long long>(tensor) * rows + orow;
-      if (g == 0) scode[out_row] = static_cast<uint16_t>(bit_field(get, 0, ns));
+    // place group g's bits, then OR the four groups: every lane of a row holds
+    // the row's full plane mask (planes >= R are zero rows: bit 0)
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) {
+      uint32_t v = words[w] << (g * 4);
+      v |= __shfl_xor(v, 16);
+      v |= __shfl_xor(v, 32);
+      words[w] = v;
+    }
+    if (valid) {
+      auto get = [&](int wd) -> uint32_t {
+        uint32_t r = 0u;
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) r = wd == w ? words[w] : r;
+        return r;
+      };
+      const long long out_row = static_cast<long long>(tensor) * rows + row;
+      if (g == 0) {
+        scode[out_row] = static_cast<uint16_t>(bit_field(get, 0, ns));
+        // any uncertified projection of this row: the exact pass redoes its codes
+        flags[out_row] = ((unsure >> r16) & 0x0001000100010001ull) ? 1 : 0;
+      }
       if (rcb == 1) {
         uint8_t *rc = reinterpret_cast<uint8_t *>(rcode) + out_row * L;
         if ((L & 3) == 0) {
           for (int j = g; j < L / 4; j += 4) {
             uint32_t word = 0;
-            for (int e = 0; e < 4; ++e)
-              word |= bit_field(get, ns + (4 * j + e) * P, P) << (8 * e);
+            for (int e = 0; e < 4; ++e) word |= bit_field(get, ns + (4 * j + e) * P, P) << (8 * e);
             reinterpret_cast<uint32_t *>(rc)[j] = word;
           }
         } else {
@@ -248,7 +294,76 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
         }
       }
     }
-    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ------------------------------------------------------------ exact fix-up --
+// Rows flagged by the bf16 pass get every code bit recomputed exactly: one wave
+// per row, lanes over hyperplanes.  Each lane forms the binary64 dot product of
+// the exact products with its rounding bound (d + 1) 2^-52 sum |p_i|, which
+// decides the sign unless the sum is within that bound of zero; only then is
+// the fixed-point accumulation used.  Bits are gathered with ballots.
+// Grid-stride over all rows: every wave reaches the end.
+template <int D>
+__global__ __launch_bounds__(256) void elsaa_k1_hash_fixup(
+    const uint16_t *__restrict__ xq, const uint16_t *__restrict__ xk,
+    const uint16_t *__restrict__ planes, int R, int ns, int L, int P, long long rows,
+    const uint8_t *__restrict__ flags, uint16_t *__restrict__ scode, void *__restrict__ rcode,
+    int rcb) {
+  const int lane = threadIdx.x & 63;
+  const long long waves = static_cast<long long>(gridDim.x) * 4;
+  const long long total = 2 * rows;
+  for (long long r0 = (static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 64; r0 < total;
+       r0 += waves * 64) {
+    // 64 rows' flags per load; flagged rows are then handled one at a time
+    unsigned long long todo = __ballot(r0 + lane < total && flags[r0 + lane] != 0);
+    while (todo) {
+      const long long r = r0 + __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const uint16_t *xr = (r < rows ? xq + r * D : xk + (r - rows) * D);
+      u16x8 xv[D / 8];
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) xv[c] = *reinterpret_cast<const u16x8 *>(xr + c * 8);
+      unsigned long long m[4];  // plane-bit masks, planes 64 q .. 64 q + 63
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int t = qd * 64 + lane;
+        bool bit = false;
+        if (qd * 64 < R) {  // wave-uniform
+          const int tt = t < R ? t : R - 1;
+          const uint16_t *pr = planes + static_cast<long long>(tt) * D;
+          u16x8 pv[D / 8];
+#pragma unroll
+          for (int c = 0; c < D / 8; ++c) pv[c] = *reinterpret_cast<const u16x8 *>(pr + c * 8);
+          double sum = 0.0, sabs = 0.0;
+#pragma unroll
+          for (int c = 0; c < D / 8; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const double prod = static_cast<double>(bf16_bits_to_f32(xv[c][e])) *
+                                  static_cast<double>(bf16_bits_to_f32(pv[c][e]));  // exact
+              sum += prod;
+              sabs += fabs(prod);
+            }
+          const double bound = static_cast<double>(D + 1) * 0x1p-52 * sabs;
+          int sgn = sum > bound ? 1 : (sum < -bound ? -1 : 2);
+          if (sgn == 2) sgn = kulisch_dot_sign<uint16_t>(xr, pr, D);
+          bit = t < R && sgn > 0;
+        }
+        m[qd] = __ballot(bit);
+      }
+      auto get = [&](int wd) -> uint32_t {
+        if (wd >= 8) return 0u;
+        const unsigned long long mm = m[wd >> 1];
+        return (wd & 1) ? static_cast<uint32_t>(mm >> 32) : static_cast<uint32_t>(mm);
+      };
+      if (lane == 0) scode[r] = static_cast<uint16_t>(bit_field(get, 0, ns));
+      for (int l = lane; l < L; l += 64) {
+        const uint32_t c = bit_field(get, ns + l * P, P);
+        if (rcb == 1) reinterpret_cast<uint8_t *>(rcode)[r * L + l] = static_cast<uint8_t>(c);
+        else reinterpret_cast<uint16_t *>(rcode)[r * L + l] = static_cast<uint16_t>(c);
+      }
+    }
   }
 }
 
@@ -313,24 +428,44 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_f32(
 
 }  // namespace
 
+template <int D, int NPT>
+void launch_bf16(const Geometry &g, const void *q, const void *k, const void *planes,
+                 const Buffers &buf, hipStream_t stream) {
+  const long long rows_per_wg = kTilesPerWg * 16;
+  const dim3 grid(static_cast<unsigned>((g.rows + rows_per_wg - 1) / rows_per_wg), 2);
+  hipLaunchKernelGGL((elsaa_k1_hash_bf16<D, NPT>), grid, dim3(256), 0, stream,
+                     static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                     static_cast<const uint16_t *>(planes), g.R, g.ns, g.L, g.P, g.rows, buf.scode,
+                     buf.rcode, g.rcb, buf.flags);
+}
+
+template <int D, int NPT = 1>
+void dispatch_npt(int npt, const Geometry &g, const void *q, const void *k, const void *planes,
+                  const Buffers &buf, hipStream_t stream) {
+  if constexpr (NPT < 16) {
+    if (npt > NPT) return dispatch_npt<D, NPT + 1>(npt, g, q, k, planes, buf, stream);
+  }
+  launch_bf16<D, NPT>(g, q, k, planes, buf, stream);
+}
+
 hipError_t launch_hash(const Geometry &g, const void *q, const void *k, const void *planes,
                        const Buffers &buf, hipStream_t stream) {
   if (g.bf16) {
-    const int R_pad = (g.R + 15) & ~15;
-    const long long n_tiles = (g.rows + kRowsPerTile - 1) / kRowsPerTile;
-    const dim3 grid(static_cast<unsigned>((n_tiles + kTilesPerWg - 1) / kTilesPerWg), 2);
-    const size_t lds = static_cast<size_t>(R_pad) * (g.D + 8) * 2 + static_cast<size_t>(R_pad) * 8 +
-                       4 * 16 * 8 * 4;
+    const int npt = g.R > 0 ? (g.R + 15) / 16 : 1;  // R <= 256: at most 16 plane tiles
+    if (g.D == 64) dispatch_npt<64>(npt, g, q, k, planes, buf, stream);
+    else dispatch_npt<128>(npt, g, q, k, planes, buf, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (g.D == 64)
-      hipLaunchKernelGGL(elsaa_k1_hash_bf16<64>, grid, dim3(256), lds, stream,
+      hipLaunchKernelGGL(elsaa_k1_hash_fixup<64>, dim3(1024), dim3(256), 0, stream,
                          static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                          static_cast<const uint16_t *>(planes), g.R, g.ns, g.L, g.P, g.rows,
-                         buf.scode, buf.rcode, g.rcb);
+                         buf.flags, buf.scode, buf.rcode, g.rcb);
     else
-      hipLaunchKernelGGL(elsaa_k1_hash_bf16<128>, grid, dim3(256), lds, stream,
+      hipLaunchKernelGGL(elsaa_k1_hash_fixup<128>, dim3(1024), dim3(256), 0, stream,
                          static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                          static_cast<const uint16_t *>(planes), g.R, g.ns, g.L, g.P, g.rows,
-                         buf.scode, buf.rcode, g.rcb);
+                         buf.flags, buf.scode, buf.rcode, g.rcb);
   } else {
     const dim3 grid(static_cast<unsigned>((g.rows + 255) / 256), 2);
     hipLaunchKernelGGL(elsaa_k1_hash_f32, grid, dim3(256), 0, stream,

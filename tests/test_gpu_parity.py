@@ -82,3 +82,38 @@ def test_deterministic():
     b = run_gpu(inp)
     for key in ("y", "race_sum", "o_sparse", "lse_s", "perm_q", "perm_k"):
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+def _integer_inputs(seed, N=2048, H=2, dtype="bf16", scale=1.0):
+    """Small-integer q, k and hyperplanes (times a power of two): many projections are
+    exactly zero or tiny, so the exact sign path decides them."""
+    wl = workloads.workload("small-bf16", B=1, H=H, N=N, dtype=dtype, race_tables=4, race_bits=5)
+    inp = workloads.generate(wl, seed)
+    rng = np.random.default_rng(seed)
+    f = (lambda a: a.astype(np.float32))
+    q = f(rng.integers(-2, 3, size=inp.q.shape) * scale)
+    k = f(rng.integers(-2, 3, size=inp.k.shape) * scale)
+    planes = f(rng.integers(-1, 2, size=inp.hyperplanes.shape))
+    if dtype == "bf16":
+        to_bits = lambda a: workloads.round_to_bf16_bits(a.astype(np.float64))
+        inp.bits["q"], inp.bits["k"], inp.bits["hyperplanes"] = to_bits(q), to_bits(k), to_bits(planes)
+    inp.q, inp.k, inp.hyperplanes = q, k, planes
+    return inp
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** 50, 2.0 ** -50])
+def test_exact_ties_and_extreme_magnitudes(scale):
+    """Exact-zero projections (bit 0), rows far outside the certified range
+    (|x| > 2^40 or < 2^-40): every such code bit comes from the exact path."""
+    inp = _integer_inputs(21, scale=scale)
+    g = run_gpu(inp)
+    r = run_oracle(inp)
+    q64 = inp.q.astype(np.float64)
+    dots = q64.reshape(-1, q64.shape[-1]) @ inp.hyperplanes.astype(np.float64).T
+    assert (dots == 0).mean() > 0.1  # the exact path is exercised
+    np.testing.assert_array_equal(g["sort_code_q"], r.sort_code_q)
+    np.testing.assert_array_equal(g["sort_code_k"], r.sort_code_k)
+    np.testing.assert_array_equal(g["race_code_q"], r.race_code_q)
+    np.testing.assert_array_equal(g["race_code_k"], r.race_code_k)
+    np.testing.assert_array_equal(g["perm_q"], r.perm_q)
+    np.testing.assert_array_equal(g["perm_k"], r.perm_k)
