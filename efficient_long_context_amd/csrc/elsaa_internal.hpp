@@ -36,6 +36,8 @@ struct Buffers {
   int32_t *perm;    // [2][BH][N]
   uint8_t *flags;   // [2][BH][N]     rows whose codes need the exact pass
   uint32_t *hist;   // [2][BH][nb_sort][sort_tiles] -> exclusive offsets
+  int32_t *rperm;   // [BH][L][N]     keys of each table sorted by bucket
+  int32_t *rstart;  // [BH][L][nb_race + 1] run start of each bucket in rperm
   float *tsum;      // [BH][L][nb_race][D]
   float *tcnt;      // [BH][L][nb_race]
   void *o_s;        // [BH][N][D] in dtype

@@ -5,202 +5,196 @@
 // branches can still be mis-scaled"): for every table l and bucket b,
 //   count[l][b] = #{keys j : code_l(k_j) = b},   sum[l][b][:] = sum of v_j over them.
 //
-// Work unit = (b, h, table l, column slice of 64 value columns, range of RB <= 32
-// consecutive buckets).  One wave owns one unit and keeps its RB bucket rows in
-// registers: lane c holds column c of every bucket of the range, indexed by a
-// wave-uniform bucket (lowered to M0-relative register moves).
-// The wave scans every key of (b, h) in index order, 64 codes per ballot, and
-// adds the value row of each key whose bucket falls in its range, eight keys
-// per straight-line round (a round that runs out of keys adds a zero row).  No
-// accumulator is shared, adds happen in key order, and no atomics are used
-// (LDS float atomics are slow on gfx950 and would make the order, hence the
-// rounding, vary), so the result is deterministic; repeated keys cost the same
-// as distinct ones.  Bucket counts come from a separate integer histogram.
-//
-// A workgroup of 8 waves shares one column slice: tiles of 64 key rows (and
-// their code block) are loaded into a ring of four register sets, converted to
-// fp32 once and staged in LDS for all 8 waves.  Barriers order LDS only, so the
-// prefetches stay in flight across them.  Workgroups of one (b, h) are mapped
-// to one XCD (dispatch is round-robin over the 8 XCDs) so its value rows are
-// fetched into one L2.
+// Built as a segmented reduction over sorted codes, in two kernels:
+//   sort    one workgroup per (b, h, table): a stable counting sort of the N
+//           key codes (integer LDS histograms per wave, a scan, and ranks from
+//           one ballot per code bit), giving the keys of every bucket as one
+//           contiguous run of the table's permutation, plus the run starts;
+//   reduce  one wave per (b, h, table, 64 value columns, part of the buckets):
+//           lanes are the 64 columns; the wave walks its buckets' runs in order,
+//           loading 16 key rows ahead, sums each run in registers and writes the
+//           bucket row and its count once.
+// No floating-point atomics (LDS float atomics are slow on gfx950 and would make
+// the summation order vary): every bucket is summed by one wave in ascending
+// key order, so the tables are deterministic.  Heavy buckets (repeated tokens)
+// are just long runs.
 #include "elsaa_internal.hpp"
 
 namespace elsaa {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kTK = 64;       // keys per staged tile
-constexpr int kMaxRB = 32;    // buckets per wave
-constexpr int kRound = 8;     // keys added per straight-line round
+constexpr int kSortWavesMax = 16;
+constexpr int kReduceBatch = 16;  // key rows in flight per wave
 
-// One thread's share of a tile: 8 consecutive values of one key row and 16
-// bytes of the tile's code block (the codes of 64 consecutive keys are one
-// contiguous block of 64 * L codes).  Loads are unconditional (addresses
-// clamped in bounds), so the compiler never waits for a prefetch before the
-// tile is staged.
-typedef float f32x32 __attribute__((ext_vector_type(32)));
-
-template <typename VT>
-struct TileRegs {
-  VT x[8];
-  uint4 c;
-};
-
-template <typename VT, typename CT>
-__global__ __launch_bounds__(kThreads) void elsaa_k4_race_build(
-    const VT *__restrict__ v, const CT *__restrict__ kcodes, int N, int D, int L, int nb, int RB,
-    int nr, int wg_per_cs, int wg_per_bh, int wg_real, float *__restrict__ tsum) {
-  extern __shared__ __align__(16) float lds[];
-  const int code_words = (kTK * L * static_cast<int>(sizeof(CT)) + 15) / 16;  // 16-byte words per tile
-  float *tile = lds;                                         // [kTK + 1][64] fp32; row kTK is zero
-  CT *tcode = reinterpret_cast<CT *>(lds + (kTK + 1) * 64);  // [kTK][L], in kThreads x 16 bytes
+// ---------------------------------------------------------------------- sort --
+template <typename CT>
+__global__ __launch_bounds__(kSortWavesMax * 64) void elsaa_k4_race_sort(
+    const CT *__restrict__ kcodes, int N, int L, int P, int chunk, int32_t *__restrict__ perm,
+    int32_t *__restrict__ bstart) {
+  extern __shared__ uint32_t cnt[];  // [waves][nb]: counts, then running offsets
+  __shared__ uint32_t part[kSortWavesMax * 64];
+  const int nb = 1 << P;
+  const int nthreads = blockDim.x, waves = nthreads >> 6;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  // XCD-aware order: consecutive logical workgroups share an XCD.
-  const int logical = static_cast<int>(xcd_logical_block(blockIdx.x, gridDim.x));
-  if (logical >= wg_real) return;  // whole workgroup exits together
-  const long long bh = logical / wg_per_bh;
-  const int wg = logical % wg_per_bh;
-  const int cs = wg / wg_per_cs;
-  const int u = (wg % wg_per_cs) * kWaves + wave;
-  const bool active = u < L * nr;
-  const int l = active ? u / nr : 0;
-  const int r = active ? u % nr : 0;
-  const int base = r * RB;
-
-  // one register vector (a wave-uniform element index compiles to M0-relative
-  // moves); larger or split vectors make the compiler copy or select whole
-  // vectors per add, so a wave owns at most 32 buckets
-  f32x32 acc = {};
-  if (tid < 64) tile[kTK * 64 + tid] = 0.0f;
-
+  const int l = blockIdx.x;
+  const long long bh = blockIdx.y;
   const long long seg = bh * N;
-  const int tk = tid >> 3, tc = (tid & 7) * 8;  // tile loader: key tk, columns tc .. tc+7
-  const VT *vsrc = v + seg * D + cs * 64 + tc;
-  const uint4 *csrc = reinterpret_cast<const uint4 *>(kcodes + seg * L);  // 16-byte aligned: 64 L | N L
-  const int n_tiles = N / kTK;  // N is a multiple of 64 (the chunk is)
-  const bool code_loader = tid < code_words;
+  const long long unit = bh * L + l;
+  const CT *c = kcodes + seg * L + l;  // code of key j at c[j * L]
+  const int j_begin = wave * chunk;
+  const int j_end = j_begin + chunk < N ? j_begin + chunk : N;
 
-  auto load = [&](TileRegs<VT> &p, int t) {
-    const int tt = t < n_tiles ? t : n_tiles - 1;  // past the end: reload the last tile
-    const VT *src = vsrc + static_cast<long long>(tt * kTK + tk) * D;
-    if constexpr (sizeof(VT) == 2) {
-      *reinterpret_cast<u16x8 *>(p.x) = *reinterpret_cast<const u16x8 *>(src);
-    } else {
-      *reinterpret_cast<f32x4 *>(p.x) = *reinterpret_cast<const f32x4 *>(src);
-      *reinterpret_cast<f32x4 *>(p.x + 4) = *reinterpret_cast<const f32x4 *>(src + 4);
-    }
-    p.c = csrc[static_cast<long long>(tt) * code_words + (code_loader ? tid : 0)];  // all threads load
-  };
+  for (int i = tid; i < waves * nb; i += nthreads) cnt[i] = 0;
+  __syncthreads();
+  uint32_t *wc = cnt + wave * nb;
+  for (int j = j_begin + lane; j < j_end; j += 64) atomicAdd(&wc[c[static_cast<long long>(j) * L]], 1u);
+  __syncthreads();
 
-  auto step = [&](TileRegs<VT> &p, int t) {
-    lds_barrier();  // previous tile fully consumed
-    f32x4 lo, hi;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lo[e] = Elem<VT>::load(p.x + e);
-      hi[e] = Elem<VT>::load(p.x + 4 + e);
-    }
-    *reinterpret_cast<f32x4 *>(tile + tk * 64 + tc) = lo;
-    *reinterpret_cast<f32x4 *>(tile + tk * 64 + tc + 4) = hi;
-    reinterpret_cast<uint4 *>(tcode)[tid] = p.c;  // unconditional: words past the block are unused
-    lds_barrier();
-    load(p, t + 4);  // refill this ring slot four tiles ahead
-    if (!active || t >= n_tiles) return;  // steps past the end only keep the ring uniform
-    const int rel = static_cast<int>(tcode[lane * L + l]) - base;
-    unsigned long long mask = __ballot(static_cast<unsigned>(rel) < static_cast<unsigned>(RB));
-    while (mask) {
-      int idx[kRound], rbs[kRound];
-#pragma unroll
-      for (int q = 0; q < kRound; ++q) {
-        const bool any = mask != 0;
-        const int i = any ? __builtin_ctzll(mask) : 0;
-        mask &= mask - 1;
-        idx[q] = any ? i : kTK;  // the zero row
-        rbs[q] = any ? __builtin_amdgcn_readlane(rel, i) : 0;
-      }
-      float val[kRound];
-#pragma unroll
-      for (int q = 0; q < kRound; ++q) val[q] = tile[idx[q] * 64 + lane];
-#pragma unroll
-      for (int q = 0; q < kRound; ++q) acc[rbs[q]] += val[q];
-    }
-  };
-
-  TileRegs<VT> p0, p1, p2, p3;
-  load(p0, 0);
-  load(p1, 1);
-  load(p2, 2);
-  load(p3, 3);
-  // uniform trip count and an unconditional body: every wave reaches every
-  // barrier, and the compiler can wait for one ring slot at a time
-  for (int t = 0; t < n_tiles; t += 4) {
-    step(p0, t);
-    step(p1, t + 1);
-    step(p2, t + 2);
-    step(p3, t + 3);
+  // bucket-major exclusive scan of the [bucket][wave] counts
+  const int per = (nb + nthreads - 1) / nthreads;
+  const int b_lo = tid * per < nb ? tid * per : nb;
+  const int b_hi = b_lo + per < nb ? b_lo + per : nb;
+  uint32_t sum = 0;
+  for (int b = b_lo; b < b_hi; ++b)
+    for (int w = 0; w < waves; ++w) sum += cnt[w * nb + b];
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < nthreads; off <<= 1) {  // inclusive Hillis-Steele scan
+    const uint32_t add = tid >= off ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
   }
+  uint32_t run = part[tid] - sum;
+  int32_t *bs = bstart + unit * (nb + 1);
+  for (int b = b_lo; b < b_hi; ++b) {
+    bs[b] = static_cast<int32_t>(run);
+    for (int w = 0; w < waves; ++w) {
+      const uint32_t t = cnt[w * nb + b];
+      cnt[w * nb + b] = run;
+      run += t;
+    }
+  }
+  if (tid == 0) bs[nb] = N;
+  __syncthreads();
 
-  if (!active) return;
-  float *out = tsum + (bh * L + l) * static_cast<long long>(nb) * D + cs * 64 + lane;
-#pragma unroll
-  for (int rb = 0; rb < kMaxRB; ++rb)
-    if (rb < RB) out[static_cast<long long>(base + rb) * D] = acc[rb];
+  // stable ranks: each wave walks its chunk in order, 64 keys per round
+  int32_t *pm = perm + unit * N;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int j0 = j_begin; j0 < j_end; j0 += 64) {
+    const int j = j0 + lane;
+    const bool valid = j < j_end;
+    const uint32_t code = valid ? static_cast<uint32_t>(c[static_cast<long long>(j) * L]) : 0u;
+    unsigned long long mask = __ballot(valid);
+    for (int bit = 0; bit < P; ++bit) {
+      const bool set = (code >> bit) & 1u;
+      const unsigned long long bb = __ballot(set);
+      mask &= set ? bb : ~bb;
+    }
+    const int rank = __popcll(mask & lt);
+    const int leader = __ffsll(static_cast<long long>(mask)) - 1;
+    uint32_t before = 0;
+    if (valid && lane == leader) {
+      before = wc[code];
+      wc[code] = before + static_cast<uint32_t>(__popcll(mask));
+    }
+    before = __shfl(before, leader < 0 ? 0 : leader);
+    if (valid) pm[before + rank] = j;
+    // the leader's counter update must land before the next round reads it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
 }
 
-// Bucket counts: one workgroup per (b, h, table), an LDS histogram of the N
-// codes with integer atomics (exact in any order).
-template <typename CT>
-__global__ __launch_bounds__(256) void elsaa_k4_race_counts(const CT *__restrict__ kcodes, int N,
-                                                            int L, int nb, float *__restrict__ tcnt) {
-  extern __shared__ uint32_t hist[];
-  const long long bh = blockIdx.y;
-  const int l = blockIdx.x;
-  for (int b = threadIdx.x; b < nb; b += 256) hist[b] = 0;
-  __syncthreads();
-  const CT *c = kcodes + bh * N * static_cast<long long>(L) + l;
-  for (int j = threadIdx.x; j < N; j += 256) atomicAdd(&hist[c[static_cast<long long>(j) * L]], 1u);
-  __syncthreads();
-  float *out = tcnt + (bh * L + l) * static_cast<long long>(nb);
-  for (int b = threadIdx.x; b < nb; b += 256) out[b] = static_cast<float>(hist[b]);
+// -------------------------------------------------------------------- reduce --
+template <typename VT>
+__global__ __launch_bounds__(256) void elsaa_k4_race_reduce(
+    const VT *__restrict__ v, const int32_t *__restrict__ perm, const int32_t *__restrict__ bstart,
+    int N, int D, int L, int P, int ncs, int parts, long long units, float *__restrict__ tsum,
+    float *__restrict__ tcnt) {
+  const int lane = threadIdx.x & 63;
+  const long long u = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (u >= units) return;  // whole wave
+  const int nb = 1 << P;
+  const int part = static_cast<int>(u % parts);
+  const int cs = static_cast<int>((u / parts) % ncs);
+  const long long tu = u / (static_cast<long long>(parts) * ncs);  // (b, h) * L + table
+  const long long bh = tu / L;
+  const int32_t *bs = bstart + tu * (nb + 1);
+  const int32_t *pm = perm + tu * N;
+  const VT *vcol = v + bh * N * static_cast<long long>(D) + cs * 64 + lane;
+
+  // buckets owned: those whose run starts in [lo, hi); the last part also owns
+  // the empty buckets that start at N
+  const int lo = static_cast<int>(static_cast<long long>(N) * part / parts);
+  const int hi = part == parts - 1 ? N + 1 : static_cast<int>(static_cast<long long>(N) * (part + 1) / parts);
+  int b0 = nb, b1 = nb;
+  for (int bb = 0; bb < nb; bb += 64) {
+    const int b = bb + lane;
+    const int s = b < nb ? bs[b] : N + 1;
+    const unsigned long long ge_lo = __ballot(b < nb && s >= lo);
+    const unsigned long long ge_hi = __ballot(b < nb && s >= hi);
+    if (b0 == nb && ge_lo) b0 = bb + __builtin_ctzll(ge_lo);
+    if (b1 == nb && ge_hi) b1 = bb + __builtin_ctzll(ge_hi);
+  }
+
+  for (int b = b0; b < b1; ++b) {
+    const int p0 = bs[b], p1 = bs[b + 1];
+    float acc = 0.0f;
+    for (int p = p0; p < p1; p += kReduceBatch) {
+      const int n = p1 - p < kReduceBatch ? p1 - p : kReduceBatch;
+      // lanes 0..15 fetch the batch's key indices (clamped inside the run)
+      const int jl = pm[p + (lane < n ? lane : n - 1)];
+      float val[kReduceBatch];
+#pragma unroll
+      for (int q = 0; q < kReduceBatch; ++q) {
+        const int j = __builtin_amdgcn_readlane(jl, q < n ? q : n - 1);
+        val[q] = Elem<VT>::load(vcol + static_cast<long long>(j) * D);
+      }
+#pragma unroll
+      for (int q = 0; q < kReduceBatch; ++q)
+        if (q < n) acc += val[q];  // ascending key order within the bucket
+    }
+    tsum[(tu * nb + b) * static_cast<long long>(D) + cs * 64 + lane] = acc;
+    if (cs == 0 && lane == 0) tcnt[tu * nb + b] = static_cast<float>(p1 - p0);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
                              hipStream_t stream) {
-  const int RB = g.nb_race < kMaxRB ? g.nb_race : kMaxRB;
-  const int nr = g.nb_race / RB;
-  const int ncs = g.D / 64;
-  const int wg_per_cs = (g.L * nr + kWaves - 1) / kWaves;
-  const int wg_per_bh = wg_per_cs * ncs;
-  const long long wg_real = static_cast<long long>(wg_per_bh) * g.BH;
-  const long long grid = (wg_real + kXcdCount - 1) / kXcdCount * kXcdCount;
-  const size_t lds = static_cast<size_t>(kTK + 1) * 64 * 4 + static_cast<size_t>(kThreads) * 16;
+  const int nb = g.nb_race;
+  int waves = 16384 / nb;  // LDS counts: waves * nb * 4 bytes <= 64 KB
+  waves = waves < 1 ? 1 : (waves > kSortWavesMax ? kSortWavesMax : waves);
+  const int chunk = ((g.N + waves - 1) / waves + 63) / 64 * 64;
   const void *rk = static_cast<const char *>(buf.rcode) + static_cast<size_t>(g.rows) * g.L * g.rcb;
-  const dim3 cgrid(g.L, g.BH);
-  const size_t clds = static_cast<size_t>(g.nb_race) * 4;
+  const dim3 sgrid(g.L, g.BH);
+  const size_t slds = static_cast<size_t>(waves) * nb * 4;
   if (g.rcb == 1)
-    hipLaunchKernelGGL(elsaa_k4_race_counts<uint8_t>, cgrid, dim3(256), clds, stream,
-                       static_cast<const uint8_t *>(rk), g.N, g.L, g.nb_race, buf.tcnt);
+    hipLaunchKernelGGL(elsaa_k4_race_sort<uint8_t>, sgrid, dim3(waves * 64), slds, stream,
+                       static_cast<const uint8_t *>(rk), g.N, g.L, g.P, chunk, buf.rperm, buf.rstart);
   else
-    hipLaunchKernelGGL(elsaa_k4_race_counts<uint16_t>, cgrid, dim3(256), clds, stream,
-                       static_cast<const uint16_t *>(rk), g.N, g.L, g.nb_race, buf.tcnt);
+    hipLaunchKernelGGL(elsaa_k4_race_sort<uint16_t>, sgrid, dim3(waves * 64), slds, stream,
+                       static_cast<const uint16_t *>(rk), g.N, g.L, g.P, chunk, buf.rperm, buf.rstart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-#define ELSAA_K4_LAUNCH(VT, CT)                                                                   \
-  hipLaunchKernelGGL((elsaa_k4_race_build<VT, CT>), dim3(grid), dim3(kThreads), lds, stream,     \
-                     static_cast<const VT *>(v), static_cast<const CT *>(rk), g.N, g.D, g.L,      \
-                     g.nb_race, RB, nr, wg_per_cs, wg_per_bh, static_cast<int>(wg_real), buf.tsum)
-  if (g.bf16) {
-    if (g.rcb == 1) ELSAA_K4_LAUNCH(uint16_t, uint8_t);
-    else ELSAA_K4_LAUNCH(uint16_t, uint16_t);
-  } else {
-    if (g.rcb == 1) ELSAA_K4_LAUNCH(float, uint8_t);
-    else ELSAA_K4_LAUNCH(float, uint16_t);
-  }
-#undef ELSAA_K4_LAUNCH
+
+  const int ncs = g.D / 64;
+  const long long tables = static_cast<long long>(g.BH) * g.L * ncs;
+  long long parts = (8192 + tables - 1) / tables;  // aim for ~8K waves
+  parts = parts < 1 ? 1 : (parts > nb ? nb : parts);
+  const long long units = tables * parts;
+  const dim3 rgrid(static_cast<unsigned>((units + 3) / 4));
+  if (g.bf16)
+    hipLaunchKernelGGL(elsaa_k4_race_reduce<uint16_t>, rgrid, dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, g.N, g.D, g.L, g.P,
+                       ncs, static_cast<int>(parts), units, buf.tsum, buf.tcnt);
+  else
+    hipLaunchKernelGGL(elsaa_k4_race_reduce<float>, rgrid, dim3(256), 0, stream,
+                       static_cast<const float *>(v), buf.rperm, buf.rstart, g.N, g.D, g.L, g.P, ncs,
+                       static_cast<int>(parts), units, buf.tsum, buf.tcnt);
   return hipGetLastError();
 }
 

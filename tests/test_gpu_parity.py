@@ -91,8 +91,9 @@ def _integer_inputs(seed, N=2048, H=2, dtype="bf16", scale=1.0):
     inp = workloads.generate(wl, seed)
     rng = np.random.default_rng(seed)
     f = (lambda a: a.astype(np.float32))
-    q = f(rng.integers(-2, 3, size=inp.q.shape) * scale)
-    k = f(rng.integers(-2, 3, size=inp.k.shape) * scale)
+    sparse = lambda shape: rng.integers(-2, 3, size=shape) * (rng.random(shape) < 0.08)
+    q = f(sparse(inp.q.shape) * scale)
+    k = f(sparse(inp.k.shape) * scale)
     planes = f(rng.integers(-1, 2, size=inp.hyperplanes.shape))
     if dtype == "bf16":
         to_bits = lambda a: workloads.round_to_bf16_bits(a.astype(np.float64))
