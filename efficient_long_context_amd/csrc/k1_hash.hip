@@ -93,6 +93,60 @@ __device__ __noinline__ int exact_dot_sign(const T *x, const T *r, int d) {
   return kulisch_dot_sign<T>(x, r, d);
 }
 
+// Exact sign of <x, r> for two rows of d bfloat16 values, one wave, lanes over
+// the elements.  A bfloat16 value is M 2^E with an integer M < 2^8 (E = e - 134
+// for a normal exponent field e, M = 128 + fraction; E = -133 and M = fraction
+// for subnormals), so every product is an integer below 2^16 times 2^(Ex + Er).
+// When the nonzero products' exponents span at most 39 they are shifted to the
+// smallest one and added as 64-bit integers (d 2^16 2^39 < 2^63: exact, and
+// integer addition is associative, so any reduction order gives the same
+// value).  Returns -1, 0, 1, or 2 when the span is wider (caller falls back).
+__device__ __forceinline__ void bf16_split(uint16_t b, int &m, int &e) {
+  const int ef = (b >> 7) & 0xff, frac = b & 0x7f;
+  m = ef ? (frac | 0x80) : frac;
+  e = ef ? ef - 134 : -133;
+}
+
+template <int D>
+__device__ int wave_exact_sign_bf16(const uint16_t *x, const uint16_t *r, int lane) {
+  constexpr int kPer = D / 64;
+  constexpr int kNone = 1 << 20;
+  int pm[kPer], pe[kPer];
+  bool neg[kPer];
+  int emin = kNone, emax = -kNone;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint16_t bx = x[lane + 64 * j], br = r[lane + 64 * j];
+    int mx, ex, mr, er;
+    bf16_split(bx, mx, ex);
+    bf16_split(br, mr, er);
+    pm[j] = mx * mr;
+    pe[j] = ex + er;
+    neg[j] = ((bx ^ br) & 0x8000) != 0;
+    if (pm[j] != 0) {
+      emin = pe[j] < emin ? pe[j] : emin;
+      emax = pe[j] > emax ? pe[j] : emax;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const int a = __shfl_xor(emin, off), b = __shfl_xor(emax, off);
+    emin = a < emin ? a : emin;
+    emax = b > emax ? b : emax;
+  }
+  if (emin == kNone) return 0;  // every product is zero
+  if (emax - emin > 39) return 2;
+  long long acc = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const long long t = static_cast<long long>(pm[j]) << (pm[j] ? pe[j] - emin : 0);
+    acc += neg[j] ? -t : t;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  return acc > 0 ? 1 : (acc < 0 ? -1 : 0);
+}
+
 // Write one row's codes: the sort code (bits [0, ns)) and L race codes (bits
 // ns + l*P + t).  `get` returns the 32-bit word w of the row's plane-bit mask.
 template <typename GetWord>
@@ -116,8 +170,9 @@ __device__ __forceinline__ uint32_t bit_field(GetWord get, int pos, int n) {
 // tau_row = |x| * max_t(c |r_t|) + d 2^-124 bounds the error of every plane's
 // projection of that row (c = (d + 2) 2^-22, twice the worst-case relative
 // error of d fp32 additions; d 2^-124 covers flushed subnormal products and
-// partial sums).  Planes outside the range, or rows that fail the check, send
-// every projection to the exact path.
+// partial sums).  Projections within tau of zero are re-decided in binary64 by
+// the whole wave; planes outside the range, rows that fail the check, and
+// projections binary64 cannot decide send the row to the exact fix-up kernel.
 template <int D, int NPT>
 __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
     const uint16_t *__restrict__ xq, const uint16_t *__restrict__ xk,
@@ -237,7 +292,7 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
     uint32_t words[kWords];
 #pragma unroll
     for (int w = 0; w < kWords; ++w) words[w] = 0u;
-    unsigned long long unsure = 0ull;
+    unsigned long long unsure = 0ull;  // bit 4 pt + i: projection not certified
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) {
       const f32x4 a4 = project(pt);
@@ -245,9 +300,63 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         words[pt >> 1] |= (a4[i] > 0.0f ? 1u : 0u) << ((pt & 1) * 16 + i);
-        unsure |= __ballot(!(fabsf(a4[i]) > tau) && pt * 16 + g * 4 + i < R);  // padding planes: bit 0
+        const bool u = !(fabsf(a4[i]) > tau) && pt * 16 + g * 4 + i < R;  // padding planes: bit 0
+        unsure |= static_cast<unsigned long long>(u) << (pt * 4 + i);
       }
     }
+    // Rows outside the certified range go to the exact fix-up kernel whole.
+    bool undecided = valid && !row_ok;
+    if (!valid || !row_ok) unsure = 0ull;
+    // Rare: each uncertified projection is re-decided by the whole wave, lanes
+    // over the d products (exact in binary64), summed by a butterfly of depth
+    // log2(64) (+1 for d = 128 with two products per lane); the sign is taken
+    // when |sum| exceeds (depth + 1) 2^-52 sum |p_i|, else from the exact
+    // integer sum; only a product exponent span too wide for it flags the row.
+    for (unsigned long long pending = __ballot(unsure != 0ull); pending;
+         pending = __ballot(unsure != 0ull)) {
+      const int src = __builtin_ctzll(pending);  // wave-uniform
+      const unsigned long long sb =
+          static_cast<unsigned long long>(static_cast<uint32_t>(__builtin_amdgcn_readlane(
+              static_cast<int>(unsure), src))) |
+          (static_cast<unsigned long long>(static_cast<uint32_t>(
+               __builtin_amdgcn_readlane(static_cast<int>(unsure >> 32), src)))
+           << 32);
+      const int bpos = __builtin_ctzll(sb);
+      const int t = (bpos >> 2) * 16 + (src >> 4) * 4 + (bpos & 3);
+      const uint16_t *xs = sx + (wave * 16 + (src & 15)) * kLdsRow;
+      const uint16_t *ps = sp + t * kLdsRow;
+      double sum = 0.0, sabs = 0.0;
+#pragma unroll
+      for (int e = lane; e < D; e += 64) {
+        const double prod = static_cast<double>(bf16_bits_to_f32(xs[e])) *
+                            static_cast<double>(bf16_bits_to_f32(ps[e]));  // exact
+        sum += prod;
+        sabs += fabs(prod);
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        sum += __shfl_xor(sum, off);
+        sabs += __shfl_xor(sabs, off);
+      }
+      constexpr int kDepth = 6 + D / 64;
+      const double bound = static_cast<double>(kDepth + 1) * 0x1p-52 * sabs;
+      // within the bound (exact ties included): the integer sum decides
+      int sgn = sum > bound ? 1 : (sum < -bound ? -1 : 2);
+      if (__builtin_amdgcn_readlane(sgn, src) == 2) sgn = wave_exact_sign_bf16<D>(xs, ps, lane);
+      if (lane == src) {
+        unsure &= unsure - 1ull;
+        if (sgn != 2) {
+          const int pt = bpos >> 2;
+          const uint32_t m = 1u << ((pt & 1) * 16 + (bpos & 3));
+#pragma unroll
+          for (int q = 0; q < kWords; ++q)
+            if ((pt >> 1) == q) words[q] = sgn > 0 ? (words[q] | m) : (words[q] & ~m);
+        } else {
+          undecided = true;
+        }
+      }
+    }
+    const unsigned long long undecided_mask = __ballot(undecided);
     // place group g's bits, then OR the four groups: every lane of a row holds
     // the row's full plane mask (planes >= R are zero rows: bit 0)
 #pragma unroll
@@ -267,8 +376,8 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
       const long long out_row = static_cast<long long>(tensor) * rows + row;
       if (g == 0) {
         scode[out_row] = static_cast<uint16_t>(bit_field(get, 0, ns));
-        // any uncertified projection of this row: the exact pass redoes its codes
-        flags[out_row] = ((unsure >> r16) & 0x0001000100010001ull) ? 1 : 0;
+        // a projection binary64 could not decide: the exact pass redoes the row
+        flags[out_row] = ((undecided_mask >> r16) & 0x0001000100010001ull) ? 1 : 0;
       }
       if (rcb == 1) {
         uint8_t *rc = reinterpret_cast<uint8_t *>(rcode) + out_row * L;
@@ -313,13 +422,24 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_fixup(
   const int lane = threadIdx.x & 63;
   const long long waves = static_cast<long long>(gridDim.x) * 4;
   const long long total = 2 * rows;
-  for (long long r0 = (static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 64; r0 < total;
-       r0 += waves * 64) {
-    // 64 rows' flags per load; flagged rows are then handled one at a time
-    unsigned long long todo = __ballot(r0 + lane < total && flags[r0 + lane] != 0);
-    while (todo) {
-      const long long r = r0 + __builtin_ctzll(todo);
-      todo &= todo - 1;
+  for (long long r0 = (static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 1024; r0 < total;
+       r0 += waves * 1024) {
+    // 1024 rows' flags per wave load (16 per lane); flagged rows are then
+    // handled one at a time
+    const long long f0 = r0 + lane * 16;
+    uint32_t fm = 0u;  // bit e: row f0 + e is flagged
+    if (f0 + 16 <= total) {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(flags + f0);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) fm |= ((w[e >> 2] >> (8 * (e & 3))) & 0xffu) ? (1u << e) : 0u;
+    } else {
+      for (int e = 0; f0 + e < total; ++e) fm |= flags[f0 + e] ? (1u << e) : 0u;
+    }
+    for (unsigned long long lanes = __ballot(fm != 0u); lanes; lanes = __ballot(fm != 0u)) {
+      const int src = __builtin_ctzll(lanes);
+      const uint32_t sm = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(fm), src));
+      const long long r = r0 + src * 16 + __builtin_ctz(sm);
+      if (lane == src) fm &= fm - 1u;
       const uint16_t *xr = (r < rows ? xq + r * D : xk + (r - rows) * D);
       u16x8 xv[D / 8];
 #pragma unroll
@@ -346,7 +466,7 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_fixup(
               sabs += fabs(prod);
             }
           const double bound = static_cast<double>(D + 1) * 0x1p-52 * sabs;
-          int sgn = sum > bound ? 1 : (sum < -bound ? -1 : 2);
+          int sgn = sum > bound ? 1 : (sum < -bound ? -1 : (sabs == 0.0 ? 0 : 2));
           if (sgn == 2) sgn = kulisch_dot_sign<uint16_t>(xr, pr, D);
           bit = t < R && sgn > 0;
         }
@@ -456,13 +576,15 @@ hipError_t launch_hash(const Geometry &g, const void *q, const void *k, const vo
     else dispatch_npt<128>(npt, g, q, k, planes, buf, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const long long fix_blocks = (2 * g.rows + 4095) / 4096;  // 4 waves x 1024 rows
+    const dim3 fgrid(static_cast<unsigned>(fix_blocks < 1024 ? fix_blocks : 1024));
     if (g.D == 64)
-      hipLaunchKernelGGL(elsaa_k1_hash_fixup<64>, dim3(1024), dim3(256), 0, stream,
+      hipLaunchKernelGGL(elsaa_k1_hash_fixup<64>, fgrid, dim3(256), 0, stream,
                          static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                          static_cast<const uint16_t *>(planes), g.R, g.ns, g.L, g.P, g.rows,
                          buf.flags, buf.scode, buf.rcode, g.rcb);
     else
-      hipLaunchKernelGGL(elsaa_k1_hash_fixup<128>, dim3(1024), dim3(256), 0, stream,
+      hipLaunchKernelGGL(elsaa_k1_hash_fixup<128>, fgrid, dim3(256), 0, stream,
                          static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                          static_cast<const uint16_t *>(planes), g.R, g.ns, g.L, g.P, g.rows,
                          buf.flags, buf.scode, buf.rcode, g.rcb);

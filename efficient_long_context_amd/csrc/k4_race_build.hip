@@ -47,7 +47,21 @@ __global__ __launch_bounds__(kSortWavesMax * 64) void elsaa_k4_race_sort(
   for (int i = tid; i < waves * nb; i += nthreads) cnt[i] = 0;
   __syncthreads();
   uint32_t *wc = cnt + wave * nb;
-  for (int j = j_begin + lane; j < j_end; j += 64) atomicAdd(&wc[c[static_cast<long long>(j) * L]], 1u);
+  // codes are read 8 rounds at a time so the loads overlap (one latency per 512 keys)
+  auto load_codes = [&](int j0, uint32_t (&code)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = j0 + q * 64 + lane;
+      code[q] = j < j_end ? static_cast<uint32_t>(c[static_cast<long long>(j) * L]) : 0xffffffffu;
+    }
+  };
+  for (int j0 = j_begin; j0 < j_end; j0 += 512) {
+    uint32_t code[8];
+    load_codes(j0, code);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (code[q] != 0xffffffffu) atomicAdd(&wc[code[q]], 1u);
+  }
   __syncthreads();
 
   // bucket-major exclusive scan of the [bucket][wave] counts
@@ -81,10 +95,15 @@ __global__ __launch_bounds__(kSortWavesMax * 64) void elsaa_k4_race_sort(
   // stable ranks: each wave walks its chunk in order, 64 keys per round
   int32_t *pm = perm + unit * N;
   const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int j0 = j_begin; j0 < j_end; j0 += 64) {
+  for (int j8 = j_begin; j8 < j_end; j8 += 512) {
+  uint32_t codes8[8];
+  load_codes(j8, codes8);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int j0 = j8 + q * 64;
     const int j = j0 + lane;
     const bool valid = j < j_end;
-    const uint32_t code = valid ? static_cast<uint32_t>(c[static_cast<long long>(j) * L]) : 0u;
+    const uint32_t code = valid ? codes8[q] : 0u;
     unsigned long long mask = __ballot(valid);
     for (int bit = 0; bit < P; ++bit) {
       const bool set = (code >> bit) & 1u;
@@ -105,6 +124,7 @@ __global__ __launch_bounds__(kSortWavesMax * 64) void elsaa_k4_race_sort(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   }
+  }
 }
 
 // -------------------------------------------------------------------- reduce --
@@ -114,7 +134,8 @@ __global__ __launch_bounds__(256) void elsaa_k4_race_reduce(
     int N, int D, int L, int P, int ncs, int parts, long long units, float *__restrict__ tsum,
     float *__restrict__ tcnt) {
   const int lane = threadIdx.x & 63;
-  const long long u = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  // consecutive units (same (b, h), same value rows) run on one XCD's L2
+  const long long u = xcd_logical_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
   if (u >= units) return;  // whole wave
   const int nb = 1 << P;
   const int part = static_cast<int>(u % parts);
@@ -186,7 +207,7 @@ hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &bu
   long long parts = (8192 + tables - 1) / tables;  // aim for ~8K waves
   parts = parts < 1 ? 1 : (parts > nb ? nb : parts);
   const long long units = tables * parts;
-  const dim3 rgrid(static_cast<unsigned>((units + 3) / 4));
+  const dim3 rgrid(static_cast<unsigned>(((units + 3) / 4 + kXcdCount - 1) / kXcdCount * kXcdCount));
   if (g.bf16)
     hipLaunchKernelGGL(elsaa_k4_race_reduce<uint16_t>, rgrid, dim3(256), 0, stream,
                        static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, g.N, g.D, g.L, g.P,

@@ -118,3 +118,34 @@ def test_exact_ties_and_extreme_magnitudes(scale):
     np.testing.assert_array_equal(g["race_code_k"], r.race_code_k)
     np.testing.assert_array_equal(g["perm_q"], r.perm_q)
     np.testing.assert_array_equal(g["perm_k"], r.perm_k)
+
+
+def test_exact_ties_wide_exponent_span():
+    """Exact ties whose nonzero products span far more than 39 binary exponents:
+    rows are cancelling pairs (c, -c) with c = small integer x 2^e, e in [-30, 30],
+    and half of the planes weight both members of each pair equally, so their
+    projections are exactly zero with products from 2^-60 to 2^60."""
+    wl = workloads.workload("small-bf16", B=1, H=2, N=2048, race_tables=4, race_bits=5)
+    inp = workloads.generate(wl, 31)
+    rng = np.random.default_rng(31)
+    d = wl.d
+
+    def paired(shape):
+        c = rng.integers(1, 128, size=shape[:-1] + (d // 2,)) * rng.choice([-1, 1], size=shape[:-1] + (d // 2,))
+        c = c * np.exp2(rng.integers(-30, 31, size=c.shape))
+        out = np.empty(shape)
+        out[..., 0::2], out[..., 1::2] = c, -c
+        return out
+
+    q, k = paired(inp.q.shape), paired(inp.k.shape)
+    planes = rng.choice([-1.0, 1.0], size=inp.hyperplanes.shape)
+    planes[0::2, 1::2] = planes[0::2, 0::2]  # even planes: equal weights within each pair
+    to_bits = lambda a: workloads.round_to_bf16_bits(a.astype(np.float64))
+    inp.bits["q"], inp.bits["k"], inp.bits["hyperplanes"] = to_bits(q), to_bits(k), to_bits(planes)
+    inp.q, inp.k, inp.hyperplanes = q.astype(np.float32), k.astype(np.float32), planes.astype(np.float32)
+    dots = inp.q.astype(np.float64).reshape(-1, d) @ planes.T
+    assert (dots[:, 0::2] == 0).all() and (dots[:, 1::2] != 0).mean() > 0.99
+    g = run_gpu(inp)
+    r = run_oracle(inp)
+    for key in ("sort_code_q", "sort_code_k", "race_code_q", "race_code_k", "perm_q", "perm_k"):
+        np.testing.assert_array_equal(g[key], getattr(r, key), err_msg=key)
