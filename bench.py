@@ -39,6 +39,7 @@ METRIC = "ELSAA fwd tokens/sec at N=16K & 32K (1 GPU); % MFMA / % HBM roofline p
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
+CALIB_BYTES = 256 << 20
 KERNEL_FILES = {
     "hash": "k1_hash.hip", "sort": "k2_sort.hip", "race_build": "k4_race_build.hip",
     "chunk_attention": "k3_chunk_attn.hip", "fuse": "k5_fuse.hip",
@@ -139,6 +140,8 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="(b, h) heads the oracle runs on (0 = enough for ~10 s)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 256 MiB device copy first (HBM counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -155,6 +158,13 @@ def main(argv=None):
 
     dev = torch.device("cuda", 0)
     ev = HipEvents()
+    if args.copy_calibration:
+        # a copy kernel of known size: 256 MiB read + 256 MiB written
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def time_workload(name: str, steps: int, warmup: int):
         wl = workloads.WORKLOADS[name]

@@ -87,8 +87,11 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   t.perm = reinterpret_cast<int32_t *>(take(2 * rows * 4));
   t.flags = reinterpret_cast<uint8_t *>(take(2 * rows));
   t.hist = reinterpret_cast<uint32_t *>(take(2 * static_cast<size_t>(g.BH) * g.nb_sort * g.sort_tiles * 4));
-  t.rperm = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * g.N * 4));
-  t.rstart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
+  // per-table key permutation and run starts: only the two-kernel RACE build uses them
+  const bool fused = elsaa::race_fused_tile(g) > 0;
+  t.rperm = reinterpret_cast<int32_t *>(take(fused ? 0 : static_cast<size_t>(g.BH) * g.L * g.N * 4));
+  t.rstart = reinterpret_cast<int32_t *>(
+      take(fused ? 0 : static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
   t.tsum = reinterpret_cast<float *>(take(static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * 4));
   t.tcnt = reinterpret_cast<float *>(take(static_cast<size_t>(g.BH) * g.L * g.nb_race * 4));
   t.o_s = take(rows * g.D * es);

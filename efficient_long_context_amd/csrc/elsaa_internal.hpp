@@ -45,7 +45,11 @@ struct Buffers {
 };
 
 constexpr int kSortTile = 2048;         // elements per sort tile (4 waves x 8 rounds x 64)
-constexpr int kRaceLdsBytes = 64 * 1024;  // LDS budget of one RACE-build table slice
+constexpr size_t kFusedLdsMax = 160 * 1024;  // LDS of one gfx950 workgroup
+
+// Tile size (keys) of the single-kernel RACE build, or 0 when one (b, h, table)
+// table does not fit in LDS and the sort + reduce pair is used instead.
+int race_fused_tile(const Geometry &g);
 
 // Launchers (each enqueues on `stream`, returns hipError_t of the launch).
 hipError_t launch_hash(const Geometry &g, const void *q, const void *k, const void *planes,

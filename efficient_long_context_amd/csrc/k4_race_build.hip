@@ -182,15 +182,326 @@ __global__ __launch_bounds__(256) void elsaa_k4_race_reduce(
   }
 }
 
+// --------------------------------------------------------------------- fused --
+// One workgroup per (b, h, table) when the whole table fits in LDS: the table
+// accumulates in LDS while the keys are taken in tiles of up to S keys.  Per
+// tile: a stable counting sort of the tile's codes into an LDS permutation
+// (per-wave integer histograms, a bucket-major scan, ballot ranks), then every
+// wave sums a balanced share of the sorted positions, bucket by bucket, in
+// registers (16-byte lane pieces, several rows per load instruction, one batch
+// in flight while the previous one is added) and adds each finished bucket's
+// row into the LDS table, which only that wave touches in this tile.  The permutation never
+// leaves the chip; value rows are read once per table.
+constexpr int kFusedWaves = 16;
+
+// A lane's 16-byte piece of a value row: kLanesPerRow lanes share a row, so
+// one load instruction fetches kRowsPerLoad rows (8 for bfloat16 rows of 64
+// columns), and a lane accumulates kCols columns of its row group.
+template <typename VT, int D> struct Piece {
+  static constexpr int kCols = 16 / static_cast<int>(sizeof(VT));
+  static constexpr int kLanesPerRow = D / kCols;
+  static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+  static __device__ __forceinline__ u32x4 load(const VT *row, int cc) {
+    return *reinterpret_cast<const u32x4 *>(row + cc * kCols);
+  }
+  static __device__ __forceinline__ void add(u32x4 r, float *a) {
+    if constexpr (sizeof(VT) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[2 * e] += __uint_as_float(r[e] << 16);
+        a[2 * e + 1] += __uint_as_float(r[e] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] += __uint_as_float(r[e]);
+    }
+  }
+};
+
+// Exclusive prefix sum of one value per thread over a workgroup of
+// kFusedWaves waves; `tmp` holds kFusedWaves words of LDS.  Two barriers.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *tmp, int lane,
+                                                         int wave) {
+  uint32_t inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += tmp[w];
+  __syncthreads();  // tmp may be reused after this
+  return before + inc - x;
+}
+
+template <typename CT, typename VT, int D>
+__global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
+    const CT *__restrict__ kcodes, const VT *__restrict__ v, int N, int L, int P, int S,
+    long long units, float *__restrict__ tsum, float *__restrict__ tcnt) {
+  using PC = Piece<VT, D>;
+  constexpr int W = kFusedWaves, kCols = PC::kCols, kLPR = PC::kLanesPerRow;
+  constexpr int kRPI = PC::kRowsPerLoad;
+  constexpr int kI = 8;              // load instructions per batch
+  constexpr int kBP = kI * kRPI;     // positions per batch
+  extern __shared__ uint32_t lds[];
+  const int nb = 1 << P;
+  float *acc = reinterpret_cast<float *>(lds);  // [nb][D]
+  uint32_t *cnt = lds + nb * D;                 // [W][nb] counts, then running offsets
+  uint32_t *bst = cnt + W * nb;                 // [nb + 1] tile-local run starts
+  uint32_t *tot = bst + nb + 1;                 // [nb] keys per bucket over all tiles
+  uint32_t *part = tot + nb;                    // [W * 64] scan
+  uint16_t *lperm = reinterpret_cast<uint16_t *>(part + W * 64);  // [S] tile-local key index
+
+  const long long tu = xcd_logical_block(blockIdx.x, gridDim.x);  // (b, h) * L + table
+  if (tu >= units) return;  // whole workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long bh = tu / L;
+  const int l = static_cast<int>(tu % L);
+  const CT *c = kcodes + bh * N * static_cast<long long>(L) + l;  // code of key j at c[j * L]
+  const VT *vb = v + bh * N * static_cast<long long>(D);
+
+  for (int i = tid; i < nb * D; i += W * 64) acc[i] = 0.0f;
+  for (int i = tid; i < nb; i += W * 64) tot[i] = 0u;
+
+  for (int t0 = 0; t0 < N; t0 += S) {
+    const int M = N - t0 < S ? N - t0 : S;
+    const int chunk = ((M + W - 1) / W + 63) / 64 * 64;
+    const int j_begin = t0 + (wave * chunk < M ? wave * chunk : M);
+    const int j_end = t0 + ((wave + 1) * chunk < M ? (wave + 1) * chunk : M);
+    for (int i = tid; i < W * nb; i += W * 64) cnt[i] = 0u;
+    __syncthreads();
+
+    uint32_t *wc = cnt + wave * nb;
+    // eight rounds of codes per call; loads are clamped, not skipped, so they
+    // all issue before the first wait
+    auto load_codes = [&](int j0, uint32_t (&code)[8]) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j0 + q * 64 + lane;
+        const uint32_t cv = static_cast<uint32_t>(c[static_cast<long long>(j < j_end ? j : j_end - 1) * L]);
+        code[q] = j < j_end ? cv : 0xffffffffu;
+      }
+    };
+    for (int j0 = j_begin; j0 < j_end; j0 += 512) {
+      uint32_t code[8];
+      load_codes(j0, code);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (code[q] != 0xffffffffu) atomicAdd(&wc[code[q]], 1u);
+    }
+    __syncthreads();
+
+    // bucket-major exclusive scan of the [bucket][wave] counts
+    {
+      const int nthreads = W * 64;
+      const int per = (nb + nthreads - 1) / nthreads;
+      const int b_lo = tid * per < nb ? tid * per : nb;
+      const int b_hi = b_lo + per < nb ? b_lo + per : nb;
+      uint32_t sum = 0;
+      for (int b = b_lo; b < b_hi; ++b)
+        for (int w = 0; w < W; ++w) sum += cnt[w * nb + b];
+      uint32_t run = block_exclusive_scan(sum, part, lane, wave);
+      for (int b = b_lo; b < b_hi; ++b) {
+        bst[b] = run;
+        const uint32_t r0 = run;
+        for (int w = 0; w < W; ++w) {
+          const uint32_t t = cnt[w * nb + b];
+          cnt[w * nb + b] = run;
+          run += t;
+        }
+        tot[b] += run - r0;
+      }
+      if (tid == 0) bst[nb] = static_cast<uint32_t>(M);
+    }
+    __syncthreads();
+
+    // stable ranks: each wave walks its chunk in order, 64 keys per round
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    for (int j8 = j_begin; j8 < j_end; j8 += 512) {
+      uint32_t codes8[8];
+      load_codes(j8, codes8);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j8 + q * 64 + lane;
+        const bool valid = j < j_end;
+        const uint32_t code = valid ? codes8[q] : 0u;
+        unsigned long long mask = __ballot(valid);
+        for (int bit = 0; bit < P; ++bit) {
+          const bool set = (code >> bit) & 1u;
+          const unsigned long long bb = __ballot(set);
+          mask &= set ? bb : ~bb;
+        }
+        const int rank = __popcll(mask & lt);
+        const int leader = __ffsll(static_cast<long long>(mask)) - 1;
+        uint32_t before = 0;
+        if (valid && lane == leader) {
+          before = wc[code];
+          wc[code] = before + static_cast<uint32_t>(__popcll(mask));
+        }
+        before = __shfl(before, leader < 0 ? 0 : leader);
+        if (valid) lperm[before + rank] = static_cast<uint16_t>(j - t0);
+        // the leader's counter update must land before the next round reads it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      }
+    }
+    __syncthreads();
+
+    // buckets owned: those whose run starts in [lo, hi); the last wave also
+    // owns the empty buckets that start at M
+    const int lo = static_cast<int>(static_cast<long long>(M) * wave / W);
+    const int hi = wave == W - 1 ? M + 1 : static_cast<int>(static_cast<long long>(M) * (wave + 1) / W);
+    int b0 = nb, b1 = nb;
+    for (int bb = 0; bb < nb; bb += 64) {
+      const int b = bb + lane;
+      const int st = b < nb ? static_cast<int>(bst[b]) : M + 1;
+      const unsigned long long ge_lo = __ballot(b < nb && st >= lo);
+      const unsigned long long ge_hi = __ballot(b < nb && st >= hi);
+      if (b0 == nb && ge_lo) b0 = bb + __builtin_ctzll(ge_lo);
+      if (b1 == nb && ge_hi) b1 = bb + __builtin_ctzll(ge_hi);
+    }
+    const int p_lo = static_cast<int>(bst[b0]), p_hi = static_cast<int>(bst[b1]);
+
+    if (p_lo < p_hi) {
+      const int rg = lane / kLPR, cc = lane % kLPR;  // row group, column piece
+      int b = b0;
+      int bend = __builtin_amdgcn_readfirstlane(static_cast<int>(bst[b0 + 1]));
+      float a[kCols];
+#pragma unroll
+      for (int k = 0; k < kCols; ++k) a[k] = 0.0f;
+      // Bucket b is complete: sum the row groups' partials (butterfly over the
+      // lanes holding the same columns), then lane (rg, cc) adds columns
+      // cc * kCols + rg + kRPI m of the bucket row into the LDS table.
+      auto flush = [&]() {
+#pragma unroll
+        for (int k = 0; k < kCols; ++k) {
+#pragma unroll
+          for (int off = kLPR; off < 64; off <<= 1) a[k] += __shfl_xor(a[k], off);
+        }
+#pragma unroll
+        for (int m = 0; m < kCols / kRPI; ++m) {
+          float val = 0.0f;
+#pragma unroll
+          for (int k = 0; k < kCols; ++k) val = (k == rg + kRPI * m) ? a[k] : val;
+          acc[b * D + cc * kCols + rg + kRPI * m] += val;
+        }
+#pragma unroll
+        for (int k = 0; k < kCols; ++k) a[k] = 0.0f;
+      };
+      auto load_batch = [&](int pbase, u32x4 (&r)[kI]) {
+        int jl[kI];
+#pragma unroll
+        for (int i = 0; i < kI; ++i) {
+          const int pos = pbase + i * kRPI + rg;
+          jl[i] = lperm[pos < p_hi ? pos : p_hi - 1];  // clamped past the end
+        }
+#pragma unroll
+        for (int i = 0; i < kI; ++i) r[i] = PC::load(vb + (static_cast<long long>(t0) + jl[i]) * D, cc);
+      };
+      // rows of positions [pbase, pbase + kBP): lane's row is position p + rg
+      auto consume = [&](int pbase, const u32x4 (&r)[kI]) {
+#pragma unroll
+        for (int i = 0; i < kI; ++i) {
+          const int p = pbase + i * kRPI;
+          if (p >= p_hi) return;
+          const int pe = p + kRPI < p_hi ? p + kRPI : p_hi;
+          const int my = p + rg;
+          if (pe < bend) {  // the whole group lies inside bucket b
+            if (my < pe) PC::add(r[i], a);
+          } else {
+            int cur = p;
+            while (cur < pe) {
+              const int stop = pe < bend ? pe : bend;
+              if (my >= cur && my < stop) PC::add(r[i], a);
+              cur = stop;
+              if (cur == bend) {
+                flush();
+                ++b;
+                bend = __builtin_amdgcn_readfirstlane(static_cast<int>(bst[b + 1]));
+              }
+            }
+          }
+        }
+      };
+      u32x4 ra[kI], rb[kI];
+      load_batch(p_lo, ra);
+      for (int pc = p_lo; pc < p_hi; pc += 2 * kBP) {
+        load_batch(pc + kBP, rb);
+        consume(pc, ra);
+        load_batch(pc + 2 * kBP, ra);
+        consume(pc + kBP, rb);
+      }
+    }
+    __syncthreads();
+  }
+
+  float *ts = tsum + tu * nb * static_cast<long long>(D);
+  for (int i = tid; i < nb * D; i += W * 64) ts[i] = acc[i];
+  for (int i = tid; i < nb; i += W * 64) tcnt[tu * nb + i] = static_cast<float>(tot[i]);
+}
+
+// LDS bytes of the fused kernel for tile size S (0 if the table does not fit).
+size_t fused_lds_bytes(int nb, int D, int S) {
+  return (static_cast<size_t>(nb) * D + static_cast<size_t>(kFusedWaves) * nb + 2 * nb + 1 +
+          kFusedWaves * 64) * 4 + static_cast<size_t>(S) * 2;
+}
+
+template <typename CT, typename VT>
+void launch_fused(const Geometry &g, const void *rk, const void *v, int S, size_t lds,
+                  const Buffers &buf, hipStream_t stream) {
+  const long long units = static_cast<long long>(g.BH) * g.L;
+  const dim3 grid(static_cast<unsigned>((units + kXcdCount - 1) / kXcdCount * kXcdCount));
+  const dim3 block(kFusedWaves * 64);
+  if (g.D == 64)
+    hipLaunchKernelGGL((elsaa_k4_race_fused<CT, VT, 64>), grid, block, lds, stream,
+                       static_cast<const CT *>(rk), static_cast<const VT *>(v), g.N, g.L, g.P, S,
+                       units, buf.tsum, buf.tcnt);
+  else
+    hipLaunchKernelGGL((elsaa_k4_race_fused<CT, VT, 128>), grid, block, lds, stream,
+                       static_cast<const CT *>(rk), static_cast<const VT *>(v), g.N, g.L, g.P, S,
+                       units, buf.tsum, buf.tcnt);
+}
+
 }  // namespace
+
+#ifndef ELSAA_FUSED_TILE_MAX
+#define ELSAA_FUSED_TILE_MAX 32768
+#endif
+
+int race_fused_tile(const Geometry &g) {
+  const size_t fixed = fused_lds_bytes(g.nb_race, g.D, 0);
+  if (fixed + 2 * 1024 > kFusedLdsMax) return 0;
+  // Tiles bound the value rows the concurrent workgroups of one XCD gather
+  // from (S rows of each (b, h)), so they stay in its L2; tile-local key
+  // indices are 16-bit.
+  int smax = static_cast<int>((kFusedLdsMax - fixed) / 2 / 1024 * 1024);
+  smax = smax < ELSAA_FUSED_TILE_MAX ? smax : ELSAA_FUSED_TILE_MAX;
+  const int n64 = (g.N + 63) / 64 * 64;
+  return n64 < smax ? n64 : smax;
+}
 
 hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
                              hipStream_t stream) {
   const int nb = g.nb_race;
+  const void *rk = static_cast<const char *>(buf.rcode) + static_cast<size_t>(g.rows) * g.L * g.rcb;
+  const int S = race_fused_tile(g);
+  if (S > 0) {
+    const size_t lds = fused_lds_bytes(nb, g.D, S);
+    if (g.rcb == 1) {
+      if (g.bf16) launch_fused<uint8_t, uint16_t>(g, rk, v, S, lds, buf, stream);
+      else launch_fused<uint8_t, float>(g, rk, v, S, lds, buf, stream);
+    } else {
+      if (g.bf16) launch_fused<uint16_t, uint16_t>(g, rk, v, S, lds, buf, stream);
+      else launch_fused<uint16_t, float>(g, rk, v, S, lds, buf, stream);
+    }
+    return hipGetLastError();
+  }
   int waves = 16384 / nb;  // LDS counts: waves * nb * 4 bytes <= 64 KB
   waves = waves < 1 ? 1 : (waves > kSortWavesMax ? kSortWavesMax : waves);
   const int chunk = ((g.N + waves - 1) / waves + 63) / 64 * 64;
-  const void *rk = static_cast<const char *>(buf.rcode) + static_cast<size_t>(g.rows) * g.L * g.rcb;
   const dim3 sgrid(g.L, g.BH);
   const size_t slds = static_cast<size_t>(waves) * nb * 4;
   if (g.rcb == 1)
