@@ -94,6 +94,10 @@ template <> struct Elem<float> {
     out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
   }
   static __device__ __forceinline__ float store_val(float f) { return f; }
+  // four consecutive values in one store; p must be 16-byte aligned
+  static __device__ __forceinline__ void store4(float *p, const float *v) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
 };
 template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ float load(const uint16_t *p) { return bf16_bits_to_f32(*p); }
@@ -104,6 +108,12 @@ template <> struct Elem<uint16_t> {
     out[2] = __uint_as_float(x.y << 16); out[3] = __uint_as_float(x.y & 0xffff0000u);
   }
   static __device__ __forceinline__ uint16_t store_val(float f) { return f32_to_bf16_bits(f); }
+  // four consecutive values in one store; p must be 8-byte aligned
+  static __device__ __forceinline__ void store4(uint16_t *p, const float *v) {
+    const uint32_t a = f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+    const uint32_t b = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+    *reinterpret_cast<uint2 *>(p) = make_uint2(a, b);
+  }
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).

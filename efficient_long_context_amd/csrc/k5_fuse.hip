@@ -17,7 +17,10 @@
 //
 // Layout: d/4 lanes per query, 4 value columns per lane (16-byte table reads),
 // the gate dot products split over the same lanes and reduced with xor
-// shuffles inside the query's lane group.
+// shuffles inside the query's lane group.  Each wave streams a contiguous run
+// of queries, loading the next step's RACE codes while the current step's
+// table rows are gathered; consecutive waves run on one XCD, so its L2 holds
+// the tables of the few (b, h) it serves.
 #include <type_traits>
 
 #include "elsaa_internal.hpp"
@@ -25,140 +28,224 @@
 namespace elsaa {
 namespace {
 
+// Waves the fuse is spread over (each streams a contiguous run of queries).
+#ifndef ELSAA_FUSE_WAVES
+#define ELSAA_FUSE_WAVES 65536
+#endif
+constexpr long long kFuseWaves = ELSAA_FUSE_WAVES;
+
 struct AuxOut {
   float *z_lr, *alpha, *g_s, *g_lr, *o_lr;
 };
 
-template <int D, typename VT, typename CT>
+// LC = number of RACE tables when it is 8 or 16 (codes of a query arrive in
+// one 16- or 32-byte load and every lane holds all of them); LC = 0 takes any
+// L with one code load per table.
+template <int D, typename VT, typename CT, int LC>
 __global__ __launch_bounds__(256) void elsaa_k5_fuse(
     const VT *__restrict__ o_s, const float *__restrict__ lse, const CT *__restrict__ qcodes,
     const float *__restrict__ tsum, const float *__restrict__ tcnt, const VT *__restrict__ x_gate,
-    const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int L,
-    int P, int DG, float lambda, long long total, VT *__restrict__ out, AuxOut aux) {
-  constexpr int kLanesPerQuery = D / 4;
-  constexpr int kQueriesPerBlock = 256 / kLanesPerQuery;
-  const int sub = threadIdx.x % kLanesPerQuery;
-  const long long gq = static_cast<long long>(blockIdx.x) * kQueriesPerBlock + threadIdx.x / kLanesPerQuery;
-  const bool valid = gq < total;
-  const long long qi = valid ? gq : 0;
-  const long long bh = qi / N;
-  const int i = static_cast<int>(qi % N);
-  const int h = static_cast<int>(bh % H);
-  const long long b = bh / H;
+    const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int L_rt,
+    int P, int DG, float lambda, long long total, long long qpw, VT *__restrict__ out, AuxOut aux) {
+  constexpr int kLPQ = D / 4;      // lanes per query, 4 value columns each
+  constexpr int kQPS = 64 / kLPQ;  // queries per wave step
+  constexpr int kCodeWords = LC * static_cast<int>(sizeof(CT)) / 4;  // 32-bit words of codes
+  const int L = LC ? LC : L_rt;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % kLPQ;
+  const long long wv = xcd_logical_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
+  const long long q_begin = wv * qpw;
+  const long long q_end = q_begin + qpw < total ? q_begin + qpw : total;
+  if (q_begin >= q_end) return;  // whole wave
   const int nb = 1 << P;
 
-  // Every independent load is issued before the first use: RACE rows (in
-  // groups of 16 tables), the sparse output, its LSE and the gate inputs.
-  // Summing as loads arrive would serialise their memory latencies.
-  const CT *qc = qcodes + qi * L;
-  const float *ts = tsum + bh * L * nb * static_cast<long long>(D) + sub * 4;
-  const float *tc = tcnt + bh * L * nb;
-  const VT *os = o_s + qi * D + sub * 4;
-  float osv[4];
-  Elem<VT>::load4(os, osv);
-  const float lse_i = lse[qi];
-
-  float z = 0.0f;
-  f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto gather = [&](auto group, int l0) {
-    constexpr int G = decltype(group)::value;
-    long long row[G];
+  // all LC codes of the lane's query as kCodeWords 32-bit words (8, 16 or 32
+  // bytes; clamped queries are computed, not stored)
+  constexpr int kCW = kCodeWords > 0 ? kCodeWords : 1;
+  uint32_t cw[kCW];
+  auto load_codes = [&](long long q0, uint32_t (&w)[kCW]) {
+    if constexpr (LC > 0) {
+      long long q = q0 + lane / kLPQ;
+      q = q < q_end ? q : q_end - 1;
+      const CT *src = qcodes + q * LC;
+      if constexpr (kCodeWords % 4 == 0) {
 #pragma unroll
-    for (int e = 0; e < G; ++e) {
-      const int l = l0 + e < L ? l0 + e : L - 1;  // clamped: extra rows are loaded, not added
-      row[e] = static_cast<long long>(l) * nb + qc[l];
-    }
-    f32x4 t[G];
-    float c[G];
+        for (int k = 0; k < kCodeWords / 4; ++k) {
+          const u32x4 v = reinterpret_cast<const u32x4 *>(src)[k];
 #pragma unroll
-    for (int e = 0; e < G; ++e) {
-      t[e] = *reinterpret_cast<const f32x4 *>(ts + row[e] * D);
-      c[e] = tc[row[e]];
-    }
-#pragma unroll
-    for (int e = 0; e < G; ++e) {
-      if (l0 + e < L) {
-        num += t[e];
-        z += c[e];
+          for (int e = 0; e < 4; ++e) w[4 * k + e] = v[e];
+        }
+      } else {
+        static_assert(kCodeWords == 2, "8 code bytes per query");
+        const uint2 v = *reinterpret_cast<const uint2 *>(src);
+        w[0] = v.x;
+        w[1] = v.y;
       }
     }
   };
-  // no loop for L <= 16: keeps the compiler from draining loads at a loop header
-  if (L <= 4) gather(std::integral_constant<int, 4>(), 0);
-  else if (L <= 8) gather(std::integral_constant<int, 8>(), 0);
-  else if (L <= 16) gather(std::integral_constant<int, 16>(), 0);
-  else for (int l0 = 0; l0 < L; l0 += 16) gather(std::integral_constant<int, 16>(), l0);
+  auto code_of = [&](int l) -> int {  // l known at compile time after unrolling
+    constexpr int cb = static_cast<int>(sizeof(CT));
+    const uint32_t word = cw[l * cb / 4];
+    return static_cast<int>((word >> ((l * cb % 4) * 8)) & (cb == 1 ? 0xffu : 0xffffu));
+  };
+  load_codes(q_begin, cw);
 
-  // gates: with d_gate = 4 x (lanes per query) each lane takes 4 consecutive
-  // inputs in one load; any other width takes the strided loop
-  const VT *xg = x_gate + (b * N + i) * DG;
-  const float *w0 = gate_w + static_cast<long long>(h) * DG;
-  const float *w1 = gate_w + static_cast<long long>(H + h) * DG;
-  float a0 = 0.0f, a1 = 0.0f;
-  if (DG == 4 * kLanesPerQuery) {
-    float xv[4];
-    Elem<VT>::load4(xg + sub * 4, xv);
-    const f32x4 wa = *reinterpret_cast<const f32x4 *>(w0 + sub * 4);
-    const f32x4 wb = *reinterpret_cast<const f32x4 *>(w1 + sub * 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a0 = __builtin_fmaf(xv[e], wa[e], a0);
-      a1 = __builtin_fmaf(xv[e], wb[e], a1);
+  // (b, h, i) of the step's first query, advanced once per step: N is a
+  // multiple of 64 (a multiple of the chunk) and runs start at multiples of
+  // kQPS, so the queries of a step share (b, h) and no division is needed
+  long long bh = q_begin / N;
+  int i0 = static_cast<int>(q_begin - bh * N);
+  int h = static_cast<int>(bh % H);
+  long long b = bh / H;
+
+  for (long long q0 = q_begin; q0 < q_end; q0 += kQPS) {
+    const long long qi = q0 + lane / kLPQ;
+    const bool valid = qi < q_end;  // always true for these sizes; kept as a guard
+    const int i = i0 + lane / kLPQ;
+    const float *ts = tsum + bh * L * nb * static_cast<long long>(D) + sub * 4;
+    const float *tc = tcnt + bh * L * nb;
+
+    // the sparse output, its LSE and the gate inputs load while the tables are gathered
+    float osv[4];
+    Elem<VT>::load4(o_s + qi * D + sub * 4, osv);
+    const float lse_i = lse[qi];
+    const VT *xg = x_gate + (b * N + i) * DG;
+    const float *w0 = gate_w + static_cast<long long>(h) * DG;
+    const float *w1 = gate_w + static_cast<long long>(H + h) * DG;
+    const bool gate_fast = DG == 4 * kLPQ;
+    float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 wa = {0.0f, 0.0f, 0.0f, 0.0f}, wb = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (gate_fast) {
+      Elem<VT>::load4(xg + sub * 4, xv);
+      wa = *reinterpret_cast<const f32x4 *>(w0 + sub * 4);
+      wb = *reinterpret_cast<const f32x4 *>(w1 + sub * 4);
     }
-  } else {
-    for (int e = sub; e < DG; e += kLanesPerQuery) {
-      const float xv = Elem<VT>::load(xg + e);
-      a0 = __builtin_fmaf(xv, w0[e], a0);
-      a1 = __builtin_fmaf(xv, w1[e], a1);
+
+    f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+    float z = 0.0f;
+    if constexpr (LC > 0) {
+      // lane sub < LC adds the count of table sub; the group sums them below
+      if (sub < LC) {
+        int c = 0;
+#pragma unroll
+        for (int l = 0; l < LC; ++l) c = sub == l ? code_of(l) : c;
+        z = tc[static_cast<long long>(sub) * nb + c];
+      }
+      f32x4 t[LC];
+#pragma unroll
+      for (int l = 0; l < LC; ++l)
+        t[l] = *reinterpret_cast<const f32x4 *>(ts + (static_cast<long long>(l) * nb + code_of(l)) * D);
+      long long qn = q0 + kQPS < q_end ? q0 + kQPS : q0;
+      load_codes(qn, cw);  // next step's codes, in flight while this step finishes
+#pragma unroll
+      for (int l = 0; l < LC; ++l) num += t[l];
+    } else {
+      const CT *qc = qcodes + qi * L;
+      for (int l0 = 0; l0 < L; l0 += 8) {
+        f32x4 t[8];
+        float cnt[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int l = l0 + e < L ? l0 + e : L - 1;  // clamped: extra rows are loaded, not added
+          const long long row = static_cast<long long>(l) * nb + qc[l];
+          t[e] = *reinterpret_cast<const f32x4 *>(ts + row * D);
+          cnt[e] = tc[row];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (l0 + e < L) {
+            num += t[e];
+            if (sub == 0) z += cnt[e];
+          }
+      }
+    }
+
+    // gates: with d_gate = 4 x (lanes per query) each lane takes 4 consecutive
+    // inputs in one load; any other width takes the strided loop
+    float a0 = 0.0f, a1 = 0.0f;
+    if (gate_fast) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a0 = __builtin_fmaf(xv[e], wa[e], a0);
+        a1 = __builtin_fmaf(xv[e], wb[e], a1);
+      }
+    } else {
+      for (int e = sub; e < DG; e += kLPQ) {
+        const float x = Elem<VT>::load(xg + e);
+        a0 = __builtin_fmaf(x, w0[e], a0);
+        a1 = __builtin_fmaf(x, w1[e], a1);
+      }
+    }
+#pragma unroll
+    for (int off = kLPQ / 2; off > 0; off >>= 1) {
+      a0 += __shfl_xor(a0, off);
+      a1 += __shfl_xor(a1, off);
+      z += __shfl_xor(z, off);
+    }
+    const float g_s = 1.0f / (1.0f + __expf(-(a0 + gate_b[h])));
+    const float g_lr = 1.0f / (1.0f + __expf(-(a1 + gate_b[H + h])));
+
+    const float z_lr = z / static_cast<float>(L);
+    f32x4 o_lr = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (z > 0.0f) o_lr = num * (1.0f / z);  // (num / L) / (z / L)
+
+    const float mass_lr = lambda * z_lr;
+    const float alpha = mass_lr > 0.0f ? 1.0f / (1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
+
+    const float ws = g_s * alpha;
+    if (valid) {
+      float yv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yv[e] = __builtin_fmaf(ws, osv[e], g_lr * o_lr[e]);
+      Elem<VT>::store4(out + qi * D + sub * 4, yv);
+      if (aux.o_lr) *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * 4) = o_lr;
+      if (sub == 0) {
+        if (aux.z_lr) aux.z_lr[qi] = z_lr;
+        if (aux.alpha) aux.alpha[qi] = alpha;
+        if (aux.g_s) aux.g_s[qi] = g_s;
+        if (aux.g_lr) aux.g_lr[qi] = g_lr;
+      }
+    }
+    i0 += kQPS;
+    if (i0 == N) {
+      i0 = 0;
+      ++bh;
+      if (++h == H) {
+        h = 0;
+        ++b;
+      }
     }
   }
-#pragma unroll
-  for (int off = kLanesPerQuery / 2; off > 0; off >>= 1) {
-    a0 += __shfl_xor(a0, off);
-    a1 += __shfl_xor(a1, off);
-  }
-  const float g_s = 1.0f / (1.0f + __expf(-(a0 + gate_b[h])));
-  const float g_lr = 1.0f / (1.0f + __expf(-(a1 + gate_b[H + h])));
+}
 
-  const float z_lr = z / static_cast<float>(L);
-  f32x4 o_lr = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (z > 0.0f) o_lr = num * (1.0f / z);  // (num / L) / (z / L)
-
-  const float mass_lr = lambda * z_lr;
-  const float alpha = mass_lr > 0.0f ? 1.0f / (1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
-
-  VT *dst = out + qi * D + sub * 4;
-  const float ws = g_s * alpha;
-  if (valid) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = Elem<VT>::store_val(__builtin_fmaf(ws, osv[e], g_lr * o_lr[e]));
-    if (aux.o_lr) *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * 4) = o_lr;
-    if (sub == 0) {
-      if (aux.z_lr) aux.z_lr[qi] = z_lr;
-      if (aux.alpha) aux.alpha[qi] = alpha;
-      if (aux.g_s) aux.g_s[qi] = g_s;
-      if (aux.g_lr) aux.g_lr[qi] = g_lr;
-    }
-  }
+template <int D, typename VT, typename CT, int LC>
+void launch_l(const Geometry &g, const void *x_gate, const float *gate_w, const float *gate_b,
+              const Buffers &buf, const AuxOut &aux, void *out, hipStream_t stream) {
+  constexpr int kQPS = 64 / (D / 4);
+  const long long total = g.rows;
+  long long qpw = (total + kFuseWaves - 1) / kFuseWaves;  // each wave streams a run of queries
+  qpw = (qpw + kQPS - 1) / kQPS * kQPS;
+  const long long waves = (total + qpw - 1) / qpw;
+  const long long blocks = ((waves + 3) / 4 + kXcdCount - 1) / kXcdCount * kXcdCount;
+  hipLaunchKernelGGL((elsaa_k5_fuse<D, VT, CT, LC>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     stream, static_cast<const VT *>(buf.o_s), buf.lse,
+                     static_cast<const CT *>(buf.rcode), buf.tsum, buf.tcnt,
+                     static_cast<const VT *>(x_gate), gate_w, gate_b, g.H, g.N, g.L, g.P, g.DG,
+                     g.lambda, total, qpw, static_cast<VT *>(out), aux);
 }
 
 template <int D, typename VT>
 hipError_t launch_d(const Geometry &g, const void *x_gate, const float *gate_w, const float *gate_b,
                     const Buffers &buf, const AuxOut &aux, void *out, hipStream_t stream) {
-  constexpr int kQueriesPerBlock = 256 / (D / 4);
-  const long long total = g.rows;
-  const dim3 grid(static_cast<unsigned>((total + kQueriesPerBlock - 1) / kQueriesPerBlock));
-  const VT *os = static_cast<const VT *>(buf.o_s);
-  const VT *xg = static_cast<const VT *>(x_gate);
-  VT *o = static_cast<VT *>(out);
-  if (g.rcb == 1)
-    hipLaunchKernelGGL((elsaa_k5_fuse<D, VT, uint8_t>), grid, dim3(256), 0, stream, os, buf.lse,
-                       static_cast<const uint8_t *>(buf.rcode), buf.tsum, buf.tcnt, xg, gate_w,
-                       gate_b, g.H, g.N, g.L, g.P, g.DG, g.lambda, total, o, aux);
-  else
-    hipLaunchKernelGGL((elsaa_k5_fuse<D, VT, uint16_t>), grid, dim3(256), 0, stream, os, buf.lse,
-                       static_cast<const uint16_t *>(buf.rcode), buf.tsum, buf.tcnt, xg, gate_w,
-                       gate_b, g.H, g.N, g.L, g.P, g.DG, g.lambda, total, o, aux);
+  if (g.rcb == 1) {
+    if (g.L == 16) launch_l<D, VT, uint8_t, 16>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+    else if (g.L == 8) launch_l<D, VT, uint8_t, 8>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+    else launch_l<D, VT, uint8_t, 0>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+  } else {
+    if (g.L == 16) launch_l<D, VT, uint16_t, 16>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+    else if (g.L == 8) launch_l<D, VT, uint16_t, 8>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+    else launch_l<D, VT, uint16_t, 0>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+  }
   return hipGetLastError();
 }
 
