@@ -92,12 +92,17 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   t.rperm = reinterpret_cast<int32_t *>(take(fused ? 0 : static_cast<size_t>(g.BH) * g.L * g.N * 4));
   t.rstart = reinterpret_cast<int32_t *>(
       take(fused ? 0 : static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
-  t.tsum = reinterpret_cast<float *>(take(static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * 4));
+  t.tsum = take(static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * es);
   t.tcnt = reinterpret_cast<float *>(take(static_cast<size_t>(g.BH) * g.L * g.nb_race * 4));
   t.o_s = take(rows * g.D * es);
   t.lse = reinterpret_cast<float *>(take(rows * 4));
   if (b) *b = t;
   return off;
+}
+
+__global__ void widen_bf16(const uint16_t *__restrict__ src, float *__restrict__ dst, long long n) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) dst[i] = elsaa::bf16_bits_to_f32(src[i]);
 }
 
 hipError_t copy_aux(const elsaa::Geometry &g, const elsaa::Buffers &buf, const elsaa_aux_t *aux,
@@ -112,15 +117,21 @@ hipError_t copy_aux(const elsaa::Geometry &g, const elsaa::Buffers &buf, const e
       {aux->race_code_k, static_cast<const char *>(buf.rcode) + rows * g.L * g.rcb, rows * g.L * g.rcb},
       {aux->perm_q, buf.perm, rows * 4},
       {aux->perm_k, buf.perm + rows, rows * 4},
-      {aux->race_sum, buf.tsum, static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * 4},
+      {aux->race_sum, g.bf16 ? nullptr : buf.tsum, static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * 4},
       {aux->race_cnt, buf.tcnt, static_cast<size_t>(g.BH) * g.L * g.nb_race * 4},
       {aux->o_sparse, buf.o_s, rows * g.D * es},
       {aux->lse_s, buf.lse, rows * 4},
   };
   for (const Item &it : items) {
-    if (!it.dst) continue;
+    if (!it.dst || !it.src) continue;
     const hipError_t e = hipMemcpyAsync(it.dst, it.src, it.bytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
+  }
+  if (g.bf16 && aux->race_sum) {  // bfloat16 tables widen to the binary32 aux layout
+    const long long n = static_cast<long long>(g.BH) * g.L * g.nb_race * g.D;
+    hipLaunchKernelGGL(widen_bf16, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t *>(buf.tsum), aux->race_sum, n);
+    return hipGetLastError();
   }
   return hipSuccess;
 }

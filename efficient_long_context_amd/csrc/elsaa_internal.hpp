@@ -38,7 +38,7 @@ struct Buffers {
   uint32_t *hist;   // [2][BH][nb_sort][sort_tiles] -> exclusive offsets
   int32_t *rperm;   // [BH][L][N]     keys of each table sorted by bucket
   int32_t *rstart;  // [BH][L][nb_race + 1] run start of each bucket in rperm
-  float *tsum;      // [BH][L][nb_race][D]
+  void *tsum;       // [BH][L][nb_race][D] bucket sums, stored in dtype
   float *tcnt;      // [BH][L][nb_race]
   void *o_s;        // [BH][N][D] in dtype
   float *lse;       // [BH][N]
@@ -72,6 +72,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two binary32 values to packed bfloat16, round to nearest even (one
+// v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -83,6 +92,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (a wave-uniform address):
+// loads through it take a 32-bit per-lane offset plus a scalar offset, and
+// offsets at or past `bytes` read zero.  Word 3 is the gfx9 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
 }
 
 template <typename T> struct Elem;
@@ -110,9 +127,7 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ uint16_t store_val(float f) { return f32_to_bf16_bits(f); }
   // four consecutive values in one store; p must be 8-byte aligned
   static __device__ __forceinline__ void store4(uint16_t *p, const float *v) {
-    const uint32_t a = f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
-    const uint32_t b = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
-    *reinterpret_cast<uint2 *>(p) = make_uint2(a, b);
+    *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
 };
 

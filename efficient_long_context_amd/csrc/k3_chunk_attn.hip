@@ -27,13 +27,7 @@ namespace {
 
 constexpr int kKBlock = 64;
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);  // v_cvt_pk_bf16_f32 (RNE)
-  return __builtin_bit_cast(uint32_t, h);
-}
 
 template <int D, int QT>
 __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kSortWavesMax * 64) void elsaa_k4_race_sort(
 template <typename VT>
 __global__ __launch_bounds__(256) void elsaa_k4_race_reduce(
     const VT *__restrict__ v, const int32_t *__restrict__ perm, const int32_t *__restrict__ bstart,
-    int N, int D, int L, int P, int ncs, int parts, long long units, float *__restrict__ tsum,
+    int N, int D, int L, int P, int ncs, int parts, long long units, VT *__restrict__ tsum,
     float *__restrict__ tcnt) {
   const int lane = threadIdx.x & 63;
   // consecutive units (same (b, h), same value rows) run on one XCD's L2
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void elsaa_k4_race_reduce(
       for (int q = 0; q < kReduceBatch; ++q)
         if (q < n) acc += val[q];  // ascending key order within the bucket
     }
-    tsum[(tu * nb + b) * static_cast<long long>(D) + cs * 64 + lane] = acc;
+    tsum[(tu * nb + b) * static_cast<long long>(D) + cs * 64 + lane] = Elem<VT>::store_val(acc);
     if (cs == 0 && lane == 0) tcnt[tu * nb + b] = static_cast<float>(p1 - p0);
   }
 }
@@ -239,7 +239,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *t
 template <typename CT, typename VT, int D>
 __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
     const CT *__restrict__ kcodes, const VT *__restrict__ v, int N, int L, int P, int S,
-    long long units, float *__restrict__ tsum, float *__restrict__ tcnt) {
+    long long units, VT *__restrict__ tsum, float *__restrict__ tcnt) {
   using PC = Piece<VT, D>;
   constexpr int W = kFusedWaves, kCols = PC::kCols, kLPR = PC::kLanesPerRow;
   constexpr int kRPI = PC::kRowsPerLoad;
@@ -438,8 +438,9 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
     __syncthreads();
   }
 
-  float *ts = tsum + tu * nb * static_cast<long long>(D);
-  for (int i = tid; i < nb * D; i += W * 64) ts[i] = acc[i];
+  // the table leaves in the value dtype (sums were kept in binary32)
+  VT *ts = tsum + tu * nb * static_cast<long long>(D);
+  for (int i = 4 * tid; i < nb * D; i += 4 * W * 64) Elem<VT>::store4(ts + i, acc + i);
   for (int i = tid; i < nb; i += W * 64) tcnt[tu * nb + i] = static_cast<float>(tot[i]);
 }
 
@@ -458,11 +459,11 @@ void launch_fused(const Geometry &g, const void *rk, const void *v, int S, size_
   if (g.D == 64)
     hipLaunchKernelGGL((elsaa_k4_race_fused<CT, VT, 64>), grid, block, lds, stream,
                        static_cast<const CT *>(rk), static_cast<const VT *>(v), g.N, g.L, g.P, S,
-                       units, buf.tsum, buf.tcnt);
+                       units, static_cast<VT *>(buf.tsum), buf.tcnt);
   else
     hipLaunchKernelGGL((elsaa_k4_race_fused<CT, VT, 128>), grid, block, lds, stream,
                        static_cast<const CT *>(rk), static_cast<const VT *>(v), g.N, g.L, g.P, S,
-                       units, buf.tsum, buf.tcnt);
+                       units, static_cast<VT *>(buf.tsum), buf.tcnt);
 }
 
 }  // namespace
@@ -522,11 +523,11 @@ hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &bu
   if (g.bf16)
     hipLaunchKernelGGL(elsaa_k4_race_reduce<uint16_t>, rgrid, dim3(256), 0, stream,
                        static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, g.N, g.D, g.L, g.P,
-                       ncs, static_cast<int>(parts), units, buf.tsum, buf.tcnt);
+                       ncs, static_cast<int>(parts), units, static_cast<uint16_t *>(buf.tsum), buf.tcnt);
   else
     hipLaunchKernelGGL(elsaa_k4_race_reduce<float>, rgrid, dim3(256), 0, stream,
                        static_cast<const float *>(v), buf.rperm, buf.rstart, g.N, g.D, g.L, g.P, ncs,
-                       static_cast<int>(parts), units, buf.tsum, buf.tcnt);
+                       static_cast<int>(parts), units, static_cast<float *>(buf.tsum), buf.tcnt);
   return hipGetLastError();
 }
 

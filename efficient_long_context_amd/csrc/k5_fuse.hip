@@ -44,7 +44,7 @@ struct AuxOut {
 template <int D, typename VT, typename CT, int LC>
 __global__ __launch_bounds__(256) void elsaa_k5_fuse(
     const VT *__restrict__ o_s, const float *__restrict__ lse, const CT *__restrict__ qcodes,
-    const float *__restrict__ tsum, const float *__restrict__ tcnt, const VT *__restrict__ x_gate,
+    const VT *__restrict__ tsum, const float *__restrict__ tcnt, const VT *__restrict__ x_gate,
     const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int L_rt,
     int P, int DG, float lambda, long long total, long long qpw, VT *__restrict__ out, AuxOut aux) {
   constexpr int kLPQ = D / 4;      // lanes per query, 4 value columns each
@@ -53,7 +53,10 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
   const int L = LC ? LC : L_rt;
   const int lane = threadIdx.x & 63;
   const int sub = lane % kLPQ;
-  const long long wv = xcd_logical_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
+  // readfirstlane: the wave index is uniform, so everything derived from it
+  // (query run, (b, h), table bases) stays in scalar registers
+  const long long wv = xcd_logical_block(blockIdx.x, gridDim.x) * 4 +
+                       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const long long q_begin = wv * qpw;
   const long long q_end = q_begin + qpw < total ? q_begin + qpw : total;
   if (q_begin >= q_end) return;  // whole wave
@@ -102,7 +105,12 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
     const long long qi = q0 + lane / kLPQ;
     const bool valid = qi < q_end;  // always true for these sizes; kept as a guard
     const int i = i0 + lane / kLPQ;
-    const float *ts = tsum + bh * L * nb * static_cast<long long>(D) + sub * 4;
+    // tables of this (b, h) through buffer resources: 32-bit per-lane offsets
+    constexpr int kES = static_cast<int>(sizeof(VT));  // table element bytes
+    const __amdgpu_buffer_rsrc_t ts_rs =
+        make_rsrc(tsum + bh * L * nb * static_cast<long long>(D), static_cast<uint32_t>(L * nb * D * kES));
+    const __amdgpu_buffer_rsrc_t tc_rs = make_rsrc(tcnt + bh * L * nb, static_cast<uint32_t>(L * nb * 4));
+    const VT *ts = tsum + bh * L * nb * static_cast<long long>(D) + sub * 4;
     const float *tc = tcnt + bh * L * nb;
 
     // the sparse output, its LSE and the gate inputs load while the tables are gathered
@@ -125,36 +133,74 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
     float z = 0.0f;
     if constexpr (LC > 0) {
       // lane sub < LC adds the count of table sub; the group sums them below
+      constexpr int cb = static_cast<int>(sizeof(CT));
       if (sub < LC) {
-        int c = 0;
+        const int widx = sub * cb / 4;
+        uint32_t wsel = cw[0];
 #pragma unroll
-        for (int l = 0; l < LC; ++l) c = sub == l ? code_of(l) : c;
-        z = tc[static_cast<long long>(sub) * nb + c];
+        for (int k = 1; k < kCW; ++k) wsel = widx == k ? cw[k] : wsel;
+        const uint32_t c = (wsel >> ((sub * cb % 4) * 8)) & (cb == 1 ? 0xffu : 0xffffu);
+        z = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(tc_rs, (static_cast<uint32_t>(sub * nb) + c) * 4u, 0, 0));
       }
-      f32x4 t[LC];
+      // byte offset of the lane's 4-column piece of row code_l of table l,
+      // relative to the table: code * d * es + 4 es sub.  For 256-byte rows
+      // (binary32, d = 64) one byte permute places the code above the lane
+      // offset.
+      const uint32_t vbase = static_cast<uint32_t>(sub) * 4u * kES;
+      auto row_off = [&](int l) -> uint32_t {
+        const uint32_t word = cw[l * cb / 4];
+        const int byte = l * cb % 4;
+        if constexpr (D * kES == 256) {
+          const uint32_t sel = cb == 1 ? (0x0c0c0000u | ((4u + byte) << 8))
+                                       : (0x0c000000u | ((5u + byte) << 16) | ((4u + byte) << 8));
+          return __builtin_amdgcn_perm(word, vbase, sel);
+        } else {
+          const uint32_t c = (word >> (byte * 8)) & (cb == 1 ? 0xffu : 0xffffu);
+          return c * static_cast<uint32_t>(D * kES) + vbase;
+        }
+      };
+      using Piece = typename std::conditional<kES == 2, uint2, f32x4>::type;
+      Piece t[LC];
 #pragma unroll
-      for (int l = 0; l < LC; ++l)
-        t[l] = *reinterpret_cast<const f32x4 *>(ts + (static_cast<long long>(l) * nb + code_of(l)) * D);
+      for (int l = 0; l < LC; ++l) {
+        if constexpr (kES == 2)
+          t[l] = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_raw_buffer_load_b64(ts_rs, row_off(l), l * nb * (D * kES), 0));
+        else
+          t[l] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, row_off(l), l * nb * (D * kES), 0));
+      }
       long long qn = q0 + kQPS < q_end ? q0 + kQPS : q0;
       load_codes(qn, cw);  // next step's codes, in flight while this step finishes
 #pragma unroll
-      for (int l = 0; l < LC; ++l) num += t[l];
+      for (int l = 0; l < LC; ++l) {
+        if constexpr (kES == 2) {
+          num[0] += __uint_as_float(t[l].x << 16);
+          num[1] += __uint_as_float(t[l].x & 0xffff0000u);
+          num[2] += __uint_as_float(t[l].y << 16);
+          num[3] += __uint_as_float(t[l].y & 0xffff0000u);
+        } else {
+          num += t[l];
+        }
+      }
     } else {
       const CT *qc = qcodes + qi * L;
       for (int l0 = 0; l0 < L; l0 += 8) {
-        f32x4 t[8];
+        float t[8][4];
         float cnt[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int l = l0 + e < L ? l0 + e : L - 1;  // clamped: extra rows are loaded, not added
           const long long row = static_cast<long long>(l) * nb + qc[l];
-          t[e] = *reinterpret_cast<const f32x4 *>(ts + row * D);
+          Elem<VT>::load4(ts + row * D, t[e]);
           cnt[e] = tc[row];
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (l0 + e < L) {
-            num += t[e];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) num[k] += t[e][k];
             if (sub == 0) z += cnt[e];
           }
       }
@@ -182,15 +228,16 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
       a1 += __shfl_xor(a1, off);
       z += __shfl_xor(z, off);
     }
-    const float g_s = 1.0f / (1.0f + __expf(-(a0 + gate_b[h])));
-    const float g_lr = 1.0f / (1.0f + __expf(-(a1 + gate_b[H + h])));
+    // reciprocals with v_rcp_f32 (1 ulp)
+    const float g_s = __builtin_amdgcn_rcpf(1.0f + __expf(-(a0 + gate_b[h])));
+    const float g_lr = __builtin_amdgcn_rcpf(1.0f + __expf(-(a1 + gate_b[H + h])));
 
-    const float z_lr = z / static_cast<float>(L);
+    const float z_lr = z * (1.0f / static_cast<float>(L));
     f32x4 o_lr = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (z > 0.0f) o_lr = num * (1.0f / z);  // (num / L) / (z / L)
+    if (z > 0.0f) o_lr = num * __builtin_amdgcn_rcpf(z);  // (num / L) / (z / L)
 
     const float mass_lr = lambda * z_lr;
-    const float alpha = mass_lr > 0.0f ? 1.0f / (1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
+    const float alpha = mass_lr > 0.0f ? __builtin_amdgcn_rcpf(1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
 
     const float ws = g_s * alpha;
     if (valid) {
@@ -229,7 +276,7 @@ void launch_l(const Geometry &g, const void *x_gate, const float *gate_w, const 
   const long long blocks = ((waves + 3) / 4 + kXcdCount - 1) / kXcdCount * kXcdCount;
   hipLaunchKernelGGL((elsaa_k5_fuse<D, VT, CT, LC>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      stream, static_cast<const VT *>(buf.o_s), buf.lse,
-                     static_cast<const CT *>(buf.rcode), buf.tsum, buf.tcnt,
+                     static_cast<const CT *>(buf.rcode), static_cast<const VT *>(buf.tsum), buf.tcnt,
                      static_cast<const VT *>(x_gate), gate_w, gate_b, g.H, g.N, g.L, g.P, g.DG,
                      g.lambda, total, qpw, static_cast<VT *>(out), aux);
 }
