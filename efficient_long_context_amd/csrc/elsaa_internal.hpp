@@ -149,6 +149,23 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Sum of x over the lanes l ^ m for every m that is a multiple of kGroup
+// below 64 (kGroup in {8, 16, 32}): lane-group reductions without LDS.
+// xor 8 inside a 16-lane row is a DPP rotation by 8; xor 16 and xor 32 are
+// the gfx950 permlane swaps, whose two results always add to the pair sum.
+template <int kGroup>
+__device__ __forceinline__ float sum_over_lane_groups(float x) {
+  static_assert(kGroup == 8 || kGroup == 16 || kGroup == 32, "group width");
+  if constexpr (kGroup <= 8)
+    x += __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x128, 0xf, 0xf, false));
+  if constexpr (kGroup <= 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

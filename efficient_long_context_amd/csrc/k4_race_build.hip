@@ -201,9 +201,7 @@ template <typename VT, int D> struct Piece {
   static constexpr int kCols = 16 / static_cast<int>(sizeof(VT));
   static constexpr int kLanesPerRow = D / kCols;
   static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
-  static __device__ __forceinline__ u32x4 load(const VT *row, int cc) {
-    return *reinterpret_cast<const u32x4 *>(row + cc * kCols);
-  }
+  static constexpr int kRowBytes = D * static_cast<int>(sizeof(VT));
   static __device__ __forceinline__ void add(u32x4 r, float *a) {
     if constexpr (sizeof(VT) == 2) {
 #pragma unroll
@@ -252,11 +250,12 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
   uint32_t *bst = cnt + W * nb;                 // [nb + 1] tile-local run starts
   uint32_t *tot = bst + nb + 1;                 // [nb] keys per bucket over all tiles
   uint32_t *part = tot + nb;                    // [W * 64] scan
-  uint16_t *lperm = reinterpret_cast<uint16_t *>(part + W * 64);  // [S] tile-local key index
+  uint16_t *lperm = reinterpret_cast<uint16_t *>(part + W * 64);  // [S + slack] tile-local key index
 
   const long long tu = xcd_logical_block(blockIdx.x, gridDim.x);  // (b, h) * L + table
   if (tu >= units) return;  // whole workgroup
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave ranges scalar
   const long long bh = tu / L;
   const int l = static_cast<int>(tu % L);
   const CT *c = kcodes + bh * N * static_cast<long long>(L) + l;  // code of key j at c[j * L]
@@ -377,10 +376,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
       // cc * kCols + rg + kRPI m of the bucket row into the LDS table.
       auto flush = [&]() {
 #pragma unroll
-        for (int k = 0; k < kCols; ++k) {
-#pragma unroll
-          for (int off = kLPR; off < 64; off <<= 1) a[k] += __shfl_xor(a[k], off);
-        }
+        for (int k = 0; k < kCols; ++k) a[k] = sum_over_lane_groups<kLPR>(a[k]);
 #pragma unroll
         for (int m = 0; m < kCols / kRPI; ++m) {
           float val = 0.0f;
@@ -391,15 +387,22 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
 #pragma unroll
         for (int k = 0; k < kCols; ++k) a[k] = 0.0f;
       };
+      // value rows of this tile through a buffer resource: 32-bit offsets
+      const __amdgpu_buffer_rsrc_t vrs =
+          make_rsrc(vb + static_cast<long long>(t0) * D, static_cast<uint32_t>(M) * PC::kRowBytes);
+      const uint32_t cbyte = static_cast<uint32_t>(cc) * 16u;
       auto load_batch = [&](int pbase, u32x4 (&r)[kI]) {
-        int jl[kI];
+        // positions past p_hi (up to 3 batches) read the next wave's entries or
+        // the slack at the end of lperm; their rows are loaded (out-of-range
+        // offsets read zero) and never added
+        uint32_t jl[kI];
+        const uint16_t *lp = lperm + pbase + rg;
 #pragma unroll
-        for (int i = 0; i < kI; ++i) {
-          const int pos = pbase + i * kRPI + rg;
-          jl[i] = lperm[pos < p_hi ? pos : p_hi - 1];  // clamped past the end
-        }
+        for (int i = 0; i < kI; ++i) jl[i] = lp[i * kRPI];
 #pragma unroll
-        for (int i = 0; i < kI; ++i) r[i] = PC::load(vb + (static_cast<long long>(t0) + jl[i]) * D, cc);
+        for (int i = 0; i < kI; ++i)
+          r[i] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, jl[i] * PC::kRowBytes + cbyte, 0, 0));
       };
       // rows of positions [pbase, pbase + kBP): lane's row is position p + rg
       auto consume = [&](int pbase, const u32x4 (&r)[kI]) {
@@ -445,9 +448,11 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
 }
 
 // LDS bytes of the fused kernel for tile size S (0 if the table does not fit).
+constexpr int kLpermSlack = 256;  // entries past S read by the gather's look-ahead
+
 size_t fused_lds_bytes(int nb, int D, int S) {
   return (static_cast<size_t>(nb) * D + static_cast<size_t>(kFusedWaves) * nb + 2 * nb + 1 +
-          kFusedWaves * 64) * 4 + static_cast<size_t>(S) * 2;
+          kFusedWaves * 64) * 4 + (static_cast<size_t>(S) + kLpermSlack) * 2;
 }
 
 template <typename CT, typename VT>
