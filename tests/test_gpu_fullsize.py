@@ -1,0 +1,134 @@
+"""Full-size parity: the three benchmark workloads at their full shapes, run
+through the same C ABI entry point and kernels the benchmark times.
+
+For every (b, h) of the run, properties that hold at any size:
+  * each permutation is a permutation of 0..N-1 that sorts its codes, ties in
+    ascending position (stable);
+  * every RACE count table is the histogram of that table's key codes, and
+    sums to N;
+  * the bucket sums of every table add up to the sum of all values;
+  * alpha lies in [0, 1], the gates in (0, 1), the output is finite.
+On sampled (b, h) slices the oracle runs at full N and every output of the
+slice is compared: codes, permutations and counts bit for bit, floating
+outputs to max|d| / max|ref| <= 2e-2 (bfloat16 inputs).
+
+The needle workload also reports the long-context diagnostic (not a gate):
+mean alpha over the 16 queries that equal the needle's direction against the
+mean over all other queries, and how many of those queries have the needle key
+inside their own-plus-previous chunk window.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_common import TOL, rel_err, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+SLICES = {
+    "vision16k-bf16": [(0, 0), (7, 5)],
+    "text32k-bf16": [(0, 0), (1, 11)],
+    "needle256k-bf16": [(0, 3)],
+}
+
+
+def _oracle_slice(inp, b, h):
+    import oracle
+    wl = inp.wl
+    sl = lambda a: np.ascontiguousarray(a[b:b + 1, h:h + 1])
+    return oracle.forward(sl(inp.q), sl(inp.k), sl(inp.v), np.ascontiguousarray(inp.x_gate[b:b + 1]),
+                          inp.hyperplanes, np.ascontiguousarray(inp.gate_w[:, h:h + 1]),
+                          np.ascontiguousarray(inp.gate_b[:, h:h + 1]), sort_bits=wl.sort_bits,
+                          chunk=wl.chunk, race_tables_n=wl.race_tables, race_bits=wl.race_bits,
+                          lam=wl.lam)
+
+
+def _check_properties(g, inp):
+    wl = inp.wl
+    N, L, nb = wl.N, wl.race_tables, 1 << wl.race_bits
+    pos = np.arange(N)
+    for t in ("q", "k"):
+        perm = g[f"perm_{t}"].reshape(-1, N)
+        code = g[f"sort_code_{t}"].reshape(-1, N)
+        for row in range(perm.shape[0]):
+            p = perm[row]
+            assert np.array_equal(np.sort(p), pos), f"perm_{t} row {row} is not a permutation"
+            c = code[row][p]
+            assert (np.diff(c) >= 0).all(), f"perm_{t} row {row} does not sort the codes"
+            same = np.diff(c) == 0
+            assert (np.diff(p)[same] > 0).all(), f"perm_{t} row {row} is not stable"
+    cnt = g["race_cnt"].reshape(-1, L, nb)
+    codes_k = g["race_code_k"].reshape(-1, N, L)
+    for row in range(cnt.shape[0]):
+        for l in range(L):
+            hist = np.bincount(codes_k[row, :, l], minlength=nb)
+            assert np.array_equal(cnt[row, l], hist), f"race_cnt ({row}, {l}) != histogram of codes"
+    assert (cnt.sum(axis=2) == N).all()
+    vsum = inp.v.astype(np.float64).reshape(-1, N, wl.d).sum(axis=1)          # [BH, d]
+    vabs = np.abs(inp.v.astype(np.float64)).reshape(-1, N, wl.d).sum(axis=1)
+    tsum = g["race_sum"].reshape(-1, L, nb, wl.d).sum(axis=2)                 # [BH, L, d]
+    err = np.abs(tsum - vsum[:, None, :]).max() / vabs.max()
+    assert err <= TOL[wl.dtype], f"table sums vs sum of values: {err:.2e}"
+    assert ((g["alpha"] >= 0) & (g["alpha"] <= 1)).all()
+    assert ((g["g_s"] > 0) & (g["g_s"] < 1) & (g["g_lr"] > 0) & (g["g_lr"] < 1)).all()
+    assert np.isfinite(g["y"]).all()
+
+
+def _compare_slice(g, r, inp, b, h, label):
+    wl = inp.wl
+    tol = TOL[wl.dtype]
+    bh = lambda a: a[b, h][None, None]
+    for key, ref in (("sort_code_q", r.sort_code_q), ("sort_code_k", r.sort_code_k),
+                     ("race_code_q", r.race_code_q), ("race_code_k", r.race_code_k),
+                     ("perm_q", r.perm_q), ("perm_k", r.perm_k), ("race_cnt", r.race_cnt)):
+        np.testing.assert_array_equal(bh(g[key]), ref, err_msg=f"{label} {key}")
+    errs = {
+        "race_sum": rel_err(bh(g["race_sum"]), r.race_sum),
+        "o_sparse": rel_err(bh(g["o_sparse"]), r.o_s),
+        "lse_s": rel_err(bh(g["lse_s"]), r.lse),
+        "z_lr": rel_err(bh(g["z_lr"]), r.z_lr),
+        "o_lowrank": rel_err(bh(g["o_lowrank"]), r.o_lr),
+        "g_s": rel_err(bh(g["g_s"]), r.g_s),
+        "g_lr": rel_err(bh(g["g_lr"]), r.g_lr),
+        "alpha": rel_err(bh(g["alpha"]), r.alpha),
+        "y": rel_err(bh(g["y"]), r.y),
+    }
+    print(f"[fullsize] {label}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{label}: over tolerance {tol}: {bad}"
+
+
+def _needle_diagnostic(g, inp):
+    wl = inp.wl
+    w = wl.chunk
+    for b in range(wl.B):
+        for h in range(wl.H):
+            aligned = inp.meta["aligned_pos"][b, h]
+            needle = int(inp.meta["needle_pos"][b, h])
+            alpha = g["alpha"][b, h]
+            others = np.ones(wl.N, dtype=bool)
+            others[aligned] = False
+            rank_q = np.empty(wl.N, dtype=np.int64)
+            rank_q[g["perm_q"][b, h]] = np.arange(wl.N)
+            rank_k_needle = int(np.nonzero(g["perm_k"][b, h] == needle)[0][0])
+            c = rank_q[aligned] // w
+            in_window = ((rank_k_needle >= np.maximum(0, (c - 1) * w)) & (rank_k_needle < (c + 1) * w)).sum()
+            print(f"[needle] b={b} h={h}: mean alpha aligned {alpha[aligned].mean():.4f} vs others "
+                  f"{alpha[others].mean():.4f}; needle in window for {in_window}/16 aligned queries",
+                  flush=True)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(SLICES))
+def test_fullsize(name):
+    wl = workloads.WORKLOADS[name]
+    print(f"[fullsize] {name}: B={wl.B} H={wl.H} N={wl.N} d={wl.d}: generating", flush=True)
+    inp = workloads.generate(wl, seed=0)
+    g = run_gpu(inp)
+    print(f"[fullsize] {name}: GPU done, checking properties over every (b, h)", flush=True)
+    _check_properties(g, inp)
+    for (b, h) in SLICES[name]:
+        r = _oracle_slice(inp, b, h)
+        _compare_slice(g, r, inp, b, h, f"{name} (b={b}, h={h})")
+    if wl.kind == "needle":
+        _needle_diagnostic(g, inp)

@@ -6,7 +6,8 @@ bit for bit; floating-point tensors must satisfy max|d| / max|ref| <= 1e-4
 Sizes here are ones the oracle finishes in seconds while still spanning many
 tiles of every kernel; each workload keeps its own hash settings, chunk,
 generator and head dimension, with B, H (and N where needed) reduced.
-Full-size runs with sampled checks live in test_gpu_fullsize.py.
+Full-size runs with per-head properties and oracle-checked slices are in
+test_gpu_fullsize.py.
 """
 import numpy as np
 import pytest
