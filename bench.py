@@ -50,7 +50,8 @@ def stage_model(wl: workloads.Workload) -> dict:
     """Algorithmic HBM bytes and flops of each stage for one forward pass.
 
     Per token-head (s = element bytes, c = RACE code bytes, T = table bytes of
-    one (b, h) = L 2^P (d + 1) 4):
+    one (b, h) = L 2^P (d s + 4): bucket sums in the value dtype, counts in
+    binary32):
       hash   read 2 d s, write 2 (2 + L c);   flops 2 * 2 d R  (q and k, R planes)
       sort   read 2 * 2 (codes), write 2 * 4 (permutations)
       race   read d s + L c, write T / N
@@ -63,7 +64,7 @@ def stage_model(wl: workloads.Workload) -> dict:
     d, L, P, N, H = wl.d, wl.race_tables, wl.race_bits, wl.N, wl.H
     th = wl.B * wl.H * wl.N
     R = wl.sort_bits + L * P
-    T = L * (1 << P) * (d + 1) * 4
+    T = L * (1 << P) * (d * s + 4)
     pairs = wl.B * wl.H * (N * 2 * wl.chunk - wl.chunk * wl.chunk)
     return {
         "hash": dict(bytes=th * (2 * d * s + 2 * (2 + L * c)), flops=th * 2 * 2 * d * R, mfma=wl.dtype == "bf16"),
@@ -77,8 +78,11 @@ def stage_model(wl: workloads.Workload) -> dict:
 
 
 def source_sha(stage: str) -> str:
-    path = os.path.join(ROOT, "efficient_long_context_amd", "csrc", KERNEL_FILES[stage])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of the stage's kernel source and the shared kernel header."""
+    h = hashlib.sha256()
+    for name in (KERNEL_FILES[stage], "elsaa_internal.hpp"):
+        h.update(open(os.path.join(ROOT, "efficient_long_context_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(stage: str, workload: str):
@@ -93,6 +97,69 @@ def measured_traffic(stage: str, workload: str):
     if rec.get("source_sha") != source_sha(stage):
         return None
     return rec.get("bytes_per_launch")
+
+
+# Kernel-name prefixes of each stage (a stage's launches, in order).
+STAGE_KERNELS = {
+    "hash": ("elsaa_k1_hash_",),
+    "sort": ("elsaa_k2_sort_",),
+    "race_build": ("elsaa_k4_race_",),
+    "chunk_attention": ("elsaa_k3_chunk_attn_",),
+    "fuse": ("elsaa_k5_fuse",),
+}
+
+
+def record_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
+    """Turn two rocprofv3 counter runs of this script (--pmc FETCH_SIZE, then
+    --pmc WRITE_SIZE, both with --copy-calibration) into HBM bytes per launch
+    of each stage, written to profiles/traffic.json.
+
+    The counters read KiB per dispatch.  Each is scaled by what it reads for the
+    calibration copy (256 MiB read and 256 MiB written, the largest
+    __amd_rocclr_copyBuffer dispatch of the run), so the scale absorbs the
+    counter's own units."""
+    import csv
+
+    def per_kernel(path, counter):
+        sums, counts, calib = {}, {}, 0.0
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            val = float(row["Counter_Value"]) * 1024.0
+            if name.startswith("__amd_rocclr_copyBuffer"):
+                calib = max(calib, val)
+                continue
+            short = name.replace("void ", "").replace("elsaa::(anonymous namespace)::", "").split("(")[0]
+            sums[short] = sums.get(short, 0.0) + val
+            counts[short] = counts.get(short, 0) + 1
+        if calib <= 0.0:
+            raise SystemExit(f"{path}: no calibration copy found (run with --copy-calibration)")
+        scale = CALIB_BYTES / calib
+        return {k: sums[k] / counts[k] * scale for k in sums}, scale
+
+    fetch, f_scale = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, w_scale = per_kernel(write_csv, "WRITE_SIZE")
+    rec = {}
+    for stage, prefixes in STAGE_KERNELS.items():
+        ks = sorted(k for k in fetch if k.startswith(prefixes))
+        if not ks:
+            continue
+        fb = sum(fetch[k] for k in ks)
+        wb = sum(write.get(k, 0.0) for k in ks)
+        rec[stage] = {"kernels": ks, "fetch_bytes": round(fb), "write_bytes": round(wb),
+                      "bytes_per_launch": round(fb + wb), "fetch_scale": round(f_scale, 4),
+                      "write_scale": round(w_scale, 4), "source_sha": source_sha(stage)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        allrec = json.load(open(path))
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[workload] = rec
+    with open(path, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec
 
 
 class HipEvents:
@@ -142,7 +209,14 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 256 MiB device copy first (HBM counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of a run of "
+                         "this script into profiles/traffic.json for --workload")
     args = ap.parse_args(argv)
+
+    if args.record_traffic:
+        print(json.dumps(record_traffic(args.workload, *args.record_traffic), indent=1))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every ELSAA stage is independent per "

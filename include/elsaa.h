@@ -69,7 +69,9 @@ typedef struct {
   void *race_code_k;      /* [B][H][N][L]                                       */
   int32_t *perm_q;        /* [B][H][N]    sorted rank -> original query index   */
   int32_t *perm_k;        /* [B][H][N]    sorted rank -> original key index     */
-  float *race_sum;        /* [B][H][L][2^P][d] per-bucket sums of values        */
+  float *race_sum;        /* [B][H][L][2^P][d] per-bucket sums of values, as
+                             stored: accumulated in binary32, then rounded once
+                             to dtype (bfloat16 runs keep bfloat16 tables)       */
   float *race_cnt;        /* [B][H][L][2^P]    per-bucket key counts            */
   void *o_sparse;         /* [B][H][N][d] sparse-branch output, in dtype        */
   float *lse_s;           /* [B][H][N]    log Z_s (natural log)                 */

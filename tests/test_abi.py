@@ -50,8 +50,9 @@ def test_valid_params_and_workspace_size():
     assert elsaa.validate(p) == elsaa.OK
     ws = elsaa.workspace_bytes(p)
     rows = 2 * 12 * 32768
-    # codes + perms + tables + o_s + lse at least
-    assert ws >= 2 * rows * 2 + 2 * rows * 16 + 2 * rows * 4 + 24 * 16 * 256 * 65 * 4 + rows * 64 * 2 + rows * 4
+    # codes + perms + tables (bf16 sums, binary32 counts) + o_s + lse at least
+    tables = 24 * 16 * 256 * (64 * 2 + 4)
+    assert ws >= 2 * rows * 2 + 2 * rows * 16 + 2 * rows * 4 + tables + rows * 64 * 2 + rows * 4
     assert ws < 400 * 2 ** 20
 
 
