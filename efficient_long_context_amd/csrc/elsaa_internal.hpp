@@ -94,6 +94,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Adds a bfloat16 half of a packed word to a binary32 accumulator in one
+// instruction: v_dot2_f32_bf16 with weights (1, 0) or (0, 1), i.e. acc + x * 1
+// + y * 0, instead of unpacking (shift or mask) and adding.  The weight words
+// are made by s_mov_b32 inside asm: left to the compiler, 0x00003f80 can be
+// re-encoded as the inline constant 1.0, which the instruction reads as the
+// other half.
+struct Bf16Adder {
+  uint32_t wlo, whi;
+  __device__ __forceinline__ Bf16Adder() {
+    asm("s_mov_b32 %0, 0x3f80" : "=s"(wlo));
+    asm("s_mov_b32 %0, 0x3f800000" : "=s"(whi));
+  }
+  __device__ __forceinline__ float lo(float acc, uint32_t w) const {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, wlo),
+                                           acc, false);
+  }
+  __device__ __forceinline__ float hi(float acc, uint32_t w) const {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, whi),
+                                           acc, false);
+  }
+};
+
 // Raw buffer resource over `bytes` bytes at `base` (a wave-uniform address):
 // loads through it take a 32-bit per-lane offset plus a scalar offset, and
 // offsets at or past `bytes` read zero.  Word 3 is the gfx9 raw-buffer format.

@@ -67,22 +67,41 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
 
   // Block loader: K piece i -> row i / (D/8), chunk i % (D/8); V piece i -> key
   // pair i % 32, chunk i / 32.  Pieces past the count are clamped reloads.
-  u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer];
-  auto load_block = [&](int kb) {
+  // The permutation entries of a block are loaded one block ahead of its rows,
+  // so a block costs one memory round trip, not two.
+  struct Idx { int kj[kKPer], v0[kVPer], v1[kVPer]; };
+  auto load_idx = [&](int kb, Idx &ix) {
+    kb = kb < hi - kKBlock ? kb : hi - kKBlock;  // clamped: past the window reloads the last block
 #pragma unroll
     for (int p = 0; p < kKPer; ++p) {
       int i = tid + p * kThreads;
       i = i < kKChunks ? i : kKChunks - 1;
-      const int j = i / (D / 8), ch = i % (D / 8);
-      kreg[p] = *reinterpret_cast<const u16x8 *>(k + (seg + pk[kb + j]) * D + ch * 8);
+      ix.kj[p] = pk[kb + i / (D / 8)];
     }
 #pragma unroll
     for (int p = 0; p < kVPer; ++p) {
       int i = tid + p * kThreads;
       i = i < kVPairs ? i : kVPairs - 1;
-      const int jp = i % (kKBlock / 2), ch = i / (kKBlock / 2);
-      vreg0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + pk[kb + 2 * jp]) * D + ch * 8);
-      vreg1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + pk[kb + 2 * jp + 1]) * D + ch * 8);
+      const int jp = i % (kKBlock / 2);
+      ix.v0[p] = pk[kb + 2 * jp];
+      ix.v1[p] = pk[kb + 2 * jp + 1];
+    }
+  };
+  u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer];
+  auto load_rows = [&](const Idx &ix) {
+#pragma unroll
+    for (int p = 0; p < kKPer; ++p) {
+      int i = tid + p * kThreads;
+      i = i < kKChunks ? i : kKChunks - 1;
+      kreg[p] = *reinterpret_cast<const u16x8 *>(k + (seg + ix.kj[p]) * D + (i % (D / 8)) * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < kVPer; ++p) {
+      int i = tid + p * kThreads;
+      i = i < kVPairs ? i : kVPairs - 1;
+      const int ch = i / (kKBlock / 2);
+      vreg0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + ix.v0[p]) * D + ch * 8);
+      vreg1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + ix.v1[p]) * D + ch * 8);
     }
   };
   auto store_block = [&]() {
@@ -114,12 +133,18 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
   float m = -INFINITY;  // running max of score * log2(e) / sqrt(d)
   float l_part = 0.0f;  // this lane's share of the running sum
 
-  load_block(lo);
+  Idx ix;
+  load_idx(lo, ix);
+  load_rows(ix);
+  load_idx(lo + kKBlock, ix);
   for (int kb = lo; kb < hi; kb += kKBlock) {
     __syncthreads();  // previous block fully consumed
     store_block();
     __syncthreads();
-    if (kb + kKBlock < hi) load_block(kb + kKBlock);  // next block in flight during the math
+    // next block's rows (clamped past the window) and the block after's
+    // permutation entries are in flight during the math
+    load_rows(ix);
+    load_idx(kb + 2 * kKBlock, ix);
 
     // S^T tiles: lane holds keys kt*16 + g*4 + i for query r16
     f32x4 s[kKBlock / 16];

@@ -202,12 +202,12 @@ template <typename VT, int D> struct Piece {
   static constexpr int kLanesPerRow = D / kCols;
   static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   static constexpr int kRowBytes = D * static_cast<int>(sizeof(VT));
-  static __device__ __forceinline__ void add(u32x4 r, float *a) {
+  static __device__ __forceinline__ void add(u32x4 r, float *a, const Bf16Adder &ad) {
     if constexpr (sizeof(VT) == 2) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        a[2 * e] += __uint_as_float(r[e] << 16);
-        a[2 * e + 1] += __uint_as_float(r[e] & 0xffff0000u);
+        a[2 * e] = ad.lo(a[2 * e], r[e]);
+        a[2 * e + 1] = ad.hi(a[2 * e + 1], r[e]);
       }
     } else {
 #pragma unroll
@@ -366,6 +366,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
 
     if (p_lo < p_hi) {
       const int rg = lane / kLPR, cc = lane % kLPR;  // row group, column piece
+      const Bf16Adder adder;
       int b = b0;
       int bend = __builtin_amdgcn_readfirstlane(static_cast<int>(bst[b0 + 1]));
       float a[kCols];
@@ -413,12 +414,12 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
           const int pe = p + kRPI < p_hi ? p + kRPI : p_hi;
           const int my = p + rg;
           if (pe < bend) {  // the whole group lies inside bucket b
-            if (my < pe) PC::add(r[i], a);
+            if (my < pe) PC::add(r[i], a, adder);
           } else {
             int cur = p;
             while (cur < pe) {
               const int stop = pe < bend ? pe : bend;
-              if (my >= cur && my < stop) PC::add(r[i], a);
+              if (my >= cur && my < stop) PC::add(r[i], a, adder);
               cur = stop;
               if (cur == bend) {
                 flush();

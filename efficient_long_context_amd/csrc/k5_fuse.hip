@@ -15,14 +15,15 @@
 // still be mis-scaled" and "The ablation isolates the actual contribution":
 // the multiplier acts on the sparse branch only, the gates are independent.)
 //
-// Layout: d/4 lanes per query, 4 value columns per lane (16-byte table reads),
-// the gate dot products split over the same lanes and reduced with xor
-// shuffles inside the query's lane group.  Each wave streams a contiguous run
-// of queries, loading the next step's RACE codes while the current step's
-// table rows are gathered; consecutive waves run on one XCD, so its L2 holds
-// the tables of the few (b, h) it serves.
-#include <type_traits>
-
+// Two layouts.  L in {8, 16} (the wide path): 16-byte lane pieces, so a load
+// instruction gathers 8 table rows of bfloat16 d = 64; a workgroup serves a
+// run of queries of one (b, h) with that (b, h)'s bucket counts staged in LDS
+// and the gate weight rows in registers; a query's L codes arrive in one
+// vector load, the next step's while the current step is gathered.  Any
+// other L: d/4 lanes per query, one code and one row load per table.  In both
+// the gate dot products are split over the query's lanes and reduced with xor
+// shuffles, and consecutive workgroups run on one XCD, so its L2 holds the
+// tables of the few (b, h) it serves.
 #include "elsaa_internal.hpp"
 
 namespace elsaa {
@@ -38,60 +39,25 @@ struct AuxOut {
   float *z_lr, *alpha, *g_s, *g_lr, *o_lr;
 };
 
-// LC = number of RACE tables when it is 8 or 16 (codes of a query arrive in
-// one 16- or 32-byte load and every lane holds all of them); LC = 0 takes any
-// L with one code load per table.
-template <int D, typename VT, typename CT, int LC>
+// ------------------------------------------------------------- any-L path --
+// Any number of tables: d/4 lanes per query, 4 value columns each, one code
+// load and one row load per table (clamped loads past L are not added).
+template <int D, typename VT, typename CT>
 __global__ __launch_bounds__(256) void elsaa_k5_fuse(
     const VT *__restrict__ o_s, const float *__restrict__ lse, const CT *__restrict__ qcodes,
     const VT *__restrict__ tsum, const float *__restrict__ tcnt, const VT *__restrict__ x_gate,
-    const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int L_rt,
+    const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int L,
     int P, int DG, float lambda, long long total, long long qpw, VT *__restrict__ out, AuxOut aux) {
   constexpr int kLPQ = D / 4;      // lanes per query, 4 value columns each
   constexpr int kQPS = 64 / kLPQ;  // queries per wave step
-  constexpr int kCodeWords = LC * static_cast<int>(sizeof(CT)) / 4;  // 32-bit words of codes
-  const int L = LC ? LC : L_rt;
   const int lane = threadIdx.x & 63;
   const int sub = lane % kLPQ;
-  // readfirstlane: the wave index is uniform, so everything derived from it
-  // (query run, (b, h), table bases) stays in scalar registers
   const long long wv = xcd_logical_block(blockIdx.x, gridDim.x) * 4 +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const long long q_begin = wv * qpw;
   const long long q_end = q_begin + qpw < total ? q_begin + qpw : total;
   if (q_begin >= q_end) return;  // whole wave
   const int nb = 1 << P;
-
-  // all LC codes of the lane's query as kCodeWords 32-bit words (8, 16 or 32
-  // bytes; clamped queries are computed, not stored)
-  constexpr int kCW = kCodeWords > 0 ? kCodeWords : 1;
-  uint32_t cw[kCW];
-  auto load_codes = [&](long long q0, uint32_t (&w)[kCW]) {
-    if constexpr (LC > 0) {
-      long long q = q0 + lane / kLPQ;
-      q = q < q_end ? q : q_end - 1;
-      const CT *src = qcodes + q * LC;
-      if constexpr (kCodeWords % 4 == 0) {
-#pragma unroll
-        for (int k = 0; k < kCodeWords / 4; ++k) {
-          const u32x4 v = reinterpret_cast<const u32x4 *>(src)[k];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[4 * k + e] = v[e];
-        }
-      } else {
-        static_assert(kCodeWords == 2, "8 code bytes per query");
-        const uint2 v = *reinterpret_cast<const uint2 *>(src);
-        w[0] = v.x;
-        w[1] = v.y;
-      }
-    }
-  };
-  auto code_of = [&](int l) -> int {  // l known at compile time after unrolling
-    constexpr int cb = static_cast<int>(sizeof(CT));
-    const uint32_t word = cw[l * cb / 4];
-    return static_cast<int>((word >> ((l * cb % 4) * 8)) & (cb == 1 ? 0xffu : 0xffffu));
-  };
-  load_codes(q_begin, cw);
 
   // (b, h, i) of the step's first query, advanced once per step: N is a
   // multiple of 64 (a multiple of the chunk) and runs start at multiples of
@@ -105,122 +71,43 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
     const long long qi = q0 + lane / kLPQ;
     const bool valid = qi < q_end;  // always true for these sizes; kept as a guard
     const int i = i0 + lane / kLPQ;
-    // tables of this (b, h) through buffer resources: 32-bit per-lane offsets
-    constexpr int kES = static_cast<int>(sizeof(VT));  // table element bytes
-    const __amdgpu_buffer_rsrc_t ts_rs =
-        make_rsrc(tsum + bh * L * nb * static_cast<long long>(D), static_cast<uint32_t>(L * nb * D * kES));
-    const __amdgpu_buffer_rsrc_t tc_rs = make_rsrc(tcnt + bh * L * nb, static_cast<uint32_t>(L * nb * 4));
     const VT *ts = tsum + bh * L * nb * static_cast<long long>(D) + sub * 4;
     const float *tc = tcnt + bh * L * nb;
 
-    // the sparse output, its LSE and the gate inputs load while the tables are gathered
     float osv[4];
     Elem<VT>::load4(o_s + qi * D + sub * 4, osv);
     const float lse_i = lse[qi];
     const VT *xg = x_gate + (b * N + i) * DG;
     const float *w0 = gate_w + static_cast<long long>(h) * DG;
     const float *w1 = gate_w + static_cast<long long>(H + h) * DG;
-    const bool gate_fast = DG == 4 * kLPQ;
-    float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4 wa = {0.0f, 0.0f, 0.0f, 0.0f}, wb = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (gate_fast) {
-      Elem<VT>::load4(xg + sub * 4, xv);
-      wa = *reinterpret_cast<const f32x4 *>(w0 + sub * 4);
-      wb = *reinterpret_cast<const f32x4 *>(w1 + sub * 4);
-    }
 
     f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
     float z = 0.0f;
-    if constexpr (LC > 0) {
-      // lane sub < LC adds the count of table sub; the group sums them below
-      constexpr int cb = static_cast<int>(sizeof(CT));
-      if (sub < LC) {
-        const int widx = sub * cb / 4;
-        uint32_t wsel = cw[0];
+    const CT *qc = qcodes + qi * L;
+    for (int l0 = 0; l0 < L; l0 += 8) {
+      float t[8][4];
+      float cnt[8];
 #pragma unroll
-        for (int k = 1; k < kCW; ++k) wsel = widx == k ? cw[k] : wsel;
-        const uint32_t c = (wsel >> ((sub * cb % 4) * 8)) & (cb == 1 ? 0xffu : 0xffffu);
-        z = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(tc_rs, (static_cast<uint32_t>(sub * nb) + c) * 4u, 0, 0));
+      for (int e = 0; e < 8; ++e) {
+        const int l = l0 + e < L ? l0 + e : L - 1;  // clamped: extra rows are loaded, not added
+        const long long row = static_cast<long long>(l) * nb + qc[l];
+        Elem<VT>::load4(ts + row * D, t[e]);
+        cnt[e] = tc[row];
       }
-      // byte offset of the lane's 4-column piece of row code_l of table l,
-      // relative to the table: code * d * es + 4 es sub.  For 256-byte rows
-      // (binary32, d = 64) one byte permute places the code above the lane
-      // offset.
-      const uint32_t vbase = static_cast<uint32_t>(sub) * 4u * kES;
-      auto row_off = [&](int l) -> uint32_t {
-        const uint32_t word = cw[l * cb / 4];
-        const int byte = l * cb % 4;
-        if constexpr (D * kES == 256) {
-          const uint32_t sel = cb == 1 ? (0x0c0c0000u | ((4u + byte) << 8))
-                                       : (0x0c000000u | ((5u + byte) << 16) | ((4u + byte) << 8));
-          return __builtin_amdgcn_perm(word, vbase, sel);
-        } else {
-          const uint32_t c = (word >> (byte * 8)) & (cb == 1 ? 0xffu : 0xffffu);
-          return c * static_cast<uint32_t>(D * kES) + vbase;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (l0 + e < L) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) num[k] += t[e][k];
+          if (sub == 0) z += cnt[e];
         }
-      };
-      using Piece = typename std::conditional<kES == 2, uint2, f32x4>::type;
-      Piece t[LC];
-#pragma unroll
-      for (int l = 0; l < LC; ++l) {
-        if constexpr (kES == 2)
-          t[l] = __builtin_bit_cast(
-              uint2, __builtin_amdgcn_raw_buffer_load_b64(ts_rs, row_off(l), l * nb * (D * kES), 0));
-        else
-          t[l] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, row_off(l), l * nb * (D * kES), 0));
-      }
-      long long qn = q0 + kQPS < q_end ? q0 + kQPS : q0;
-      load_codes(qn, cw);  // next step's codes, in flight while this step finishes
-#pragma unroll
-      for (int l = 0; l < LC; ++l) {
-        if constexpr (kES == 2) {
-          num[0] += __uint_as_float(t[l].x << 16);
-          num[1] += __uint_as_float(t[l].x & 0xffff0000u);
-          num[2] += __uint_as_float(t[l].y << 16);
-          num[3] += __uint_as_float(t[l].y & 0xffff0000u);
-        } else {
-          num += t[l];
-        }
-      }
-    } else {
-      const CT *qc = qcodes + qi * L;
-      for (int l0 = 0; l0 < L; l0 += 8) {
-        float t[8][4];
-        float cnt[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int l = l0 + e < L ? l0 + e : L - 1;  // clamped: extra rows are loaded, not added
-          const long long row = static_cast<long long>(l) * nb + qc[l];
-          Elem<VT>::load4(ts + row * D, t[e]);
-          cnt[e] = tc[row];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (l0 + e < L) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) num[k] += t[e][k];
-            if (sub == 0) z += cnt[e];
-          }
-      }
     }
 
-    // gates: with d_gate = 4 x (lanes per query) each lane takes 4 consecutive
-    // inputs in one load; any other width takes the strided loop
     float a0 = 0.0f, a1 = 0.0f;
-    if (gate_fast) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a0 = __builtin_fmaf(xv[e], wa[e], a0);
-        a1 = __builtin_fmaf(xv[e], wb[e], a1);
-      }
-    } else {
-      for (int e = sub; e < DG; e += kLPQ) {
-        const float x = Elem<VT>::load(xg + e);
-        a0 = __builtin_fmaf(x, w0[e], a0);
-        a1 = __builtin_fmaf(x, w1[e], a1);
-      }
+    for (int e = sub; e < DG; e += kLPQ) {
+      const float x = Elem<VT>::load(xg + e);
+      a0 = __builtin_fmaf(x, w0[e], a0);
+      a1 = __builtin_fmaf(x, w1[e], a1);
     }
 #pragma unroll
     for (int off = kLPQ / 2; off > 0; off >>= 1) {
@@ -228,11 +115,10 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
       a1 += __shfl_xor(a1, off);
       z += __shfl_xor(z, off);
     }
-    // reciprocals with v_rcp_f32 (1 ulp)
     const float g_s = __builtin_amdgcn_rcpf(1.0f + __expf(-(a0 + gate_b[h])));
     const float g_lr = __builtin_amdgcn_rcpf(1.0f + __expf(-(a1 + gate_b[H + h])));
 
-    const float z_lr = z * (1.0f / static_cast<float>(L));
+    const float z_lr = z / static_cast<float>(L);
     f32x4 o_lr = {0.0f, 0.0f, 0.0f, 0.0f};
     if (z > 0.0f) o_lr = num * __builtin_amdgcn_rcpf(z);  // (num / L) / (z / L)
 
@@ -265,16 +151,268 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
   }
 }
 
+// ---------------------------------------------------------------- wide path --
+// L in {8, 16}: 16-byte lane pieces (8 lanes per query for bfloat16 rows of 64
+// columns), so one load instruction gathers 8 table rows.  A workgroup serves
+// a run of R queries of one (b, h): the bucket counts of that (b, h) are staged
+// in LDS once (L 2^P <= 16384 words) and read there, the two gate weight rows
+// are loaded once, and each wave streams R/4 queries.
+template <typename VT, int GE> struct GateIn;  // GE consecutive gate inputs of one lane
+template <> struct GateIn<uint16_t, 8> {
+  static __device__ __forceinline__ void load(const uint16_t *p, float *x) {
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+};
+template <> struct GateIn<uint16_t, 4> {
+  static __device__ __forceinline__ void load(const uint16_t *p, float *x) { Elem<uint16_t>::load4(p, x); }
+};
+template <> struct GateIn<float, 4> {
+  static __device__ __forceinline__ void load(const float *p, float *x) { Elem<float>::load4(p, x); }
+};
+template <> struct GateIn<float, 2> {
+  static __device__ __forceinline__ void load(const float *p, float *x) {
+    const float2 v = *reinterpret_cast<const float2 *>(p);
+    x[0] = v.x;
+    x[1] = v.y;
+  }
+};
+
 template <int D, typename VT, typename CT, int LC>
-void launch_l(const Geometry &g, const void *x_gate, const float *gate_w, const float *gate_b,
-              const Buffers &buf, const AuxOut &aux, void *out, hipStream_t stream) {
+__global__ __launch_bounds__(256) void elsaa_k5_fuse_wide(
+    const VT *__restrict__ o_s, const float *__restrict__ lse, const CT *__restrict__ qcodes,
+    const VT *__restrict__ tsum, const float *__restrict__ tcnt, const VT *__restrict__ x_gate,
+    const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int P,
+    int DG, float lambda, int R, long long units, VT *__restrict__ out, AuxOut aux) {
+  constexpr int kES = static_cast<int>(sizeof(VT));
+  constexpr int kCols = 16 / kES;         // value columns per lane
+  constexpr int kLPQ = D / kCols;         // lanes per query
+  constexpr int kQPS = 64 / kLPQ;         // queries per wave step
+  constexpr int kRowBytes = D * kES;
+  constexpr int cb = static_cast<int>(sizeof(CT));
+  constexpr int kCW = LC * cb / 4;        // 32-bit words of one query's codes
+  constexpr int kGE = 64 / kLPQ;          // gate inputs per lane when d_gate = 64
+  constexpr int kCntPer = (LC + kLPQ - 1) / kLPQ;  // counts summed by one lane
+  extern __shared__ float cnt_lds[];      // [L][2^P] counts of this (b, h)
+
+  const long long unit = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (unit >= units) return;  // whole workgroup
+  const int runs = N / R;
+  const long long bh = unit / runs;
+  const int i_run = static_cast<int>(unit % runs) * R;
+  const int h = static_cast<int>(bh % H);
+  const long long b = bh / H;
+  const int nb = 1 << P;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = lane % kLPQ;
+
+  // bucket counts of this (b, h) into LDS
+  {
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(tcnt + bh * LC * nb);
+    for (int i = tid; i < LC * nb / 4; i += 256) reinterpret_cast<f32x4 *>(cnt_lds)[i] = src[i];
+  }
+  // gate weights of head h (this lane's kGE columns)
+  const bool gate_fast = DG == 64;
+  float wa[kGE], wb[kGE];
+#pragma unroll
+  for (int e = 0; e < kGE; ++e) {
+    wa[e] = gate_fast ? gate_w[static_cast<long long>(h) * DG + sub * kGE + e] : 0.0f;
+    wb[e] = gate_fast ? gate_w[static_cast<long long>(H + h) * DG + sub * kGE + e] : 0.0f;
+  }
+  const float gb0 = gate_b[h], gb1 = gate_b[H + h];
+  const __amdgpu_buffer_rsrc_t ts_rs =
+      make_rsrc(tsum + bh * LC * nb * static_cast<long long>(D), static_cast<uint32_t>(LC * nb * kRowBytes));
+  const uint32_t vbase = static_cast<uint32_t>(sub) * 16u;
+  const Bf16Adder adder;
+  __syncthreads();
+
+  const int per_wave = R / 4;
+  const int i_begin = i_run + wave * per_wave;
+  auto load_codes = [&](int i0, uint32_t (&w)[kCW]) {
+    const CT *src = qcodes + (bh * N + i0 + lane / kLPQ) * LC;
+    if constexpr (kCW % 4 == 0) {
+#pragma unroll
+      for (int k = 0; k < kCW / 4; ++k) {
+        const u32x4 v = reinterpret_cast<const u32x4 *>(src)[k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[4 * k + e] = v[e];
+      }
+    } else {
+      static_assert(kCW == 2, "8 code bytes per query");
+      const uint2 v = *reinterpret_cast<const uint2 *>(src);
+      w[0] = v.x;
+      w[1] = v.y;
+    }
+  };
+  uint32_t cw[kCW];
+  load_codes(i_begin, cw);
+
+  for (int step = 0; step < per_wave; step += kQPS) {
+    const int i = i_begin + step + lane / kLPQ;
+    const long long qi = bh * N + i;
+
+    // table rows of the L buckets (offsets relative to table l, whose base
+    // goes in the scalar offset)
+    u32x4 t[LC];
+#pragma unroll
+    for (int l = 0; l < LC; ++l) {
+      const uint32_t word = cw[l * cb / 4];
+      const int byte = l * cb % 4;
+      uint32_t off;
+      if constexpr (kRowBytes == 256) {
+        const uint32_t sel = cb == 1 ? (0x0c0c0000u | ((4u + byte) << 8))
+                                     : (0x0c000000u | ((5u + byte) << 16) | ((4u + byte) << 8));
+        off = __builtin_amdgcn_perm(word, vbase, sel);
+      } else {
+        const uint32_t c = (word >> (byte * 8)) & (cb == 1 ? 0xffu : 0xffffu);
+        off = c * static_cast<uint32_t>(kRowBytes) + vbase;
+      }
+      t[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, off, l * nb * kRowBytes, 0));
+    }
+    // sparse output, its LSE and the gate inputs of this step
+    float osv[kCols];
+    {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(o_s + qi * D + sub * kCols);
+      if constexpr (kES == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          osv[2 * e] = __uint_as_float(w[e] << 16);
+          osv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) osv[e] = __uint_as_float(w[e]);
+      }
+    }
+    const float lse_i = lse[qi];
+    const VT *xg = x_gate + (b * N + i) * DG;
+    float xv[kGE];
+    if (gate_fast) GateIn<VT, kGE>::load(xg + sub * kGE, xv);
+
+    // counts from LDS: lane sub adds tables sub, sub + kLPQ, ...
+    float z = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kCntPer; ++r) {
+      const int l = sub + r * kLPQ;
+      if (l < LC) {
+        const int widx = l * cb / 4;
+        uint32_t wsel = cw[0];
+#pragma unroll
+        for (int k = 1; k < kCW; ++k) wsel = widx == k ? cw[k] : wsel;
+        const uint32_t c = (wsel >> ((l * cb % 4) * 8)) & (cb == 1 ? 0xffu : 0xffffu);
+        z += cnt_lds[l * nb + c];
+      }
+    }
+    // next step's codes, in flight while this step finishes
+    load_codes(step + kQPS < per_wave ? i_begin + step + kQPS : i_begin + step, cw);
+
+    float num[kCols];
+#pragma unroll
+    for (int k = 0; k < kCols; ++k) num[k] = 0.0f;
+#pragma unroll
+    for (int l = 0; l < LC; ++l) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (kES == 2) {
+          num[2 * e] = adder.lo(num[2 * e], t[l][e]);
+          num[2 * e + 1] = adder.hi(num[2 * e + 1], t[l][e]);
+        } else {
+          num[e] += __uint_as_float(t[l][e]);
+        }
+      }
+    }
+
+    float a0 = 0.0f, a1 = 0.0f;
+    if (gate_fast) {
+#pragma unroll
+      for (int e = 0; e < kGE; ++e) {
+        a0 = __builtin_fmaf(xv[e], wa[e], a0);
+        a1 = __builtin_fmaf(xv[e], wb[e], a1);
+      }
+    } else {
+      for (int e = sub; e < DG; e += kLPQ) {
+        const float x = Elem<VT>::load(xg + e);
+        a0 = __builtin_fmaf(x, gate_w[static_cast<long long>(h) * DG + e], a0);
+        a1 = __builtin_fmaf(x, gate_w[static_cast<long long>(H + h) * DG + e], a1);
+      }
+    }
+#pragma unroll
+    for (int off = kLPQ / 2; off > 0; off >>= 1) {
+      a0 += __shfl_xor(a0, off);
+      a1 += __shfl_xor(a1, off);
+      z += __shfl_xor(z, off);
+    }
+    // reciprocals with v_rcp_f32 (1 ulp)
+    const float g_s = __builtin_amdgcn_rcpf(1.0f + __expf(-(a0 + gb0)));
+    const float g_lr = __builtin_amdgcn_rcpf(1.0f + __expf(-(a1 + gb1)));
+    const float z_lr = z * (1.0f / static_cast<float>(LC));
+    const float rz = z > 0.0f ? __builtin_amdgcn_rcpf(z) : 0.0f;  // (num / L) / (z / L); 0 where z = 0
+    const float mass_lr = lambda * z_lr;
+    const float alpha = mass_lr > 0.0f ? __builtin_amdgcn_rcpf(1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
+    const float ws = g_s * alpha;
+
+    float o_lr[kCols], yv[kCols];
+#pragma unroll
+    for (int k = 0; k < kCols; ++k) {
+      o_lr[k] = num[k] * rz;
+      yv[k] = __builtin_fmaf(ws, osv[k], g_lr * o_lr[k]);
+    }
+    if constexpr (kES == 2) {
+      *reinterpret_cast<u32x4 *>(out + qi * D + sub * kCols) =
+          u32x4{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
+                pack_bf16x2(yv[6], yv[7])};
+    } else {
+      *reinterpret_cast<f32x4 *>(out + qi * D + sub * kCols) = f32x4{yv[0], yv[1], yv[2], yv[3]};
+    }
+    if (aux.o_lr) {
+#pragma unroll
+      for (int k = 0; k < kCols; k += 4)
+        *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * kCols + k) =
+            f32x4{o_lr[k], o_lr[k + 1], o_lr[k + 2], o_lr[k + 3]};
+    }
+    if (sub == 0) {
+      if (aux.z_lr) aux.z_lr[qi] = z_lr;
+      if (aux.alpha) aux.alpha[qi] = alpha;
+      if (aux.g_s) aux.g_s[qi] = g_s;
+      if (aux.g_lr) aux.g_lr[qi] = g_lr;
+    }
+  }
+}
+
+template <int D, typename VT, typename CT, int LC>
+void launch_wide(const Geometry &g, const void *x_gate, const float *gate_w, const float *gate_b,
+                 const Buffers &buf, const AuxOut &aux, void *out, hipStream_t stream) {
+  constexpr int kQPS = 64 / (D / (16 / static_cast<int>(sizeof(VT))));
+  // queries per workgroup: the largest of 512, 256, 128, 64 that divides N and
+  // gives every wave whole steps (N is a multiple of 64)
+  int R = 512;
+  while (R > 64 && (g.N % R != 0)) R /= 2;
+  while (R / 4 < kQPS) R *= 2;  // not reached for d <= 128
+  const long long units = static_cast<long long>(g.BH) * (g.N / R);
+  const long long grid = (units + kXcdCount - 1) / kXcdCount * kXcdCount;
+  const size_t lds = static_cast<size_t>(LC) * g.nb_race * 4;
+  hipLaunchKernelGGL((elsaa_k5_fuse_wide<D, VT, CT, LC>), dim3(static_cast<unsigned>(grid)), dim3(256), lds,
+                     stream, static_cast<const VT *>(buf.o_s), buf.lse,
+                     static_cast<const CT *>(buf.rcode), static_cast<const VT *>(buf.tsum), buf.tcnt,
+                     static_cast<const VT *>(x_gate), gate_w, gate_b, g.H, g.N, g.P, g.DG, g.lambda, R,
+                     units, static_cast<VT *>(out), aux);
+}
+
+template <int D, typename VT, typename CT>
+void launch_any(const Geometry &g, const void *x_gate, const float *gate_w, const float *gate_b,
+                const Buffers &buf, const AuxOut &aux, void *out, hipStream_t stream) {
   constexpr int kQPS = 64 / (D / 4);
   const long long total = g.rows;
   long long qpw = (total + kFuseWaves - 1) / kFuseWaves;  // each wave streams a run of queries
   qpw = (qpw + kQPS - 1) / kQPS * kQPS;
   const long long waves = (total + qpw - 1) / qpw;
   const long long blocks = ((waves + 3) / 4 + kXcdCount - 1) / kXcdCount * kXcdCount;
-  hipLaunchKernelGGL((elsaa_k5_fuse<D, VT, CT, LC>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+  hipLaunchKernelGGL((elsaa_k5_fuse<D, VT, CT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      stream, static_cast<const VT *>(buf.o_s), buf.lse,
                      static_cast<const CT *>(buf.rcode), static_cast<const VT *>(buf.tsum), buf.tcnt,
                      static_cast<const VT *>(x_gate), gate_w, gate_b, g.H, g.N, g.L, g.P, g.DG,
@@ -285,13 +423,13 @@ template <int D, typename VT>
 hipError_t launch_d(const Geometry &g, const void *x_gate, const float *gate_w, const float *gate_b,
                     const Buffers &buf, const AuxOut &aux, void *out, hipStream_t stream) {
   if (g.rcb == 1) {
-    if (g.L == 16) launch_l<D, VT, uint8_t, 16>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
-    else if (g.L == 8) launch_l<D, VT, uint8_t, 8>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
-    else launch_l<D, VT, uint8_t, 0>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+    if (g.L == 16) launch_wide<D, VT, uint8_t, 16>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+    else if (g.L == 8) launch_wide<D, VT, uint8_t, 8>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+    else launch_any<D, VT, uint8_t>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
   } else {
-    if (g.L == 16) launch_l<D, VT, uint16_t, 16>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
-    else if (g.L == 8) launch_l<D, VT, uint16_t, 8>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
-    else launch_l<D, VT, uint16_t, 0>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+    if (g.L == 16) launch_wide<D, VT, uint16_t, 16>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+    else if (g.L == 8) launch_wide<D, VT, uint16_t, 8>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+    else launch_any<D, VT, uint16_t>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
   }
   return hipGetLastError();
 }
