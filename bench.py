@@ -253,7 +253,7 @@ def main(argv=None):
         for _ in range(warmup):
             f(*call)
         torch.cuda.synchronize()
-        stage_ev = [ev.create(6) for _ in range(steps)]
+        stage_ev = [ev.create(2 * len(elsaa.STAGES)) for _ in range(steps)]
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
@@ -262,7 +262,7 @@ def main(argv=None):
         stop.record()
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(stop)
-        stage_ms = {st: float(np.mean([ev.elapsed_ms(e[j], e[j + 1]) for e in stage_ev]))
+        stage_ms = {st: float(np.mean([ev.elapsed_ms(e[2 * j], e[2 * j + 1]) for e in stage_ev]))
                     for j, st in enumerate(elsaa.STAGES)}
         for e in stage_ev:
             ev.destroy(e)

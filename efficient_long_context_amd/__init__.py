@@ -189,7 +189,8 @@ class Forward:
 
     def __call__(self, q, k, v, x_gate, hyperplanes, gate_w, gate_b, stream=None,
                  stage_events=None):
-        """stage_events: optional ctypes array of 6 hipEvent_t handles (see elsaa.h)."""
+        """stage_events: optional ctypes array of 10 hipEvent_t handles, a (begin,
+        end) pair per stage in STAGES order (see elsaa.h)."""
         torch = self.torch
         B, H, N, d, dg = (self.shape[x] for x in ("B", "H", "N", "d", "d_gate"))
         R = self.cfg["sort_bits"] + self.cfg["race_tables"] * self.cfg["race_bits"]

@@ -51,6 +51,11 @@ constexpr size_t kFusedLdsMax = 160 * 1024;  // LDS of one gfx950 workgroup
 // table does not fit in LDS and the sort + reduce pair is used instead.
 int race_fused_tile(const Geometry &g);
 
+// Fraction of the device's compute units the RACE build leaves idle on
+// average over its run (one workgroup per unit and CU on the single-kernel
+// path; the sort kernel's grid on the two-kernel path).
+double race_build_idle_fraction(const Geometry &g, int cus);
+
 // Launchers (each enqueues on `stream`, returns hipError_t of the launch).
 hipError_t launch_hash(const Geometry &g, const void *q, const void *k, const void *planes,
                        const Buffers &buf, hipStream_t stream);

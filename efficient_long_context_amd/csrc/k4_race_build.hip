@@ -490,6 +490,13 @@ int race_fused_tile(const Geometry &g) {
   return n64 < smax ? n64 : smax;
 }
 
+double race_build_idle_fraction(const Geometry &g, int cus) {
+  if (cus <= 0) return 0.0;
+  const long long units = static_cast<long long>(g.BH) * g.L;  // workgroups, one CU each
+  const long long rounds = (units + cus - 1) / cus;
+  return 1.0 - static_cast<double>(units) / static_cast<double>(rounds * cus);
+}
+
 hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
                              hipStream_t stream) {
   const int nb = g.nb_race;

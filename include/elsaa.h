@@ -21,7 +21,12 @@
  *
  * Conventions
  *   - Every data pointer is a DEVICE pointer owned by the caller; the library
- *     allocates nothing and keeps no state between calls.
+ *     allocates no memory.  Its only state is one extra stream and two events
+ *     per device, created on first use and kept until the process ends: the
+ *     RACE table build runs on that stream, forked from params->stream after
+ *     the hash stage and joined back before the fusion, so it overlaps the
+ *     sort and chunk attention.  The whole call is ordered on params->stream
+ *     as seen by the caller (including under stream capture).
  *   - All tensors are dense, row-major, contiguous.
  *   - Work is enqueued on params->stream (a hipStream_t; NULL = the default
  *     stream) and is asynchronous: the caller synchronises before reading.
@@ -103,12 +108,12 @@ typedef struct {
   size_t workspace_bytes;
   void *stream;        /* hipStream_t; NULL = default stream                      */
   elsaa_aux_t *aux;    /* host pointer to optional outputs; NULL = none           */
-  void *const *stage_events; /* host array of 6 hipEvent_t, or NULL.  Event i is
-                        recorded on `stream` just before stage i is enqueued
-                        (0 hash, 1 sort, 2 RACE build, 3 chunk attention,
-                        4 gather/gates/fusion) and event 5 after the last one,
-                        so elapsed(i, i+1) times stage i.  The caller creates
-                        and owns the events.                                     */
+  void *const *stage_events; /* host array of 10 hipEvent_t, or NULL.  Events
+                        2i and 2i+1 are recorded just before and just after
+                        stage i (0 hash, 1 sort, 2 RACE build, 3 chunk
+                        attention, 4 gather/gates/fusion) on the stream that
+                        runs it, so elapsed(2i, 2i+1) times stage i.  The
+                        caller creates and owns the events.                      */
 } elsaa_params_t;
 
 /* Host-only check of every field of *p except the device pointers' targets.
