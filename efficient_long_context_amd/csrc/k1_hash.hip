@@ -366,6 +366,7 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
       v |= __shfl_xor(v, 32);
       words[w] = v;
     }
+    const bool byte_codes = P == 8 && ns % 8 == 0 && L % 4 == 0;
     if (valid) {
       auto get = [&](int wd) -> uint32_t {
         uint32_t r = 0u;
@@ -375,11 +376,19 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
       };
       const long long out_row = static_cast<long long>(tensor) * rows + row;
       if (g == 0) {
-        scode[out_row] = static_cast<uint16_t>(bit_field(get, 0, ns));
+        scode[out_row] = static_cast<uint16_t>(words[0] & ((1u << ns) - 1u));  // ns <= 12
         // a projection binary64 could not decide: the exact pass redoes the row
         flags[out_row] = ((undecided_mask >> r16) & 0x0001000100010001ull) ? 1 : 0;
       }
-      if (rcb == 1) {
+      if (byte_codes) {
+        // 8-bit codes starting on a byte: code word j is bytes ns/8 + 4j .. +3
+        // of the plane mask, one byte-funnel of two mask words
+        uint32_t *rc = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(rcode) + out_row * L);
+        for (int j = g; j < L / 4; j += 4) {
+          const int bytepos = ns / 8 + 4 * j;
+          rc[j] = __builtin_amdgcn_alignbyte(get(bytepos / 4 + 1), get(bytepos / 4), bytepos % 4);
+        }
+      } else if (rcb == 1) {
         uint8_t *rc = reinterpret_cast<uint8_t *>(rcode) + out_row * L;
         if ((L & 3) == 0) {
           for (int j = g; j < L / 4; j += 4) {
