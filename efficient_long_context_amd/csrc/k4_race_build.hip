@@ -316,35 +316,18 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
     }
     __syncthreads();
 
-    // stable ranks: each wave walks its chunk in order, 64 keys per round
-    const unsigned long long lt = (1ull << lane) - 1ull;
+    // Positions: each key takes the next slot of its (wave, bucket) counter
+    // with an LDS atomic that returns the old value.  Keys of one bucket keep
+    // the order of the waves, and of the rounds inside a wave; inside one
+    // round the hardware's lane order decides.  The order only fixes how a
+    // bucket's rows are summed.
     for (int j8 = j_begin; j8 < j_end; j8 += 512) {
       uint32_t codes8[8];
       load_codes(j8, codes8);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int j = j8 + q * 64 + lane;
-        const bool valid = j < j_end;
-        const uint32_t code = valid ? codes8[q] : 0u;
-        unsigned long long mask = __ballot(valid);
-        for (int bit = 0; bit < P; ++bit) {
-          const bool set = (code >> bit) & 1u;
-          const unsigned long long bb = __ballot(set);
-          mask &= set ? bb : ~bb;
-        }
-        const int rank = __popcll(mask & lt);
-        const int leader = __ffsll(static_cast<long long>(mask)) - 1;
-        uint32_t before = 0;
-        if (valid && lane == leader) {
-          before = wc[code];
-          wc[code] = before + static_cast<uint32_t>(__popcll(mask));
-        }
-        before = __shfl(before, leader < 0 ? 0 : leader);
-        if (valid) lperm[before + rank] = static_cast<uint16_t>(j - t0);
-        // the leader's counter update must land before the next round reads it
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        if (j < j_end) lperm[atomicAdd(&wc[codes8[q]], 1u)] = static_cast<uint16_t>(j - t0);
       }
     }
     __syncthreads();
