@@ -100,6 +100,7 @@ int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
   g->sort_tiles = (p->N + elsaa::kSortTile - 1) / elsaa::kSortTile;
   g->bf16 = p->dtype == ELSAA_DTYPE_BF16;
   g->lambda = p->lambda;
+  g->cus = 256;
   return ELSAA_OK;
 }
 
@@ -222,7 +223,8 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
   // Overlap pays when the RACE build alone would leave compute units idle (a
   // partial last round of its one-workgroup-per-CU kernel); otherwise it runs
   // in order on the caller's stream.
-  const bool fork = elsaa::race_build_idle_fraction(g, side->cus) >= 0.25;
+  g.cus = side->cus;
+  const bool fork = elsaa::race_build_idle_fraction(g) >= 0.25;
   hipStream_t r = fork ? side->stream : s;
 
   // stage_events[2i] / [2i+1] bracket stage i on the stream that runs it

@@ -27,6 +27,7 @@ struct Geometry {
   int sort_tiles;  // ceil(N / kSortTile)
   bool bf16;
   float lambda;
+  int cus;       // compute units of the device (set at launch; 256 otherwise)
 };
 
 // Device buffers carved out of the caller's workspace.
@@ -54,7 +55,7 @@ int race_fused_tile(const Geometry &g);
 // Fraction of the device's compute units the RACE build leaves idle on
 // average over its run (one workgroup per unit and CU on the single-kernel
 // path; the sort kernel's grid on the two-kernel path).
-double race_build_idle_fraction(const Geometry &g, int cus);
+double race_build_idle_fraction(const Geometry &g);
 
 // Launchers (each enqueues on `stream`, returns hipError_t of the launch).
 hipError_t launch_hash(const Geometry &g, const void *q, const void *k, const void *planes,

@@ -236,7 +236,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *t
 
 template <typename CT, typename VT, int D>
 __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
-    const CT *__restrict__ kcodes, const VT *__restrict__ v, int N, int L, int P, int S,
+    const CT *__restrict__ kcodes, const VT *__restrict__ v, int N, int L, int P, int S, int G,
     long long units, VT *__restrict__ tsum, float *__restrict__ tcnt) {
   using PC = Piece<VT, D>;
   constexpr int W = kFusedWaves, kCols = PC::kCols, kLPR = PC::kLanesPerRow;
@@ -252,12 +252,18 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
   uint32_t *part = tot + nb;                    // [W * 64] scan
   uint16_t *lperm = reinterpret_cast<uint16_t *>(part + W * 64);  // [S + slack] tile-local key index
 
-  const long long tu = xcd_logical_block(blockIdx.x, gridDim.x);  // (b, h) * L + table
-  if (tu >= units) return;  // whole workgroup
+  // unit = ((b, h) * L + table) * G + bucket group; the G workgroups of a
+  // table each sort all its keys and sum the buckets [gb0, gb1)
+  const long long unit = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (unit >= units) return;  // whole workgroup
+  const long long tu = unit / G;
+  const int grp = static_cast<int>(unit % G);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave ranges scalar
   const long long bh = tu / L;
   const int l = static_cast<int>(tu % L);
+  const int gb0 = static_cast<int>(static_cast<long long>(nb) * grp / G);
+  const int gb1 = static_cast<int>(static_cast<long long>(nb) * (grp + 1) / G);
   const CT *c = kcodes + bh * N * static_cast<long long>(L) + l;  // code of key j at c[j * L]
   const VT *vb = v + bh * N * static_cast<long long>(D);
 
@@ -332,18 +338,21 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
     }
     __syncthreads();
 
-    // buckets owned: those whose run starts in [lo, hi); the last wave also
-    // owns the empty buckets that start at M
-    const int lo = static_cast<int>(static_cast<long long>(M) * wave / W);
-    const int hi = wave == W - 1 ? M + 1 : static_cast<int>(static_cast<long long>(M) * (wave + 1) / W);
-    int b0 = nb, b1 = nb;
-    for (int bb = 0; bb < nb; bb += 64) {
+    // The group's positions [PL, PH) split evenly over the waves: a wave owns
+    // the group's buckets whose run starts in [lo, hi); the last wave also
+    // owns the empty buckets that start at PH
+    const int PL = static_cast<int>(bst[gb0]), PH = static_cast<int>(bst[gb1]);
+    const long long Mg = PH - PL;
+    const int lo = PL + static_cast<int>(Mg * wave / W);
+    const int hi = wave == W - 1 ? PH + 1 : PL + static_cast<int>(Mg * (wave + 1) / W);
+    int b0 = gb1, b1 = gb1;
+    for (int bb = gb0; bb < gb1; bb += 64) {
       const int b = bb + lane;
-      const int st = b < nb ? static_cast<int>(bst[b]) : M + 1;
-      const unsigned long long ge_lo = __ballot(b < nb && st >= lo);
-      const unsigned long long ge_hi = __ballot(b < nb && st >= hi);
-      if (b0 == nb && ge_lo) b0 = bb + __builtin_ctzll(ge_lo);
-      if (b1 == nb && ge_hi) b1 = bb + __builtin_ctzll(ge_hi);
+      const int st = b < gb1 ? static_cast<int>(bst[b]) : PH + 1;
+      const unsigned long long ge_lo = __ballot(b < gb1 && st >= lo);
+      const unsigned long long ge_hi = __ballot(b < gb1 && st >= hi);
+      if (b0 == gb1 && ge_lo) b0 = bb + __builtin_ctzll(ge_lo);
+      if (b1 == gb1 && ge_hi) b1 = bb + __builtin_ctzll(ge_hi);
     }
     const int p_lo = static_cast<int>(bst[b0]), p_hi = static_cast<int>(bst[b1]);
 
@@ -427,8 +436,30 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
 
   // the table leaves in the value dtype (sums were kept in binary32)
   VT *ts = tsum + tu * nb * static_cast<long long>(D);
-  for (int i = 4 * tid; i < nb * D; i += 4 * W * 64) Elem<VT>::store4(ts + i, acc + i);
-  for (int i = tid; i < nb; i += W * 64) tcnt[tu * nb + i] = static_cast<float>(tot[i]);
+  for (int i = gb0 * D + 4 * tid; i < gb1 * D; i += 4 * W * 64) Elem<VT>::store4(ts + i, acc + i);
+  for (int i = gb0 + tid; i < gb1; i += W * 64) tcnt[tu * nb + i] = static_cast<float>(tot[i]);
+}
+
+#ifndef ELSAA_RACE_GROUPS
+#define ELSAA_RACE_GROUPS 0  // 0: chosen per shape
+#endif
+
+double idle_fraction(long long units, int cus) {
+  if (cus <= 0) return 0.0;
+  const long long rounds = (units + cus - 1) / cus;
+  return 1.0 - static_cast<double>(units) / static_cast<double>(rounds * cus);
+}
+
+// Bucket groups per table on the single-kernel path: each group is a
+// workgroup that sorts the table's keys and sums its share of the buckets.
+// Groups repeat the sort, so they are used only to give small problems (fewer
+// tables than compute units) enough workgroups: up to 4 per table.
+int race_groups(const Geometry &g) {
+  if (ELSAA_RACE_GROUPS > 0) return ELSAA_RACE_GROUPS;
+  const long long tables = static_cast<long long>(g.BH) * g.L;
+  int G = 1;
+  while (G < 4 && G < g.nb_race && tables * G < g.cus) G *= 2;
+  return G;
 }
 
 // LDS bytes of the fused kernel for tile size S (0 if the table does not fit).
@@ -442,16 +473,17 @@ size_t fused_lds_bytes(int nb, int D, int S) {
 template <typename CT, typename VT>
 void launch_fused(const Geometry &g, const void *rk, const void *v, int S, size_t lds,
                   const Buffers &buf, hipStream_t stream) {
-  const long long units = static_cast<long long>(g.BH) * g.L;
+  const int G = race_groups(g);
+  const long long units = static_cast<long long>(g.BH) * g.L * G;
   const dim3 grid(static_cast<unsigned>((units + kXcdCount - 1) / kXcdCount * kXcdCount));
   const dim3 block(kFusedWaves * 64);
   if (g.D == 64)
     hipLaunchKernelGGL((elsaa_k4_race_fused<CT, VT, 64>), grid, block, lds, stream,
-                       static_cast<const CT *>(rk), static_cast<const VT *>(v), g.N, g.L, g.P, S,
+                       static_cast<const CT *>(rk), static_cast<const VT *>(v), g.N, g.L, g.P, S, G,
                        units, static_cast<VT *>(buf.tsum), buf.tcnt);
   else
     hipLaunchKernelGGL((elsaa_k4_race_fused<CT, VT, 128>), grid, block, lds, stream,
-                       static_cast<const CT *>(rk), static_cast<const VT *>(v), g.N, g.L, g.P, S,
+                       static_cast<const CT *>(rk), static_cast<const VT *>(v), g.N, g.L, g.P, S, G,
                        units, static_cast<VT *>(buf.tsum), buf.tcnt);
 }
 
@@ -473,11 +505,9 @@ int race_fused_tile(const Geometry &g) {
   return n64 < smax ? n64 : smax;
 }
 
-double race_build_idle_fraction(const Geometry &g, int cus) {
-  if (cus <= 0) return 0.0;
-  const long long units = static_cast<long long>(g.BH) * g.L;  // workgroups, one CU each
-  const long long rounds = (units + cus - 1) / cus;
-  return 1.0 - static_cast<double>(units) / static_cast<double>(rounds * cus);
+double race_build_idle_fraction(const Geometry &g) {
+  const long long tables = static_cast<long long>(g.BH) * g.L;  // workgroups, one CU each
+  return idle_fraction(race_fused_tile(g) > 0 ? tables * race_groups(g) : tables, g.cus);
 }
 
 hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
