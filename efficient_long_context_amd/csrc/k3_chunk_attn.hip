@@ -29,21 +29,23 @@ constexpr int kKBlock = 64;
 
 
 
-template <int D, int QT>
+template <int D, int QT, int NB>
 __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N, int w,
     int tiles_per_seg, int n_tiles, float scale_log2, uint16_t *__restrict__ o_s,
     float *__restrict__ lse) {
   constexpr int kThreads = QT * 4;      // 16 queries per wave
+  constexpr int kKeys = NB * kKBlock;   // keys staged at once
   constexpr int kKRow = D + 8;          // padded K row in LDS (bf16 elements)
-  constexpr int kVRow = kKBlock + 8;    // padded V^T row in LDS
-  constexpr int kKChunks = kKBlock * (D / 8);              // 16-byte pieces of a K block
-  constexpr int kVPairs = (kKBlock / 2) * (D / 8);         // (key pair, 8-column) pieces of V
+  constexpr int kVRow = kKeys + 8;      // padded V^T row in LDS
+  constexpr int kKChunks = kKeys * (D / 8);          // 16-byte pieces of the staged K rows
+  constexpr int kVPairs = (kKeys / 2) * (D / 8);     // (key pair, 8-column) pieces of V
   constexpr int kKPer = (kKChunks + kThreads - 1) / kThreads;
   constexpr int kVPer = (kVPairs + kThreads - 1) / kThreads;
-  __shared__ __align__(16) uint16_t Ks[kKBlock * kKRow];
-  __shared__ __align__(16) uint16_t Vt[D * kVRow];
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t *Ks = smem;                  // [kKeys][kKRow]
+  uint16_t *Vt = smem + kKeys * kKRow;  // [D][kVRow]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
@@ -65,46 +67,46 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
   for (int kk = 0; kk < D / 32; ++kk)
     bq[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(qrow + kk * 32 + g * 8));
 
-  // Block loader: K piece i -> row i / (D/8), chunk i % (D/8); V piece i -> key
-  // pair i % 32, chunk i / 32.  Pieces past the count are clamped reloads.
-  // The permutation entries of a block are loaded one block ahead of its rows,
-  // so a block costs one memory round trip, not two.
-  struct Idx { int kj[kKPer], v0[kVPer], v1[kVPer]; };
-  auto load_idx = [&](int kb, Idx &ix) {
-    kb = kb < hi - kKBlock ? kb : hi - kKBlock;  // clamped: past the window reloads the last block
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY;  // running max of score * log2(e) / sqrt(d)
+  float l_part = 0.0f;  // this lane's share of the running sum
+
+  // Stages of up to NB key blocks: all of a stage's rows are requested at
+  // once (K piece i -> row i / (D/8), chunk i % (D/8); V piece i -> key pair
+  // i % (kKeys/2), chunk i / (kKeys/2)), staged in LDS (V transposed) behind
+  // one barrier, then the stage's blocks are processed without further syncs.
+  // With a window of 2w <= kKeys keys the whole window is one stage.
+  for (int s0 = lo; s0 < hi; s0 += kKeys) {
+    const int nkeys = hi - s0 < kKeys ? hi - s0 : kKeys;  // a multiple of 64
+    int kj[kKPer], v0[kVPer], v1[kVPer];
 #pragma unroll
     for (int p = 0; p < kKPer; ++p) {
-      int i = tid + p * kThreads;
-      i = i < kKChunks ? i : kKChunks - 1;
-      ix.kj[p] = pk[kb + i / (D / 8)];
+      int j = (tid + p * kThreads) / (D / 8);
+      j = j < nkeys ? j : nkeys - 1;  // clamped: rows past the stage are reloads, not used
+      kj[p] = pk[s0 + j];
     }
 #pragma unroll
     for (int p = 0; p < kVPer; ++p) {
-      int i = tid + p * kThreads;
-      i = i < kVPairs ? i : kVPairs - 1;
-      const int jp = i % (kKBlock / 2);
-      ix.v0[p] = pk[kb + 2 * jp];
-      ix.v1[p] = pk[kb + 2 * jp + 1];
+      int jp = (tid + p * kThreads) % (kKeys / 2);
+      jp = 2 * jp + 1 < nkeys ? jp : nkeys / 2 - 1;
+      v0[p] = pk[s0 + 2 * jp];
+      v1[p] = pk[s0 + 2 * jp + 1];
     }
-  };
-  u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer];
-  auto load_rows = [&](const Idx &ix) {
+    u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer];
 #pragma unroll
     for (int p = 0; p < kKPer; ++p) {
-      int i = tid + p * kThreads;
-      i = i < kKChunks ? i : kKChunks - 1;
-      kreg[p] = *reinterpret_cast<const u16x8 *>(k + (seg + ix.kj[p]) * D + (i % (D / 8)) * 8);
+      const int i = tid + p * kThreads;
+      kreg[p] = *reinterpret_cast<const u16x8 *>(k + (seg + kj[p]) * D + (i % (D / 8)) * 8);
     }
 #pragma unroll
     for (int p = 0; p < kVPer; ++p) {
-      int i = tid + p * kThreads;
-      i = i < kVPairs ? i : kVPairs - 1;
-      const int ch = i / (kKBlock / 2);
-      vreg0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + ix.v0[p]) * D + ch * 8);
-      vreg1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + ix.v1[p]) * D + ch * 8);
+      const int ch = ((tid + p * kThreads) / (kKeys / 2)) % (D / 8);
+      vreg0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + v0[p]) * D + ch * 8);
+      vreg1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + v1[p]) * D + ch * 8);
     }
-  };
-  auto store_block = [&]() {
+    if (s0 != lo) __syncthreads();  // previous stage fully consumed
 #pragma unroll
     for (int p = 0; p < kKPer; ++p) {
       const int i = tid + p * kThreads;
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
     for (int p = 0; p < kVPer; ++p) {
       const int i = tid + p * kThreads;
       if (i < kVPairs) {
-        const int jp = i % (kKBlock / 2), ch = i / (kKBlock / 2);
+        const int jp = i % (kKeys / 2), ch = i / (kKeys / 2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t word = static_cast<uint32_t>(vreg0[p][e]) | (static_cast<uint32_t>(vreg1[p][e]) << 16);
@@ -125,76 +127,60 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
         }
       }
     }
-  };
-
-  f32x4 o[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY;  // running max of score * log2(e) / sqrt(d)
-  float l_part = 0.0f;  // this lane's share of the running sum
-
-  Idx ix;
-  load_idx(lo, ix);
-  load_rows(ix);
-  load_idx(lo + kKBlock, ix);
-  for (int kb = lo; kb < hi; kb += kKBlock) {
-    __syncthreads();  // previous block fully consumed
-    store_block();
     __syncthreads();
-    // next block's rows (clamped past the window) and the block after's
-    // permutation entries are in flight during the math
-    load_rows(ix);
-    load_idx(kb + 2 * kKBlock, ix);
 
-    // S^T tiles: lane holds keys kt*16 + g*4 + i for query r16
-    f32x4 s[kKBlock / 16];
+    for (int blk = 0; blk < nkeys / kKBlock; ++blk) {
+      const uint16_t *Kb = Ks + blk * kKBlock * kKRow;
+      // S^T tiles: lane holds keys kt*16 + g*4 + i for query r16
+      f32x4 s[kKBlock / 16];
 #pragma unroll
-    for (int kt = 0; kt < kKBlock / 16; ++kt) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int kt = 0; kt < kKBlock / 16; ++kt) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u16x8 *>(Ks + (kt * 16 + r16) * kKRow + kk * 32 + g * 8));
-        acc = mfma16x16x32(a, bq[kk], acc);
+        for (int kk = 0; kk < D / 32; ++kk) {
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u16x8 *>(Kb + (kt * 16 + r16) * kKRow + kk * 32 + g * 8));
+          acc = mfma16x16x32(a, bq[kk], acc);
+        }
+        s[kt] = acc;
       }
-      s[kt] = acc;
-    }
-    float bmax = -INFINITY;
+      float bmax = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < kKBlock / 16; ++kt)
+      for (int kt = 0; kt < kKBlock / 16; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[kt][i]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float m_new = fmaxf(m, bmax * scale_log2);
-    const float corr = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block (m = -inf)
-    m = m_new;
-    l_part *= corr;
+        for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[kt][i]);
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      const float m_new = fmaxf(m, bmax * scale_log2);
+      const float corr = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block (m = -inf)
+      m = m_new;
+      l_part *= corr;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] *= corr;
+      for (int dt = 0; dt < D / 16; ++dt) o[dt] *= corr;
 
-    // P = exp2(s * scale - m); PV over two 32-key steps
+      // P = exp2(s * scale - m); PV over two 32-key steps
 #pragma unroll
-    for (int m2 = 0; m2 < kKBlock / 32; ++m2) {
-      uint32_t pw[4];
+      for (int m2 = 0; m2 < kKBlock / 32; ++m2) {
+        uint32_t pw[4];
 #pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2][i], scale_log2, -m));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2][i + 1], scale_log2, -m));
-        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2 + 1][i], scale_log2, -m));
-        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2 + 1][i + 1], scale_log2, -m));
-        l_part += (p0 + p1) + (p2 + p3);
-        pw[i / 2] = pack_bf16x2(p0, p1);
-        pw[2 + i / 2] = pack_bf16x2(p2, p3);
-      }
-      const bf16x8 bp = __builtin_bit_cast(bf16x8, (uint4){pw[0], pw[1], pw[2], pw[3]});
+        for (int i = 0; i < 4; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2][i], scale_log2, -m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2][i + 1], scale_log2, -m));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2 + 1][i], scale_log2, -m));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2 + 1][i + 1], scale_log2, -m));
+          l_part += (p0 + p1) + (p2 + p3);
+          pw[i / 2] = pack_bf16x2(p0, p1);
+          pw[2 + i / 2] = pack_bf16x2(p2, p3);
+        }
+        const bf16x8 bp = __builtin_bit_cast(bf16x8, (uint4){pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const uint16_t *vr = Vt + (dt * 16 + r16) * kVRow + m2 * 32 + g * 4;
-        const uint2 lo4 = *reinterpret_cast<const uint2 *>(vr);
-        const uint2 hi4 = *reinterpret_cast<const uint2 *>(vr + 16);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, (uint4){lo4.x, lo4.y, hi4.x, hi4.y});
-        o[dt] = mfma16x16x32(av, bp, o[dt]);
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const uint16_t *vr = Vt + (dt * 16 + r16) * kVRow + blk * kKBlock + m2 * 32 + g * 4;
+          const uint2 lo4 = *reinterpret_cast<const uint2 *>(vr);
+          const uint2 hi4 = *reinterpret_cast<const uint2 *>(vr + 16);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, (uint4){lo4.x, lo4.y, hi4.x, hi4.y});
+          o[dt] = mfma16x16x32(av, bp, o[dt]);
+        }
       }
     }
   }
@@ -249,14 +235,19 @@ __global__ __launch_bounds__(128) void elsaa_k3_chunk_attn_f32(
   lse[seg + qidx] = (m + log2f(l)) * 0.69314718055994530942f;
 }
 
-template <int D, int QT>
+// LDS bytes of the bf16 kernel staging NB key blocks.
+constexpr size_t attn_lds_bytes(int D, int NB) {
+  return (static_cast<size_t>(NB) * kKBlock * (D + 8) + static_cast<size_t>(D) * (NB * kKBlock + 8)) * 2;
+}
+
+template <int D, int QT, int NB>
 hipError_t launch_bf16(const Geometry &g, const void *q, const void *k, const void *v,
                        const Buffers &buf, float scale_log2, hipStream_t stream) {
   const int tiles_per_seg = g.N / QT;
   const long long n_tiles = static_cast<long long>(tiles_per_seg) * g.BH;
   const long long grid = (n_tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
-  hipLaunchKernelGGL((elsaa_k3_chunk_attn_bf16<D, QT>), dim3(static_cast<unsigned>(grid)),
-                     dim3(QT * 4), 0, stream, static_cast<const uint16_t *>(q),
+  hipLaunchKernelGGL((elsaa_k3_chunk_attn_bf16<D, QT, NB>), dim3(static_cast<unsigned>(grid)),
+                     dim3(QT * 4), attn_lds_bytes(D, NB), stream, static_cast<const uint16_t *>(q),
                      static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), buf.perm,
                      buf.perm + g.rows, g.N, g.w, tiles_per_seg, static_cast<int>(n_tiles),
                      scale_log2, static_cast<uint16_t *>(buf.o_s), buf.lse);
@@ -271,12 +262,15 @@ hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *
   const int32_t *pq = buf.perm;
   const int32_t *pk = buf.perm + g.rows;
   if (g.bf16) {
+    // 128-query tiles when w allows; key stages of 4 blocks (d = 64: the whole
+    // 256-key window of w = 128) or 2, keeping LDS <= 72 KB (two workgroups
+    // per CU)
     const bool wide = g.w % 128 == 0;
     if (g.D == 64)
-      return wide ? launch_bf16<64, 128>(g, q, k, v, buf, scale_log2, stream)
-                  : launch_bf16<64, 64>(g, q, k, v, buf, scale_log2, stream);
-    return wide ? launch_bf16<128, 128>(g, q, k, v, buf, scale_log2, stream)
-                : launch_bf16<128, 64>(g, q, k, v, buf, scale_log2, stream);
+      return wide ? launch_bf16<64, 128, 4>(g, q, k, v, buf, scale_log2, stream)
+                  : launch_bf16<64, 64, 2>(g, q, k, v, buf, scale_log2, stream);
+    return wide ? launch_bf16<128, 128, 2>(g, q, k, v, buf, scale_log2, stream)
+                : launch_bf16<128, 64, 2>(g, q, k, v, buf, scale_log2, stream);
   }
   const dim3 grid((g.N + 127) / 128, g.BH);
   if (g.D == 64)
