@@ -25,8 +25,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-# Per-source extra flags (none needed at present).
-EXTRA: dict = {}
+# Per-source extra flags.  The hash kernel reads every MFMA result with plain
+# VALU instructions; its accumulators are kept in VGPRs (no AGPR copies).
+EXTRA: dict = {"k1_hash.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

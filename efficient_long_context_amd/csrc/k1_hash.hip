@@ -19,7 +19,6 @@
 namespace elsaa {
 namespace {
 
-constexpr int kTilesPerWg = 64;  // 1024 rows per workgroup
 
 __device__ __forceinline__ bool in_safe_range(float a) {
   a = fabsf(a);
@@ -173,11 +172,29 @@ __device__ __forceinline__ uint32_t bit_field(GetWord get, int pos, int n) {
 // partial sums).  Projections within tau of zero are re-decided in binary64 by
 // the whole wave; planes outside the range, rows that fail the check, and
 // projections binary64 cannot decide send the row to the exact fix-up kernel.
+//
+// Bits.  A lane's MFMA result holds four planes of one row.  Rather than
+// testing each projection, its sign bit is shifted into a per-lane word (one
+// v_alignbit per projection) and the smallest |projection| of the lane is
+// kept (v_min3); only a wave with some projection at or below tau redoes the
+// projections and re-decides those one by one.  The planes are staged in LDS
+// in the order that makes the shifted-in bits land on their final positions:
+// lane group g of tile pair (2w, 2w+1) owns byte g of mask word w (see
+// tile_plane); a last unpaired tile gives each group a nibble.  Padding rows
+// of the last tile repeat plane 0, so every projection is real and no
+// per-lane padding test is needed (bits of planes >= R are never read).
+//
+// Plane held by row m of plane tile pt, for npt tiles in all.
+__host__ __device__ constexpr int tile_plane(int pt, int m, int npt) {
+  return 32 * (pt >> 1) + ((pt | 1) < npt ? 8 * (m >> 2) + 7 - 4 * (pt & 1) : 4 * (m >> 2) + 3) - (m & 3);
+}
+
 template <int D, int NPT>
 __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
     const uint16_t *__restrict__ xq, const uint16_t *__restrict__ xk,
     const uint16_t *__restrict__ planes, int R, int ns, int L, int P, long long rows,
-    uint16_t *__restrict__ scode, void *__restrict__ rcode, int rcb, uint8_t *__restrict__ flags) {
+    uint16_t *__restrict__ scode, void *__restrict__ rcode, int rcb, uint8_t *__restrict__ flags,
+    long long rows_per_wg) {
   constexpr int kLdsRow = D + 8;  // padded row (bf16 elements)
   constexpr int kRPad = NPT * 16;
   constexpr int kWords = (kRPad + 31) / 32;
@@ -191,18 +208,18 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
   const int tensor = blockIdx.y;
   const uint16_t *x = tensor ? xk : xq;
 
-  // Stage the hyperplanes (zero rows beyond R).
+  // Stage the hyperplanes in tile order (rows past R repeat plane 0).
   for (int idx = tid; idx < kRPad * (D / 8); idx += 256) {
-    const int t = idx / (D / 8), ch = idx % (D / 8);
-    u16x8 val = (u16x8)0;
-    if (t < R) val = *reinterpret_cast<const u16x8 *>(planes + static_cast<size_t>(t) * D + ch * 8);
-    *reinterpret_cast<u16x8 *>(sp + t * kLdsRow + ch * 8) = val;
+    const int pr = idx / (D / 8), ch = idx % (D / 8);
+    const int t = tile_plane(pr >> 4, pr & 15, NPT);
+    const u16x8 val = *reinterpret_cast<const u16x8 *>(planes + static_cast<size_t>(t < R ? t : 0) * D + ch * 8);
+    *reinterpret_cast<u16x8 *>(sp + pr * kLdsRow + ch * 8) = val;
   }
   __syncthreads();
-  if (wave == 0) {  // plane norms: wave 0, lane t handles planes t, t+64, ...
+  if (wave == 0) {  // plane norms: wave 0, lane t handles staged rows t, t+64, ...
     float rmax = 0.0f;
     int ok = 1;
-    for (int t = lane; t < R; t += 64) {
+    for (int t = lane; t < kRPad; t += 64) {
       float ss = 0.0f, amax = 0.0f;
       for (int e = 0; e < D; ++e) {
         const float f = bf16_bits_to_f32(sp[t * kLdsRow + e]);
@@ -227,8 +244,8 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
   const float c_abs = static_cast<float>(D) * 0x1p-124f;
 
   const int g = lane >> 4, r16 = lane & 15;
-  const long long row_begin = static_cast<long long>(blockIdx.x) * (kTilesPerWg * 16);
-  const long long row_end = row_begin + kTilesPerWg * 16 < rows ? row_begin + kTilesPerWg * 16 : rows;
+  const long long row_begin = static_cast<long long>(blockIdx.x) * rows_per_wg;
+  const long long row_end = row_begin + rows_per_wg < rows ? row_begin + rows_per_wg : rows;
 
   u16x8 pre[kPieces];
   auto load_step = [&](long long r0) {
@@ -257,25 +274,25 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
     const bool valid = row < row_end;
     const uint16_t *xr = sx + lrow * kLdsRow;
 
-    // |x| and max |x_i| of the row (lane group g holds a quarter of it)
-    float ss = 0.0f, amax = 0.0f;
+    // |x|^2 of the row (lane group g holds a quarter of it): bfloat16 squares
+    // are exact in binary32, summed by v_dot2_f32_bf16
+    float ss = 0.0f;
     bf16x8 b[D / 32];
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      const u16x8 raw = *reinterpret_cast<const u16x8 *>(xr + kk * 32 + g * 8);
+      const u32x4 raw = *reinterpret_cast<const u32x4 *>(xr + kk * 32 + g * 8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float f = bf16_bits_to_f32(raw[i]);
-        ss = __builtin_fmaf(f, f, ss);
-        amax = fmaxf(amax, fabsf(f));
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wv = raw[i];  // (bit_cast of raw[i] itself reads element 0 with this clang)
+        const bf16x2 h = __builtin_bit_cast(bf16x2, wv);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss, false);
       }
       b[kk] = __builtin_bit_cast(bf16x8, raw);
     }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const bool row_ok = planes_ok && amax >= 0x1p-40f && amax <= 0x1p40f;
+    ss = sum_over_lane_groups<16>(ss);
+    // Range check: |x|^2 in [2^-72, 2^80] puts every element at or below 2^40
+    // and the largest at or above 2^-40 (d <= 128); NaN and Inf fail it.
+    const bool row_ok = planes_ok && ss >= 0x1p-72f && ss <= 0x1p80f;
     // tau = +inf sends every projection of this row to the exact path
     const float tau = row_ok ? __builtin_fmaf(sqrtf(ss), c_plane, c_abs) : INFINITY;
 
@@ -287,84 +304,103 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
             bf16x8, *reinterpret_cast<const u16x8 *>(sp + (pt * 16 + r16) * kLdsRow + kk * 32 + g * 8));
         a4 = mfma16x16x32(a, b[kk], a4);
       }
-      return a4;  // lane holds <plane pt*16 + g*4 + i, row r16>
+      return a4;  // lane holds the projections of row r16 on staged rows pt*16 + g*4 + i
+    };
+    // bit position of projection (pt, i) in its lane's word, in shifted-in order
+    auto bit_pos = [](int pt, int i) {
+      return ((pt | 1) < NPT ? 7 - 4 * (pt & 1) : 3) - i;
     };
     uint32_t words[kWords];
 #pragma unroll
     for (int w = 0; w < kWords; ++w) words[w] = 0u;
-    unsigned long long unsure = 0ull;  // bit 4 pt + i: projection not certified
+    float amin = INFINITY;  // smallest |projection| of this lane
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) {
       const f32x4 a4 = project(pt);
-      // bit position before the per-lane shift by 4g is (pt & 1) * 16 + i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        words[pt >> 1] |= (a4[i] > 0.0f ? 1u : 0u) << ((pt & 1) * 16 + i);
-        const bool u = !(fabsf(a4[i]) > tau) && pt * 16 + g * 4 + i < R;  // padding planes: bit 0
-        unsure |= static_cast<unsigned long long>(u) << (pt * 4 + i);
+        words[pt >> 1] = __builtin_amdgcn_alignbit(words[pt >> 1], __float_as_uint(a4[i]), 31);
+        amin = fminf(amin, fabsf(a4[i]));
       }
     }
-    // Rows outside the certified range go to the exact fix-up kernel whole.
+    // sign bit 1 = negative: the code bit is its complement wherever |p| > tau
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) words[w] = ~words[w];
     bool undecided = valid && !row_ok;
-    if (!valid || !row_ok) unsure = 0ull;
     // Rare: each uncertified projection is re-decided by the whole wave, lanes
     // over the d products (exact in binary64), summed by a butterfly of depth
     // log2(64) (+1 for d = 128 with two products per lane); the sign is taken
     // when |sum| exceeds (depth + 1) 2^-52 sum |p_i|, else from the exact
     // integer sum; only a product exponent span too wide for it flags the row.
-    for (unsigned long long pending = __ballot(unsure != 0ull); pending;
-         pending = __ballot(unsure != 0ull)) {
-      const int src = __builtin_ctzll(pending);  // wave-uniform
-      const unsigned long long sb =
-          static_cast<unsigned long long>(static_cast<uint32_t>(__builtin_amdgcn_readlane(
-              static_cast<int>(unsure), src))) |
-          (static_cast<unsigned long long>(static_cast<uint32_t>(
-               __builtin_amdgcn_readlane(static_cast<int>(unsure >> 32), src)))
-           << 32);
-      const int bpos = __builtin_ctzll(sb);
-      const int t = (bpos >> 2) * 16 + (src >> 4) * 4 + (bpos & 3);
-      const uint16_t *xs = sx + (wave * 16 + (src & 15)) * kLdsRow;
-      const uint16_t *ps = sp + t * kLdsRow;
-      double sum = 0.0, sabs = 0.0;
+    if (__ballot(valid && !(amin > tau)) != 0ull) {
+      unsigned long long unsure = 0ull;  // bit 4 pt + i: projection not certified
+      // recomputed, not kept: the plane reads below must not be merged with the
+      // first pass's, which would hold all its projections live
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int e = lane; e < D; e += 64) {
-        const double prod = static_cast<double>(bf16_bits_to_f32(xs[e])) *
-                            static_cast<double>(bf16_bits_to_f32(ps[e]));  // exact
-        sum += prod;
-        sabs += fabs(prod);
+      for (int pt = 0; pt < NPT; ++pt) {
+        const f32x4 a4 = project(pt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          unsure |= static_cast<unsigned long long>(!(fabsf(a4[i]) > tau)) << (pt * 4 + i);
       }
+      // rows outside the certified range go to the exact fix-up kernel whole
+      if (!valid || !row_ok) unsure = 0ull;
+      for (unsigned long long pending = __ballot(unsure != 0ull); pending;
+           pending = __ballot(unsure != 0ull)) {
+        const int src = __builtin_ctzll(pending);  // wave-uniform
+        const unsigned long long sb =
+            static_cast<unsigned long long>(static_cast<uint32_t>(__builtin_amdgcn_readlane(
+                static_cast<int>(unsure), src))) |
+            (static_cast<unsigned long long>(static_cast<uint32_t>(
+                 __builtin_amdgcn_readlane(static_cast<int>(unsure >> 32), src)))
+             << 32);
+        const int bpos = __builtin_ctzll(sb);
+        const uint16_t *xs = sx + (wave * 16 + (src & 15)) * kLdsRow;
+        const uint16_t *ps = sp + ((bpos >> 2) * 16 + (src >> 4) * 4 + (bpos & 3)) * kLdsRow;
+        double sum = 0.0, sabs = 0.0;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        sum += __shfl_xor(sum, off);
-        sabs += __shfl_xor(sabs, off);
-      }
-      constexpr int kDepth = 6 + D / 64;
-      const double bound = static_cast<double>(kDepth + 1) * 0x1p-52 * sabs;
-      // within the bound (exact ties included): the integer sum decides
-      int sgn = sum > bound ? 1 : (sum < -bound ? -1 : 2);
-      if (__builtin_amdgcn_readlane(sgn, src) == 2) sgn = wave_exact_sign_bf16<D>(xs, ps, lane);
-      if (lane == src) {
-        unsure &= unsure - 1ull;
-        if (sgn != 2) {
-          const int pt = bpos >> 2;
-          const uint32_t m = 1u << ((pt & 1) * 16 + (bpos & 3));
+        for (int e = lane; e < D; e += 64) {
+          const double prod = static_cast<double>(bf16_bits_to_f32(xs[e])) *
+                              static_cast<double>(bf16_bits_to_f32(ps[e]));  // exact
+          sum += prod;
+          sabs += fabs(prod);
+        }
 #pragma unroll
-          for (int q = 0; q < kWords; ++q)
-            if ((pt >> 1) == q) words[q] = sgn > 0 ? (words[q] | m) : (words[q] & ~m);
-        } else {
-          undecided = true;
+        for (int off = 32; off > 0; off >>= 1) {
+          sum += __shfl_xor(sum, off);
+          sabs += __shfl_xor(sabs, off);
+        }
+        constexpr int kDepth = 6 + D / 64;
+        const double bound = static_cast<double>(kDepth + 1) * 0x1p-52 * sabs;
+        // within the bound (exact ties included): the integer sum decides
+        int sgn = sum > bound ? 1 : (sum < -bound ? -1 : 2);
+        if (__builtin_amdgcn_readlane(sgn, src) == 2) sgn = wave_exact_sign_bf16<D>(xs, ps, lane);
+        if (lane == src) {
+          unsure &= unsure - 1ull;
+          if (sgn != 2) {
+            const int pt = bpos >> 2;
+            const uint32_t m = 1u << bit_pos(pt, bpos & 3);
+#pragma unroll
+            for (int q = 0; q < kWords; ++q)
+              if ((pt >> 1) == q) words[q] = sgn > 0 ? (words[q] | m) : (words[q] & ~m);
+          } else {
+            undecided = true;
+          }
         }
       }
     }
     const unsigned long long undecided_mask = __ballot(undecided);
-    // place group g's bits, then OR the four groups: every lane of a row holds
-    // the row's full plane mask (planes >= R are zero rows: bit 0)
+    // place group g's byte (nibble for an unpaired last tile), then OR the
+    // four groups: every lane of a row holds the row's full plane mask
 #pragma unroll
     for (int w = 0; w < kWords; ++w) {
-      uint32_t v = words[w] << (g * 4);
-      v |= __shfl_xor(v, 16);
-      v |= __shfl_xor(v, 32);
-      words[w] = v;
+      const int nbits = 2 * w + 1 < NPT ? 8 : 4;
+      uint32_t v = (words[w] & ((1u << nbits) - 1u)) << (g * nbits);
+      const auto r16s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      v = r16s[0] | r16s[1];
+      const auto r32s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      words[w] = r32s[0] | r32s[1];
     }
     const bool byte_codes = P == 8 && ns % 8 == 0 && L % 4 == 0;
     if (valid) {
@@ -560,12 +596,26 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_f32(
 template <int D, int NPT>
 void launch_bf16(const Geometry &g, const void *q, const void *k, const void *planes,
                  const Buffers &buf, hipStream_t stream) {
-  const long long rows_per_wg = kTilesPerWg * 16;
-  const dim3 grid(static_cast<unsigned>((g.rows + rows_per_wg - 1) / rows_per_wg), 2);
+  // One round of workgroups, equal shares of 64-row steps: as many
+  // workgroups as the device holds at once (two tensors, grid.y), so no
+  // partial second round leaves compute units idle.
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, elsaa_k1_hash_bf16<D, NPT>, 256, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    return n;
+  }();
+  const long long steps = (g.rows + 63) / 64;
+  long long wgs = static_cast<long long>(g.cus) * per_cu / 2;
+  wgs = wgs < 1 ? 1 : (wgs < steps ? wgs : steps);
+  const long long steps_per_wg = (steps + wgs - 1) / wgs;
+  wgs = (steps + steps_per_wg - 1) / steps_per_wg;
+  const dim3 grid(static_cast<unsigned>(wgs), 2);
   hipLaunchKernelGGL((elsaa_k1_hash_bf16<D, NPT>), grid, dim3(256), 0, stream,
                      static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                      static_cast<const uint16_t *>(planes), g.R, g.ns, g.L, g.P, g.rows, buf.scode,
-                     buf.rcode, g.rcb, buf.flags);
+                     buf.rcode, g.rcb, buf.flags, steps_per_wg * 64);
 }
 
 template <int D, int NPT = 1>

@@ -216,6 +216,67 @@ template <typename VT, int D> struct Piece {
   }
 };
 
+// Lanes l and l ^ m (m a multiple of kLPR below 64) hold partial sums of the
+// same kCols columns.  Sums them, leaving each lane kCols / (64 / kLPR) of the
+// column totals: one exchange per lane bit halves what a lane holds (bit 4 and
+// bit 5 with the gfx950 permlane swaps, whose two outputs are the lane's own
+// and its partner's value of the pair's even or odd member; bit 3 with a DPP
+// row rotation by 8).  The lane keeps column transposed_column(m) in out[m].
+template <int kCols, int kLPR>
+__device__ __forceinline__ void lane_group_transpose_sum(const float (&in)[kCols],
+                                                         float (&out)[kCols * kLPR / 64], int lane) {
+  static_assert(kLPR == 8 || kLPR == 16 || kLPR == 32, "lane group width");
+  float v[kCols];
+#pragma unroll
+  for (int k = 0; k < kCols; ++k) v[k] = in[k];
+  int n = kCols;
+  if constexpr (kLPR <= 16) {  // lane bit 4: keep index 2j + bit4
+#pragma unroll
+    for (int j = 0; j < kCols / 2; ++j) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2 * j]), __float_as_uint(v[2 * j + 1]),
+                                                      false, false);
+      v[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    n /= 2;
+  }
+  {  // lane bit 5: keep index 2j + bit5
+#pragma unroll
+    for (int j = 0; j < kCols / 2; ++j) {
+      if (2 * j + 1 < n) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2 * j]),
+                                                        __float_as_uint(v[2 * j + 1]), false, false);
+        v[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+    }
+    n /= 2;
+  }
+  if constexpr (kLPR <= 8) {  // lane bit 3: keep index 2j + bit3
+    const bool odd = (lane >> 3) & 1;
+#pragma unroll
+    for (int j = 0; j < kCols / 2; ++j) {
+      if (2 * j + 1 < n) {
+        const float keep = odd ? v[2 * j + 1] : v[2 * j];
+        const float send = odd ? v[2 * j] : v[2 * j + 1];
+        v[j] = keep + __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(send), 0x128, 0xf, 0xf, false));
+      }
+    }
+    n /= 2;
+  }
+#pragma unroll
+  for (int m = 0; m < kCols * kLPR / 64; ++m) out[m] = v[m];
+}
+
+// Column (of the lane's kCols) whose total lane_group_transpose_sum leaves in
+// out[m]: the kept indices compose bit4, then bit5, then bit3 of the lane.
+template <int kCols, int kLPR>
+__device__ __forceinline__ int transposed_column(int m, int lane) {
+  int k = m;
+  if constexpr (kLPR <= 8) k = 2 * k + ((lane >> 3) & 1);
+  k = 2 * k + ((lane >> 5) & 1);
+  if constexpr (kLPR <= 16) k = 2 * k + ((lane >> 4) & 1);
+  return k;
+}
+
 // Exclusive prefix sum of one value per thread over a workgroup of
 // kFusedWaves waves; `tmp` holds kFusedWaves words of LDS.  Two barriers.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *tmp, int lane,
@@ -357,26 +418,24 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
     const int p_lo = static_cast<int>(bst[b0]), p_hi = static_cast<int>(bst[b1]);
 
     if (p_lo < p_hi) {
-      const int rg = lane / kLPR, cc = lane % kLPR;  // row group, column piece
+      const int cc = lane % kLPR;  // column piece
+      const int my_off = lane / kLPR;  // this lane's row within a load: position p + my_off
       const Bf16Adder adder;
       int b = b0;
       int bend = __builtin_amdgcn_readfirstlane(static_cast<int>(bst[b0 + 1]));
       float a[kCols];
 #pragma unroll
       for (int k = 0; k < kCols; ++k) a[k] = 0.0f;
-      // Bucket b is complete: sum the row groups' partials (butterfly over the
-      // lanes holding the same columns), then lane (rg, cc) adds columns
-      // cc * kCols + rg + kRPI m of the bucket row into the LDS table.
+      // Bucket b is complete: sum the partials of the lanes holding the same
+      // columns (a transposing reduction: every exchange halves the values a
+      // lane holds) and add the lane's kCols / kRPI column sums into the LDS
+      // table.
       auto flush = [&]() {
+        float r[kCols / kRPI];
+        lane_group_transpose_sum<kCols, kLPR>(a, r, lane);
 #pragma unroll
-        for (int k = 0; k < kCols; ++k) a[k] = sum_over_lane_groups<kLPR>(a[k]);
-#pragma unroll
-        for (int m = 0; m < kCols / kRPI; ++m) {
-          float val = 0.0f;
-#pragma unroll
-          for (int k = 0; k < kCols; ++k) val = (k == rg + kRPI * m) ? a[k] : val;
-          acc[b * D + cc * kCols + rg + kRPI * m] += val;
-        }
+        for (int m = 0; m < kCols / kRPI; ++m)
+          acc[b * D + cc * kCols + transposed_column<kCols, kLPR>(m, lane)] += r[m];
 #pragma unroll
         for (int k = 0; k < kCols; ++k) a[k] = 0.0f;
       };
@@ -389,7 +448,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
         // the slack at the end of lperm; their rows are loaded (out-of-range
         // offsets read zero) and never added
         uint32_t jl[kI];
-        const uint16_t *lp = lperm + pbase + rg;
+        const uint16_t *lp = lperm + pbase + my_off;
 #pragma unroll
         for (int i = 0; i < kI; ++i) jl[i] = lp[i * kRPI];
 #pragma unroll
@@ -397,28 +456,32 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
           r[i] = __builtin_bit_cast(
               u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, jl[i] * PC::kRowBytes + cbyte, 0, 0));
       };
-      // rows of positions [pbase, pbase + kBP): lane's row is position p + rg
+      // rows of positions [pbase, pbase + kBP).  Bucket ends never pass p_hi,
+      // so one scalar test per load (its rows end before bucket b does) picks
+      // the plain add; a load that reaches a bucket end takes the per-lane
+      // path, which also flushes the bucket
       auto consume = [&](int pbase, const u32x4 (&r)[kI]) {
 #pragma unroll
         for (int i = 0; i < kI; ++i) {
           const int p = pbase + i * kRPI;
-          if (p >= p_hi) return;
           const int pe = p + kRPI < p_hi ? p + kRPI : p_hi;
-          const int my = p + rg;
-          if (pe < bend) {  // the whole group lies inside bucket b
-            if (my < pe) PC::add(r[i], a, adder);
-          } else {
-            int cur = p;
-            while (cur < pe) {
-              const int stop = pe < bend ? pe : bend;
-              if (my >= cur && my < stop) PC::add(r[i], a, adder);
-              cur = stop;
+          const int my = p + my_off;
+          // rows before the end of bucket b (all of them, mostly)
+          const int stop0 = pe < bend ? pe : bend;
+          if (my < stop0) PC::add(r[i], a, adder);
+          if (pe >= bend && p < p_hi) {  // the load reaches the end of bucket b
+            int cur = stop0;
+            do {
               if (cur == bend) {
                 flush();
                 ++b;
-                bend = __builtin_amdgcn_readfirstlane(static_cast<int>(bst[b + 1]));
+                // past the wave's last bucket (then cur == p_hi): no end to meet
+                bend = b < b1 ? __builtin_amdgcn_readfirstlane(static_cast<int>(bst[b + 1])) : 0x7fffffff;
               }
-            }
+              const int stop = pe < bend ? pe : bend;
+              if (my >= cur && my < stop) PC::add(r[i], a, adder);
+              cur = stop;
+            } while (cur < pe || cur == bend);
           }
         }
       };
