@@ -38,7 +38,7 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
   constexpr int kThreads = QT * 4;      // 16 queries per wave
   constexpr int kKeys = NB * kKBlock;   // keys staged at once
   constexpr int kKRow = D + 8;          // padded K row in LDS (bf16 elements)
-  constexpr int kVRow = kKeys + 8;      // padded V^T row in LDS
+  constexpr int kVRow = kKeys + 4;      // padded V^T row in LDS: 2-word bank shift per row
   constexpr int kKChunks = kKeys * (D / 8);          // 16-byte pieces of the staged K rows
   constexpr int kVPairs = (kKeys / 2) * (D / 8);     // (key pair, 8-column) pieces of V
   constexpr int kKPer = (kKChunks + kThreads - 1) / kThreads;
@@ -70,8 +70,17 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY;  // running max of score * log2(e) / sqrt(d)
-  float l_part = 0.0f;  // this lane's share of the running sum
+  // m: the reference point of the exponentials, score * log2(e) / sqrt(d)
+  // units; it trails the running maximum by less than kLazy, so every
+  // exp2(s - m) stays below 2^kLazy and o and l are rescaled only when the
+  // maximum grows past it (the final o / l does not depend on m).
+  constexpr float kLazy = 8.0f;
+  float m = -INFINITY;
+  // running sum of the bfloat16 weights P (the ones fed to the PV product):
+  // a 16x16x32 product of an all-ones A with P, every lane of query r16
+  // holds the column sum
+  f32x4 l_acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, (u16x8)0x3f80);
 
   // Stages of up to NB key blocks: all of a stage's rows are requested at
   // once (K piece i -> row i / (D/8), chunk i % (D/8); V piece i -> key pair
@@ -149,14 +158,21 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
       for (int kt = 0; kt < kKBlock / 16; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[kt][i]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      const float m_new = fmaxf(m, bmax * scale_log2);
-      const float corr = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block (m = -inf)
-      m = m_new;
-      l_part *= corr;
+      {  // max over the 4 lane groups (lanes r16, r16 + 16, r16 + 32, r16 + 48)
+        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+        bmax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+        bmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+      }
+      const float m_blk = bmax * scale_log2;
+      if (__ballot(m_blk > m + kLazy)) {  // some query of the wave moves its reference point
+        const float m_new = fmaxf(m, m_blk);
+        const float corr = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block (m = -inf)
+        m = m_new;
+        l_acc *= corr;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[dt] *= corr;
+        for (int dt = 0; dt < D / 16; ++dt) o[dt] *= corr;
+      }
 
       // P = exp2(s * scale - m); PV over two 32-key steps
 #pragma unroll
@@ -168,11 +184,11 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2][i + 1], scale_log2, -m));
           const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2 + 1][i], scale_log2, -m));
           const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2 + 1][i + 1], scale_log2, -m));
-          l_part += (p0 + p1) + (p2 + p3);
           pw[i / 2] = pack_bf16x2(p0, p1);
           pw[2 + i / 2] = pack_bf16x2(p2, p3);
         }
         const bf16x8 bp = __builtin_bit_cast(bf16x8, (uint4){pw[0], pw[1], pw[2], pw[3]});
+        l_acc = mfma16x16x32(ones, bp, l_acc);
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
           const uint16_t *vr = Vt + (dt * 16 + r16) * kVRow + blk * kKBlock + m2 * 32 + g * 4;
@@ -185,8 +201,7 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
     }
   }
 
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = l_acc[0];
   const float inv = 1.0f / l_tot;
   uint16_t *orow = o_s + (seg + qidx) * D;
 #pragma unroll
@@ -237,7 +252,7 @@ __global__ __launch_bounds__(128) void elsaa_k3_chunk_attn_f32(
 
 // LDS bytes of the bf16 kernel staging NB key blocks.
 constexpr size_t attn_lds_bytes(int D, int NB) {
-  return (static_cast<size_t>(NB) * kKBlock * (D + 8) + static_cast<size_t>(D) * (NB * kKBlock + 8)) * 2;
+  return (static_cast<size_t>(NB) * kKBlock * (D + 8) + static_cast<size_t>(D) * (NB * kKBlock + 4)) * 2;
 }
 
 template <int D, int QT, int NB>
