@@ -29,6 +29,93 @@ constexpr int kKBlock = 64;
 
 
 
+// One stage of staged keys (nkeys, a multiple of 64, of at most kKeys) for
+// QG groups of 16 queries of a wave: S^T = K Q^T on MFMA (each K fragment read
+// from LDS serves every group), the online softmax in the exp2 domain with a
+// lazily moved reference point m, P rounded to bfloat16, O^T += V^T P^T (each
+// V fragment serves every group) and the running row sum of P (an all-ones A
+// times P).  m trails the running maximum by less than kLazy, so every
+// exp2(s - m) stays below 2^kLazy and o and l are rescaled only when the
+// maximum grows past it (the final o / l does not depend on m).
+template <int D, int kKeys, int QG>
+__device__ __forceinline__ void attend_stage(const uint16_t *Ks, const uint16_t *Vt, int nkeys,
+                                             const bf16x8 (&bq)[QG][D / 32], f32x4 (&o)[QG][D / 16],
+                                             f32x4 (&l_acc)[QG], float (&m)[QG], float scale_log2,
+                                             const bf16x8 &ones, int g, int r16) {
+  constexpr int kKRow = D + 8;
+  constexpr int kVRow = kKeys + 4;
+  constexpr float kLazy = 8.0f;
+  for (int blk = 0; blk < nkeys / kKBlock; ++blk) {
+    const uint16_t *Kb = Ks + blk * kKBlock * kKRow;
+    // S^T tiles: lane holds keys kt*16 + g*4 + i for query r16 of each group
+    f32x4 s[QG][kKBlock / 16];
+#pragma unroll
+    for (int kt = 0; kt < kKBlock / 16; ++kt) {
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) s[qg][kt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u16x8 *>(Kb + (kt * 16 + r16) * kKRow + kk * 32 + g * 8));
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) s[qg][kt] = mfma16x16x32(a, bq[qg][kk], s[qg][kt]);
+      }
+    }
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < kKBlock / 16; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[qg][kt][i]);
+      // max over the 4 lane groups (lanes r16, r16 + 16, r16 + 32, r16 + 48)
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+      bmax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+      bmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+      const float m_blk = bmax * scale_log2;
+      if (__ballot(m_blk > m[qg] + kLazy)) {  // some query of the group moves its reference point
+        const float m_new = fmaxf(m[qg], m_blk);
+        const float corr = __builtin_amdgcn_exp2f(m[qg] - m_new);  // 0 on the first block (m = -inf)
+        m[qg] = m_new;
+        l_acc[qg] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[qg][dt] *= corr;
+      }
+    }
+
+    // P = exp2(s * scale - m); PV over two 32-key steps
+#pragma unroll
+    for (int m2 = 0; m2 < kKBlock / 32; ++m2) {
+      bf16x8 bp[QG];
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        uint32_t pw[4];
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][2 * m2][i], scale_log2, -m[qg]));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][2 * m2][i + 1], scale_log2, -m[qg]));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][2 * m2 + 1][i], scale_log2, -m[qg]));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][2 * m2 + 1][i + 1], scale_log2, -m[qg]));
+          pw[i / 2] = pack_bf16x2(p0, p1);
+          pw[2 + i / 2] = pack_bf16x2(p2, p3);
+        }
+        bp[qg] = __builtin_bit_cast(bf16x8, (uint4){pw[0], pw[1], pw[2], pw[3]});
+        l_acc[qg] = mfma16x16x32(ones, bp[qg], l_acc[qg]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const uint16_t *vr = Vt + (dt * 16 + r16) * kVRow + blk * kKBlock + m2 * 32 + g * 4;
+        const uint2 lo4 = *reinterpret_cast<const uint2 *>(vr);
+        const uint2 hi4 = *reinterpret_cast<const uint2 *>(vr + 16);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, (uint4){lo4.x, lo4.y, hi4.x, hi4.y});
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) o[qg][dt] = mfma16x16x32(av, bp[qg], o[qg][dt]);
+      }
+    }
+  }
+}
+
 template <int D, int QT, int NB>
 __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -62,24 +149,20 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
   // Q^T operand: lane holds query r16 of this wave, d-slice g*8 .. +7 of each 32.
   const int qidx = perm_q[seg + r0 + wave * 16 + r16];
   const uint16_t *qrow = q + (seg + qidx) * D;
-  bf16x8 bq[D / 32];
+  bf16x8 bq[1][D / 32];
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk)
-    bq[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(qrow + kk * 32 + g * 8));
+    bq[0][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(qrow + kk * 32 + g * 8));
 
-  f32x4 o[D / 16];
+  f32x4 o[1][D / 16];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  // m: the reference point of the exponentials, score * log2(e) / sqrt(d)
-  // units; it trails the running maximum by less than kLazy, so every
-  // exp2(s - m) stays below 2^kLazy and o and l are rescaled only when the
-  // maximum grows past it (the final o / l does not depend on m).
-  constexpr float kLazy = 8.0f;
-  float m = -INFINITY;
-  // running sum of the bfloat16 weights P (the ones fed to the PV product):
-  // a 16x16x32 product of an all-ones A with P, every lane of query r16
-  // holds the column sum
-  f32x4 l_acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int dt = 0; dt < D / 16; ++dt) o[0][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  // m: the reference point of the exponentials, in score * log2(e) / sqrt(d)
+  // units; l_acc: the running sum of the bfloat16 weights P (those fed to
+  // the PV product) as a 16x16x32 product of an all-ones A with P: every
+  // lane of query r16 holds the column sum
+  float m[1] = {-INFINITY};
+  f32x4 l_acc[1] = {{0.0f, 0.0f, 0.0f, 0.0f}};
   const bf16x8 ones = __builtin_bit_cast(bf16x8, (u16x8)0x3f80);
 
   // Stages of up to NB key blocks: all of a stage's rows are requested at
@@ -138,79 +221,386 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
     }
     __syncthreads();
 
-    for (int blk = 0; blk < nkeys / kKBlock; ++blk) {
-      const uint16_t *Kb = Ks + blk * kKBlock * kKRow;
-      // S^T tiles: lane holds keys kt*16 + g*4 + i for query r16
-      f32x4 s[kKBlock / 16];
-#pragma unroll
-      for (int kt = 0; kt < kKBlock / 16; ++kt) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u16x8 *>(Kb + (kt * 16 + r16) * kKRow + kk * 32 + g * 8));
-          acc = mfma16x16x32(a, bq[kk], acc);
-        }
-        s[kt] = acc;
-      }
-      float bmax = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < kKBlock / 16; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[kt][i]);
-      {  // max over the 4 lane groups (lanes r16, r16 + 16, r16 + 32, r16 + 48)
-        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
-        bmax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
-        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
-        bmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
-      }
-      const float m_blk = bmax * scale_log2;
-      if (__ballot(m_blk > m + kLazy)) {  // some query of the wave moves its reference point
-        const float m_new = fmaxf(m, m_blk);
-        const float corr = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block (m = -inf)
-        m = m_new;
-        l_acc *= corr;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[dt] *= corr;
-      }
-
-      // P = exp2(s * scale - m); PV over two 32-key steps
-#pragma unroll
-      for (int m2 = 0; m2 < kKBlock / 32; ++m2) {
-        uint32_t pw[4];
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2][i], scale_log2, -m));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2][i + 1], scale_log2, -m));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2 + 1][i], scale_log2, -m));
-          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m2 + 1][i + 1], scale_log2, -m));
-          pw[i / 2] = pack_bf16x2(p0, p1);
-          pw[2 + i / 2] = pack_bf16x2(p2, p3);
-        }
-        const bf16x8 bp = __builtin_bit_cast(bf16x8, (uint4){pw[0], pw[1], pw[2], pw[3]});
-        l_acc = mfma16x16x32(ones, bp, l_acc);
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const uint16_t *vr = Vt + (dt * 16 + r16) * kVRow + blk * kKBlock + m2 * 32 + g * 4;
-          const uint2 lo4 = *reinterpret_cast<const uint2 *>(vr);
-          const uint2 hi4 = *reinterpret_cast<const uint2 *>(vr + 16);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, (uint4){lo4.x, lo4.y, hi4.x, hi4.y});
-          o[dt] = mfma16x16x32(av, bp, o[dt]);
-        }
-      }
-    }
+    attend_stage<D, kKeys, 1>(Ks, Vt, nkeys, bq, o, l_acc, m, scale_log2, ones, g, r16);
   }
 
-  const float l_tot = l_acc[0];
+  const float l_tot = l_acc[0][0];
   const float inv = 1.0f / l_tot;
   uint16_t *orow = o_s + (seg + qidx) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
-    const uint2 outv = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
-                        pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
+    const uint2 outv = {pack_bf16x2(o[0][dt][0] * inv, o[0][dt][1] * inv),
+                        pack_bf16x2(o[0][dt][2] * inv, o[0][dt][3] * inv)};
     *reinterpret_cast<uint2 *>(orow + dt * 16 + g * 4) = outv;
   }
-  if (g == 0) lse[seg + qidx] = (m + log2f(l_tot)) * 0.69314718055994530942f;
+  if (g == 0) lse[seg + qidx] = (m[0] + log2f(l_tot)) * 0.69314718055994530942f;
+}
+
+// Pipelined bf16 kernel for 128-query tiles (w a multiple of 128): one
+// persistent workgroup per compute unit walks a contiguous run of tiles
+// (neighbouring tiles share key rows, which then come from the XCD's L2).  A
+// job is one stage of up to NB key blocks of one tile.  Waves 0-3 (consumers,
+// 32 queries each as two groups of 16 that share every K and V fragment read
+// from LDS) compute job n from one LDS buffer while waves 4-7 (producers)
+// write job n+1's K rows and transposed V rows, loaded into registers during
+// job n-1, into the other buffer, then request job n+2's rows and job n+3's
+// key indices.  One barrier per job separates the two; it orders LDS only, so
+// loads stay in flight across it.  Consumers also load the next tile's query
+// rows one tile ahead.
+template <int D, int NB>
+__global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_pc(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N, int w,
+    int tiles_per_seg, long long n_tiles, long long tiles_per_wg, float scale_log2,
+    uint16_t *__restrict__ o_s, float *__restrict__ lse) {
+  constexpr int QT = 128;
+  constexpr int QG = 2;  // query groups of 16 per consumer wave
+  constexpr int kConsumerWaves = QT / (16 * QG);
+  constexpr int kPThreads = 256;                   // producer threads
+  constexpr int kKeys = NB * kKBlock;
+  constexpr int kKRow = D + 8;
+  constexpr int kVRow = kKeys + 4;
+  constexpr int kBufElems = kKeys * kKRow + D * kVRow;
+  constexpr int kKChunks = kKeys * (D / 8);        // 16-byte pieces of K rows
+  constexpr int kVPairs = (kKeys / 2) * (D / 8);   // (key pair, 8-column) pieces of V
+  static_assert(kKChunks % kPThreads == 0 && kVPairs % kPThreads == 0, "producer share");
+  constexpr int kKPer = kKChunks / kPThreads;
+  constexpr int kVPer = kVPairs / kPThreads;
+  extern __shared__ __align__(16) uint16_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long t_begin = xcd_logical_block(blockIdx.x, gridDim.x) * tiles_per_wg;
+  const long long t_end = t_begin + tiles_per_wg < n_tiles ? t_begin + tiles_per_wg : n_tiles;
+  if (t_begin >= t_end) return;  // whole workgroup
+
+  // Jobs: (tile, first key of the stage); a tile's window is [lo, hi).  The
+  // sequence is the same in every wave; a job at tile t_end means "none".
+  struct Job { long long tile; int s0, lo, hi; };
+  auto first_job = [&](long long t) {
+    const int c = static_cast<int>(t % tiles_per_seg) * QT / w;
+    Job j{t, 0, c > 0 ? (c - 1) * w : 0, (c + 1) * w};
+    j.s0 = j.lo;
+    return j;
+  };
+  auto next_job = [&](const Job &j) {
+    if (j.s0 + kKeys < j.hi) return Job{j.tile, j.s0 + kKeys, j.lo, j.hi};
+    return first_job(j.tile + 1);
+  };
+
+  if (wave >= kConsumerWaves) {
+    // ------------------------------------------------------------ producer
+    const int ptid = tid - kConsumerWaves * 64;
+    int kj[kKPer], v0[kVPer], v1[kVPer];  // key indices of the next job to load
+    u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer];
+    auto load_idx = [&](const Job &j) {
+      const int32_t *pk = perm_k + (j.tile / tiles_per_seg) * N;
+      const int nkeys = j.hi - j.s0 < kKeys ? j.hi - j.s0 : kKeys;
+#pragma unroll
+      for (int p = 0; p < kKPer; ++p) {
+        int r = (ptid + p * kPThreads) / (D / 8);
+        r = r < nkeys ? r : nkeys - 1;  // rows past the stage are reloads, never used
+        kj[p] = pk[j.s0 + r];
+      }
+#pragma unroll
+      for (int p = 0; p < kVPer; ++p) {
+        int jp = (ptid + p * kPThreads) % (kKeys / 2);
+        jp = 2 * jp + 1 < nkeys ? jp : nkeys / 2 - 1;
+        v0[p] = pk[j.s0 + 2 * jp];
+        v1[p] = pk[j.s0 + 2 * jp + 1];
+      }
+    };
+    auto load_rows = [&](const Job &j) {
+      const long long seg = (j.tile / tiles_per_seg) * N;
+#pragma unroll
+      for (int p = 0; p < kKPer; ++p)
+        kreg[p] = *reinterpret_cast<const u16x8 *>(k + (seg + kj[p]) * D + ((ptid + p * kPThreads) % (D / 8)) * 8);
+#pragma unroll
+      for (int p = 0; p < kVPer; ++p) {
+        const int ch = (ptid + p * kPThreads) / (kKeys / 2);
+        vreg0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + v0[p]) * D + ch * 8);
+        vreg1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + v1[p]) * D + ch * 8);
+      }
+    };
+    auto store_rows = [&](uint16_t *buf) {
+      uint16_t *Ks = buf, *Vt = buf + kKeys * kKRow;
+#pragma unroll
+      for (int p = 0; p < kKPer; ++p) {
+        const int i = ptid + p * kPThreads;
+        *reinterpret_cast<u16x8 *>(Ks + (i / (D / 8)) * kKRow + (i % (D / 8)) * 8) = kreg[p];
+      }
+#pragma unroll
+      for (int p = 0; p < kVPer; ++p) {
+        const int i = ptid + p * kPThreads;
+        const int jp = i % (kKeys / 2), ch = i / (kKeys / 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = static_cast<uint32_t>(vreg0[p][e]) | (static_cast<uint32_t>(vreg1[p][e]) << 16);
+          *reinterpret_cast<uint32_t *>(Vt + (ch * 8 + e) * kVRow + 2 * jp) = word;
+        }
+      }
+    };
+    Job cur = first_job(t_begin);  // job 0
+    load_idx(cur);
+    load_rows(cur);
+    Job nxt = next_job(cur);  // job 1
+    if (nxt.tile < t_end) load_idx(nxt);
+    store_rows(smem);  // job 0 -> buffer 0
+    if (nxt.tile < t_end) {
+      load_rows(nxt);
+      const Job n2 = next_job(nxt);
+      if (n2.tile < t_end) load_idx(n2);
+    }
+    lds_barrier();  // job 0 ready
+    for (int n = 1; nxt.tile < t_end; ++n) {  // nxt = job n, its rows in flight
+      store_rows(smem + (n & 1) * kBufElems);  // buffer n&1 was read during job n-2
+      const Job n1 = next_job(nxt);
+      if (n1.tile < t_end) {
+        load_rows(n1);  // indices loaded one job ago
+        const Job n2 = next_job(n1);
+        if (n2.tile < t_end) load_idx(n2);
+      }
+      lds_barrier();  // job n ready; consumers done with job n-1
+      nxt = n1;
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- consumer
+  const int g = lane >> 4, r16 = lane & 15;
+  // query rows: group qg's query of this lane, d-slice g*8 .. +7 of each 32
+  auto q_index = [&](long long t, int qg) -> int {
+    const long long tt = t < t_end ? t : t_end - 1;
+    return perm_q[(tt / tiles_per_seg) * N + (tt % tiles_per_seg) * QT + (wave * QG + qg) * 16 + r16];
+  };
+  auto load_q = [&](long long t, int qi, bf16x8 (&dst)[D / 32]) {
+    const long long tt = t < t_end ? t : t_end - 1;
+    const uint16_t *qrow = q + ((tt / tiles_per_seg) * N + qi) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      dst[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(qrow + kk * 32 + g * 8));
+  };
+  bf16x8 bq[QG][D / 32], bq_next[QG][D / 32];
+  int qidx[QG], qidx_n1[QG], qidx_n2[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    qidx[qg] = q_index(t_begin, qg);
+    qidx_n1[qg] = q_index(t_begin + 1, qg);
+    qidx_n2[qg] = 0;
+  }
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) load_q(t_begin, qidx[qg], bq[qg]);
+
+  f32x4 o[QG][D / 16], l_acc[QG];
+  float m[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[qg][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    l_acc[qg] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    m[qg] = -INFINITY;
+  }
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, (u16x8)0x3f80);
+
+  Job cur = first_job(t_begin);
+  for (int n = 0; cur.tile < t_end; ++n) {
+    lds_barrier();  // job n staged in buffer n&1
+    if (cur.s0 == cur.lo) {  // first job of a tile: the next tile's query rows, the one after's indices
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) load_q(cur.tile + 1, qidx_n1[qg], bq_next[qg]);
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) qidx_n2[qg] = q_index(cur.tile + 2, qg);
+    }
+    const uint16_t *buf = smem + (n & 1) * kBufElems;
+    const int nkeys = cur.hi - cur.s0 < kKeys ? cur.hi - cur.s0 : kKeys;
+    attend_stage<D, kKeys, QG>(buf, buf + kKeys * kKRow, nkeys, bq, o, l_acc, m, scale_log2, ones, g, r16);
+    const Job nx = next_job(cur);
+    if (nx.tile != cur.tile) {  // tile complete: normalise, write, reset
+      const long long seg = (cur.tile / tiles_per_seg) * N;
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        const float l_tot = l_acc[qg][0];
+        const float inv = 1.0f / l_tot;
+        uint16_t *orow = o_s + (seg + qidx[qg]) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const uint2 outv = {pack_bf16x2(o[qg][dt][0] * inv, o[qg][dt][1] * inv),
+                              pack_bf16x2(o[qg][dt][2] * inv, o[qg][dt][3] * inv)};
+          *reinterpret_cast<uint2 *>(orow + dt * 16 + g * 4) = outv;
+          o[qg][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        if (g == 0) lse[seg + qidx[qg]] = (m[qg] + log2f(l_tot)) * 0.69314718055994530942f;
+        l_acc[qg] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        m[qg] = -INFINITY;
+        qidx[qg] = qidx_n1[qg];
+        qidx_n1[qg] = qidx_n2[qg];
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) bq[qg][kk] = bq_next[qg][kk];
+      }
+    }
+    cur = nx;
+  }
+}
+
+// Sliding-window kernel for d = 64 and w = 128 (a 128-query tile is one
+// chunk, whose window is the previous chunk and its own).  Consecutive tiles
+// of a persistent workgroup share a chunk, so each tile gathers only its own
+// chunk's 128 K and V rows: chunks live in a ring of three LDS slots (tile m
+// reads slots m % 3 and (m + 1) % 3, and its own chunk is written to slot
+// (m + 1) % 3 while tile m - 1 is computed).  Waves 0-7 compute (16 queries
+// each), waves 8-11 produce: they store the chunk loaded during the previous
+// tile, then request the next chunk's rows and the one after's key indices.
+// One LDS-only barrier per tile.
+__global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N,
+    int tiles_per_seg, long long n_tiles, long long tiles_per_wg, float scale_log2,
+    uint16_t *__restrict__ o_s, float *__restrict__ lse) {
+  constexpr int D = 64, W = 128;
+  constexpr int kConsumerWaves = 8;
+  constexpr int kPThreads = 256;
+  constexpr int kKRow = D + 8;
+  constexpr int kVRow = W + 4;
+  constexpr int kSlotElems = W * kKRow + D * kVRow;
+  constexpr int kKChunks = W * (D / 8);
+  constexpr int kVPairs = (W / 2) * (D / 8);
+  constexpr int kKPer = kKChunks / kPThreads;  // 4
+  constexpr int kVPer = kVPairs / kPThreads;   // 2
+  extern __shared__ __align__(16) uint16_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long t_begin = xcd_logical_block(blockIdx.x, gridDim.x) * tiles_per_wg;
+  const long long t_end = t_begin + tiles_per_wg < n_tiles ? t_begin + tiles_per_wg : n_tiles;
+  if (t_begin >= t_end) return;  // whole workgroup
+  const int c_begin = static_cast<int>(t_begin % tiles_per_seg);
+
+  if (wave >= kConsumerWaves) {
+    // ------------------------------------------------------------ producer
+    const int ptid = tid - kConsumerWaves * 64;
+    int kj[kKPer], v0[kVPer], v1[kVPer];
+    u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer];
+    // chunk c of the segment of tile t (c = -1: none)
+    auto load_idx = [&](long long t, int c) {
+      const int32_t *pk = perm_k + (t / tiles_per_seg) * N + c * W;
+#pragma unroll
+      for (int p = 0; p < kKPer; ++p) kj[p] = pk[(ptid + p * kPThreads) / (D / 8)];
+#pragma unroll
+      for (int p = 0; p < kVPer; ++p) {
+        const int jp = (ptid + p * kPThreads) % (W / 2);
+        v0[p] = pk[2 * jp];
+        v1[p] = pk[2 * jp + 1];
+      }
+    };
+    auto load_rows = [&](long long t) {
+      const long long seg = (t / tiles_per_seg) * N;
+#pragma unroll
+      for (int p = 0; p < kKPer; ++p)
+        kreg[p] = *reinterpret_cast<const u16x8 *>(k + (seg + kj[p]) * D + ((ptid + p * kPThreads) % (D / 8)) * 8);
+#pragma unroll
+      for (int p = 0; p < kVPer; ++p) {
+        const int ch = (ptid + p * kPThreads) / (W / 2);
+        vreg0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + v0[p]) * D + ch * 8);
+        vreg1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + v1[p]) * D + ch * 8);
+      }
+    };
+    auto store_rows = [&](int slot) {
+      uint16_t *Ks = smem + slot * kSlotElems, *Vt = Ks + W * kKRow;
+#pragma unroll
+      for (int p = 0; p < kKPer; ++p) {
+        const int i = ptid + p * kPThreads;
+        *reinterpret_cast<u16x8 *>(Ks + (i / (D / 8)) * kKRow + (i % (D / 8)) * 8) = kreg[p];
+      }
+#pragma unroll
+      for (int p = 0; p < kVPer; ++p) {
+        const int i = ptid + p * kPThreads;
+        const int jp = i % (W / 2), ch = i / (W / 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = static_cast<uint32_t>(vreg0[p][e]) | (static_cast<uint32_t>(vreg1[p][e]) << 16);
+          *reinterpret_cast<uint32_t *>(Vt + (ch * 8 + e) * kVRow + 2 * jp) = word;
+        }
+      }
+    };
+    // prologue: the first tile's previous chunk (slot 0) and own chunk (slot 1)
+    if (c_begin > 0) {
+      load_idx(t_begin, c_begin - 1);
+      load_rows(t_begin);
+      store_rows(0);
+    }
+    load_idx(t_begin, c_begin);
+    load_rows(t_begin);
+    if (t_begin + 1 < t_end) load_idx(t_begin + 1, static_cast<int>((t_begin + 1) % tiles_per_seg));
+    store_rows(1);
+    if (t_begin + 1 < t_end) {
+      load_rows(t_begin + 1);
+      if (t_begin + 2 < t_end) load_idx(t_begin + 2, static_cast<int>((t_begin + 2) % tiles_per_seg));
+    }
+    lds_barrier();  // tile 0 ready
+    for (long long t = t_begin + 1; t < t_end; ++t) {  // tile m = t - t_begin: own chunk in flight
+      const int m = static_cast<int>(t - t_begin);
+      store_rows((m + 1) % 3);
+      if (t + 1 < t_end) {
+        load_rows(t + 1);
+        if (t + 2 < t_end) load_idx(t + 2, static_cast<int>((t + 2) % tiles_per_seg));
+      }
+      lds_barrier();  // tile m ready; tile m - 1 computed
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- consumer
+  const int g = lane >> 4, r16 = lane & 15;
+  auto q_index = [&](long long t) -> int {
+    const long long tt = t < t_end ? t : t_end - 1;
+    return perm_q[(tt / tiles_per_seg) * N + (tt % tiles_per_seg) * W + wave * 16 + r16];
+  };
+  auto load_q = [&](long long t, int qi, bf16x8 (&dst)[D / 32]) {
+    const long long tt = t < t_end ? t : t_end - 1;
+    const uint16_t *qrow = q + ((tt / tiles_per_seg) * N + qi) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      dst[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(qrow + kk * 32 + g * 8));
+  };
+  bf16x8 bq[1][D / 32], bq_next[D / 32];
+  int qidx = q_index(t_begin);
+  int qidx_n1 = q_index(t_begin + 1);
+  load_q(t_begin, qidx, bq[0]);
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, (u16x8)0x3f80);
+
+  for (long long t = t_begin; t < t_end; ++t) {
+    const int m_idx = static_cast<int>(t - t_begin);
+    const int c = static_cast<int>(t % tiles_per_seg);
+    lds_barrier();  // tile m_idx's chunks staged
+    load_q(t + 1, qidx_n1, bq_next);
+    const int qidx_n2 = q_index(t + 2);
+    f32x4 o[1][D / 16], l_acc[1] = {{0.0f, 0.0f, 0.0f, 0.0f}};
+    float m[1] = {-INFINITY};
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[0][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    if (c > 0) {
+      const uint16_t *prev = smem + (m_idx % 3) * kSlotElems;
+      attend_stage<D, W, 1>(prev, prev + W * kKRow, W, bq, o, l_acc, m, scale_log2, ones, g, r16);
+    }
+    const uint16_t *own = smem + ((m_idx + 1) % 3) * kSlotElems;
+    attend_stage<D, W, 1>(own, own + W * kKRow, W, bq, o, l_acc, m, scale_log2, ones, g, r16);
+
+    const long long seg = (t / tiles_per_seg) * N;
+    const float l_tot = l_acc[0][0];
+    const float inv = 1.0f / l_tot;
+    uint16_t *orow = o_s + (seg + qidx) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const uint2 outv = {pack_bf16x2(o[0][dt][0] * inv, o[0][dt][1] * inv),
+                          pack_bf16x2(o[0][dt][2] * inv, o[0][dt][3] * inv)};
+      *reinterpret_cast<uint2 *>(orow + dt * 16 + g * 4) = outv;
+    }
+    if (g == 0) lse[seg + qidx] = (m[0] + log2f(l_tot)) * 0.69314718055994530942f;
+    qidx = qidx_n1;
+    qidx_n1 = qidx_n2;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) bq[0][kk] = bq_next[kk];
+  }
 }
 
 // fp32 inputs: one thread per sorted query, binary32 arithmetic throughout.
@@ -269,6 +659,42 @@ hipError_t launch_bf16(const Geometry &g, const void *q, const void *k, const vo
   return hipGetLastError();
 }
 
+// LDS bytes of the pipelined kernel: two stage buffers.
+constexpr size_t attn_pc_lds_bytes(int D, int NB) { return 2 * attn_lds_bytes(D, NB); }
+
+template <int D, int NB>
+hipError_t launch_bf16_pc(const Geometry &g, const void *q, const void *k, const void *v,
+                          const Buffers &buf, float scale_log2, hipStream_t stream) {
+  const int tiles_per_seg = g.N / 128;
+  const long long n_tiles = static_cast<long long>(tiles_per_seg) * g.BH;
+  // one workgroup per compute unit (two stage buffers fill its LDS), a
+  // multiple of the XCD count, each taking a contiguous run of tiles
+  long long wgs = (g.cus + kXcdCount - 1) / kXcdCount * kXcdCount;
+  if (wgs > n_tiles) wgs = (n_tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
+  const long long tiles_per_wg = (n_tiles + wgs - 1) / wgs;
+  hipLaunchKernelGGL((elsaa_k3_chunk_attn_pc<D, NB>), dim3(static_cast<unsigned>(wgs)), dim3(512),
+                     attn_pc_lds_bytes(D, NB), stream, static_cast<const uint16_t *>(q),
+                     static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), buf.perm,
+                     buf.perm + g.rows, g.N, g.w, tiles_per_seg, n_tiles, tiles_per_wg, scale_log2,
+                     static_cast<uint16_t *>(buf.o_s), buf.lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_slide(const Geometry &g, const void *q, const void *k, const void *v,
+                             const Buffers &buf, float scale_log2, hipStream_t stream) {
+  const int tiles_per_seg = g.N / 128;
+  const long long n_tiles = static_cast<long long>(tiles_per_seg) * g.BH;
+  long long wgs = (g.cus + kXcdCount - 1) / kXcdCount * kXcdCount;
+  if (wgs > n_tiles) wgs = (n_tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
+  const long long tiles_per_wg = (n_tiles + wgs - 1) / wgs;
+  const size_t lds = 3 * (static_cast<size_t>(128) * (64 + 8) + static_cast<size_t>(64) * (128 + 4)) * 2;
+  hipLaunchKernelGGL(elsaa_k3_chunk_attn_slide, dim3(static_cast<unsigned>(wgs)), dim3(768), lds, stream,
+                     static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                     static_cast<const uint16_t *>(v), buf.perm, buf.perm + g.rows, g.N, tiles_per_seg,
+                     n_tiles, tiles_per_wg, scale_log2, static_cast<uint16_t *>(buf.o_s), buf.lse);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *k, const void *v,
@@ -281,10 +707,11 @@ hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *
     // 256-key window of w = 128) or 2, keeping LDS <= 72 KB (two workgroups
     // per CU)
     const bool wide = g.w % 128 == 0;
+    if (g.D == 64 && g.w == 128) return launch_bf16_slide(g, q, k, v, buf, scale_log2, stream);
     if (g.D == 64)
-      return wide ? launch_bf16<64, 128, 4>(g, q, k, v, buf, scale_log2, stream)
+      return wide ? launch_bf16_pc<64, 4>(g, q, k, v, buf, scale_log2, stream)
                   : launch_bf16<64, 64, 2>(g, q, k, v, buf, scale_log2, stream);
-    return wide ? launch_bf16<128, 128, 2>(g, q, k, v, buf, scale_log2, stream)
+    return wide ? launch_bf16_pc<128, 2>(g, q, k, v, buf, scale_log2, stream)
                 : launch_bf16<128, 64, 2>(g, q, k, v, buf, scale_log2, stream);
   }
   const dim3 grid((g.N + 127) / 128, g.BH);
