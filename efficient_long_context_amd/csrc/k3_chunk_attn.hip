@@ -116,6 +116,79 @@ __device__ __forceinline__ void attend_stage(const uint16_t *Ks, const uint16_t 
   }
 }
 
+// NBLK key blocks of 64 (K row-major with rows of D + 8, V transposed with
+// rows of kVRow) for the 16 queries of a wave, fully unrolled and software
+// pipelined: block b + 1's S^T products are issued before block b's softmax,
+// so the matrix cores work while the vector ALUs exponentiate.  Same
+// arithmetic as attend_stage.
+template <int D, int kVRow, int NBLK>
+__device__ __forceinline__ void attend_blocks(const uint16_t *const (&Kb)[NBLK], const uint16_t *const (&Vb)[NBLK],
+                                              const bf16x8 (&bq)[D / 32], f32x4 (&o)[D / 16], f32x4 &l_acc,
+                                              float &m, float scale_log2, const bf16x8 &ones, int g, int r16) {
+  constexpr int kKRow = D + 8;
+  constexpr float kLazy = 8.0f;
+  auto scores = [&](const uint16_t *K, f32x4 (&s)[kKBlock / 16]) {
+#pragma unroll
+    for (int kt = 0; kt < kKBlock / 16; ++kt) {
+      s[kt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u16x8 *>(K + (kt * 16 + r16) * kKRow + kk * 32 + g * 8));
+        s[kt] = mfma16x16x32(a, bq[kk], s[kt]);
+      }
+    }
+  };
+  f32x4 s[2][kKBlock / 16];
+  scores(Kb[0], s[0]);
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+    f32x4 (&sc)[kKBlock / 16] = s[b & 1];
+    if (b + 1 < NBLK) scores(Kb[b + 1], s[(b + 1) & 1]);
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < kKBlock / 16; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sc[kt][i]);
+    const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+    bmax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+    const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+    bmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+    const float m_blk = bmax * scale_log2;
+    if (__ballot(m_blk > m + kLazy)) {
+      const float m_new = fmaxf(m, m_blk);
+      const float corr = __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l_acc *= corr;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[dt] *= corr;
+    }
+#pragma unroll
+    for (int m2 = 0; m2 < kKBlock / 32; ++m2) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * m2][i], scale_log2, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * m2][i + 1], scale_log2, -m));
+        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * m2 + 1][i], scale_log2, -m));
+        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * m2 + 1][i + 1], scale_log2, -m));
+        pw[i / 2] = pack_bf16x2(p0, p1);
+        pw[2 + i / 2] = pack_bf16x2(p2, p3);
+      }
+      const bf16x8 bp = __builtin_bit_cast(bf16x8, (uint4){pw[0], pw[1], pw[2], pw[3]});
+      l_acc = mfma16x16x32(ones, bp, l_acc);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const uint16_t *vr = Vb[b] + (dt * 16 + r16) * kVRow + m2 * 32 + g * 4;
+        const uint2 lo4 = *reinterpret_cast<const uint2 *>(vr);
+        const uint2 hi4 = *reinterpret_cast<const uint2 *>(vr + 16);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, (uint4){lo4.x, lo4.y, hi4.x, hi4.y});
+        o[dt] = mfma16x16x32(av, bp, o[dt]);
+      }
+    }
+  }
+}
+
 template <int D, int QT, int NB>
 __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -447,10 +520,11 @@ __global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_pc(
 // of a persistent workgroup share a chunk, so each tile gathers only its own
 // chunk's 128 K and V rows: chunks live in a ring of three LDS slots (tile m
 // reads slots m % 3 and (m + 1) % 3, and its own chunk is written to slot
-// (m + 1) % 3 while tile m - 1 is computed).  Waves 0-7 compute (16 queries
-// each), waves 8-11 produce: they store the chunk loaded during the previous
-// tile, then request the next chunk's rows and the one after's key indices.
-// One LDS-only barrier per tile.
+// (m + 1) % 3 while tile m - 1 is computed).  The tile's query rows and
+// original indices go to one of two LDS query slots the same way.  Waves 0-7
+// compute (16 queries each) and issue no global loads; waves 8-11 produce:
+// they store what they loaded during the previous tile, then request the next
+// tile's rows and the one after's indices.  One LDS-only barrier per tile.
 __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N,
@@ -461,28 +535,32 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
   constexpr int kPThreads = 256;
   constexpr int kKRow = D + 8;
   constexpr int kVRow = W + 4;
-  constexpr int kSlotElems = W * kKRow + D * kVRow;
+  constexpr int kSlotElems = W * kKRow + D * kVRow;  // one chunk: K rows, V^T
+  constexpr int kQSlotElems = W * kKRow;             // one tile's query rows
   constexpr int kKChunks = W * (D / 8);
   constexpr int kVPairs = (W / 2) * (D / 8);
-  constexpr int kKPer = kKChunks / kPThreads;  // 4
+  constexpr int kKPer = kKChunks / kPThreads;  // 4 (also the query pieces per thread)
   constexpr int kVPer = kVPairs / kPThreads;   // 2
   extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t *qslots = smem + 3 * kSlotElems;                                  // [2][W][kKRow]
+  int32_t *qidx_lds = reinterpret_cast<int32_t *>(qslots + 2 * kQSlotElems);  // [2][W]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long t_begin = xcd_logical_block(blockIdx.x, gridDim.x) * tiles_per_wg;
   const long long t_end = t_begin + tiles_per_wg < n_tiles ? t_begin + tiles_per_wg : n_tiles;
   if (t_begin >= t_end) return;  // whole workgroup
-  const int c_begin = static_cast<int>(t_begin % tiles_per_seg);
 
   if (wave >= kConsumerWaves) {
     // ------------------------------------------------------------ producer
     const int ptid = tid - kConsumerWaves * 64;
-    int kj[kKPer], v0[kVPer], v1[kVPer];
-    u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer];
-    // chunk c of the segment of tile t (c = -1: none)
-    auto load_idx = [&](long long t, int c) {
-      const int32_t *pk = perm_k + (t / tiles_per_seg) * N + c * W;
+    int kj[kKPer], v0[kVPer], v1[kVPer], qj[kKPer];
+    u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer], qreg[kKPer];
+    int qown[kKPer];  // original indices of the query rows of this thread's pieces
+    // key indices of chunk c and query indices of tile t (whose chunk is c)
+    auto load_idx = [&](long long t, int c, bool with_q) {
+      const long long seg = (t / tiles_per_seg) * N;
+      const int32_t *pk = perm_k + seg + c * W;
 #pragma unroll
       for (int p = 0; p < kKPer; ++p) kj[p] = pk[(ptid + p * kPThreads) / (D / 8)];
 #pragma unroll
@@ -491,8 +569,13 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
         v0[p] = pk[2 * jp];
         v1[p] = pk[2 * jp + 1];
       }
+      if (with_q) {
+        const int32_t *pq = perm_q + seg + c * W;
+#pragma unroll
+        for (int p = 0; p < kKPer; ++p) qj[p] = pq[(ptid + p * kPThreads) / (D / 8)];
+      }
     };
-    auto load_rows = [&](long long t) {
+    auto load_rows = [&](long long t, bool with_q) {
       const long long seg = (t / tiles_per_seg) * N;
 #pragma unroll
       for (int p = 0; p < kKPer; ++p)
@@ -503,8 +586,15 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
         vreg0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + v0[p]) * D + ch * 8);
         vreg1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + v1[p]) * D + ch * 8);
       }
+      if (with_q) {
+#pragma unroll
+        for (int p = 0; p < kKPer; ++p)
+          qreg[p] = *reinterpret_cast<const u16x8 *>(q + (seg + qj[p]) * D + ((ptid + p * kPThreads) % (D / 8)) * 8);
+#pragma unroll
+        for (int p = 0; p < kKPer; ++p) qown[p] = qj[p];
+      }
     };
-    auto store_rows = [&](int slot) {
+    auto store_rows = [&](int slot, int qslot, bool with_q) {
       uint16_t *Ks = smem + slot * kSlotElems, *Vt = Ks + W * kKRow;
 #pragma unroll
       for (int p = 0; p < kKPer; ++p) {
@@ -521,28 +611,49 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
           *reinterpret_cast<uint32_t *>(Vt + (ch * 8 + e) * kVRow + 2 * jp) = word;
         }
       }
+      if (with_q) {
+        uint16_t *Qs = qslots + qslot * kQSlotElems;
+#pragma unroll
+        for (int p = 0; p < kKPer; ++p) {
+          const int i = ptid + p * kPThreads;
+          *reinterpret_cast<u16x8 *>(Qs + (i / (D / 8)) * kKRow + (i % (D / 8)) * 8) = qreg[p];
+        }
+      }
     };
-    // prologue: the first tile's previous chunk (slot 0) and own chunk (slot 1)
+    // piece p of thread ptid is query row ptid / 8 + 32 p; the threads that
+    // hold a row's first piece write its original index
+    auto store_qidx = [&](int qslot) {
+      if (ptid % (D / 8) == 0) {
+#pragma unroll
+        for (int p = 0; p < kKPer; ++p)
+          qidx_lds[qslot * W + (ptid + p * kPThreads) / (D / 8)] = qown[p];
+      }
+    };
+    const int c_begin = static_cast<int>(t_begin % tiles_per_seg);
+    // prologue: the first tile's previous chunk (slot 0), own chunk (slot 1)
+    // and query rows (query slot 0)
     if (c_begin > 0) {
-      load_idx(t_begin, c_begin - 1);
-      load_rows(t_begin);
-      store_rows(0);
+      load_idx(t_begin, c_begin - 1, false);
+      load_rows(t_begin, false);
+      store_rows(0, 0, false);
     }
-    load_idx(t_begin, c_begin);
-    load_rows(t_begin);
-    if (t_begin + 1 < t_end) load_idx(t_begin + 1, static_cast<int>((t_begin + 1) % tiles_per_seg));
-    store_rows(1);
+    load_idx(t_begin, c_begin, true);
+    load_rows(t_begin, true);
+    if (t_begin + 1 < t_end) load_idx(t_begin + 1, static_cast<int>((t_begin + 1) % tiles_per_seg), true);
+    store_rows(1, 0, true);
+    store_qidx(0);
     if (t_begin + 1 < t_end) {
-      load_rows(t_begin + 1);
-      if (t_begin + 2 < t_end) load_idx(t_begin + 2, static_cast<int>((t_begin + 2) % tiles_per_seg));
+      load_rows(t_begin + 1, true);
+      if (t_begin + 2 < t_end) load_idx(t_begin + 2, static_cast<int>((t_begin + 2) % tiles_per_seg), true);
     }
     lds_barrier();  // tile 0 ready
-    for (long long t = t_begin + 1; t < t_end; ++t) {  // tile m = t - t_begin: own chunk in flight
+    for (long long t = t_begin + 1; t < t_end; ++t) {  // tile m = t - t_begin: its rows in flight
       const int m = static_cast<int>(t - t_begin);
-      store_rows((m + 1) % 3);
+      store_rows((m + 1) % 3, m & 1, true);
+      store_qidx(m & 1);
       if (t + 1 < t_end) {
-        load_rows(t + 1);
-        if (t + 2 < t_end) load_idx(t + 2, static_cast<int>((t + 2) % tiles_per_seg));
+        load_rows(t + 1, true);
+        if (t + 2 < t_end) load_idx(t + 2, static_cast<int>((t + 2) % tiles_per_seg), true);
       }
       lds_barrier();  // tile m ready; tile m - 1 computed
     }
@@ -551,56 +662,51 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
 
   // -------------------------------------------------------------- consumer
   const int g = lane >> 4, r16 = lane & 15;
-  auto q_index = [&](long long t) -> int {
-    const long long tt = t < t_end ? t : t_end - 1;
-    return perm_q[(tt / tiles_per_seg) * N + (tt % tiles_per_seg) * W + wave * 16 + r16];
-  };
-  auto load_q = [&](long long t, int qi, bf16x8 (&dst)[D / 32]) {
-    const long long tt = t < t_end ? t : t_end - 1;
-    const uint16_t *qrow = q + ((tt / tiles_per_seg) * N + qi) * D;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      dst[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(qrow + kk * 32 + g * 8));
-  };
-  bf16x8 bq[1][D / 32], bq_next[D / 32];
-  int qidx = q_index(t_begin);
-  int qidx_n1 = q_index(t_begin + 1);
-  load_q(t_begin, qidx, bq[0]);
   const bf16x8 ones = __builtin_bit_cast(bf16x8, (u16x8)0x3f80);
-
   for (long long t = t_begin; t < t_end; ++t) {
     const int m_idx = static_cast<int>(t - t_begin);
     const int c = static_cast<int>(t % tiles_per_seg);
-    lds_barrier();  // tile m_idx's chunks staged
-    load_q(t + 1, qidx_n1, bq_next);
-    const int qidx_n2 = q_index(t + 2);
-    f32x4 o[1][D / 16], l_acc[1] = {{0.0f, 0.0f, 0.0f, 0.0f}};
-    float m[1] = {-INFINITY};
+    lds_barrier();  // tile m_idx's chunks and query rows staged
+    const uint16_t *Qs = qslots + (m_idx & 1) * kQSlotElems + (wave * 16 + r16) * kKRow;
+    bf16x8 bq[D / 32];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[0][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kk = 0; kk < D / 32; ++kk)
+      bq[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(Qs + kk * 32 + g * 8));
+    const int qidx = qidx_lds[(m_idx & 1) * W + wave * 16 + r16];
+    f32x4 o[D / 16], l_acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t *own = smem + ((m_idx + 1) % 3) * kSlotElems;
     if (c > 0) {
       const uint16_t *prev = smem + (m_idx % 3) * kSlotElems;
-      attend_stage<D, W, 1>(prev, prev + W * kKRow, W, bq, o, l_acc, m, scale_log2, ones, g, r16);
+      const uint16_t *const kb[4] = {prev, prev + 64 * kKRow, own, own + 64 * kKRow};
+      const uint16_t *const vb[4] = {prev + W * kKRow, prev + W * kKRow + 64, own + W * kKRow, own + W * kKRow + 64};
+      attend_blocks<D, kVRow, 4>(kb, vb, bq, o, l_acc, m, scale_log2, ones, g, r16);
+    } else {
+      const uint16_t *const kb[2] = {own, own + 64 * kKRow};
+      const uint16_t *const vb[2] = {own + W * kKRow, own + W * kKRow + 64};
+      attend_blocks<D, kVRow, 2>(kb, vb, bq, o, l_acc, m, scale_log2, ones, g, r16);
     }
-    const uint16_t *own = smem + ((m_idx + 1) % 3) * kSlotElems;
-    attend_stage<D, W, 1>(own, own + W * kKRow, W, bq, o, l_acc, m, scale_log2, ones, g, r16);
-
     const long long seg = (t / tiles_per_seg) * N;
-    const float l_tot = l_acc[0][0];
+    const float l_tot = l_acc[0];
     const float inv = 1.0f / l_tot;
     uint16_t *orow = o_s + (seg + qidx) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const uint2 outv = {pack_bf16x2(o[0][dt][0] * inv, o[0][dt][1] * inv),
-                          pack_bf16x2(o[0][dt][2] * inv, o[0][dt][3] * inv)};
+      const uint2 outv = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
+                          pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
       *reinterpret_cast<uint2 *>(orow + dt * 16 + g * 4) = outv;
     }
-    if (g == 0) lse[seg + qidx] = (m[0] + log2f(l_tot)) * 0.69314718055994530942f;
-    qidx = qidx_n1;
-    qidx_n1 = qidx_n2;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) bq[0][kk] = bq_next[kk];
+    if (g == 0) lse[seg + qidx] = (m + log2f(l_tot)) * 0.69314718055994530942f;
   }
+}
+
+// LDS bytes of the sliding-window kernel: three chunk slots, two query slots
+// and two query-index slots.
+constexpr size_t attn_slide_lds_bytes() {
+  return (3 * (static_cast<size_t>(128) * (64 + 8) + static_cast<size_t>(64) * (128 + 4)) +
+          2 * static_cast<size_t>(128) * (64 + 8)) * 2 + 2 * 128 * 4;
 }
 
 // fp32 inputs: one thread per sorted query, binary32 arithmetic throughout.
@@ -687,8 +793,8 @@ hipError_t launch_bf16_slide(const Geometry &g, const void *q, const void *k, co
   long long wgs = (g.cus + kXcdCount - 1) / kXcdCount * kXcdCount;
   if (wgs > n_tiles) wgs = (n_tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
   const long long tiles_per_wg = (n_tiles + wgs - 1) / wgs;
-  const size_t lds = 3 * (static_cast<size_t>(128) * (64 + 8) + static_cast<size_t>(64) * (128 + 4)) * 2;
-  hipLaunchKernelGGL(elsaa_k3_chunk_attn_slide, dim3(static_cast<unsigned>(wgs)), dim3(768), lds, stream,
+  hipLaunchKernelGGL(elsaa_k3_chunk_attn_slide, dim3(static_cast<unsigned>(wgs)), dim3(768),
+                     attn_slide_lds_bytes(), stream,
                      static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                      static_cast<const uint16_t *>(v), buf.perm, buf.perm + g.rows, g.N, tiles_per_seg,
                      n_tiles, tiles_per_wg, scale_log2, static_cast<uint16_t *>(buf.o_s), buf.lse);

@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
   uint16_t *lperm = reinterpret_cast<uint16_t *>(part + W * 64);  // [S + slack] tile-local key index
 
   // unit = ((b, h) * L + table) * G + bucket group; the G workgroups of a
-  // table each sort all its keys and sum the buckets [gb0, gb1)
+  // table each count, rank and sum only the keys of their buckets [gb0, gb1)
   const long long unit = xcd_logical_block(blockIdx.x, gridDim.x);
   if (unit >= units) return;  // whole workgroup
   const long long tu = unit / G;
@@ -350,12 +350,16 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
         code[q] = j < j_end ? cv : 0xffffffffu;
       }
     };
+    // only the keys of the group's buckets [gb0, gb1) are counted and ranked
+    auto mine = [&](uint32_t code) {
+      return code != 0xffffffffu && code >= static_cast<uint32_t>(gb0) && code < static_cast<uint32_t>(gb1);
+    };
     for (int j0 = j_begin; j0 < j_end; j0 += 512) {
       uint32_t code[8];
       load_codes(j0, code);
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (code[q] != 0xffffffffu) atomicAdd(&wc[code[q]], 1u);
+        if (mine(code[q])) atomicAdd(&wc[code[q]], 1u);
     }
     __syncthreads();
 
@@ -379,7 +383,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
         }
         tot[b] += run - r0;
       }
-      if (tid == 0) bst[nb] = static_cast<uint32_t>(M);
+      // end of the last run: the number of the group's keys in this tile
+      if (b_lo < nb && b_hi == nb) bst[nb] = run;
     }
     __syncthreads();
 
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int j = j8 + q * 64 + lane;
-        if (j < j_end) lperm[atomicAdd(&wc[codes8[q]], 1u)] = static_cast<uint16_t>(j - t0);
+        if (mine(codes8[q])) lperm[atomicAdd(&wc[codes8[q]], 1u)] = static_cast<uint16_t>(j - t0);
       }
     }
     __syncthreads();
