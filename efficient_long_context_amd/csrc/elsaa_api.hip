@@ -121,10 +121,10 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   t.flags = reinterpret_cast<uint8_t *>(take(2 * rows));
   t.hist = reinterpret_cast<uint32_t *>(take(2 * static_cast<size_t>(g.BH) * g.nb_sort * g.sort_tiles * 4));
   // per-table key permutation and run starts: only the two-kernel RACE build uses them
-  const bool fused = elsaa::race_fused_tile(g) > 0;
-  t.rperm = reinterpret_cast<int32_t *>(take(fused ? 0 : static_cast<size_t>(g.BH) * g.L * g.N * 4));
+  const bool split = elsaa::race_split(g);
+  t.rperm = reinterpret_cast<int32_t *>(take(split ? static_cast<size_t>(g.BH) * g.L * g.N * 4 : 0));
   t.rstart = reinterpret_cast<int32_t *>(
-      take(fused ? 0 : static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
+      take(split ? static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4 : 0));
   t.tsum = take(static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * es);
   t.tcnt = reinterpret_cast<float *>(take(static_cast<size_t>(g.BH) * g.L * g.nb_race * 4));
   t.o_s = take(rows * g.D * es);
@@ -138,6 +138,13 @@ __global__ void widen_bf16(const uint16_t *__restrict__ src, float *__restrict__
   if (i < n) dst[i] = elsaa::bf16_bits_to_f32(src[i]);
 }
 
+// Key RACE codes are kept table-major [L][rows]; the aux layout is [rows][L].
+template <typename CT>
+__global__ void codes_to_row_major(const CT *__restrict__ src, CT *__restrict__ dst, long long rows, int L) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;  // destination element
+  if (i < rows * L) dst[i] = src[(i % L) * rows + i / L];
+}
+
 hipError_t copy_aux(const elsaa::Geometry &g, const elsaa::Buffers &buf, const elsaa_aux_t *aux,
                     hipStream_t s) {
   const size_t rows = static_cast<size_t>(g.rows);
@@ -147,7 +154,6 @@ hipError_t copy_aux(const elsaa::Geometry &g, const elsaa::Buffers &buf, const e
       {aux->sort_code_q, buf.scode, rows * 2},
       {aux->sort_code_k, buf.scode + rows, rows * 2},
       {aux->race_code_q, buf.rcode, rows * g.L * g.rcb},
-      {aux->race_code_k, static_cast<const char *>(buf.rcode) + rows * g.L * g.rcb, rows * g.L * g.rcb},
       {aux->perm_q, buf.perm, rows * 4},
       {aux->perm_k, buf.perm + rows, rows * 4},
       {aux->race_sum, g.bf16 ? nullptr : buf.tsum, static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * 4},
@@ -158,6 +164,19 @@ hipError_t copy_aux(const elsaa::Geometry &g, const elsaa::Buffers &buf, const e
   for (const Item &it : items) {
     if (!it.dst || !it.src) continue;
     const hipError_t e = hipMemcpyAsync(it.dst, it.src, it.bytes, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  if (aux->race_code_k) {
+    const long long n = g.rows * g.L;
+    const void *src = static_cast<const char *>(buf.rcode) + rows * g.L * g.rcb;
+    if (g.rcb == 1)
+      hipLaunchKernelGGL(codes_to_row_major<uint8_t>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                         static_cast<const uint8_t *>(src), static_cast<uint8_t *>(aux->race_code_k), g.rows, g.L);
+    else
+      hipLaunchKernelGGL(codes_to_row_major<uint16_t>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                         s, static_cast<const uint16_t *>(src), static_cast<uint16_t *>(aux->race_code_k), g.rows,
+                         g.L);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (g.bf16 && aux->race_sum) {  // bfloat16 tables widen to the binary32 aux layout

@@ -403,20 +403,68 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
       words[w] = r32s[0] | r32s[1];
     }
     const bool byte_codes = P == 8 && ns % 8 == 0 && L % 4 == 0;
-    if (valid) {
-      auto get = [&](int wd) -> uint32_t {
-        uint32_t r = 0u;
+    auto get = [&](int wd) -> uint32_t {
+      uint32_t r = 0u;
 #pragma unroll
-        for (int w = 0; w < kWords; ++w) r = wd == w ? words[w] : r;
-        return r;
-      };
+      for (int w = 0; w < kWords; ++w) r = wd == w ? words[w] : r;
+      return r;
+    };
+    // Key codes with byte codes: each quad of lanes (rows 4k .. 4k+3 of a lane
+    // group) transposes its four code words (tables 4j .. 4j+3) so that lane
+    // i holds rows 4k .. 4k+3 of table 4j + i, one 4-byte store per lane
+    // into the table-major key codes.  Runs with every lane active (DPP).
+    const bool quad_store = tensor == 1 && byte_codes && rows % 4 == 0;
+    if (quad_store) {
+      const unsigned long long vm = __ballot(valid);
+      const bool quad_valid = ((vm >> (lane & ~3)) & 0xfull) == 0xfull;
+      uint8_t *kc = reinterpret_cast<uint8_t *>(rcode) + rows * L;
+      for (int j = g; j < L / 4; j += 4) {
+        const int bytepos = ns / 8 + 4 * j;
+        const uint32_t word = __builtin_amdgcn_alignbyte(get(bytepos / 4 + 1), get(bytepos / 4), bytepos % 4);
+        // 4x4 byte transpose in two pair exchanges (quad_perm [1,0,3,2], then [2,3,0,1])
+        const uint32_t y = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(word), 0xB1, 0xf, 0xf, false));
+        const uint32_t t = __builtin_amdgcn_perm(y, word, (lane & 1) ? 0x03070105u : 0x06020400u);
+        const uint32_t z = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(t), 0x4E, 0xf, 0xf, false));
+        const uint32_t f = __builtin_amdgcn_perm(z, t, (lane & 2) ? 0x03020706u : 0x05040100u);
+        if (quad_valid) {
+          *reinterpret_cast<uint32_t *>(kc + static_cast<long long>(4 * j + (lane & 3)) * rows + row - (lane & 3)) = f;
+        } else if (valid) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kc[static_cast<long long>(4 * j + e) * rows + row] = static_cast<uint8_t>(word >> (8 * e));
+        }
+      }
+    }
+    if (valid) {
       const long long out_row = static_cast<long long>(tensor) * rows + row;
       if (g == 0) {
         scode[out_row] = static_cast<uint16_t>(words[0] & ((1u << ns) - 1u));  // ns <= 12
         // a projection binary64 could not decide: the exact pass redoes the row
         flags[out_row] = ((undecided_mask >> r16) & 0x0001000100010001ull) ? 1 : 0;
       }
-      if (byte_codes) {
+      if (tensor == 1) {
+        // key codes, table-major: the 16 lanes of a lane group write 16
+        // consecutive rows of each table
+        if (rcb == 1) {
+          uint8_t *kc = reinterpret_cast<uint8_t *>(rcode) + rows * L + row;
+          if (quad_store) {
+            // written above
+          } else if (byte_codes) {
+            for (int j = g; j < L / 4; j += 4) {
+              const int bytepos = ns / 8 + 4 * j;
+              const uint32_t word = __builtin_amdgcn_alignbyte(get(bytepos / 4 + 1), get(bytepos / 4), bytepos % 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) kc[static_cast<long long>(4 * j + e) * rows] = static_cast<uint8_t>(word >> (8 * e));
+            }
+          } else {
+            for (int l = g; l < L; l += 4)
+              kc[static_cast<long long>(l) * rows] = static_cast<uint8_t>(bit_field(get, ns + l * P, P));
+          }
+        } else {
+          uint16_t *kc = reinterpret_cast<uint16_t *>(rcode) + rows * L + row;
+          for (int l = g; l < L; l += 4)
+            kc[static_cast<long long>(l) * rows] = static_cast<uint16_t>(bit_field(get, ns + l * P, P));
+        }
+      } else if (byte_codes) {
         // 8-bit codes starting on a byte: code word j is bytes ns/8 + 4j .. +3
         // of the plane mask, one byte-funnel of two mask words
         uint32_t *rc = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(rcode) + out_row * L);
@@ -525,8 +573,9 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_fixup(
       if (lane == 0) scode[r] = static_cast<uint16_t>(bit_field(get, 0, ns));
       for (int l = lane; l < L; l += 64) {
         const uint32_t c = bit_field(get, ns + l * P, P);
-        if (rcb == 1) reinterpret_cast<uint8_t *>(rcode)[r * L + l] = static_cast<uint8_t>(c);
-        else reinterpret_cast<uint16_t *>(rcode)[r * L + l] = static_cast<uint16_t>(c);
+        const long long ci = race_code_index(r >= rows ? 1 : 0, r >= rows ? r - rows : r, l, rows, L);
+        if (rcb == 1) reinterpret_cast<uint8_t *>(rcode)[ci] = static_cast<uint8_t>(c);
+        else reinterpret_cast<uint16_t *>(rcode)[ci] = static_cast<uint16_t>(c);
       }
     }
   }
@@ -575,9 +624,9 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_f32(
       if (t < ns) {
         scode[out_row] = static_cast<uint16_t>(code);
       } else {
-        const int l = (t - ns) / P;
-        if (rcb == 1) reinterpret_cast<uint8_t *>(rcode)[out_row * L + l] = static_cast<uint8_t>(code);
-        else reinterpret_cast<uint16_t *>(rcode)[out_row * L + l] = static_cast<uint16_t>(code);
+        const long long ci = race_code_index(tensor, row, (t - ns) / P, rows, L);
+        if (rcb == 1) reinterpret_cast<uint8_t *>(rcode)[ci] = static_cast<uint8_t>(code);
+        else reinterpret_cast<uint16_t *>(rcode)[ci] = static_cast<uint16_t>(code);
       }
       code = 0;
     }
@@ -585,8 +634,9 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_f32(
   if (ns == 0) scode[out_row] = 0;
   if (P == 0) {
     for (int l = 0; l < L; ++l) {
-      if (rcb == 1) reinterpret_cast<uint8_t *>(rcode)[out_row * L + l] = 0;
-      else reinterpret_cast<uint16_t *>(rcode)[out_row * L + l] = 0;
+      const long long ci = race_code_index(tensor, row, l, rows, L);
+      if (rcb == 1) reinterpret_cast<uint8_t *>(rcode)[ci] = 0;
+      else reinterpret_cast<uint16_t *>(rcode)[ci] = 0;
     }
   }
 }

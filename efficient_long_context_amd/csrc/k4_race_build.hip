@@ -23,164 +23,6 @@
 namespace elsaa {
 namespace {
 
-constexpr int kSortWavesMax = 16;
-constexpr int kReduceBatch = 16;  // key rows in flight per wave
-
-// ---------------------------------------------------------------------- sort --
-template <typename CT>
-__global__ __launch_bounds__(kSortWavesMax * 64) void elsaa_k4_race_sort(
-    const CT *__restrict__ kcodes, int N, int L, int P, int chunk, int32_t *__restrict__ perm,
-    int32_t *__restrict__ bstart) {
-  extern __shared__ uint32_t cnt[];  // [waves][nb]: counts, then running offsets
-  __shared__ uint32_t part[kSortWavesMax * 64];
-  const int nb = 1 << P;
-  const int nthreads = blockDim.x, waves = nthreads >> 6;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l = blockIdx.x;
-  const long long bh = blockIdx.y;
-  const long long seg = bh * N;
-  const long long unit = bh * L + l;
-  const CT *c = kcodes + seg * L + l;  // code of key j at c[j * L]
-  const int j_begin = wave * chunk;
-  const int j_end = j_begin + chunk < N ? j_begin + chunk : N;
-
-  for (int i = tid; i < waves * nb; i += nthreads) cnt[i] = 0;
-  __syncthreads();
-  uint32_t *wc = cnt + wave * nb;
-  // codes are read 8 rounds at a time so the loads overlap (one latency per 512 keys)
-  auto load_codes = [&](int j0, uint32_t (&code)[8]) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int j = j0 + q * 64 + lane;
-      code[q] = j < j_end ? static_cast<uint32_t>(c[static_cast<long long>(j) * L]) : 0xffffffffu;
-    }
-  };
-  for (int j0 = j_begin; j0 < j_end; j0 += 512) {
-    uint32_t code[8];
-    load_codes(j0, code);
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (code[q] != 0xffffffffu) atomicAdd(&wc[code[q]], 1u);
-  }
-  __syncthreads();
-
-  // bucket-major exclusive scan of the [bucket][wave] counts
-  const int per = (nb + nthreads - 1) / nthreads;
-  const int b_lo = tid * per < nb ? tid * per : nb;
-  const int b_hi = b_lo + per < nb ? b_lo + per : nb;
-  uint32_t sum = 0;
-  for (int b = b_lo; b < b_hi; ++b)
-    for (int w = 0; w < waves; ++w) sum += cnt[w * nb + b];
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < nthreads; off <<= 1) {  // inclusive Hillis-Steele scan
-    const uint32_t add = tid >= off ? part[tid - off] : 0u;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  uint32_t run = part[tid] - sum;
-  int32_t *bs = bstart + unit * (nb + 1);
-  for (int b = b_lo; b < b_hi; ++b) {
-    bs[b] = static_cast<int32_t>(run);
-    for (int w = 0; w < waves; ++w) {
-      const uint32_t t = cnt[w * nb + b];
-      cnt[w * nb + b] = run;
-      run += t;
-    }
-  }
-  if (tid == 0) bs[nb] = N;
-  __syncthreads();
-
-  // stable ranks: each wave walks its chunk in order, 64 keys per round
-  int32_t *pm = perm + unit * N;
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int j8 = j_begin; j8 < j_end; j8 += 512) {
-  uint32_t codes8[8];
-  load_codes(j8, codes8);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int j0 = j8 + q * 64;
-    const int j = j0 + lane;
-    const bool valid = j < j_end;
-    const uint32_t code = valid ? codes8[q] : 0u;
-    unsigned long long mask = __ballot(valid);
-    for (int bit = 0; bit < P; ++bit) {
-      const bool set = (code >> bit) & 1u;
-      const unsigned long long bb = __ballot(set);
-      mask &= set ? bb : ~bb;
-    }
-    const int rank = __popcll(mask & lt);
-    const int leader = __ffsll(static_cast<long long>(mask)) - 1;
-    uint32_t before = 0;
-    if (valid && lane == leader) {
-      before = wc[code];
-      wc[code] = before + static_cast<uint32_t>(__popcll(mask));
-    }
-    before = __shfl(before, leader < 0 ? 0 : leader);
-    if (valid) pm[before + rank] = j;
-    // the leader's counter update must land before the next round reads it
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  }
-  }
-}
-
-// -------------------------------------------------------------------- reduce --
-template <typename VT>
-__global__ __launch_bounds__(256) void elsaa_k4_race_reduce(
-    const VT *__restrict__ v, const int32_t *__restrict__ perm, const int32_t *__restrict__ bstart,
-    int N, int D, int L, int P, int ncs, int parts, long long units, VT *__restrict__ tsum,
-    float *__restrict__ tcnt) {
-  const int lane = threadIdx.x & 63;
-  // consecutive units (same (b, h), same value rows) run on one XCD's L2
-  const long long u = xcd_logical_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
-  if (u >= units) return;  // whole wave
-  const int nb = 1 << P;
-  const int part = static_cast<int>(u % parts);
-  const int cs = static_cast<int>((u / parts) % ncs);
-  const long long tu = u / (static_cast<long long>(parts) * ncs);  // (b, h) * L + table
-  const long long bh = tu / L;
-  const int32_t *bs = bstart + tu * (nb + 1);
-  const int32_t *pm = perm + tu * N;
-  const VT *vcol = v + bh * N * static_cast<long long>(D) + cs * 64 + lane;
-
-  // buckets owned: those whose run starts in [lo, hi); the last part also owns
-  // the empty buckets that start at N
-  const int lo = static_cast<int>(static_cast<long long>(N) * part / parts);
-  const int hi = part == parts - 1 ? N + 1 : static_cast<int>(static_cast<long long>(N) * (part + 1) / parts);
-  int b0 = nb, b1 = nb;
-  for (int bb = 0; bb < nb; bb += 64) {
-    const int b = bb + lane;
-    const int s = b < nb ? bs[b] : N + 1;
-    const unsigned long long ge_lo = __ballot(b < nb && s >= lo);
-    const unsigned long long ge_hi = __ballot(b < nb && s >= hi);
-    if (b0 == nb && ge_lo) b0 = bb + __builtin_ctzll(ge_lo);
-    if (b1 == nb && ge_hi) b1 = bb + __builtin_ctzll(ge_hi);
-  }
-
-  for (int b = b0; b < b1; ++b) {
-    const int p0 = bs[b], p1 = bs[b + 1];
-    float acc = 0.0f;
-    for (int p = p0; p < p1; p += kReduceBatch) {
-      const int n = p1 - p < kReduceBatch ? p1 - p : kReduceBatch;
-      // lanes 0..15 fetch the batch's key indices (clamped inside the run)
-      const int jl = pm[p + (lane < n ? lane : n - 1)];
-      float val[kReduceBatch];
-#pragma unroll
-      for (int q = 0; q < kReduceBatch; ++q) {
-        const int j = __builtin_amdgcn_readlane(jl, q < n ? q : n - 1);
-        val[q] = Elem<VT>::load(vcol + static_cast<long long>(j) * D);
-      }
-#pragma unroll
-      for (int q = 0; q < kReduceBatch; ++q)
-        if (q < n) acc += val[q];  // ascending key order within the bucket
-    }
-    tsum[(tu * nb + b) * static_cast<long long>(D) + cs * 64 + lane] = Elem<VT>::store_val(acc);
-    if (cs == 0 && lane == 0) tcnt[tu * nb + b] = static_cast<float>(p1 - p0);
-  }
-}
 
 // --------------------------------------------------------------------- fused --
 // One workgroup per (b, h, table) when the whole table fits in LDS: the table
@@ -325,7 +167,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
   const int l = static_cast<int>(tu % L);
   const int gb0 = static_cast<int>(static_cast<long long>(nb) * grp / G);
   const int gb1 = static_cast<int>(static_cast<long long>(nb) * (grp + 1) / G);
-  const CT *c = kcodes + bh * N * static_cast<long long>(L) + l;  // code of key j at c[j * L]
+  const long long rows = units / G / L * N;  // keys of all (b, h)
+  const CT *c = kcodes + static_cast<long long>(l) * rows + bh * N;  // code of key j at c[j]
   const VT *vb = v + bh * N * static_cast<long long>(D);
 
   for (int i = tid; i < nb * D; i += W * 64) acc[i] = 0.0f;
@@ -346,7 +189,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int j = j0 + q * 64 + lane;
-        const uint32_t cv = static_cast<uint32_t>(c[static_cast<long long>(j < j_end ? j : j_end - 1) * L]);
+        const uint32_t cv = static_cast<uint32_t>(c[j < j_end ? j : j_end - 1]);
         code[q] = j < j_end ? cv : 0xffffffffu;
       }
     };
@@ -508,6 +351,233 @@ __global__ __launch_bounds__(kFusedWaves * 64) void elsaa_k4_race_fused(
   for (int i = gb0 + tid; i < gb1; i += W * 64) tcnt[tu * nb + i] = static_cast<float>(tot[i]);
 }
 
+// ----------------------------------------------------------- rank + gather --
+// Two kernels, for any table size.
+//   rank    one workgroup per (b, h, table): a counting sort of the table's N
+//           key codes (per-wave LDS histograms, a bucket-major scan, then each
+//           key takes the next slot of its (wave, bucket) counter from an LDS
+//           atomic that returns the old value), writing the sorted key
+//           indices, the run start of every bucket and the bucket counts;
+//   gather  one wave per (b, h, table, part of the positions): the wave owns
+//           the buckets whose run starts in its part, stages their key
+//           indices in LDS and sums the value rows bucket by bucket as the
+//           fused kernel does, writing each finished bucket row once.  Waves
+//           of one (b, h) are consecutive and so share an XCD's L2, which then
+//           holds the value rows all its tables gather.
+template <typename CT>
+__global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
+    const CT *__restrict__ kcodes, int N, int L, int P, long long rows, int staged,
+    int32_t *__restrict__ rperm, int32_t *__restrict__ rstart, float *__restrict__ tcnt) {
+  extern __shared__ uint32_t lds[];
+  const int nb = 1 << P;
+  const int W = static_cast<int>(blockDim.x >> 6);
+  uint32_t *cnt = lds;           // [W][nb] counts, then running offsets
+  uint32_t *part = lds + W * nb;  // [W] scan
+  uint16_t *lperm = reinterpret_cast<uint16_t *>(part + W);  // [N] when staged (N <= 65536)
+  const long long unit = blockIdx.x;  // (b, h) * L + table
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long bh = unit / L;
+  const int l = static_cast<int>(unit % L);
+  const CT *c = kcodes + static_cast<long long>(l) * rows + bh * N;  // code of key j at c[j]
+  const int chunk = ((N + W - 1) / W + 63) / 64 * 64;
+  const int j_begin = wave * chunk < N ? wave * chunk : N;
+  const int j_end = j_begin + chunk < N ? j_begin + chunk : N;
+
+  for (int i = tid; i < W * nb; i += W * 64) cnt[i] = 0u;
+  __syncthreads();
+  uint32_t *wc = cnt + wave * nb;
+  auto load_codes = [&](int j0, uint32_t (&code)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = j0 + q * 64 + lane;
+      const uint32_t cv = static_cast<uint32_t>(c[j < j_end ? j : j_end - 1]);
+      code[q] = j < j_end ? cv : 0xffffffffu;
+    }
+  };
+  for (int j0 = j_begin; j0 < j_end; j0 += 512) {
+    uint32_t code[8];
+    load_codes(j0, code);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (code[q] != 0xffffffffu) atomicAdd(&wc[code[q]], 1u);
+  }
+  __syncthreads();
+  {  // bucket-major exclusive scan of the [bucket][wave] counts
+    const int nthreads = W * 64;
+    const int per = (nb + nthreads - 1) / nthreads;
+    const int b_lo = tid * per < nb ? tid * per : nb;
+    const int b_hi = b_lo + per < nb ? b_lo + per : nb;
+    uint32_t sum = 0;
+    for (int b = b_lo; b < b_hi; ++b)
+      for (int w = 0; w < W; ++w) sum += cnt[w * nb + b];
+    uint32_t run = block_exclusive_scan(sum, part, lane, wave);
+    int32_t *rs = rstart + unit * (nb + 1);
+    for (int b = b_lo; b < b_hi; ++b) {
+      rs[b] = static_cast<int32_t>(run);
+      const uint32_t r0 = run;
+      for (int w = 0; w < W; ++w) {
+        const uint32_t t = cnt[w * nb + b];
+        cnt[w * nb + b] = run;
+        run += t;
+      }
+      tcnt[unit * nb + b] = static_cast<float>(run - r0);
+    }
+    if (tid == 0) rs[nb] = N;
+  }
+  __syncthreads();
+  // sorted key indices: staged in LDS and written out in order (coalesced),
+  // or scattered straight to memory when N does not fit
+  int32_t *rp = rperm + unit * N;
+  for (int j8 = j_begin; j8 < j_end; j8 += 512) {
+    uint32_t codes8[8];
+    load_codes(j8, codes8);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = j8 + q * 64 + lane;
+      if (codes8[q] != 0xffffffffu) {
+        const uint32_t pos = atomicAdd(&wc[codes8[q]], 1u);
+        if (staged) lperm[pos] = static_cast<uint16_t>(j);
+        else rp[pos] = j;
+      }
+    }
+  }
+  if (staged) {
+    __syncthreads();
+    for (int i = tid; i < N; i += W * 64) rp[i] = lperm[i];
+  }
+}
+
+constexpr int kGatherWaves = 4;       // waves per gather workgroup
+constexpr int kGatherStage = 1024;    // key indices a wave stages in LDS at once
+constexpr int kGatherSlack = 256;     // staged entries read past the end by the look-ahead
+
+template <typename VT, int D>
+__global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
+    const VT *__restrict__ v, const int32_t *__restrict__ rperm, const int32_t *__restrict__ rstart,
+    int N, int L, int P, int parts, long long waves_total, VT *__restrict__ tsum) {
+  using PC = Piece<VT, D>;
+  constexpr int kCols = PC::kCols, kLPR = PC::kLanesPerRow;
+  constexpr int kRPI = PC::kRowsPerLoad;
+  constexpr int kI = 8;              // load instructions per batch
+  constexpr int kBP = kI * kRPI;     // positions per batch
+  __shared__ uint32_t stage_all[kGatherWaves][kGatherStage + kGatherSlack];
+  const int nb = 1 << P;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const long long u = xcd_logical_block(blockIdx.x, gridDim.x) * kGatherWaves + wave;
+  if (u >= waves_total) return;  // whole wave; the kernel has no barriers
+  uint32_t *stage = stage_all[wave];
+  const int prt = static_cast<int>(u % parts);
+  const long long unit = u / parts;  // (b, h) * L + table
+  const long long bh = unit / L;
+  const int32_t *rs = rstart + unit * (nb + 1);
+  const int32_t *rp = rperm + unit * N;
+  VT *ts = tsum + unit * nb * static_cast<long long>(D);
+
+  // owned buckets: those whose run starts in [lo, hi); the last part also owns
+  // the empty buckets that start at N
+  const int lo = static_cast<int>(static_cast<long long>(N) * prt / parts);
+  const int hi = prt == parts - 1 ? N + 1 : static_cast<int>(static_cast<long long>(N) * (prt + 1) / parts);
+  int b0 = nb, b1 = nb;
+  for (int bb = 0; bb < nb; bb += 64) {
+    const int b = bb + lane;
+    const int st = b < nb ? rs[b] : N + 1;
+    const unsigned long long ge_lo = __ballot(b < nb && st >= lo);
+    const unsigned long long ge_hi = __ballot(b < nb && st >= hi);
+    if (b0 == nb && ge_lo) b0 = bb + __builtin_ctzll(ge_lo);
+    if (b1 == nb && ge_hi) b1 = bb + __builtin_ctzll(ge_hi);
+    if (b1 != nb) break;
+  }
+  b0 = __builtin_amdgcn_readfirstlane(b0);
+  b1 = __builtin_amdgcn_readfirstlane(b1);
+  if (b0 >= b1) return;
+  const int p_lo = __builtin_amdgcn_readfirstlane(rs[b0]);
+  const int p_hi = __builtin_amdgcn_readfirstlane(rs[b1]);
+
+  const int cc = lane % kLPR;       // column piece
+  const int my_off = lane / kLPR;   // this lane's row within a load
+  const Bf16Adder adder;
+  int b = b0;
+  int bend = __builtin_amdgcn_readfirstlane(rs[b0 + 1]);
+  float a[kCols];
+#pragma unroll
+  for (int k = 0; k < kCols; ++k) a[k] = 0.0f;
+  // bucket b is complete: transposing lane reduction, then the lane's column
+  // sums go straight to the table row
+  auto flush = [&]() {
+    float r[kCols / kRPI];
+    lane_group_transpose_sum<kCols, kLPR>(a, r, lane);
+#pragma unroll
+    for (int m = 0; m < kCols / kRPI; ++m)
+      ts[b * static_cast<long long>(D) + cc * kCols + transposed_column<kCols, kLPR>(m, lane)] =
+          Elem<VT>::store_val(r[m]);
+#pragma unroll
+    for (int k = 0; k < kCols; ++k) a[k] = 0.0f;
+  };
+  if (p_lo == p_hi) {  // only empty buckets
+    for (; b < b1; ++b) flush();
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t vrs =
+      make_rsrc(v + bh * N * static_cast<long long>(D), static_cast<uint32_t>(N) * PC::kRowBytes);
+  const uint32_t cbyte = static_cast<uint32_t>(cc) * 16u;
+  for (int s0 = p_lo; s0 < p_hi; s0 += kGatherStage) {
+    const int s1 = s0 + kGatherStage < p_hi ? s0 + kGatherStage : p_hi;
+    // stage the key indices of positions [s0, s1) (entries past s1 are stale:
+    // the look-ahead may load their rows, which are never added)
+    for (int i = lane; i < s1 - s0; i += 64) stage[i] = static_cast<uint32_t>(rp[s0 + i]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    auto load_batch = [&](int pbase, u32x4 (&r)[kI]) {
+      uint32_t jl[kI];
+      const uint32_t *lp = stage + (pbase - s0) + my_off;
+#pragma unroll
+      for (int i = 0; i < kI; ++i) jl[i] = lp[i * kRPI];
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+        r[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, jl[i] * PC::kRowBytes + cbyte, 0, 0));
+    };
+    auto consume = [&](int pbase, const u32x4 (&r)[kI]) {
+#pragma unroll
+      for (int i = 0; i < kI; ++i) {
+        const int p = pbase + i * kRPI;
+        const int pe = p + kRPI < s1 ? p + kRPI : s1;
+        const int my = p + my_off;
+        const int stop0 = pe < bend ? pe : bend;
+        if (my < stop0) PC::add(r[i], a, adder);
+        if (pe >= bend && p < s1) {
+          int cur = stop0;
+          do {
+            if (cur == bend) {
+              flush();
+              ++b;
+              bend = b < b1 ? __builtin_amdgcn_readfirstlane(rs[b + 1]) : 0x7fffffff;
+            }
+            const int stop = pe < bend ? pe : bend;
+            if (my >= cur && my < stop) PC::add(r[i], a, adder);
+            cur = stop;
+          } while (cur < pe || cur == bend);
+        }
+      }
+    };
+    u32x4 ra[kI], rb[kI];
+    load_batch(s0, ra);
+    for (int pc = s0; pc < s1; pc += 2 * kBP) {
+      load_batch(pc + kBP, rb);
+      consume(pc, ra);
+      load_batch(pc + 2 * kBP, ra);
+      consume(pc + kBP, rb);
+    }
+    // the stage may be overwritten only after every lane has read it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+}
+
 #ifndef ELSAA_RACE_GROUPS
 #define ELSAA_RACE_GROUPS 0  // 0: chosen per shape
 #endif
@@ -573,17 +643,27 @@ int race_fused_tile(const Geometry &g) {
   return n64 < smax ? n64 : smax;
 }
 
+#ifndef ELSAA_RACE_SPLIT
+#define ELSAA_RACE_SPLIT 1  // 1: rank + gather kernels; 0: single kernel where the table fits in LDS
+#endif
+#ifndef ELSAA_GATHER_POS
+#define ELSAA_GATHER_POS 512  // positions per gather wave (before rounding to whole buckets)
+#endif
+
+bool race_split(const Geometry &g) { return ELSAA_RACE_SPLIT || race_fused_tile(g) == 0; }
+
 double race_build_idle_fraction(const Geometry &g) {
-  const long long tables = static_cast<long long>(g.BH) * g.L;  // workgroups, one CU each
-  return idle_fraction(race_fused_tile(g) > 0 ? tables * race_groups(g) : tables, g.cus);
+  // the gather kernel of the two-kernel build fills the device
+  if (race_split(g)) return 0.0;
+  return idle_fraction(static_cast<long long>(g.BH) * g.L * race_groups(g), g.cus);
 }
 
 hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
                              hipStream_t stream) {
   const int nb = g.nb_race;
   const void *rk = static_cast<const char *>(buf.rcode) + static_cast<size_t>(g.rows) * g.L * g.rcb;
-  const int S = race_fused_tile(g);
-  if (S > 0) {
+  if (!race_split(g)) {
+    const int S = race_fused_tile(g);
     const size_t lds = fused_lds_bytes(nb, g.D, S);
     if (g.rcb == 1) {
       if (g.bf16) launch_fused<uint8_t, uint16_t>(g, rk, v, S, lds, buf, stream);
@@ -594,34 +674,52 @@ hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &bu
     }
     return hipGetLastError();
   }
-  int waves = 16384 / nb;  // LDS counts: waves * nb * 4 bytes <= 64 KB
-  waves = waves < 1 ? 1 : (waves > kSortWavesMax ? kSortWavesMax : waves);
-  const int chunk = ((g.N + waves - 1) / waves + 63) / 64 * 64;
-  const dim3 sgrid(g.L, g.BH);
-  const size_t slds = static_cast<size_t>(waves) * nb * 4;
+  const long long units = static_cast<long long>(g.BH) * g.L;
+  int waves = 16384 / nb;  // LDS counters: waves * nb * 4 bytes <= 64 KB
+  waves = waves < 1 ? 1 : (waves > 16 ? 16 : waves);
+  // stage the sorted indices in LDS when N fits, keeping two workgroups per CU
+  constexpr size_t kRankLdsTwoPerCu = 78 * 1024;
+  auto rank_lds = [&](int w, bool st) {
+    return (static_cast<size_t>(w) * nb + w) * 4 + (st ? static_cast<size_t>(g.N) * 2 : 0);
+  };
+  bool staged = g.N <= 65536;
+  while (staged && waves > 4 && rank_lds(waves, true) > kRankLdsTwoPerCu) waves /= 2;
+  if (rank_lds(waves, staged) > kRankLdsTwoPerCu) staged = false;
+  const size_t rlds = rank_lds(waves, staged);
   if (g.rcb == 1)
-    hipLaunchKernelGGL(elsaa_k4_race_sort<uint8_t>, sgrid, dim3(waves * 64), slds, stream,
-                       static_cast<const uint8_t *>(rk), g.N, g.L, g.P, chunk, buf.rperm, buf.rstart);
+    hipLaunchKernelGGL(elsaa_k4_race_rank<uint8_t>, dim3(static_cast<unsigned>(units)), dim3(waves * 64), rlds,
+                       stream, static_cast<const uint8_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0, buf.rperm,
+                       buf.rstart, buf.tcnt);
   else
-    hipLaunchKernelGGL(elsaa_k4_race_sort<uint16_t>, sgrid, dim3(waves * 64), slds, stream,
-                       static_cast<const uint16_t *>(rk), g.N, g.L, g.P, chunk, buf.rperm, buf.rstart);
+    hipLaunchKernelGGL(elsaa_k4_race_rank<uint16_t>, dim3(static_cast<unsigned>(units)), dim3(waves * 64), rlds,
+                       stream, static_cast<const uint16_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0, buf.rperm,
+                       buf.rstart, buf.tcnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int ncs = g.D / 64;
-  const long long tables = static_cast<long long>(g.BH) * g.L * ncs;
-  long long parts = (8192 + tables - 1) / tables;  // aim for ~8K waves
-  parts = parts < 1 ? 1 : (parts > nb ? nb : parts);
-  const long long units = tables * parts;
-  const dim3 rgrid(static_cast<unsigned>(((units + 3) / 4 + kXcdCount - 1) / kXcdCount * kXcdCount));
-  if (g.bf16)
-    hipLaunchKernelGGL(elsaa_k4_race_reduce<uint16_t>, rgrid, dim3(256), 0, stream,
-                       static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, g.N, g.D, g.L, g.P,
-                       ncs, static_cast<int>(parts), units, static_cast<uint16_t *>(buf.tsum), buf.tcnt);
-  else
-    hipLaunchKernelGGL(elsaa_k4_race_reduce<float>, rgrid, dim3(256), 0, stream,
-                       static_cast<const float *>(v), buf.rperm, buf.rstart, g.N, g.D, g.L, g.P, ncs,
-                       static_cast<int>(parts), units, static_cast<float *>(buf.tsum), buf.tcnt);
+  const int parts = (g.N + ELSAA_GATHER_POS - 1) / ELSAA_GATHER_POS;
+  const long long waves_total = units * parts;
+  const long long wgs = (waves_total + kGatherWaves - 1) / kGatherWaves;
+  const dim3 grid(static_cast<unsigned>((wgs + kXcdCount - 1) / kXcdCount * kXcdCount));
+  if (g.bf16) {
+    if (g.D == 64)
+      hipLaunchKernelGGL((elsaa_k4_race_gather<uint16_t, 64>), grid, dim3(kGatherWaves * 64), 0, stream,
+                         static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, g.N, g.L, g.P, parts,
+                         waves_total, static_cast<uint16_t *>(buf.tsum));
+    else
+      hipLaunchKernelGGL((elsaa_k4_race_gather<uint16_t, 128>), grid, dim3(kGatherWaves * 64), 0, stream,
+                         static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, g.N, g.L, g.P, parts,
+                         waves_total, static_cast<uint16_t *>(buf.tsum));
+  } else {
+    if (g.D == 64)
+      hipLaunchKernelGGL((elsaa_k4_race_gather<float, 64>), grid, dim3(kGatherWaves * 64), 0, stream,
+                         static_cast<const float *>(v), buf.rperm, buf.rstart, g.N, g.L, g.P, parts, waves_total,
+                         static_cast<float *>(buf.tsum));
+    else
+      hipLaunchKernelGGL((elsaa_k4_race_gather<float, 128>), grid, dim3(kGatherWaves * 64), 0, stream,
+                         static_cast<const float *>(v), buf.rperm, buf.rstart, g.N, g.L, g.P, parts, waves_total,
+                         static_cast<float *>(buf.tsum));
+  }
   return hipGetLastError();
 }
 
