@@ -190,7 +190,7 @@ __host__ __device__ constexpr int tile_plane(int pt, int m, int npt) {
 }
 
 template <int D, int NPT>
-__global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void elsaa_k1_hash_bf16(
     const uint16_t *__restrict__ xq, const uint16_t *__restrict__ xk,
     const uint16_t *__restrict__ planes, int R, int ns, int L, int P, long long rows,
     uint16_t *__restrict__ scode, void *__restrict__ rcode, int rcb, uint8_t *__restrict__ flags,
@@ -203,6 +203,9 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
   __shared__ __align__(16) uint16_t sp[kRPad * kLdsRow];
   __shared__ __align__(16) uint16_t sx[kStepRows * kLdsRow];
   __shared__ float s_red[2];  // max_t c|r_t| and "all planes in range"
+  // key byte codes of one step, table-major [table][64 rows], written out one
+  // step later as whole 16-byte row pieces per table (L <= 64)
+  __shared__ __align__(16) uint8_t kcl[64 * kStepRows];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tensor = blockIdx.y;
@@ -259,8 +262,28 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
   };
 
   load_step(row_begin);
+  // Key byte codes (the table-major layout the RACE build reads): each step's
+  // codes are staged in kcl and stored after the next barrier, lane 4t + c
+  // writing rows 16c .. 16c+15 of table t (16-byte stores when rows allow).
+  const bool staged_kcodes = tensor == 1 && P == 8 && ns % 8 == 0 && L % 4 == 0 && L <= 64;
+  auto flush_kcodes = [&](long long rs) {
+    if (wave != 0) return;
+    uint8_t *kc = reinterpret_cast<uint8_t *>(rcode) + rows * L + rs;
+    for (int t = lane >> 2; t < L; t += 16) {
+      const int c = lane & 3;
+      const long long r = rs + 16 * c;
+      const uint8_t *src = kcl + t * kStepRows + 16 * c;
+      if (rows % 16 == 0 && r + 16 <= row_end) {
+        *reinterpret_cast<u32x4 *>(kc + static_cast<long long>(t) * rows + 16 * c) =
+            *reinterpret_cast<const u32x4 *>(src);
+      } else {
+        for (int e = 0; e < 16 && r + e < row_end; ++e) kc[static_cast<long long>(t) * rows + 16 * c + e] = src[e];
+      }
+    }
+  };
   for (long long r0 = row_begin; r0 < row_end; r0 += kStepRows) {
-    __syncthreads();  // previous step's rows fully read
+    __syncthreads();  // previous step's rows fully read and its key codes staged
+    if (staged_kcodes && r0 != row_begin) flush_kcodes(r0 - kStepRows);
 #pragma unroll
     for (int p = 0; p < kPieces; ++p) {
       const int i = tid + p * 256;
@@ -409,31 +432,6 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
       for (int w = 0; w < kWords; ++w) r = wd == w ? words[w] : r;
       return r;
     };
-    // Key codes with byte codes: each quad of lanes (rows 4k .. 4k+3 of a lane
-    // group) transposes its four code words (tables 4j .. 4j+3) so that lane
-    // i holds rows 4k .. 4k+3 of table 4j + i, one 4-byte store per lane
-    // into the table-major key codes.  Runs with every lane active (DPP).
-    const bool quad_store = tensor == 1 && byte_codes && rows % 4 == 0;
-    if (quad_store) {
-      const unsigned long long vm = __ballot(valid);
-      const bool quad_valid = ((vm >> (lane & ~3)) & 0xfull) == 0xfull;
-      uint8_t *kc = reinterpret_cast<uint8_t *>(rcode) + rows * L;
-      for (int j = g; j < L / 4; j += 4) {
-        const int bytepos = ns / 8 + 4 * j;
-        const uint32_t word = __builtin_amdgcn_alignbyte(get(bytepos / 4 + 1), get(bytepos / 4), bytepos % 4);
-        // 4x4 byte transpose in two pair exchanges (quad_perm [1,0,3,2], then [2,3,0,1])
-        const uint32_t y = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(word), 0xB1, 0xf, 0xf, false));
-        const uint32_t t = __builtin_amdgcn_perm(y, word, (lane & 1) ? 0x03070105u : 0x06020400u);
-        const uint32_t z = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(t), 0x4E, 0xf, 0xf, false));
-        const uint32_t f = __builtin_amdgcn_perm(z, t, (lane & 2) ? 0x03020706u : 0x05040100u);
-        if (quad_valid) {
-          *reinterpret_cast<uint32_t *>(kc + static_cast<long long>(4 * j + (lane & 3)) * rows + row - (lane & 3)) = f;
-        } else if (valid) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kc[static_cast<long long>(4 * j + e) * rows + row] = static_cast<uint8_t>(word >> (8 * e));
-        }
-      }
-    }
     if (valid) {
       const long long out_row = static_cast<long long>(tensor) * rows + row;
       if (g == 0) {
@@ -441,30 +439,14 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
         // a projection binary64 could not decide: the exact pass redoes the row
         flags[out_row] = ((undecided_mask >> r16) & 0x0001000100010001ull) ? 1 : 0;
       }
-      if (tensor == 1) {
-        // key codes, table-major: the 16 lanes of a lane group write 16
-        // consecutive rows of each table
-        if (rcb == 1) {
-          uint8_t *kc = reinterpret_cast<uint8_t *>(rcode) + rows * L + row;
-          if (quad_store) {
-            // written above
-          } else if (byte_codes) {
-            for (int j = g; j < L / 4; j += 4) {
-              const int bytepos = ns / 8 + 4 * j;
-              const uint32_t word = __builtin_amdgcn_alignbyte(get(bytepos / 4 + 1), get(bytepos / 4), bytepos % 4);
+      if (staged_kcodes) {
+        for (int j = g; j < L / 4; j += 4) {
+          const int bytepos = ns / 8 + 4 * j;
+          const uint32_t word = __builtin_amdgcn_alignbyte(get(bytepos / 4 + 1), get(bytepos / 4), bytepos % 4);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) kc[static_cast<long long>(4 * j + e) * rows] = static_cast<uint8_t>(word >> (8 * e));
-            }
-          } else {
-            for (int l = g; l < L; l += 4)
-              kc[static_cast<long long>(l) * rows] = static_cast<uint8_t>(bit_field(get, ns + l * P, P));
-          }
-        } else {
-          uint16_t *kc = reinterpret_cast<uint16_t *>(rcode) + rows * L + row;
-          for (int l = g; l < L; l += 4)
-            kc[static_cast<long long>(l) * rows] = static_cast<uint16_t>(bit_field(get, ns + l * P, P));
+          for (int e = 0; e < 4; ++e) kcl[(4 * j + e) * kStepRows + lrow] = static_cast<uint8_t>(word >> (8 * e));
         }
-      } else if (byte_codes) {
+      } else if (byte_codes && tensor == 0) {
         // 8-bit codes starting on a byte: code word j is bytes ns/8 + 4j .. +3
         // of the plane mask, one byte-funnel of two mask words
         uint32_t *rc = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(rcode) + out_row * L);
@@ -472,30 +454,19 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_bf16(
           const int bytepos = ns / 8 + 4 * j;
           rc[j] = __builtin_amdgcn_alignbyte(get(bytepos / 4 + 1), get(bytepos / 4), bytepos % 4);
         }
-      } else if (rcb == 1) {
-        uint8_t *rc = reinterpret_cast<uint8_t *>(rcode) + out_row * L;
-        if ((L & 3) == 0) {
-          for (int j = g; j < L / 4; j += 4) {
-            uint32_t word = 0;
-            for (int e = 0; e < 4; ++e) word |= bit_field(get, ns + (4 * j + e) * P, P) << (8 * e);
-            reinterpret_cast<uint32_t *>(rc)[j] = word;
-          }
-        } else {
-          for (int l = g; l < L; l += 4) rc[l] = static_cast<uint8_t>(bit_field(get, ns + l * P, P));
-        }
       } else {
-        uint16_t *rc = reinterpret_cast<uint16_t *>(rcode) + out_row * L;
-        if ((L & 1) == 0) {
-          for (int j = g; j < L / 2; j += 4) {
-            const uint32_t word = bit_field(get, ns + (2 * j) * P, P) |
-                                  (bit_field(get, ns + (2 * j + 1) * P, P) << 16);
-            reinterpret_cast<uint32_t *>(rc)[j] = word;
-          }
-        } else {
-          for (int l = g; l < L; l += 4) rc[l] = static_cast<uint16_t>(bit_field(get, ns + l * P, P));
+        for (int l = g; l < L; l += 4) {
+          const uint32_t code = bit_field(get, ns + l * P, P);
+          const long long ci = race_code_index(tensor, row, l, rows, L);
+          if (rcb == 1) reinterpret_cast<uint8_t *>(rcode)[ci] = static_cast<uint8_t>(code);
+          else reinterpret_cast<uint16_t *>(rcode)[ci] = static_cast<uint16_t>(code);
         }
       }
     }
+  }
+  if (staged_kcodes && row_begin < row_end) {  // the last step's key codes
+    __syncthreads();
+    flush_kcodes(row_begin + (row_end - 1 - row_begin) / kStepRows * kStepRows);
   }
 }
 
