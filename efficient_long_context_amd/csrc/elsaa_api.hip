@@ -1,13 +1,10 @@
 // elsaa_api.hip -- host side of the C ABI declared in include/elsaa.h:
 // validation, workspace layout and the launch sequence of the forward pass.
 //
-// Launch order (no host synchronisation).  On the caller's stream:
-//   hash (q and k)  ->  sort (hist, scan, scatter; q and k)  ->  chunk attention
-//   ->  [join]  ->  RACE gather + gates + fusion  ->  optional aux copies.
-// The RACE build depends only on the hash.  When it alone would leave compute
-// units idle it runs on a second stream of the library's (one per device,
-// default priority), forked from the caller's stream after the hash and joined
-// before the fusion, so the sort and attention workgroups fill those units.
+// Launch order (no host synchronisation), all on the caller's stream:
+//   hash (q and k)  ->  RACE build (rank, gather)  ->  sort (hist, scan,
+//   scatter; q and k)  ->  chunk attention  ->  RACE gather + gates + fusion
+//   ->  optional aux copies.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -32,29 +29,20 @@ int fail(int status, const char *fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// The library's second stream on each device, with its fork / join events.
-// Created on first use and kept until the process ends.  The mutex also makes
-// each call's fork-launch-join sequence atomic with respect to other threads.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  int cus = 0;  // compute units of the device
-};
+// Compute units of each device, queried once (the persistent kernels size
+// their grids by it).
 constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
+std::mutex g_cus_mu;
+int g_cus[kMaxDevices] = {0};
 
-hipError_t side_stream(int device, SideStream **out) {
+hipError_t device_cus(int device, int *cus) {
   if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
-  SideStream &ss = g_side[device];
-  if (!ss.stream) {
-    hipError_t e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&ss.cus, hipDeviceAttributeMultiprocessorCount, device);
+  std::lock_guard<std::mutex> lock(g_cus_mu);
+  if (g_cus[device] == 0) {
+    const hipError_t e = hipDeviceGetAttribute(&g_cus[device], hipDeviceAttributeMultiprocessorCount, device);
     if (e != hipSuccess) return e;
   }
-  *out = &ss;
+  *cus = g_cus[device];
   return hipSuccess;
 }
 
@@ -120,11 +108,9 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   t.perm = reinterpret_cast<int32_t *>(take(2 * rows * 4));
   t.flags = reinterpret_cast<uint8_t *>(take(2 * rows));
   t.hist = reinterpret_cast<uint32_t *>(take(2 * static_cast<size_t>(g.BH) * g.nb_sort * g.sort_tiles * 4));
-  // per-table key permutation and run starts: only the two-kernel RACE build uses them
-  const bool split = elsaa::race_split(g);
-  t.rperm = reinterpret_cast<int32_t *>(take(split ? static_cast<size_t>(g.BH) * g.L * g.N * 4 : 0));
-  t.rstart = reinterpret_cast<int32_t *>(
-      take(split ? static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4 : 0));
+  // per-table key permutation and run starts of the RACE build
+  t.rperm = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * g.N * 4));
+  t.rstart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
   t.tsum = take(static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * es);
   t.tcnt = reinterpret_cast<float *>(take(static_cast<size_t>(g.BH) * g.L * g.nb_race * 4));
   t.o_s = take(rows * g.D * es);
@@ -235,41 +221,30 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
 
   int device = 0;
   hipError_t e = hipGetDevice(&device);
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream *side = nullptr;
-  if (e == hipSuccess) e = side_stream(device, &side);
+  if (e == hipSuccess) e = device_cus(device, &g.cus);
   if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
-  // Overlap pays when the RACE build alone would leave compute units idle (a
-  // partial last round of its one-workgroup-per-CU kernel); otherwise it runs
-  // in order on the caller's stream.
-  g.cus = side->cus;
-  const bool fork = elsaa::race_build_idle_fraction(g) >= 0.25;
-  hipStream_t r = fork ? side->stream : s;
 
-  // stage_events[2i] / [2i+1] bracket stage i on the stream that runs it
+  // stage_events[2i] / [2i+1] bracket stage i (hash, sort, RACE build, chunk
+  // attention, fusion)
   void *const *ev = params->stage_events;
-  auto mark = [&](int i, hipStream_t on) -> hipError_t {
-    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), on) : hipSuccess;
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
   };
-  e = mark(0, s);
+  e = mark(0);
   if (e == hipSuccess) e = elsaa::launch_hash(g, q, k, hyperplanes, buf, s);
-  if (e == hipSuccess) e = mark(1, s);
-  if (e == hipSuccess && fork) e = hipEventRecord(side->fork, s);
-  if (e == hipSuccess && fork) e = hipStreamWaitEvent(r, side->fork, 0);
-  if (e == hipSuccess) e = mark(4, r);
-  if (e == hipSuccess) e = elsaa::launch_race_build(g, v, buf, r);
-  if (e == hipSuccess) e = mark(5, r);
-  if (e == hipSuccess && fork) e = hipEventRecord(side->join, r);
-  if (e == hipSuccess) e = mark(2, s);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess) e = mark(4);
+  if (e == hipSuccess) e = elsaa::launch_race_build(g, v, buf, s);
+  if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = elsaa::launch_sort(g, buf, s);
-  if (e == hipSuccess) e = mark(3, s);
-  if (e == hipSuccess) e = mark(6, s);
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess) e = elsaa::launch_chunk_attention(g, q, k, v, buf, s);
-  if (e == hipSuccess) e = mark(7, s);
-  if (e == hipSuccess && fork) e = hipStreamWaitEvent(s, side->join, 0);
-  if (e == hipSuccess) e = mark(8, s);
+  if (e == hipSuccess) e = mark(7);
+  if (e == hipSuccess) e = mark(8);
   if (e == hipSuccess) e = elsaa::launch_fuse(g, x_gate, params->gate_w, params->gate_b, buf, params->aux, out, s);
-  if (e == hipSuccess) e = mark(9, s);
+  if (e == hipSuccess) e = mark(9);
   if (e == hipSuccess && params->aux) e = copy_aux(g, buf, params->aux, s);
   if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';

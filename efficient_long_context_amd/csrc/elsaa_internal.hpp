@@ -37,7 +37,7 @@ struct Buffers {
   int32_t *perm;    // [2][BH][N]
   uint8_t *flags;   // [2][BH][N]     rows whose codes need the exact pass
   uint32_t *hist;   // [2][BH][nb_sort][sort_tiles] -> exclusive offsets
-  int32_t *rperm;   // [BH][L][N]     keys of each table sorted by bucket (two-kernel build)
+  int32_t *rperm;   // [BH][L][N]     keys of each table sorted by bucket
   int32_t *rstart;  // [BH][L][nb_race + 1] run start of each bucket in rperm
   void *tsum;       // [BH][L][nb_race][D] bucket sums, stored in dtype
   float *tcnt;      // [BH][L][nb_race]
@@ -55,20 +55,6 @@ __host__ __device__ __forceinline__ long long race_code_index(int tensor, long l
 }
 
 constexpr int kSortTile = 2048;         // elements per sort tile (4 waves x 8 rounds x 64)
-constexpr size_t kFusedLdsMax = 160 * 1024;  // LDS of one gfx950 workgroup
-
-// Tile size (keys) of the single-kernel RACE build, or 0 when one (b, h, table)
-// table does not fit in LDS and the sort + reduce pair is used instead.
-int race_fused_tile(const Geometry &g);
-
-// True when the RACE build runs as two kernels (rank, then gather), which
-// need the per-table key permutation and run starts in the workspace.
-bool race_split(const Geometry &g);
-
-// Fraction of the device's compute units the RACE build leaves idle on
-// average over its run (one workgroup per unit and CU on the single-kernel
-// path; the sort kernel's grid on the two-kernel path).
-double race_build_idle_fraction(const Geometry &g);
 
 // Launchers (each enqueues on `stream`, returns hipError_t of the launch).
 hipError_t launch_hash(const Geometry &g, const void *q, const void *k, const void *planes,

@@ -21,12 +21,8 @@
  *
  * Conventions
  *   - Every data pointer is a DEVICE pointer owned by the caller; the library
- *     allocates no memory.  Its only state is one extra stream and two events
- *     per device, created on first use and kept until the process ends: the
- *     RACE table build runs on that stream, forked from params->stream after
- *     the hash stage and joined back before the fusion, so it overlaps the
- *     sort and chunk attention.  The whole call is ordered on params->stream
- *     as seen by the caller (including under stream capture).
+ *     allocates no memory.  Its only state is the compute-unit count of each
+ *     device, queried on first use.
  *   - All tensors are dense, row-major, contiguous.
  *   - Work is enqueued on params->stream (a hipStream_t; NULL = the default
  *     stream) and is asynchronous: the caller synchronises before reading.
@@ -111,9 +107,9 @@ typedef struct {
   void *const *stage_events; /* host array of 10 hipEvent_t, or NULL.  Events
                         2i and 2i+1 are recorded just before and just after
                         stage i (0 hash, 1 sort, 2 RACE build, 3 chunk
-                        attention, 4 gather/gates/fusion) on the stream that
-                        runs it, so elapsed(2i, 2i+1) times stage i.  The
-                        caller creates and owns the events.                      */
+                        attention, 4 gather/gates/fusion) on params->stream,
+                        so elapsed(2i, 2i+1) times stage i.  The caller
+                        creates and owns the events.                             */
 } elsaa_params_t;
 
 /* Host-only check of every field of *p except the device pointers' targets.
