@@ -33,6 +33,7 @@ CASES = {
     "bf16-sort12": ("small-bf16", dict(B=1, H=1, N=8192, sort_bits=12)),
     "bf16-P12-L4": ("small-bf16", dict(B=1, H=1, race_tables=4, race_bits=12)),
     "bf16-d128-w64": ("needle256k-bf16", dict(H=2, N=4096, chunk=64, sort_bits=7, race_tables=5, race_bits=9)),
+    "bf16-w256": ("small-bf16", dict(B=2, H=2, N=4096, chunk=256)),
 }
 
 
