@@ -158,9 +158,10 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
 // in LDS once (L 2^P <= 16384 words) and read there, the two gate weight rows
 // are loaded once, and each wave streams R/4 queries.
 template <typename VT, int GE> struct GateIn;  // GE consecutive gate inputs of one lane
+// unpack: the lane's GE gate inputs from their raw words (loaded as 16, 8 or
+// 4 bytes into the leading words of a u32x4)
 template <> struct GateIn<uint16_t, 8> {
-  static __device__ __forceinline__ void load(const uint16_t *p, float *x) {
-    const u32x4 w = *reinterpret_cast<const u32x4 *>(p);
+  static __device__ __forceinline__ void unpack(const u32x4 &w, float *x) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       x[2 * e] = __uint_as_float(w[e] << 16);
@@ -169,16 +170,24 @@ template <> struct GateIn<uint16_t, 8> {
   }
 };
 template <> struct GateIn<uint16_t, 4> {
-  static __device__ __forceinline__ void load(const uint16_t *p, float *x) { Elem<uint16_t>::load4(p, x); }
+  static __device__ __forceinline__ void unpack(const u32x4 &w, float *x) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
 };
 template <> struct GateIn<float, 4> {
-  static __device__ __forceinline__ void load(const float *p, float *x) { Elem<float>::load4(p, x); }
+  static __device__ __forceinline__ void unpack(const u32x4 &w, float *x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
+  }
 };
 template <> struct GateIn<float, 2> {
-  static __device__ __forceinline__ void load(const float *p, float *x) {
-    const float2 v = *reinterpret_cast<const float2 *>(p);
-    x[0] = v.x;
-    x[1] = v.y;
+  static __device__ __forceinline__ void unpack(const u32x4 &w, float *x) {
+    x[0] = __uint_as_float(w[0]);
+    x[1] = __uint_as_float(w[1]);
   }
 };
 
@@ -251,10 +260,33 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse_wide(
   };
   uint32_t cw[kCW];
   load_codes(i_begin, cw);
+  // the streamed inputs of a step (sparse output, its LSE, gate inputs) are
+  // requested one step ahead, so their HBM latency overlaps the table gathers
+  auto load_stream = [&](int i0, u32x4 &os_raw, float &lse_v, u32x4 &xg_raw) {
+    const int ii = i0 + lane / kLPQ;
+    const long long q0 = bh * N + ii;
+    os_raw = *reinterpret_cast<const u32x4 *>(o_s + q0 * D + sub * kCols);
+    lse_v = lse[q0];
+    if (gate_fast) {
+      const VT *xg = x_gate + (b * N + ii) * DG + sub * kGE;
+      if constexpr (kGE * kES == 16) xg_raw = *reinterpret_cast<const u32x4 *>(xg);
+      else if constexpr (kGE * kES == 8) {
+        const uint2 t2 = *reinterpret_cast<const uint2 *>(xg);
+        xg_raw = u32x4{t2.x, t2.y, 0u, 0u};
+      } else {
+        xg_raw = u32x4{*reinterpret_cast<const uint32_t *>(xg), 0u, 0u, 0u};
+      }
+    }
+  };
+  u32x4 os_next = {0u, 0u, 0u, 0u}, xg_next = {0u, 0u, 0u, 0u};
+  float lse_next = 0.0f;
+  load_stream(i_begin, os_next, lse_next, xg_next);
 
   for (int step = 0; step < per_wave; step += kQPS) {
     const int i = i_begin + step + lane / kLPQ;
     const long long qi = bh * N + i;
+    const u32x4 os_raw = os_next, xg_raw = xg_next;
+    const float lse_i = lse_next;
 
     // table rows of the L buckets (offsets relative to table l, whose base
     // goes in the scalar offset)
@@ -274,25 +306,23 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse_wide(
       }
       t[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, off, l * nb * kRowBytes, 0));
     }
-    // sparse output, its LSE and the gate inputs of this step
+    // the next step's streamed inputs
+    load_stream(step + kQPS < per_wave ? i_begin + step + kQPS : i_begin + step, os_next, lse_next, xg_next);
+    // sparse output and gate inputs of this step
     float osv[kCols];
-    {
-      const u32x4 w = *reinterpret_cast<const u32x4 *>(o_s + qi * D + sub * kCols);
-      if constexpr (kES == 2) {
+    if constexpr (kES == 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          osv[2 * e] = __uint_as_float(w[e] << 16);
-          osv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) osv[e] = __uint_as_float(w[e]);
+      for (int e = 0; e < 4; ++e) {
+        osv[2 * e] = __uint_as_float(os_raw[e] << 16);
+        osv[2 * e + 1] = __uint_as_float(os_raw[e] & 0xffff0000u);
       }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) osv[e] = __uint_as_float(os_raw[e]);
     }
-    const float lse_i = lse[qi];
     const VT *xg = x_gate + (b * N + i) * DG;
     float xv[kGE];
-    if (gate_fast) GateIn<VT, kGE>::load(xg + sub * kGE, xv);
+    if (gate_fast) GateIn<VT, kGE>::unpack(xg_raw, xv);
 
     // counts from LDS: lane sub adds tables sub, sub + kLPQ, ...
     float z = 0.0f;
