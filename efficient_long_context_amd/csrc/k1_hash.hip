@@ -199,13 +199,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
   constexpr int kRPad = NPT * 16;
   constexpr int kWords = (kRPad + 31) / 32;
   constexpr int kStepRows = 64;
-  constexpr int kPieces = kStepRows * (D / 8) / 256;  // 16-byte pieces per thread per step
   __shared__ __align__(16) uint16_t sp[kRPad * kLdsRow];
-  __shared__ __align__(16) uint16_t sx[kStepRows * kLdsRow];
   __shared__ float s_red[2];  // max_t c|r_t| and "all planes in range"
-  // key byte codes of one step, table-major [table][64 rows], written out one
-  // step later as whole 16-byte row pieces per table (L <= 64)
-  __shared__ __align__(16) uint8_t kcl[64 * kStepRows];
+  // per wave: key byte codes of its 16 rows, table-major [table][16 rows]
+  // (L <= 64), transposed here and stored as one 16-byte piece per table
+  __shared__ __align__(16) uint8_t kcl[4][64 * 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tensor = blockIdx.y;
@@ -250,52 +248,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
   const long long row_begin = static_cast<long long>(blockIdx.x) * rows_per_wg;
   const long long row_end = row_begin + rows_per_wg < rows ? row_begin + rows_per_wg : rows;
 
-  u16x8 pre[kPieces];
-  auto load_step = [&](long long r0) {
+  // Each wave hashes rows r0 + 16 w .. +15 of every 64-row step of the
+  // workgroup's range, on its own (no workgroup barrier in the loop): a
+  // lane's 16-byte piece of its row (d-slice kk*32 + g*8 .. +7) is exactly
+  // its part of the MFMA operand, so rows go from memory straight to
+  // registers, the next step's in flight while this one is hashed.
+  auto load_rows = [&](long long r0, u32x4 (&dst)[D / 32]) {
+    const long long row = r0 + wave * 16 + r16;
+    const long long rr = row < rows ? row : rows - 1;  // clamped; results of clamped rows are discarded
 #pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-      const int i = tid + p * 256;
-      const long long row = r0 + i / (D / 8);
-      const long long rr = row < rows ? row : rows - 1;  // clamped; results of clamped rows are discarded
-      pre[p] = *reinterpret_cast<const u16x8 *>(x + rr * D + (i % (D / 8)) * 8);
-    }
+    for (int kk = 0; kk < D / 32; ++kk) dst[kk] = *reinterpret_cast<const u32x4 *>(x + rr * D + kk * 32 + g * 8);
   };
-
-  load_step(row_begin);
-  // Key byte codes (the table-major layout the RACE build reads): each step's
-  // codes are staged in kcl and stored after the next barrier, lane 4t + c
-  // writing rows 16c .. 16c+15 of table t (16-byte stores when rows allow).
+  // key byte codes (the table-major layout the RACE build reads)
   const bool staged_kcodes = tensor == 1 && P == 8 && ns % 8 == 0 && L % 4 == 0 && L <= 64;
-  auto flush_kcodes = [&](long long rs) {
-    if (wave != 0) return;
-    uint8_t *kc = reinterpret_cast<uint8_t *>(rcode) + rows * L + rs;
-    for (int t = lane >> 2; t < L; t += 16) {
-      const int c = lane & 3;
-      const long long r = rs + 16 * c;
-      const uint8_t *src = kcl + t * kStepRows + 16 * c;
-      if (rows % 16 == 0 && r + 16 <= row_end) {
-        *reinterpret_cast<u32x4 *>(kc + static_cast<long long>(t) * rows + 16 * c) =
-            *reinterpret_cast<const u32x4 *>(src);
-      } else {
-        for (int e = 0; e < 16 && r + e < row_end; ++e) kc[static_cast<long long>(t) * rows + 16 * c + e] = src[e];
-      }
-    }
-  };
+  uint8_t *kw = kcl[wave];
+  u32x4 nxt[D / 32];
+  load_rows(row_begin, nxt);
   for (long long r0 = row_begin; r0 < row_end; r0 += kStepRows) {
-    __syncthreads();  // previous step's rows fully read and its key codes staged
-    if (staged_kcodes && r0 != row_begin) flush_kcodes(r0 - kStepRows);
+    u32x4 cur[D / 32];
 #pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-      const int i = tid + p * 256;
-      *reinterpret_cast<u16x8 *>(sx + (i / (D / 8)) * kLdsRow + (i % (D / 8)) * 8) = pre[p];
-    }
-    __syncthreads();
-    if (r0 + kStepRows < row_end) load_step(r0 + kStepRows);  // in flight while this step is hashed
+    for (int kk = 0; kk < D / 32; ++kk) cur[kk] = nxt[kk];
+    if (r0 + kStepRows < row_end) load_rows(r0 + kStepRows, nxt);  // in flight while this step is hashed
 
     const int lrow = wave * 16 + r16;
     const long long row = r0 + lrow;
     const bool valid = row < row_end;
-    const uint16_t *xr = sx + lrow * kLdsRow;
 
     // |x|^2 of the row (lane group g holds a quarter of it): bfloat16 squares
     // are exact in binary32, summed by v_dot2_f32_bf16
@@ -303,7 +280,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
     bf16x8 b[D / 32];
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      const u32x4 raw = *reinterpret_cast<const u32x4 *>(xr + kk * 32 + g * 8);
+      const u32x4 raw = cur[kk];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t wv = raw[i];  // (bit_cast of raw[i] itself reads element 0 with this clang)
@@ -379,7 +356,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
                  __builtin_amdgcn_readlane(static_cast<int>(unsure >> 32), src)))
              << 32);
         const int bpos = __builtin_ctzll(sb);
-        const uint16_t *xs = sx + (wave * 16 + (src & 15)) * kLdsRow;
+        // the source lane's row, read from memory (this path is rare)
+        const uint16_t *xs = x + ((r0 + wave * 16 + (src & 15)) < rows ? (r0 + wave * 16 + (src & 15)) : rows - 1) * D;
         const uint16_t *ps = sp + ((bpos >> 2) * 16 + (src >> 4) * 4 + (bpos & 3)) * kLdsRow;
         double sum = 0.0, sabs = 0.0;
 #pragma unroll
@@ -444,7 +422,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
           const int bytepos = ns / 8 + 4 * j;
           const uint32_t word = __builtin_amdgcn_alignbyte(get(bytepos / 4 + 1), get(bytepos / 4), bytepos % 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) kcl[(4 * j + e) * kStepRows + lrow] = static_cast<uint8_t>(word >> (8 * e));
+          for (int e = 0; e < 4; ++e) kw[(4 * j + e) * 16 + r16] = static_cast<uint8_t>(word >> (8 * e));
         }
       } else if (byte_codes && tensor == 0) {
         // 8-bit codes starting on a byte: code word j is bytes ns/8 + 4j .. +3
@@ -463,10 +441,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
         }
       }
     }
-  }
-  if (staged_kcodes && row_begin < row_end) {  // the last step's key codes
-    __syncthreads();
-    flush_kcodes(row_begin + (row_end - 1 - row_begin) / kStepRows * kStepRows);
+    if (staged_kcodes) {  // lane t stores table t's 16 rows of this wave
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      const long long rs = r0 + wave * 16;
+      for (int t = lane; t < L; t += 64) {
+        uint8_t *dst = reinterpret_cast<uint8_t *>(rcode) + rows * L + static_cast<long long>(t) * rows + rs;
+        const uint8_t *src = kw + t * 16;
+        if (rows % 16 == 0 && rs + 16 <= row_end) {
+          *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+        } else {
+          for (int e = 0; e < 16 && rs + e < row_end; ++e) dst[e] = src[e];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");  // read before the next step writes
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
   }
 }
 
