@@ -5,7 +5,8 @@
 A step is one whole forward pass (hash, sort, RACE build, chunk attention,
 gather/gates/fusion) over one batch of seeded synthetic input already resident
 in HBM.  W untimed steps, then K steps timed between two device
-synchronisations.  Prints ONE JSON line:
+synchronisations (no instrumentation inside), then K more steps with the
+library's stage events for the per-stage split.  Prints ONE JSON line:
   value        tokens/s (B*N per step) of the whole job
   roofline     the dominant kernel (largest share of the step): algorithmic
                bytes (or flops) per launch over its mean duration, measured with
@@ -253,15 +254,20 @@ def main(argv=None):
         for _ in range(warmup):
             f(*call)
         torch.cuda.synchronize()
-        stage_ev = [ev.create(2 * len(elsaa.STAGES)) for _ in range(steps)]
+        # the timed steps run without stage events; a second pass with the
+        # library's stage events (the same number of steps) splits the time
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
         for i in range(steps):
-            f(*call, stage_events=stage_ev[i])
+            f(*call)
         stop.record()
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(stop)
+        stage_ev = [ev.create(2 * len(elsaa.STAGES)) for _ in range(steps)]
+        for i in range(steps):
+            f(*call, stage_events=stage_ev[i])
+        torch.cuda.synchronize()
         stage_ms = {st: float(np.mean([ev.elapsed_ms(e[2 * j], e[2 * j + 1]) for e in stage_ev]))
                     for j, st in enumerate(elsaa.STAGES)}
         for e in stage_ev:
