@@ -111,6 +111,7 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   // per-table key permutation and run starts of the RACE build
   t.rperm = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * g.N * 4));
   t.rstart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
+  t.rpart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (elsaa::race_parts(g.N) + 1) * 8));
   t.tsum = take(static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * es);
   t.tcnt = reinterpret_cast<float *>(take(static_cast<size_t>(g.BH) * g.L * g.nb_race * 4));
   t.o_s = take(rows * g.D * es);

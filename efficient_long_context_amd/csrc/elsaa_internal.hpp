@@ -39,6 +39,7 @@ struct Buffers {
   uint32_t *hist;   // [2][BH][nb_sort][sort_tiles] -> exclusive offsets
   int32_t *rperm;   // [BH][L][N]     keys of each table sorted by bucket
   int32_t *rstart;  // [BH][L][nb_race + 1] run start of each bucket in rperm
+  int32_t *rpart;   // [BH][L][parts + 1][2] per gather part: first owned bucket, its run start
   void *tsum;       // [BH][L][nb_race][D] bucket sums, stored in dtype
   float *tcnt;      // [BH][L][nb_race]
   void *o_s;        // [BH][N][D] in dtype
@@ -53,6 +54,11 @@ __host__ __device__ __forceinline__ long long race_code_index(int tensor, long l
                                                               int L) {
   return tensor == 0 ? row * L + l : rows * L + static_cast<long long>(l) * rows + row;
 }
+
+// Positions of one table's sorted keys per RACE gather wave ("part"), before
+// rounding to whole buckets.
+constexpr int kGatherPos = 512;
+__host__ __device__ __forceinline__ int race_parts(int N) { return (N + kGatherPos - 1) / kGatherPos; }
 
 constexpr int kSortTile = 2048;         // elements per sort tile (4 waves x 8 rounds x 64)
 

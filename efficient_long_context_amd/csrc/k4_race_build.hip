@@ -143,8 +143,9 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *t
 //           which then holds the value rows its tables gather.
 template <typename CT>
 __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
-    const CT *__restrict__ kcodes, int N, int L, int P, long long rows, int staged,
-    int32_t *__restrict__ rperm, int32_t *__restrict__ rstart, float *__restrict__ tcnt) {
+    const CT *__restrict__ kcodes, int N, int L, int P, long long rows, int staged, int parts,
+    int32_t *__restrict__ rperm, int32_t *__restrict__ rstart, int32_t *__restrict__ rpart,
+    float *__restrict__ tcnt) {
   extern __shared__ uint32_t lds[];
   const int nb = 1 << P;
   const int W = static_cast<int>(blockDim.x >> 6);
@@ -190,6 +191,10 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
       for (int w = 0; w < W; ++w) sum += cnt[w * nb + b];
     uint32_t run = block_exclusive_scan(sum, part, lane, wave);
     int32_t *rs = rstart + unit * (nb + 1);
+    // gather part p (positions from lo_p = N p / parts) owns the buckets whose
+    // run starts in [lo_p, lo_{p+1}); its first one is the first bucket starting
+    // at or after lo_p: bucket b + 1 when lo_p lies in (start_b, end_b]
+    int32_t *rp2 = rpart + unit * (parts + 1) * 2;
     for (int b = b_lo; b < b_hi; ++b) {
       rs[b] = static_cast<int32_t>(run);
       const uint32_t r0 = run;
@@ -199,8 +204,22 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
         run += t;
       }
       tcnt[unit * nb + b] = static_cast<float>(run - r0);
+      if (run > r0) {
+        long long pp = static_cast<long long>(r0) * parts / N;
+        while (pp < parts && static_cast<long long>(N) * pp / parts <= static_cast<long long>(r0)) ++pp;
+        for (; pp < parts && static_cast<long long>(N) * pp / parts <= static_cast<long long>(run); ++pp) {
+          rp2[2 * pp] = b + 1;
+          rp2[2 * pp + 1] = static_cast<int32_t>(run);
+        }
+      }
     }
-    if (tid == 0) rs[nb] = N;
+    if (tid == 0) {
+      rs[nb] = N;
+      rp2[0] = 0;  // part 0 starts at bucket 0, position 0
+      rp2[1] = 0;
+      rp2[2 * parts] = nb;  // end of the last part
+      rp2[2 * parts + 1] = N;
+    }
   }
   __syncthreads();
   // sorted key indices: staged in LDS and written out in order (coalesced),
@@ -232,7 +251,8 @@ constexpr int kGatherSlack = 256;     // staged entries read past the end by the
 template <typename VT, int D>
 __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
     const VT *__restrict__ v, const int32_t *__restrict__ rperm, const int32_t *__restrict__ rstart,
-    int N, int L, int P, int parts, long long waves_total, VT *__restrict__ tsum) {
+    const int32_t *__restrict__ rpart, int N, int L, int P, int parts, long long waves_total,
+    VT *__restrict__ tsum) {
   using PC = Piece<VT, D>;
   constexpr int kCols = PC::kCols, kLPR = PC::kLanesPerRow;
   constexpr int kRPI = PC::kRowsPerLoad;
@@ -252,25 +272,16 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   const int32_t *rp = rperm + unit * N;
   VT *ts = tsum + unit * nb * static_cast<long long>(D);
 
-  // owned buckets: those whose run starts in [lo, hi); the last part also owns
-  // the empty buckets that start at N
-  const int lo = static_cast<int>(static_cast<long long>(N) * prt / parts);
-  const int hi = prt == parts - 1 ? N + 1 : static_cast<int>(static_cast<long long>(N) * (prt + 1) / parts);
-  int b0 = nb, b1 = nb;
-  for (int bb = 0; bb < nb; bb += 64) {
-    const int b = bb + lane;
-    const int st = b < nb ? rs[b] : N + 1;
-    const unsigned long long ge_lo = __ballot(b < nb && st >= lo);
-    const unsigned long long ge_hi = __ballot(b < nb && st >= hi);
-    if (b0 == nb && ge_lo) b0 = bb + __builtin_ctzll(ge_lo);
-    if (b1 == nb && ge_hi) b1 = bb + __builtin_ctzll(ge_hi);
-    if (b1 != nb) break;
-  }
-  b0 = __builtin_amdgcn_readfirstlane(b0);
-  b1 = __builtin_amdgcn_readfirstlane(b1);
+  // owned buckets [b0, b1) and their positions [p_lo, p_hi), from the part
+  // table the rank kernel wrote (the buckets whose run starts in this part's
+  // positions; the last part also owns the empty buckets that start at N)
+  const int2 *pt = reinterpret_cast<const int2 *>(rpart) + unit * (parts + 1) + prt;
+  const int2 here = pt[0], next = pt[1];
+  const int b0 = __builtin_amdgcn_readfirstlane(here.x);
+  const int p_lo = __builtin_amdgcn_readfirstlane(here.y);
+  const int b1 = __builtin_amdgcn_readfirstlane(next.x);
+  const int p_hi = __builtin_amdgcn_readfirstlane(next.y);
   if (b0 >= b1) return;
-  const int p_lo = __builtin_amdgcn_readfirstlane(rs[b0]);
-  const int p_hi = __builtin_amdgcn_readfirstlane(rs[b1]);
 
   const int cc = lane % kLPR;       // column piece
   const int my_off = lane / kLPR;   // this lane's row within a load
@@ -357,9 +368,6 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
 
 }  // namespace
 
-#ifndef ELSAA_GATHER_POS
-#define ELSAA_GATHER_POS 512  // positions per gather wave (before rounding to whole buckets)
-#endif
 
 hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
                              hipStream_t stream) {
@@ -379,36 +387,36 @@ hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &bu
   const size_t rlds = rank_lds(waves, staged);
   if (g.rcb == 1)
     hipLaunchKernelGGL(elsaa_k4_race_rank<uint8_t>, dim3(static_cast<unsigned>(units)), dim3(waves * 64), rlds,
-                       stream, static_cast<const uint8_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0, buf.rperm,
-                       buf.rstart, buf.tcnt);
+                       stream, static_cast<const uint8_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0, race_parts(g.N),
+                       buf.rperm, buf.rstart, buf.rpart, buf.tcnt);
   else
     hipLaunchKernelGGL(elsaa_k4_race_rank<uint16_t>, dim3(static_cast<unsigned>(units)), dim3(waves * 64), rlds,
-                       stream, static_cast<const uint16_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0, buf.rperm,
-                       buf.rstart, buf.tcnt);
+                       stream, static_cast<const uint16_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0, race_parts(g.N),
+                       buf.rperm, buf.rstart, buf.rpart, buf.tcnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int parts = (g.N + ELSAA_GATHER_POS - 1) / ELSAA_GATHER_POS;
+  const int parts = race_parts(g.N);
   const long long waves_total = units * parts;
   const long long wgs = (waves_total + kGatherWaves - 1) / kGatherWaves;
   const dim3 grid(static_cast<unsigned>((wgs + kXcdCount - 1) / kXcdCount * kXcdCount));
   if (g.bf16) {
     if (g.D == 64)
       hipLaunchKernelGGL((elsaa_k4_race_gather<uint16_t, 64>), grid, dim3(kGatherWaves * 64), 0, stream,
-                         static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, g.N, g.L, g.P, parts,
+                         static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts,
                          waves_total, static_cast<uint16_t *>(buf.tsum));
     else
       hipLaunchKernelGGL((elsaa_k4_race_gather<uint16_t, 128>), grid, dim3(kGatherWaves * 64), 0, stream,
-                         static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, g.N, g.L, g.P, parts,
+                         static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts,
                          waves_total, static_cast<uint16_t *>(buf.tsum));
   } else {
     if (g.D == 64)
       hipLaunchKernelGGL((elsaa_k4_race_gather<float, 64>), grid, dim3(kGatherWaves * 64), 0, stream,
-                         static_cast<const float *>(v), buf.rperm, buf.rstart, g.N, g.L, g.P, parts, waves_total,
+                         static_cast<const float *>(v), buf.rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts, waves_total,
                          static_cast<float *>(buf.tsum));
     else
       hipLaunchKernelGGL((elsaa_k4_race_gather<float, 128>), grid, dim3(kGatherWaves * 64), 0, stream,
-                         static_cast<const float *>(v), buf.rperm, buf.rstart, g.N, g.L, g.P, parts, waves_total,
+                         static_cast<const float *>(v), buf.rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts, waves_total,
                          static_cast<float *>(buf.tsum));
   }
   return hipGetLastError();
