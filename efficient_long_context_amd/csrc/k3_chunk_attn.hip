@@ -520,11 +520,14 @@ __global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_pc(
 // of a persistent workgroup share a chunk, so each tile gathers only its own
 // chunk's 128 K and V rows: chunks live in a ring of three LDS slots (tile m
 // reads slots m % 3 and (m + 1) % 3, and its own chunk is written to slot
-// (m + 1) % 3 while tile m - 1 is computed).  The tile's query rows and
-// original indices go to one of two LDS query slots the same way.  Waves 0-7
-// compute (16 queries each) and issue no global loads; waves 8-11 produce:
-// they store what they loaded during the previous tile, then request the next
-// tile's rows and the one after's indices.  One LDS-only barrier per tile.
+// (m + 1) % 3 while tile m - 1 is computed).  Waves 8-11 produce: they store
+// a tile's K and V rows, requested three tiles earlier into one of three
+// register sets, then request the rows of the tile three ahead into that set
+// (gathered rows come from HBM, and a tile of compute does not cover their
+// latency) and write the original indices of its queries to one of four LDS
+// index slots.  Waves 0-7 compute 16 queries each; they load their query rows
+// for the next tile while computing the current one.  One LDS-only barrier
+// per tile.
 __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N,
@@ -536,70 +539,69 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
   constexpr int kKRow = D + 8;
   constexpr int kVRow = W + 4;
   constexpr int kSlotElems = W * kKRow + D * kVRow;  // one chunk: K rows, V^T
-  constexpr int kQSlotElems = W * kKRow;             // one tile's query rows
   constexpr int kKChunks = W * (D / 8);
   constexpr int kVPairs = (W / 2) * (D / 8);
-  constexpr int kKPer = kKChunks / kPThreads;  // 4 (also the query pieces per thread)
+  constexpr int kKPer = kKChunks / kPThreads;  // 4
   constexpr int kVPer = kVPairs / kPThreads;   // 2
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t *qslots = smem + 3 * kSlotElems;                                  // [2][W][kKRow]
-  int32_t *qidx_lds = reinterpret_cast<int32_t *>(qslots + 2 * kQSlotElems);  // [2][W]
+  int32_t *qidx_lds = reinterpret_cast<int32_t *>(smem + 3 * kSlotElems);  // [4][W], tile m in m % 4
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long t_begin = xcd_logical_block(blockIdx.x, gridDim.x) * tiles_per_wg;
   const long long t_end = t_begin + tiles_per_wg < n_tiles ? t_begin + tiles_per_wg : n_tiles;
   if (t_begin >= t_end) return;  // whole workgroup
+  auto chunk_of = [&](long long t) { return static_cast<int>(t % tiles_per_seg); };
+  auto seg_of = [&](long long t) { return (t / tiles_per_seg) * N; };
+  // piece of a row at a 32-bit byte offset from its segment's first row (a
+  // segment is at most 2^18 rows of 128 bytes): a uniform base plus one
+  // offset register per load
+  auto piece = [](const uint16_t *base, int row, int ch) {
+    const uint32_t off = static_cast<uint32_t>(row) * (D * 2) + static_cast<uint32_t>(ch) * 16;
+    return *reinterpret_cast<const u16x8 *>(reinterpret_cast<const char *>(base) + off);
+  };
 
   if (wave >= kConsumerWaves) {
     // ------------------------------------------------------------ producer
     const int ptid = tid - kConsumerWaves * 64;
-    int kj[kKPer], v0[kVPer], v1[kVPer], qj[kKPer];
-    u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer], qreg[kKPer];
-    int qown[kKPer];  // original indices of the query rows of this thread's pieces
+    // Thread ptid's K pieces are rows ptid / 8 + 32 p, chunk ptid % 8; its V
+    // pieces are chunks ptid / 64 + 4 p of the key pair ptid % 64 (one pair
+    // for every p); thread ptid < 128 also fetches the tile's query ptid.
+    struct Idx {  // key indices of a chunk, query index of a tile
+      int kj[kKPer], v0, v1, qj;
+    };
+    struct Rows {  // this thread's pieces of a chunk's K and V rows
+      u16x8 k[kKPer], v0[kVPer], v1[kVPer];
+    };
     // key indices of chunk c and query indices of tile t (whose chunk is c)
-    auto load_idx = [&](long long t, int c, bool with_q) {
-      const long long seg = (t / tiles_per_seg) * N;
+    auto load_idx = [&](Idx &ix, long long t, int c, bool with_q) {
+      const long long seg = seg_of(t);
       const int32_t *pk = perm_k + seg + c * W;
 #pragma unroll
-      for (int p = 0; p < kKPer; ++p) kj[p] = pk[(ptid + p * kPThreads) / (D / 8)];
-#pragma unroll
-      for (int p = 0; p < kVPer; ++p) {
-        const int jp = (ptid + p * kPThreads) % (W / 2);
-        v0[p] = pk[2 * jp];
-        v1[p] = pk[2 * jp + 1];
-      }
-      if (with_q) {
-        const int32_t *pq = perm_q + seg + c * W;
-#pragma unroll
-        for (int p = 0; p < kKPer; ++p) qj[p] = pq[(ptid + p * kPThreads) / (D / 8)];
-      }
+      for (int p = 0; p < kKPer; ++p) ix.kj[p] = pk[(ptid + p * kPThreads) / (D / 8)];
+      static_assert(kPThreads % (W / 2) == 0, "every V piece of a thread is one key pair");
+      ix.v0 = pk[2 * (ptid % (W / 2))];
+      ix.v1 = pk[2 * (ptid % (W / 2)) + 1];
+      if (with_q) ix.qj = perm_q[seg + c * W + ptid % W];  // threads from W on: a repeat, not stored
     };
-    auto load_rows = [&](long long t, bool with_q) {
-      const long long seg = (t / tiles_per_seg) * N;
+    auto load_rows = [&](Rows &r, const Idx &ix, long long t) {
+      const long long seg = seg_of(t);
+      const uint16_t *ks = k + seg * D, *vs = v + seg * D;
 #pragma unroll
-      for (int p = 0; p < kKPer; ++p)
-        kreg[p] = *reinterpret_cast<const u16x8 *>(k + (seg + kj[p]) * D + ((ptid + p * kPThreads) % (D / 8)) * 8);
+      for (int p = 0; p < kKPer; ++p) r.k[p] = piece(ks, ix.kj[p], (ptid + p * kPThreads) % (D / 8));
 #pragma unroll
       for (int p = 0; p < kVPer; ++p) {
         const int ch = (ptid + p * kPThreads) / (W / 2);
-        vreg0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + v0[p]) * D + ch * 8);
-        vreg1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + v1[p]) * D + ch * 8);
-      }
-      if (with_q) {
-#pragma unroll
-        for (int p = 0; p < kKPer; ++p)
-          qreg[p] = *reinterpret_cast<const u16x8 *>(q + (seg + qj[p]) * D + ((ptid + p * kPThreads) % (D / 8)) * 8);
-#pragma unroll
-        for (int p = 0; p < kKPer; ++p) qown[p] = qj[p];
+        r.v0[p] = piece(vs, ix.v0, ch);
+        r.v1[p] = piece(vs, ix.v1, ch);
       }
     };
-    auto store_rows = [&](int slot, int qslot, bool with_q) {
+    auto store_rows = [&](const Rows &r, int slot) {
       uint16_t *Ks = smem + slot * kSlotElems, *Vt = Ks + W * kKRow;
 #pragma unroll
       for (int p = 0; p < kKPer; ++p) {
         const int i = ptid + p * kPThreads;
-        *reinterpret_cast<u16x8 *>(Ks + (i / (D / 8)) * kKRow + (i % (D / 8)) * 8) = kreg[p];
+        *reinterpret_cast<u16x8 *>(Ks + (i / (D / 8)) * kKRow + (i % (D / 8)) * 8) = r.k[p];
       }
 #pragma unroll
       for (int p = 0; p < kVPer; ++p) {
@@ -607,72 +609,93 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
         const int jp = i % (W / 2), ch = i / (W / 2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t word = static_cast<uint32_t>(vreg0[p][e]) | (static_cast<uint32_t>(vreg1[p][e]) << 16);
+          const uint32_t word = static_cast<uint32_t>(r.v0[p][e]) | (static_cast<uint32_t>(r.v1[p][e]) << 16);
           *reinterpret_cast<uint32_t *>(Vt + (ch * 8 + e) * kVRow + 2 * jp) = word;
         }
       }
-      if (with_q) {
-        uint16_t *Qs = qslots + qslot * kQSlotElems;
-#pragma unroll
-        for (int p = 0; p < kKPer; ++p) {
-          const int i = ptid + p * kPThreads;
-          *reinterpret_cast<u16x8 *>(Qs + (i / (D / 8)) * kKRow + (i % (D / 8)) * 8) = qreg[p];
-        }
-      }
     };
-    // piece p of thread ptid is query row ptid / 8 + 32 p; the threads that
-    // hold a row's first piece write its original index
-    auto store_qidx = [&](int qslot) {
-      if (ptid % (D / 8) == 0) {
-#pragma unroll
-        for (int p = 0; p < kKPer; ++p)
-          qidx_lds[qslot * W + (ptid + p * kPThreads) / (D / 8)] = qown[p];
-      }
+    // original indices of tile t's queries to index slot (t - t_begin) % 4
+    auto store_qidx = [&](const Idx &ix, long long t) {
+      if (ptid < W) qidx_lds[static_cast<int>((t - t_begin) & 3) * W + ptid] = ix.qj;
     };
-    const int c_begin = static_cast<int>(t_begin % tiles_per_seg);
-    // prologue: the first tile's previous chunk (slot 0), own chunk (slot 1)
-    // and query rows (query slot 0)
+    Idx i0, i1, i2;
+    Rows r0, r1, r2;
+    // Every step issues the same loads (past the last tile they repeat it and
+    // are not stored), so the count of loads in flight at each wait is the
+    // same on every path and each wait covers only the set it stores.
+    auto clamp_t = [&](long long t) { return t < t_end ? t : t_end - 1; };
+    auto indices = [&](Idx &ix, long long t) { load_idx(ix, clamp_t(t), chunk_of(clamp_t(t)), true); };
+    auto rows = [&](Rows &r, const Idx &ix, long long t) {
+      load_rows(r, ix, clamp_t(t));
+      store_qidx(ix, t);
+    };
+    // prologue: the first tile's previous chunk goes to slot 0; then tiles 0,
+    // 1 and 2 are requested, and tile 3's indices, in the order of the steps
+    // (tile j + 1's indices, then tile j's rows)
+    const int c_begin = chunk_of(t_begin);
     if (c_begin > 0) {
-      load_idx(t_begin, c_begin - 1, false);
-      load_rows(t_begin, false);
-      store_rows(0, 0, false);
+      load_idx(i0, t_begin, c_begin - 1, false);
+      load_rows(r0, i0, t_begin);
+      store_rows(r0, 0);
     }
-    load_idx(t_begin, c_begin, true);
-    load_rows(t_begin, true);
-    if (t_begin + 1 < t_end) load_idx(t_begin + 1, static_cast<int>((t_begin + 1) % tiles_per_seg), true);
-    store_rows(1, 0, true);
-    store_qidx(0);
-    if (t_begin + 1 < t_end) {
-      load_rows(t_begin + 1, true);
-      if (t_begin + 2 < t_end) load_idx(t_begin + 2, static_cast<int>((t_begin + 2) % tiles_per_seg), true);
-    }
-    lds_barrier();  // tile 0 ready
-    for (long long t = t_begin + 1; t < t_end; ++t) {  // tile m = t - t_begin: its rows in flight
+    indices(i0, t_begin);
+    indices(i1, t_begin + 1);
+    rows(r0, i0, t_begin);
+    indices(i2, t_begin + 2);
+    rows(r1, i1, t_begin + 1);
+    indices(i0, t_begin + 3);
+    rows(r2, i2, t_begin + 2);
+    // tile m = t - t_begin: its chunk to slot (m + 1) % 3 (tile m - 1 is being
+    // computed from the other two); then tile m + 4's indices into the set
+    // tile m + 1 used, and tile m + 3's rows (indices loaded one step ago)
+    // into the set just stored.  Tile m + 3's index slot held tile m - 1's,
+    // which the computing waves read before barrier m - 1.
+    auto step = [&](Rows &r, const Idx &use, Idx &next, long long t) {
       const int m = static_cast<int>(t - t_begin);
-      store_rows((m + 1) % 3, m & 1, true);
-      store_qidx(m & 1);
-      if (t + 1 < t_end) {
-        load_rows(t + 1, true);
-        if (t + 2 < t_end) load_idx(t + 2, static_cast<int>((t + 2) % tiles_per_seg), true);
-      }
+      store_rows(r, (m + 1) % 3);
+      indices(next, t + 4);
+      rows(r, use, t + 3);
       lds_barrier();  // tile m ready; tile m - 1 computed
+    };
+    long long t = t_begin;
+    for (; t + 2 < t_end; t += 3) {
+      step(r0, i0, i1, t);
+      step(r1, i1, i2, t + 1);
+      step(r2, i2, i0, t + 2);
     }
+    if (t < t_end) step(r0, i0, i1, t);
+    if (t + 1 < t_end) step(r1, i1, i2, t + 1);
     return;
   }
 
   // -------------------------------------------------------------- consumer
   const int g = lane >> 4, r16 = lane & 15;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, (u16x8)0x3f80);
+  const int qrow = wave * 16 + r16;  // this lane's query of every tile
+  // Q^T operand: lane holds its query's d-slice g*8 .. +7 of each 32
+  auto load_q = [&](u16x8 (&dst)[D / 32], long long t, int qi) {
+    const uint16_t *qs = q + seg_of(t) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) dst[kk] = piece(qs, qi, kk * 4 + g);
+  };
+  u16x8 qnext[D / 32];
+  int qidx_next = 0;
   for (long long t = t_begin; t < t_end; ++t) {
     const int m_idx = static_cast<int>(t - t_begin);
-    const int c = static_cast<int>(t % tiles_per_seg);
-    lds_barrier();  // tile m_idx's chunks and query rows staged
-    const uint16_t *Qs = qslots + (m_idx & 1) * kQSlotElems + (wave * 16 + r16) * kKRow;
+    const int c = chunk_of(t);
+    lds_barrier();  // tile m_idx's chunks staged
+    if (m_idx == 0) {
+      qidx_next = qidx_lds[qrow];
+      load_q(qnext, t, qidx_next);
+    }
     bf16x8 bq[D / 32];
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      bq[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(Qs + kk * 32 + g * 8));
-    const int qidx = qidx_lds[(m_idx & 1) * W + wave * 16 + r16];
+    for (int kk = 0; kk < D / 32; ++kk) bq[kk] = __builtin_bit_cast(bf16x8, qnext[kk]);
+    const int qidx = qidx_next;
+    if (t + 1 < t_end) {  // the next tile's query rows, in flight during this tile
+      qidx_next = qidx_lds[((m_idx + 1) & 3) * W + qrow];
+      load_q(qnext, t + 1, qidx_next);
+    }
     f32x4 o[D / 16], l_acc = {0.0f, 0.0f, 0.0f, 0.0f};
     float m = -INFINITY;
 #pragma unroll
@@ -688,7 +711,7 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
       const uint16_t *const vb[2] = {own + W * kKRow, own + W * kKRow + 64};
       attend_blocks<D, kVRow, 2>(kb, vb, bq, o, l_acc, m, scale_log2, ones, g, r16);
     }
-    const long long seg = (t / tiles_per_seg) * N;
+    const long long seg = seg_of(t);
     const float l_tot = l_acc[0];
     const float inv = 1.0f / l_tot;
     uint16_t *orow = o_s + (seg + qidx) * D;
@@ -702,11 +725,10 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
   }
 }
 
-// LDS bytes of the sliding-window kernel: three chunk slots, two query slots
-// and two query-index slots.
+// LDS bytes of the sliding-window kernel: three chunk slots and four
+// query-index slots.
 constexpr size_t attn_slide_lds_bytes() {
-  return (3 * (static_cast<size_t>(128) * (64 + 8) + static_cast<size_t>(64) * (128 + 4)) +
-          2 * static_cast<size_t>(128) * (64 + 8)) * 2 + 2 * 128 * 4;
+  return 3 * (static_cast<size_t>(128) * (64 + 8) + static_cast<size_t>(64) * (128 + 4)) * 2 + 4 * 128 * 4;
 }
 
 // fp32 inputs: one thread per sorted query, binary32 arithmetic throughout.
