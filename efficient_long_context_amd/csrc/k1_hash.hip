@@ -201,8 +201,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
   constexpr int kStepRows = 64;
   __shared__ __align__(16) uint16_t sp[kRPad * kLdsRow];
   __shared__ float s_red[2];  // max_t c|r_t| and "all planes in range"
-  // per wave: key byte codes of its 16 rows, table-major [table][16 rows]
-  // (L <= 64), transposed here and stored as one 16-byte piece per table
+  // per wave, for 8-bit codes: keys -- the codes of its 16 rows, table-major
+  // [table][16 rows] (L <= 64), stored as one 16-byte piece per table;
+  // queries -- the plane masks of its 16 rows, row-major with kQRowB bytes a
+  // row (an odd number of words, so the 16 rows fall in distinct banks)
+  constexpr int kQRowB = 4 * ((kWords + 1) | 1);
+  static_assert(16 * kQRowB <= 64 * 16, "query mask rows fit the wave's buffer");
   __shared__ __align__(16) uint8_t kcl[4][64 * 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -259,8 +263,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) dst[kk] = *reinterpret_cast<const u32x4 *>(x + rr * D + kk * 32 + g * 8);
   };
-  // key byte codes (the table-major layout the RACE build reads)
-  const bool staged_kcodes = tensor == 1 && P == 8 && ns % 8 == 0 && L % 4 == 0 && L <= 64;
+  // 8-bit codes on byte boundaries go through the wave's LDS buffer
+  const bool byte_codes = P == 8 && ns % 8 == 0 && L % 4 == 0 && L <= 64;
   uint8_t *kw = kcl[wave];
   u32x4 nxt[D / 32];
   load_rows(row_begin, nxt);
@@ -392,8 +396,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
       }
     }
     const unsigned long long undecided_mask = __ballot(undecided);
-    // place group g's byte (nibble for an unpaired last tile), then OR the
-    // four groups: every lane of a row holds the row's full plane mask
+    const long long out_row = static_cast<long long>(tensor) * rows + row;
+    if (byte_codes) {
+      // 8-bit codes starting on a byte boundary (ns is 0 or 8).  Group g holds
+      // byte g of every plane-mask word w (mask byte 4 w + g) in the low 8 bits
+      // of words[w]; an unpaired last tile gives nibble g of the word's low
+      // half instead, and pairs of groups are merged into bytes 4 w + g / 2.
+      // Each lane writes its bytes to the wave's LDS buffer: the row-major mask
+      // of its row (queries) or its codes in table-major order (keys).
+      uint32_t byte0 = 0u;  // mask byte 0 (the sort code), valid in group 0
+#pragma unroll
+      for (int w = 0; w < kWords; ++w) {
+        uint32_t byte;
+        int bidx;  // mask byte this lane writes, -1 for none
+        if (2 * w + 1 < NPT) {
+          byte = words[w] & 0xffu;
+          bidx = 4 * w + g;
+        } else {
+          const uint32_t v = (words[w] & 0xfu) << (4 * (g & 1));
+          const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // groups g and g ^ 1
+          byte = sw[0] | sw[1];
+          bidx = (g & 1) ? -1 : 4 * w + (g >> 1);
+        }
+        if (w == 0) byte0 = byte;
+        const int l = bidx - ns / 8;  // table of a key code byte
+        const bool put = tensor == 0 ? bidx >= 0 : (bidx >= 0 && l >= 0 && l < L);
+        const int at = tensor == 0 ? r16 * kQRowB + bidx : l * 16 + r16;
+        if (put) kw[at] = static_cast<uint8_t>(byte);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      if (valid && g == 0) {
+        scode[out_row] = static_cast<uint16_t>(byte0 & ((1u << ns) - 1u));
+        // a projection binary64 could not decide: the exact pass redoes the row
+        flags[out_row] = ((undecided_mask >> r16) & 0x0001000100010001ull) ? 1 : 0;
+      }
+      if (tensor == 0) {
+        // row-major codes: code word j is mask bytes ns/8 + 4j .. +3, a byte
+        // funnel of two aligned words of the row; the wave's 16 rows are
+        // consecutive, so its stores cover one contiguous block
+        if (valid) {
+          const uint8_t *rowb = kw + r16 * kQRowB;
+          uint32_t *rc = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(rcode) + out_row * L);
+          for (int j = g; j < L / 4; j += 4) {
+            const int bp = ns / 8 + 4 * j;
+            const uint32_t lo = *reinterpret_cast<const uint32_t *>(rowb + (bp & ~3));
+            const uint32_t hi = *reinterpret_cast<const uint32_t *>(rowb + (bp & ~3) + 4);
+            rc[j] = __builtin_amdgcn_alignbyte(hi, lo, bp & 3);
+          }
+        }
+      } else {  // table-major codes: lane t stores table t's 16 rows of this wave
+        const long long rs = r0 + wave * 16;
+        for (int t = lane; t < L; t += 64) {
+          uint8_t *dst = reinterpret_cast<uint8_t *>(rcode) + rows * L + static_cast<long long>(t) * rows + rs;
+          const uint8_t *src = kw + t * 16;
+          if (rows % 16 == 0 && rs + 16 <= row_end) {
+            *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+          } else {
+            for (int e = 0; e < 16 && rs + e < row_end; ++e) dst[e] = src[e];
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");  // read before the next step writes
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      continue;
+    }
+    // Other code widths: OR the four groups' bytes (nibbles for an unpaired
+    // last tile) so every lane of a row holds the row's full plane mask, then
+    // cut each code out of it.
 #pragma unroll
     for (int w = 0; w < kWords; ++w) {
       const int nbits = 2 * w + 1 < NPT ? 8 : 4;
@@ -403,7 +475,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
       const auto r32s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
       words[w] = r32s[0] | r32s[1];
     }
-    const bool byte_codes = P == 8 && ns % 8 == 0 && L % 4 == 0;
     auto get = [&](int wd) -> uint32_t {
       uint32_t r = 0u;
 #pragma unroll
@@ -411,53 +482,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
       return r;
     };
     if (valid) {
-      const long long out_row = static_cast<long long>(tensor) * rows + row;
       if (g == 0) {
         scode[out_row] = static_cast<uint16_t>(words[0] & ((1u << ns) - 1u));  // ns <= 12
-        // a projection binary64 could not decide: the exact pass redoes the row
         flags[out_row] = ((undecided_mask >> r16) & 0x0001000100010001ull) ? 1 : 0;
       }
-      if (staged_kcodes) {
-        for (int j = g; j < L / 4; j += 4) {
-          const int bytepos = ns / 8 + 4 * j;
-          const uint32_t word = __builtin_amdgcn_alignbyte(get(bytepos / 4 + 1), get(bytepos / 4), bytepos % 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kw[(4 * j + e) * 16 + r16] = static_cast<uint8_t>(word >> (8 * e));
-        }
-      } else if (byte_codes && tensor == 0) {
-        // 8-bit codes starting on a byte: code word j is bytes ns/8 + 4j .. +3
-        // of the plane mask, one byte-funnel of two mask words
-        uint32_t *rc = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(rcode) + out_row * L);
-        for (int j = g; j < L / 4; j += 4) {
-          const int bytepos = ns / 8 + 4 * j;
-          rc[j] = __builtin_amdgcn_alignbyte(get(bytepos / 4 + 1), get(bytepos / 4), bytepos % 4);
-        }
-      } else {
-        for (int l = g; l < L; l += 4) {
-          const uint32_t code = bit_field(get, ns + l * P, P);
-          const long long ci = race_code_index(tensor, row, l, rows, L);
-          if (rcb == 1) reinterpret_cast<uint8_t *>(rcode)[ci] = static_cast<uint8_t>(code);
-          else reinterpret_cast<uint16_t *>(rcode)[ci] = static_cast<uint16_t>(code);
-        }
+      for (int l = g; l < L; l += 4) {
+        const uint32_t code = bit_field(get, ns + l * P, P);
+        const long long ci = race_code_index(tensor, row, l, rows, L);
+        if (rcb == 1) reinterpret_cast<uint8_t *>(rcode)[ci] = static_cast<uint8_t>(code);
+        else reinterpret_cast<uint16_t *>(rcode)[ci] = static_cast<uint16_t>(code);
       }
-    }
-    if (staged_kcodes) {  // lane t stores table t's 16 rows of this wave
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-      const long long rs = r0 + wave * 16;
-      for (int t = lane; t < L; t += 64) {
-        uint8_t *dst = reinterpret_cast<uint8_t *>(rcode) + rows * L + static_cast<long long>(t) * rows + rs;
-        const uint8_t *src = kw + t * 16;
-        if (rows % 16 == 0 && rs + 16 <= row_end) {
-          *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
-        } else {
-          for (int e = 0; e < 16 && rs + e < row_end; ++e) dst[e] = src[e];
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");  // read before the next step writes
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     }
   }
 }

@@ -34,6 +34,10 @@ CASES = {
     "bf16-P12-L4": ("small-bf16", dict(B=1, H=1, race_tables=4, race_bits=12)),
     "bf16-d128-w64": ("needle256k-bf16", dict(H=2, N=4096, chunk=64, sort_bits=7, race_tables=5, race_bits=9)),
     "bf16-w256": ("small-bf16", dict(B=2, H=2, N=4096, chunk=256)),
+    # 8-bit codes on byte boundaries: an even number of plane tiles with no
+    # sort code, and 12 tables (three code words a row)
+    "bf16-bytecodes-ns0-L4": ("small-bf16", dict(B=1, H=2, sort_bits=0, race_tables=4, race_bits=8)),
+    "bf16-bytecodes-L12": ("small-bf16", dict(B=1, H=2, race_tables=12, race_bits=8, sort_bits=8)),
 }
 
 
@@ -86,10 +90,12 @@ def test_deterministic():
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
 
 
-def _integer_inputs(seed, N=2048, H=2, dtype="bf16", scale=1.0):
+def _integer_inputs(seed, N=2048, H=2, dtype="bf16", scale=1.0, **hash_settings):
     """Small-integer q, k and hyperplanes (times a power of two): many projections are
     exactly zero or tiny, so the exact sign path decides them."""
-    wl = workloads.workload("small-bf16", B=1, H=H, N=N, dtype=dtype, race_tables=4, race_bits=5)
+    settings = dict(race_tables=4, race_bits=5)
+    settings.update(hash_settings)
+    wl = workloads.workload("small-bf16", B=1, H=H, N=N, dtype=dtype, **settings)
     inp = workloads.generate(wl, seed)
     rng = np.random.default_rng(seed)
     f = (lambda a: a.astype(np.float32))
@@ -104,11 +110,14 @@ def _integer_inputs(seed, N=2048, H=2, dtype="bf16", scale=1.0):
     return inp
 
 
-@pytest.mark.parametrize("scale", [1.0, 2.0 ** 50, 2.0 ** -50])
-def test_exact_ties_and_extreme_magnitudes(scale):
+@pytest.mark.parametrize("scale,codes", [(1.0, "5-bit"), (2.0 ** 50, "5-bit"), (2.0 ** -50, "5-bit"),
+                                          (1.0, "8-bit"), (2.0 ** 50, "8-bit")])
+def test_exact_ties_and_extreme_magnitudes(scale, codes):
     """Exact-zero projections (bit 0), rows far outside the certified range
-    (|x| > 2^40 or < 2^-40): every such code bit comes from the exact path."""
-    inp = _integer_inputs(21, scale=scale)
+    (|x| > 2^40 or < 2^-40): every such code bit comes from the exact path.
+    8-bit codes on byte boundaries take the byte-code output path."""
+    hs = {} if codes == "5-bit" else dict(sort_bits=8, race_tables=4, race_bits=8)
+    inp = _integer_inputs(21, scale=scale, **hs)
     g = run_gpu(inp)
     r = run_oracle(inp)
     q64 = inp.q.astype(np.float64)
