@@ -173,6 +173,24 @@ __device__ __forceinline__ long long xcd_logical_block(long long hw_block, long 
   return (hw_block % kXcdCount) * (grid / kXcdCount) + hw_block / kXcdCount;
 }
 
+// Exclusive prefix sum of one value per thread over the workgroup; `tmp`
+// holds one word of LDS per wave.  Two barriers.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *tmp, int lane,
+                                                         int wave) {
+  uint32_t inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += tmp[w];
+  __syncthreads();  // tmp may be reused after this
+  return before + inc - x;
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits
 // for every outstanding global load of the wave (its release fence covers all
 // address spaces), which would drain register prefetches issued ahead of it.

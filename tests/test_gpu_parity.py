@@ -38,6 +38,8 @@ CASES = {
     # sort code, and 12 tables (three code words a row)
     "bf16-bytecodes-ns0-L4": ("small-bf16", dict(B=1, H=2, sort_bits=0, race_tables=4, race_bits=8)),
     "bf16-bytecodes-L12": ("small-bf16", dict(B=1, H=2, race_tables=12, race_bits=8, sort_bits=8)),
+    # segments longer than one workgroup's LDS sort: the tiled three-pass sort
+    "bf16-long-segment-sort": ("small-bf16", dict(B=1, H=1, N=65536 + 192, chunk=64)),
 }
 
 
