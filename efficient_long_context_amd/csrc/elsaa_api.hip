@@ -212,10 +212,25 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
   if (st != ELSAA_OK) return st;
   if (!q || !k || !v || !x_gate || !out || (!hyperplanes && g.R > 0))
     return fail(ELSAA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  auto misaligned = [](const void *ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; };
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(x_gate, 16) ||
+      misaligned(hyperplanes, 16) || misaligned(out, 16))
+    return fail(ELSAA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (misaligned(params->gate_w, 4) || misaligned(params->gate_b, 4))
+    return fail(ELSAA_ERR_INVALID_ARG, "gate parameters must be 4-byte aligned");
+  if (const elsaa_aux_t *a = params->aux) {
+    const void *ptrs[] = {a->sort_code_q, a->sort_code_k, a->race_code_q, a->race_code_k, a->perm_q, a->perm_k,
+                          a->race_sum, a->race_cnt, a->o_sparse, a->lse_s, a->z_lr, a->alpha, a->g_s, a->g_lr,
+                          a->o_lowrank};
+    for (const void *ptr : ptrs)
+      if (misaligned(ptr, 16)) return fail(ELSAA_ERR_INVALID_ARG, "aux output pointers must be 16-byte aligned");
+  }
   const size_t need = carve(g, nullptr, nullptr);
   if (!params->workspace || params->workspace_bytes < need)
     return fail(ELSAA_ERR_WORKSPACE, "workspace of %zu bytes required (given %zu%s)", need,
                 params->workspace_bytes, params->workspace ? "" : ", NULL");
+  if (misaligned(params->workspace, 256))
+    return fail(ELSAA_ERR_WORKSPACE, "the workspace must be 256-byte aligned");
   elsaa::Buffers buf;
   carve(g, static_cast<char *>(params->workspace), &buf);
   hipStream_t s = static_cast<hipStream_t>(params->stream);

@@ -144,23 +144,60 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
   const int j_begin = wave * chunk < N ? wave * chunk : N;
   const int j_end = j_begin + chunk < N ? j_begin + chunk : N;
 
-  for (int i = tid; i < W * nb; i += W * 64) cnt[i] = 0u;
-  __syncthreads();
-  uint32_t *wc = cnt + wave * nb;
-  auto load_codes = [&](int j0, uint32_t (&code)[8]) {
+  // The wave's codes in 16-byte pieces (kVec codes each): piece p of a batch
+  // starting at jb is codes jb + (64 p + lane) kVec .. +kVec-1, so each piece
+  // load of the wave reads one contiguous kilobyte.  When N is a multiple of
+  // 64 every piece lies wholly inside or outside the run and is 16-byte
+  // aligned; otherwise its codes are read one by one.  The first batch stays
+  // in registers for the ranking pass (all of the run when it fits).
+  constexpr int kVec = 16 / static_cast<int>(sizeof(CT));
+  constexpr int kPieces = 4;
+  constexpr int kBatch = 64 * kPieces * kVec;
+  const bool vec = N % 64 == 0;
+  auto load_batch = [&](int jb, u32x4 (&pc)[kPieces]) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int j = j0 + q * 64 + lane;
-      const uint32_t cv = static_cast<uint32_t>(c[j < j_end ? j : j_end - 1]);
-      code[q] = j < j_end ? cv : 0xffffffffu;
+    for (int p = 0; p < kPieces; ++p) {
+      const int j = jb + (p * 64 + lane) * kVec;
+      if (vec) {
+        pc[p] = (u32x4){0u, 0u, 0u, 0u};
+        if (j < j_end) pc[p] = *reinterpret_cast<const u32x4 *>(c + j);
+      } else {
+        CT t[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) t[e] = j + e < j_end ? c[j + e] : CT(0);
+        pc[p] = __builtin_bit_cast(u32x4, t);
+      }
     }
   };
-  for (int j0 = j_begin; j0 < j_end; j0 += 512) {
-    uint32_t code[8];
-    load_codes(j0, code);
+  auto code_of = [](const u32x4 &pc, int e) -> uint32_t {
+    constexpr int kBits = 8 * static_cast<int>(sizeof(CT));
+    const uint32_t word = pc[e * kBits / 32];
+    return (word >> ((e * kBits) % 32)) & ((1u << kBits) - 1u);
+  };
+  // calls f(code, j) for every code of the batch at jb inside the run
+  auto for_batch = [&](int jb, const u32x4 (&pc)[kPieces], auto &&f) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (code[q] != 0xffffffffu) atomicAdd(&wc[code[q]], 1u);
+    for (int p = 0; p < kPieces; ++p) {
+      const int j = jb + (p * 64 + lane) * kVec;
+      if (j < j_end) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e)
+          if (vec || j + e < j_end) f(code_of(pc[p], e), j + e);
+      }
+    }
+  };
+
+  for (int i = tid; i < W * nb; i += W * 64) cnt[i] = 0u;
+  u32x4 first[kPieces];
+  if (j_begin < j_end) load_batch(j_begin, first);
+  __syncthreads();
+  uint32_t *wc = cnt + wave * nb;
+  auto count = [&](uint32_t code, int) { atomicAdd(&wc[code], 1u); };
+  if (j_begin < j_end) for_batch(j_begin, first, count);
+  for (int jb = j_begin + kBatch; jb < j_end; jb += kBatch) {
+    u32x4 pc[kPieces];
+    load_batch(jb, pc);
+    for_batch(jb, pc, count);
   }
   __syncthreads();
   {  // bucket-major exclusive scan of the [bucket][wave] counts
@@ -207,18 +244,16 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
   // sorted key indices: staged in LDS and written out in order (coalesced),
   // or scattered straight to memory when N does not fit
   int32_t *rp = rperm + unit * N;
-  for (int j8 = j_begin; j8 < j_end; j8 += 512) {
-    uint32_t codes8[8];
-    load_codes(j8, codes8);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int j = j8 + q * 64 + lane;
-      if (codes8[q] != 0xffffffffu) {
-        const uint32_t pos = atomicAdd(&wc[codes8[q]], 1u);
-        if (staged) lperm[pos] = static_cast<uint16_t>(j);
-        else rp[pos] = j;
-      }
-    }
+  auto place = [&](uint32_t code, int j) {
+    const uint32_t pos = atomicAdd(&wc[code], 1u);
+    if (staged) lperm[pos] = static_cast<uint16_t>(j);
+    else rp[pos] = j;
+  };
+  if (j_begin < j_end) for_batch(j_begin, first, place);
+  for (int jb = j_begin + kBatch; jb < j_end; jb += kBatch) {
+    u32x4 pc[kPieces];
+    load_batch(jb, pc);
+    for_batch(jb, pc, place);
   }
   if (staged) {
     __syncthreads();

@@ -23,7 +23,11 @@
  *   - Every data pointer is a DEVICE pointer owned by the caller; the library
  *     allocates no memory.  Its only state is the compute-unit count of each
  *     device, queried on first use.
- *   - All tensors are dense, row-major, contiguous.
+ *   - All tensors are dense, row-major, contiguous.  Tensor pointers (inputs,
+ *     outputs and aux outputs) are 16-byte aligned, gate parameters 4-byte
+ *     aligned, and the workspace 256-byte aligned (hipMalloc and PyTorch
+ *     allocations are); a misaligned pointer is rejected (ELSAA_ERR_INVALID_ARG,
+ *     or ELSAA_ERR_WORKSPACE for the workspace).
  *   - Work is enqueued on params->stream (a hipStream_t; NULL = the default
  *     stream) and is asynchronous: the caller synchronises before reading.
  *   - Every argument is validated on the host before the first launch; on an

@@ -100,6 +100,23 @@ def test_forward_rejects_before_launch():
     assert lib.elsaa_forward(fake, fake, fake, fake, fake, None, fake) == elsaa.ERR_INVALID_ARG
 
 
+def test_forward_rejects_misaligned_pointers():
+    lib = elsaa.lib()
+    fake = ctypes.c_void_p(0x10000)
+    need = elsaa.workspace_bytes(params())
+    p = params(workspace_ptr=0x20000, workspace_bytes=need)
+    odd = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+    for i in range(6):
+        args = [fake] * 6
+        args[i] = odd
+        q, k, v, x, planes, out = args
+        assert lib.elsaa_forward(q, k, v, x, planes, ctypes.byref(p), out) == elsaa.ERR_INVALID_ARG
+        assert "16-byte" in elsaa.last_error()
+    p = params(workspace_ptr=0x20080, workspace_bytes=need)  # 128-byte aligned only
+    assert lib.elsaa_forward(fake, fake, fake, fake, fake, ctypes.byref(p), fake) == elsaa.ERR_WORKSPACE
+    assert "256-byte" in elsaa.last_error()
+
+
 def test_struct_layout_matches_header():
     # elsaa_params_t: 9 int32, float, enum, then 8-byte aligned pointers
     assert ctypes.sizeof(elsaa.ElsaaParams) == 48 + 8 * 2 + 8 + 8 + 8 + 8 + 8
