@@ -146,27 +146,19 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
 
   // The wave's codes in 16-byte pieces (kVec codes each): piece p of a batch
   // starting at jb is codes jb + (64 p + lane) kVec .. +kVec-1, so each piece
-  // load of the wave reads one contiguous kilobyte.  When N is a multiple of
-  // 64 every piece lies wholly inside or outside the run and is 16-byte
-  // aligned; otherwise its codes are read one by one.  The first batch stays
-  // in registers for the ranking pass (all of the run when it fits).
+  // load of the wave reads one contiguous kilobyte.  N is a multiple of 64
+  // (the chunk is), so every piece lies wholly inside or outside the run and
+  // is 16-byte aligned.  The first batch stays in registers for the ranking
+  // pass (all of the run when it fits).
   constexpr int kVec = 16 / static_cast<int>(sizeof(CT));
   constexpr int kPieces = 4;
   constexpr int kBatch = 64 * kPieces * kVec;
-  const bool vec = N % 64 == 0;
   auto load_batch = [&](int jb, u32x4 (&pc)[kPieces]) {
 #pragma unroll
     for (int p = 0; p < kPieces; ++p) {
       const int j = jb + (p * 64 + lane) * kVec;
-      if (vec) {
-        pc[p] = (u32x4){0u, 0u, 0u, 0u};
-        if (j < j_end) pc[p] = *reinterpret_cast<const u32x4 *>(c + j);
-      } else {
-        CT t[kVec];
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) t[e] = j + e < j_end ? c[j + e] : CT(0);
-        pc[p] = __builtin_bit_cast(u32x4, t);
-      }
+      pc[p] = (u32x4){0u, 0u, 0u, 0u};
+      if (j < j_end) pc[p] = *reinterpret_cast<const u32x4 *>(c + j);
     }
   };
   auto code_of = [](const u32x4 &pc, int e) -> uint32_t {
@@ -181,8 +173,7 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
       const int j = jb + (p * 64 + lane) * kVec;
       if (j < j_end) {
 #pragma unroll
-        for (int e = 0; e < kVec; ++e)
-          if (vec || j + e < j_end) f(code_of(pc[p], e), j + e);
+        for (int e = 0; e < kVec; ++e) f(code_of(pc[p], e), j + e);
       }
     }
   };
