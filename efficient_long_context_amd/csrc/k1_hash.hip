@@ -207,6 +207,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
   // row (an odd number of words, so the 16 rows fall in distinct banks)
   constexpr int kQRowB = 4 * ((kWords + 1) | 1);
   static_assert(16 * kQRowB <= 64 * 16, "query mask rows fit the wave's buffer");
+  // The same buffer holds the row of the projection the wave's exact path is
+  // deciding (d bf16), which ends before the codes are written.
+  static_assert(D * 2 <= 64 * 16, "one row fits the wave's buffer");
   __shared__ __align__(16) uint8_t kcl[4][64 * 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -350,6 +353,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
       }
       // rows outside the certified range go to the exact fix-up kernel whole
       if (!valid || !row_ok) unsure = 0ull;
+      uint16_t *xs = reinterpret_cast<uint16_t *>(kw);  // the source lane's row, staged below
       for (unsigned long long pending = __ballot(unsure != 0ull); pending;
            pending = __ballot(unsure != 0ull)) {
         const int src = __builtin_ctzll(pending);  // wave-uniform
@@ -360,8 +364,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
                  __builtin_amdgcn_readlane(static_cast<int>(unsure >> 32), src)))
              << 32);
         const int bpos = __builtin_ctzll(sb);
-        // the source lane's row, read from memory (this path is rare)
-        const uint16_t *xs = x + ((r0 + wave * 16 + (src & 15)) < rows ? (r0 + wave * 16 + (src & 15)) : rows - 1) * D;
+        // the source lane's row to LDS from the operand registers of its four
+        // lanes (lanes of the previous projection have read theirs: LDS
+        // accesses of a wave complete in order)
+        if (r16 == (src & 15)) {
+#pragma unroll
+          for (int kk = 0; kk < D / 32; ++kk) *reinterpret_cast<u32x4 *>(xs + kk * 32 + g * 8) = cur[kk];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         const uint16_t *ps = sp + ((bpos >> 2) * 16 + (src >> 4) * 4 + (bpos & 3)) * kLdsRow;
         double sum = 0.0, sabs = 0.0;
 #pragma unroll
