@@ -106,7 +106,7 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   t.scode = reinterpret_cast<uint16_t *>(take(2 * rows * 2));
   t.rcode = take(2 * rows * g.L * g.rcb);
   t.perm = reinterpret_cast<int32_t *>(take(2 * rows * 4));
-  t.flags = reinterpret_cast<uint8_t *>(take(2 * rows));
+  t.flags = reinterpret_cast<uint8_t *>(take(2 * rows + 4));  // + one word: any row flagged
   t.hist = reinterpret_cast<uint32_t *>(take(2 * static_cast<size_t>(g.BH) * g.nb_sort * g.sort_tiles * 4));
   // per-table key permutation and run starts of the RACE build
   t.rperm = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * g.N * 4));

@@ -35,7 +35,8 @@ struct Buffers {
   uint16_t *scode;  // [2][BH][N]     q codes then k codes
   void *rcode;      // q codes [BH*N][L], then k codes [L][BH*N]; uint8 or uint16
   int32_t *perm;    // [2][BH][N]
-  uint8_t *flags;   // [2][BH][N]     rows whose codes need the exact pass
+  uint8_t *flags;   // [2][BH][N]     rows whose codes need the exact pass,
+                    // then one word: nonzero when any row may be flagged
   uint32_t *hist;   // [2][BH][nb_sort][sort_tiles] -> exclusive offsets
   int32_t *rperm;   // [BH][L][N]     keys of each table sorted by bucket
   int32_t *rstart;  // [BH][L][nb_race + 1] run start of each bucket in rperm
@@ -45,6 +46,14 @@ struct Buffers {
   void *o_s;        // [BH][N][D] in dtype
   float *lse;       // [BH][N]
 };
+
+// The word after the exact-pass flags (2 rows bytes): the hash sets it when it flags
+// a row, the fix-up kernel skips its scan while it is zero, and the RACE rank
+// kernel (which runs after the fix-up) clears it for the next call.  Stale
+// contents only cost a scan that finds nothing.
+__host__ __device__ __forceinline__ uint32_t *flagged_any(uint8_t *flags, long long rows) {
+  return reinterpret_cast<uint32_t *>(flags + 2 * rows);
+}
 
 // Element index of the RACE code of (row, table l) in Buffers::rcode: query
 // codes are row-major [rows][L] (the fusion reads a query's L codes

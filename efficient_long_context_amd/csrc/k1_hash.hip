@@ -413,6 +413,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
       }
     }
     const unsigned long long undecided_mask = __ballot(undecided);
+    if (undecided_mask != 0ull && lane == 0) *flagged_any(flags, rows) = 1u;
     const long long out_row = static_cast<long long>(tensor) * rows + row;
     if (byte_codes) {
       // 8-bit codes starting on a byte boundary (ns is 0 or 8).  Group g holds
@@ -526,6 +527,7 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_fixup(
     const uint16_t *__restrict__ planes, int R, int ns, int L, int P, long long rows,
     const uint8_t *__restrict__ flags, uint16_t *__restrict__ scode, void *__restrict__ rcode,
     int rcb) {
+  if (*flagged_any(const_cast<uint8_t *>(flags), rows) == 0u) return;  // no row flagged
   const int lane = threadIdx.x & 63;
   const long long waves = static_cast<long long>(gridDim.x) * 4;
   const long long total = 2 * rows;

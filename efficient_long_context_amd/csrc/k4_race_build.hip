@@ -127,8 +127,9 @@ template <typename CT>
 __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
     const CT *__restrict__ kcodes, int N, int L, int P, long long rows, int staged, int parts,
     int32_t *__restrict__ rperm, int32_t *__restrict__ rstart, int32_t *__restrict__ rpart,
-    float *__restrict__ tcnt) {
+    float *__restrict__ tcnt, uint32_t *__restrict__ hash_flagged) {
   extern __shared__ uint32_t lds[];
+  if (blockIdx.x == 0 && threadIdx.x == 0) *hash_flagged = 0u;  // the fix-up has run
   const int nb = 1 << P;
   const int W = static_cast<int>(blockDim.x >> 6);
   uint32_t *cnt = lds;           // [W][nb] counts, then running offsets
@@ -396,11 +397,11 @@ hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &bu
   if (g.rcb == 1)
     hipLaunchKernelGGL(elsaa_k4_race_rank<uint8_t>, dim3(static_cast<unsigned>(units)), dim3(waves * 64), rlds,
                        stream, static_cast<const uint8_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0, race_parts(g.N),
-                       buf.rperm, buf.rstart, buf.rpart, buf.tcnt);
+                       buf.rperm, buf.rstart, buf.rpart, buf.tcnt, flagged_any(buf.flags, g.rows));
   else
     hipLaunchKernelGGL(elsaa_k4_race_rank<uint16_t>, dim3(static_cast<unsigned>(units)), dim3(waves * 64), rlds,
                        stream, static_cast<const uint16_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0, race_parts(g.N),
-                       buf.rperm, buf.rstart, buf.rpart, buf.tcnt);
+                       buf.rperm, buf.rstart, buf.rpart, buf.tcnt, flagged_any(buf.flags, g.rows));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
