@@ -40,6 +40,9 @@ CASES = {
     "bf16-bytecodes-L12": ("small-bf16", dict(B=1, H=2, race_tables=12, race_bits=8, sort_bits=8)),
     # segments longer than one workgroup's LDS sort: the tiled three-pass sort
     "bf16-long-segment-sort": ("small-bf16", dict(B=1, H=1, N=65536 + 192, chunk=64)),
+    # 4096 buckets with 16K codes a segment (the tiled sort: the counters and
+    # the codes do not fit one workgroup)
+    "bf16-sort12-N16k": ("small-bf16", dict(B=1, H=1, N=16384, sort_bits=12)),
 }
 
 
