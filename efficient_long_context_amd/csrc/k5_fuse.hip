@@ -192,7 +192,7 @@ template <> struct GateIn<float, 2> {
 };
 
 template <int D, typename VT, typename CT, int LC>
-__global__ __launch_bounds__(256) void elsaa_k5_fuse_wide(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void elsaa_k5_fuse_wide(
     const VT *__restrict__ o_s, const float *__restrict__ lse, const CT *__restrict__ qcodes,
     const VT *__restrict__ tsum, const float *__restrict__ tcnt, const VT *__restrict__ x_gate,
     const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int P,
@@ -227,12 +227,9 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse_wide(
   }
   // gate weights of head h (this lane's kGE columns)
   const bool gate_fast = DG == 64;
-  float wa[kGE], wb[kGE];
-#pragma unroll
-  for (int e = 0; e < kGE; ++e) {
-    wa[e] = gate_fast ? gate_w[static_cast<long long>(h) * DG + sub * kGE + e] : 0.0f;
-    wb[e] = gate_fast ? gate_w[static_cast<long long>(H + h) * DG + sub * kGE + e] : 0.0f;
-  }
+  __shared__ float gw_lds[2][64];  // gate weights of head h when d_gate = 64
+  if (gate_fast && tid < 128)
+    gw_lds[tid >> 6][tid & 63] = gate_w[static_cast<long long>((tid >> 6) * H + h) * DG + (tid & 63)];
   const float gb0 = gate_b[h], gb1 = gate_b[H + h];
   const __amdgpu_buffer_rsrc_t ts_rs =
       make_rsrc(tsum + bh * LC * nb * static_cast<long long>(D), static_cast<uint32_t>(LC * nb * kRowBytes));
@@ -242,20 +239,31 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse_wide(
 
   const int per_wave = R / 4;
   const int i_begin = i_run + wave * per_wave;
+  // the streamed tensors of this (b, h) through buffer resources: a scalar
+  // base and 32-bit lane offsets keep the per-lane addresses in one register
+  const __amdgpu_buffer_rsrc_t qc_rs =
+      make_rsrc(qcodes + bh * N * LC, static_cast<uint32_t>(N) * LC * cb);
+  const __amdgpu_buffer_rsrc_t os_rs =
+      make_rsrc(o_s + bh * N * static_cast<long long>(D), static_cast<uint32_t>(N) * kRowBytes);
+  const __amdgpu_buffer_rsrc_t lse_rs = make_rsrc(lse + bh * N, static_cast<uint32_t>(N) * 4u);
+  const __amdgpu_buffer_rsrc_t xg_rs =
+      make_rsrc(x_gate + b * N * DG, static_cast<uint32_t>(N) * DG * kES);
+  const __amdgpu_buffer_rsrc_t out_rs =
+      make_rsrc(out + bh * N * static_cast<long long>(D), static_cast<uint32_t>(N) * kRowBytes);
   auto load_codes = [&](int i0, uint32_t (&w)[kCW]) {
-    const CT *src = qcodes + (bh * N + i0 + lane / kLPQ) * LC;
+    const uint32_t off = static_cast<uint32_t>(i0 + lane / kLPQ) * (LC * cb);
     if constexpr (kCW % 4 == 0) {
 #pragma unroll
       for (int k = 0; k < kCW / 4; ++k) {
-        const u32x4 v = reinterpret_cast<const u32x4 *>(src)[k];
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qc_rs, off, 16 * k, 0));
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[4 * k + e] = v[e];
       }
     } else {
       static_assert(kCW == 2, "8 code bytes per query");
-      const uint2 v = *reinterpret_cast<const uint2 *>(src);
-      w[0] = v.x;
-      w[1] = v.y;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(qc_rs, off, 0, 0);
+      w[0] = v[0];
+      w[1] = v[1];
     }
   };
   uint32_t cw[kCW];
@@ -263,18 +271,18 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse_wide(
   // the streamed inputs of a step (sparse output, its LSE, gate inputs) are
   // requested one step ahead, so their HBM latency overlaps the table gathers
   auto load_stream = [&](int i0, u32x4 &os_raw, float &lse_v, u32x4 &xg_raw) {
-    const int ii = i0 + lane / kLPQ;
-    const long long q0 = bh * N + ii;
-    os_raw = *reinterpret_cast<const u32x4 *>(o_s + q0 * D + sub * kCols);
-    lse_v = lse[q0];
+    const uint32_t ii = static_cast<uint32_t>(i0 + lane / kLPQ);
+    os_raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(os_rs, ii * kRowBytes + vbase, 0, 0));
+    lse_v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lse_rs, ii * 4u, 0, 0));
     if (gate_fast) {
-      const VT *xg = x_gate + (b * N + ii) * DG + sub * kGE;
-      if constexpr (kGE * kES == 16) xg_raw = *reinterpret_cast<const u32x4 *>(xg);
-      else if constexpr (kGE * kES == 8) {
-        const uint2 t2 = *reinterpret_cast<const uint2 *>(xg);
-        xg_raw = u32x4{t2.x, t2.y, 0u, 0u};
+      const uint32_t xo = (ii * static_cast<uint32_t>(DG) + static_cast<uint32_t>(sub * kGE)) * kES;
+      if constexpr (kGE * kES == 16) {
+        xg_raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xg_rs, xo, 0, 0));
+      } else if constexpr (kGE * kES == 8) {
+        const auto t2 = __builtin_amdgcn_raw_buffer_load_b64(xg_rs, xo, 0, 0);
+        xg_raw = u32x4{t2[0], t2[1], 0u, 0u};
       } else {
-        xg_raw = u32x4{*reinterpret_cast<const uint32_t *>(xg), 0u, 0u, 0u};
+        xg_raw = u32x4{__builtin_amdgcn_raw_buffer_load_b32(xg_rs, xo, 0, 0), 0u, 0u, 0u};
       }
     }
   };
@@ -306,8 +314,6 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse_wide(
       }
       t[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, off, l * nb * kRowBytes, 0));
     }
-    // the next step's streamed inputs
-    load_stream(step + kQPS < per_wave ? i_begin + step + kQPS : i_begin + step, os_next, lse_next, xg_next);
     // sparse output and gate inputs of this step
     float osv[kCols];
     if constexpr (kES == 2) {
@@ -357,12 +363,15 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse_wide(
       }
     }
 
+    // the next step's streamed inputs
+    load_stream(step + kQPS < per_wave ? i_begin + step + kQPS : i_begin + step, os_next, lse_next, xg_next);
+
     float a0 = 0.0f, a1 = 0.0f;
     if (gate_fast) {
 #pragma unroll
       for (int e = 0; e < kGE; ++e) {
-        a0 = __builtin_fmaf(xv[e], wa[e], a0);
-        a1 = __builtin_fmaf(xv[e], wb[e], a1);
+        a0 = __builtin_fmaf(xv[e], gw_lds[0][sub * kGE + e], a0);
+        a1 = __builtin_fmaf(xv[e], gw_lds[1][sub * kGE + e], a1);
       }
     } else {
       for (int e = sub; e < DG; e += kLPQ) {
@@ -392,12 +401,16 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse_wide(
       o_lr[k] = num[k] * rz;
       yv[k] = __builtin_fmaf(ws, osv[k], g_lr * o_lr[k]);
     }
+    const uint32_t yo = static_cast<uint32_t>(i) * kRowBytes + vbase;
     if constexpr (kES == 2) {
-      *reinterpret_cast<u32x4 *>(out + qi * D + sub * kCols) =
+      __builtin_amdgcn_raw_buffer_store_b128(
           u32x4{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
-                pack_bf16x2(yv[6], yv[7])};
+                pack_bf16x2(yv[6], yv[7])},
+          out_rs, yo, 0, 0);
     } else {
-      *reinterpret_cast<f32x4 *>(out + qi * D + sub * kCols) = f32x4{yv[0], yv[1], yv[2], yv[3]};
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]), __float_as_uint(yv[3])},
+          out_rs, yo, 0, 0);
     }
     if (aux.o_lr) {
 #pragma unroll
