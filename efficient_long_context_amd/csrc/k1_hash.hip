@@ -92,6 +92,41 @@ __device__ __noinline__ int exact_dot_sign(const T *x, const T *r, int d) {
   return kulisch_dot_sign<T>(x, r, d);
 }
 
+// Sum over the 64 lanes of a wave of a binary64 value, every lane receiving
+// the total, without a round trip through LDS: two quad permutes (lane bits 0
+// and 1), the half-row and row mirrors (bits 2 and 3), then the permlane swaps
+// across lane bits 4 and 5.  A pairwise tree of depth 6; each step adds a
+// value and its partner's, in an order the two lanes share.
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(u)), kCtrl, 0xf, 0xf, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(u >> 32)), kCtrl, 0xf, 0xf, false));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+template <bool kBit5>
+__device__ __forceinline__ double swap_add_f64(double x) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+  const auto rl = kBit5 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                        : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto rh = kBit5 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                        : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const double a = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(rh[0]) << 32) | rl[0]));
+  const double b = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(rh[1]) << 32) | rl[1]));
+  return a + b;  // (lower row's value) + (upper row's value) in both lanes
+}
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  x += dpp_f64<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_f64<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp_f64<0x141>(x);  // row_half_mirror: the other quad of the 8
+  x += dpp_f64<0x140>(x);  // row_mirror: the other 8 of the row of 16
+  x = swap_add_f64<false>(x);
+  return swap_add_f64<true>(x);
+}
+
 // Exact sign of <x, r> for two rows of d bfloat16 values, one wave, lanes over
 // the elements.  A bfloat16 value is M 2^E with an integer M < 2^8 (E = e - 134
 // for a normal exponent field e, M = 128 + fraction; E = -133 and M = fraction
@@ -320,37 +355,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
     uint32_t words[kWords];
 #pragma unroll
     for (int w = 0; w < kWords; ++w) words[w] = 0u;
-    float amin = INFINITY;  // smallest |projection| of this lane
+    // bit pt: some certified-range row of the wave has a projection on plane
+    // tile pt within tau of zero (wave-uniform; one compare per tile)
+    uint32_t tile_mask = 0u;
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) {
       const f32x4 a4 = project(pt);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
         words[pt >> 1] = __builtin_amdgcn_alignbit(words[pt >> 1], __float_as_uint(a4[i]), 31);
-        amin = fminf(amin, fabsf(a4[i]));
-      }
+      const float tmin = fminf(fminf(fabsf(a4[0]), fabsf(a4[1])), fminf(fabsf(a4[2]), fabsf(a4[3])));
+      tile_mask |= (__ballot(valid && row_ok && !(tmin > tau)) != 0ull ? 1u : 0u) << pt;
     }
     // sign bit 1 = negative: the code bit is its complement wherever |p| > tau
 #pragma unroll
     for (int w = 0; w < kWords; ++w) words[w] = ~words[w];
     bool undecided = valid && !row_ok;
     // Each uncertified projection is re-decided by the whole wave, lanes over
-    // the d products (exact in binary64), summed by a butterfly of depth
+    // the d products (exact in binary64), summed by a cross-lane tree of depth
     // log2(64) (+1 for d = 128 with two products per lane); the sign is taken
     // when |sum| exceeds (depth + 1) 2^-52 sum |p_i|, else from the exact
     // integer sum; only a product exponent span too wide for it flags the row.
     // About 1e-4 of the projections of unit-scale rows are uncertified, which
-    // is one wave step in four at 16 x 136 projections a step.
-    if (__ballot(valid && !(amin > tau)) != 0ull) {
+    // is one wave step in four at 16 x 136 projections a step, and mostly one
+    // plane tile of the step: only the marked tiles are projected again.
+    if (tile_mask != 0u) {
       unsigned long long unsure = 0ull;  // bit 4 pt + i: projection not certified
       // recomputed, not kept: the plane reads below must not be merged with the
       // first pass's, which would hold all its projections live
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
-        const f32x4 a4 = project(pt);
-        const float tmin = fminf(fminf(fabsf(a4[0]), fabsf(a4[1])), fminf(fabsf(a4[2]), fabsf(a4[3])));
-        if (__ballot(valid && !(tmin > tau)) != 0ull) {  // per-projection bits only for such tiles
+        if ((tile_mask >> pt) & 1u) {
+          const f32x4 a4 = project(pt);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             unsure |= static_cast<unsigned long long>(!(fabsf(a4[i]) > tau)) << (pt * 4 + i);
@@ -388,11 +425,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
           sum += prod;
           sabs += fabs(prod);
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          sum += __shfl_xor(sum, off);
-          sabs += __shfl_xor(sabs, off);
-        }
+        sum = wave_sum_f64(sum);
+        sabs = wave_sum_f64(sabs);
         constexpr int kDepth = 6 + D / 64;
         const double bound = static_cast<double>(kDepth + 1) * 0x1p-52 * sabs;
         // within the bound (exact ties included): the integer sum decides
