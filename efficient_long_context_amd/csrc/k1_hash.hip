@@ -310,7 +310,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
     u32x4 cur[D / 32];
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) cur[kk] = nxt[kk];
-    if (r0 + kStepRows < row_end) load_rows(r0 + kStepRows, nxt);  // in flight while this step is hashed
+    // in flight while this step is hashed (unconditional: the last step loads
+    // clamped rows it never uses, and no branch splits the wait for them)
+    load_rows(r0 + kStepRows, nxt);
 
     const int lrow = wave * 16 + r16;
     const long long row = r0 + lrow;
@@ -447,6 +449,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
       }
     }
     const unsigned long long undecided_mask = __ballot(undecided);
+    // The next step's rows are waited for here, after the last change to the
+    // mask words and before this step's code stores: the memory counter
+    // retires in issue order, so a wait placed after the stores would also
+    // wait for their completion.
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) asm volatile("" : "+v"(words[0]) : "v"(nxt[kk]) : "memory");
     if (undecided_mask != 0ull && lane == 0) *flagged_any(flags, rows) = 1u;
     const long long out_row = static_cast<long long>(tensor) * rows + row;
     if (byte_codes) {
