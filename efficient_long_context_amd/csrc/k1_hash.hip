@@ -297,7 +297,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
   // registers, the next step's in flight while this one is hashed.
   auto load_rows = [&](long long r0, u32x4 (&dst)[D / 32]) {
     const long long row = r0 + wave * 16 + r16;
-    const long long rr = row < rows ? row : rows - 1;  // clamped; results of clamped rows are discarded
+    // clamped to the range's last row (just read, so a cache hit); results of
+    // clamped rows are discarded
+    const long long rr = row < row_end ? row : row_end - 1;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) dst[kk] = *reinterpret_cast<const u32x4 *>(x + rr * D + kk * 32 + g * 8);
   };
