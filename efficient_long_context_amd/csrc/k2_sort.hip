@@ -207,18 +207,18 @@ __global__ __launch_bounds__(1024) void elsaa_k2_sort_segment(const uint16_t *__
       const bool valid = code[q] != 0xffffffffu;
       const uint32_t cv = valid ? code[q] : 0u;
       const unsigned long long same = same_code_lanes(cv, valid, ns);
-      const int leader = __ffsll(static_cast<long long>(same)) - 1;  // its lowest lane
-      uint32_t before = 0;
-      if (valid && lane == leader) {
-        before = wc[cv];
+      // every lane of a group of equal codes reads the group's counter (one
+      // address, a broadcast) and writes back the same advanced value, so no
+      // leader lane and no shuffle is needed
+      const uint32_t before = wc[cv];
+      if (valid) {
         wc[cv] = before + static_cast<uint32_t>(__popcll(same));
+        lperm[before + static_cast<uint32_t>(__popcll(same & lt))] = static_cast<uint16_t>(j_begin + q * 64 + lane);
       }
-      before = __shfl(before, leader < 0 ? 0 : leader);
-      if (valid) lperm[before + static_cast<uint32_t>(__popcll(same & lt))] = static_cast<uint16_t>(j_begin + q * 64 + lane);
-      // the leader's counter update lands before the next round reads it
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      // No wait between rounds: a wave's LDS accesses are carried out in
+      // issue order, so the next round's read of a counter sees this round's
+      // update, and the compiler keeps the (possibly aliasing) read after the
+      // write.
     }
   }
   __syncthreads();
