@@ -123,10 +123,12 @@ __device__ __forceinline__ int transposed_column(int m, int lane) {
 //           lane reduction whose column sums are stored as the table row.
 //           Waves of one (b, h) are consecutive and so share an XCD's L2,
 //           which then holds the value rows its tables gather.
-template <typename CT>
+//   The sorted key indices are 16-bit (PT = uint16_t) whenever N <= 65536,
+//   halving the permutation's write here and its read in the gather.
+template <typename CT, typename PT>
 __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
     const CT *__restrict__ kcodes, int N, int L, int P, long long rows, int staged, int parts,
-    int32_t *__restrict__ rperm, int32_t *__restrict__ rstart, int32_t *__restrict__ rpart,
+    PT *__restrict__ rperm, int32_t *__restrict__ rstart, int32_t *__restrict__ rpart,
     float *__restrict__ tcnt, uint32_t *__restrict__ hash_flagged) {
   extern __shared__ uint32_t lds[];
   if (blockIdx.x == 0 && threadIdx.x == 0) *hash_flagged = 0u;  // the fix-up has run
@@ -134,7 +136,8 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
   const int W = static_cast<int>(blockDim.x >> 6);
   uint32_t *cnt = lds;           // [W][nb] counts, then running offsets
   uint32_t *part = lds + W * nb;  // [W] scan
-  uint16_t *lperm = reinterpret_cast<uint16_t *>(part + W);  // [N] when staged (N <= 65536)
+  // [N] when staged (N <= 65536), 16-byte aligned for the vector copy-out
+  uint16_t *lperm = reinterpret_cast<uint16_t *>(lds + (W * nb + W + 3) / 4 * 4);
   const long long unit = blockIdx.x;  // (b, h) * L + table
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -235,11 +238,11 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
   __syncthreads();
   // sorted key indices: staged in LDS and written out in order (coalesced),
   // or scattered straight to memory when N does not fit
-  int32_t *rp = rperm + unit * N;
+  PT *rp = rperm + unit * N;
   auto place = [&](uint32_t code, int j) {
     const uint32_t pos = atomicAdd(&wc[code], 1u);
     if (staged) lperm[pos] = static_cast<uint16_t>(j);
-    else rp[pos] = j;
+    else rp[pos] = static_cast<PT>(j);
   };
   if (j_begin < j_end) for_batch(j_begin, first, place);
   for (int jb = j_begin + kBatch; jb < j_end; jb += kBatch) {
@@ -249,7 +252,12 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
   }
   if (staged) {
     __syncthreads();
-    for (int i = tid; i < N; i += W * 64) rp[i] = lperm[i];
+    if constexpr (sizeof(PT) == 2) {  // 8 indices a 16-byte piece (N is a multiple of 64)
+      for (int i = tid; i < N / 8; i += W * 64)
+        reinterpret_cast<u32x4 *>(rp)[i] = reinterpret_cast<const u32x4 *>(lperm)[i];
+    } else {
+      for (int i = tid; i < N; i += W * 64) rp[i] = static_cast<PT>(lperm[i]);
+    }
   }
 }
 
@@ -257,9 +265,9 @@ constexpr int kGatherWaves = 4;       // waves per gather workgroup
 constexpr int kGatherStage = 1024;    // key indices a wave stages in LDS at once
 constexpr int kGatherSlack = 256;     // staged entries read past the end by the look-ahead
 
-template <typename VT, int D>
+template <typename VT, int D, typename PT>
 __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
-    const VT *__restrict__ v, const int32_t *__restrict__ rperm, const int32_t *__restrict__ rstart,
+    const VT *__restrict__ v, const PT *__restrict__ rperm, const int32_t *__restrict__ rstart,
     const int32_t *__restrict__ rpart, int N, int L, int P, int parts, long long waves_total,
     VT *__restrict__ tsum) {
   using PC = Piece<VT, D>;
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   const long long unit = u / parts;  // (b, h) * L + table
   const long long bh = unit / L;
   const int32_t *rs = rstart + unit * (nb + 1);
-  const int32_t *rp = rperm + unit * N;
+  const PT *rp = rperm + unit * N;
   VT *ts = tsum + unit * nb * static_cast<long long>(D);
 
   // owned buckets [b0, b1) and their positions [p_lo, p_hi), from the part
@@ -378,30 +386,33 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
 }  // namespace
 
 
-hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
-                             hipStream_t stream) {
+namespace {
+
+template <typename PT>
+hipError_t launch_race_build_pt(const Geometry &g, const void *v, const Buffers &buf, hipStream_t stream) {
   const int nb = g.nb_race;
   const void *rk = static_cast<const char *>(buf.rcode) + static_cast<size_t>(g.rows) * g.L * g.rcb;
+  PT *rperm = reinterpret_cast<PT *>(buf.rperm);
   const long long units = static_cast<long long>(g.BH) * g.L;
   int waves = 16384 / nb;  // LDS counters: waves * nb * 4 bytes <= 64 KB
   waves = waves < 1 ? 1 : (waves > 16 ? 16 : waves);
   // stage the sorted indices in LDS when N fits, keeping two workgroups per CU
   constexpr size_t kRankLdsTwoPerCu = 78 * 1024;
-  auto rank_lds = [&](int w, bool st) {
-    return (static_cast<size_t>(w) * nb + w) * 4 + (st ? static_cast<size_t>(g.N) * 2 : 0);
+  auto rank_lds = [&](int w, bool st) {  // + 16: the staged indices start 16-byte aligned
+    return (static_cast<size_t>(w) * nb + w) * 4 + (st ? static_cast<size_t>(g.N) * 2 + 16 : 0);
   };
   bool staged = g.N <= 65536;
   while (staged && waves > 4 && rank_lds(waves, true) > kRankLdsTwoPerCu) waves /= 2;
   if (rank_lds(waves, staged) > kRankLdsTwoPerCu) staged = false;
   const size_t rlds = rank_lds(waves, staged);
   if (g.rcb == 1)
-    hipLaunchKernelGGL(elsaa_k4_race_rank<uint8_t>, dim3(static_cast<unsigned>(units)), dim3(waves * 64), rlds,
-                       stream, static_cast<const uint8_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0, race_parts(g.N),
-                       buf.rperm, buf.rstart, buf.rpart, buf.tcnt, flagged_any(buf.flags, g.rows));
+    hipLaunchKernelGGL((elsaa_k4_race_rank<uint8_t, PT>), dim3(static_cast<unsigned>(units)), dim3(waves * 64),
+                       rlds, stream, static_cast<const uint8_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0,
+                       race_parts(g.N), rperm, buf.rstart, buf.rpart, buf.tcnt, flagged_any(buf.flags, g.rows));
   else
-    hipLaunchKernelGGL(elsaa_k4_race_rank<uint16_t>, dim3(static_cast<unsigned>(units)), dim3(waves * 64), rlds,
-                       stream, static_cast<const uint16_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0, race_parts(g.N),
-                       buf.rperm, buf.rstart, buf.rpart, buf.tcnt, flagged_any(buf.flags, g.rows));
+    hipLaunchKernelGGL((elsaa_k4_race_rank<uint16_t, PT>), dim3(static_cast<unsigned>(units)), dim3(waves * 64),
+                       rlds, stream, static_cast<const uint16_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0,
+                       race_parts(g.N), rperm, buf.rstart, buf.rpart, buf.tcnt, flagged_any(buf.flags, g.rows));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -409,26 +420,32 @@ hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &bu
   const long long waves_total = units * parts;
   const long long wgs = (waves_total + kGatherWaves - 1) / kGatherWaves;
   const dim3 grid(static_cast<unsigned>((wgs + kXcdCount - 1) / kXcdCount * kXcdCount));
+  auto gather = [&](auto vt, auto dc) {
+    using VT = decltype(vt);
+    constexpr int D = decltype(dc)::value;
+    hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT>), grid, dim3(kGatherWaves * 64), 0, stream,
+                       static_cast<const VT *>(v), rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts,
+                       waves_total, static_cast<VT *>(buf.tsum));
+  };
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
   if (g.bf16) {
-    if (g.D == 64)
-      hipLaunchKernelGGL((elsaa_k4_race_gather<uint16_t, 64>), grid, dim3(kGatherWaves * 64), 0, stream,
-                         static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts,
-                         waves_total, static_cast<uint16_t *>(buf.tsum));
-    else
-      hipLaunchKernelGGL((elsaa_k4_race_gather<uint16_t, 128>), grid, dim3(kGatherWaves * 64), 0, stream,
-                         static_cast<const uint16_t *>(v), buf.rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts,
-                         waves_total, static_cast<uint16_t *>(buf.tsum));
+    if (g.D == 64) gather(uint16_t{}, D64{});
+    else gather(uint16_t{}, D128{});
   } else {
-    if (g.D == 64)
-      hipLaunchKernelGGL((elsaa_k4_race_gather<float, 64>), grid, dim3(kGatherWaves * 64), 0, stream,
-                         static_cast<const float *>(v), buf.rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts, waves_total,
-                         static_cast<float *>(buf.tsum));
-    else
-      hipLaunchKernelGGL((elsaa_k4_race_gather<float, 128>), grid, dim3(kGatherWaves * 64), 0, stream,
-                         static_cast<const float *>(v), buf.rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts, waves_total,
-                         static_cast<float *>(buf.tsum));
+    if (g.D == 64) gather(float{}, D64{});
+    else gather(float{}, D128{});
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
+                             hipStream_t stream) {
+  // 16-bit key indices whenever they fit (the workspace holds 32-bit ones)
+  return g.N <= 65536 ? launch_race_build_pt<uint16_t>(g, v, buf, stream)
+                      : launch_race_build_pt<int32_t>(g, v, buf, stream);
 }
 
 }  // namespace elsaa
