@@ -678,23 +678,32 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) dst[kk] = piece(qs, qi, kk * 4 + g);
   };
+  // The query rows of tile t + 1 are loaded during tile t and waited for
+  // before tile t's output stores (the vector memory counter retires in issue
+  // order: a wait after the stores would wait for them too).  Every load is
+  // unconditional (the last tile loads its own rows again), so no branch
+  // merges a pending and a completed load.
   u16x8 qnext[D / 32];
   int qidx_next = 0;
+  if (t_begin < t_end) {
+    lds_barrier();  // tile 0's chunks staged
+    qidx_next = qidx_lds[qrow];
+    load_q(qnext, t_begin, qidx_next);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) asm volatile("" ::"v"(qnext[kk]) : "memory");
+  }
   for (long long t = t_begin; t < t_end; ++t) {
     const int m_idx = static_cast<int>(t - t_begin);
     const int c = chunk_of(t);
-    lds_barrier();  // tile m_idx's chunks staged
-    if (m_idx == 0) {
-      qidx_next = qidx_lds[qrow];
-      load_q(qnext, t, qidx_next);
-    }
+    if (m_idx > 0) lds_barrier();  // tile m_idx's chunks staged
     bf16x8 bq[D / 32];
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) bq[kk] = __builtin_bit_cast(bf16x8, qnext[kk]);
     const int qidx = qidx_next;
-    if (t + 1 < t_end) {  // the next tile's query rows, in flight during this tile
-      qidx_next = qidx_lds[((m_idx + 1) & 3) * W + qrow];
-      load_q(qnext, t + 1, qidx_next);
+    {  // the next tile's query rows, in flight during this tile
+      const bool more = t + 1 < t_end;
+      qidx_next = more ? qidx_lds[((m_idx + 1) & 3) * W + qrow] : qidx;
+      load_q(qnext, more ? t + 1 : t, qidx_next);
     }
     f32x4 o[D / 16], l_acc = {0.0f, 0.0f, 0.0f, 0.0f};
     float m = -INFINITY;
@@ -713,7 +722,9 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
     }
     const long long seg = seg_of(t);
     const float l_tot = l_acc[0];
-    const float inv = 1.0f / l_tot;
+    float inv = 1.0f / l_tot;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) asm volatile("" : "+v"(inv) : "v"(qnext[kk]) : "memory");
     uint16_t *orow = o_s + (seg + qidx) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
