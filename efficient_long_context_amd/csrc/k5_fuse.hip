@@ -314,6 +314,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
       }
       t[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, off, l * nb * kRowBytes, 0));
     }
+    // the next step's streamed inputs
+    load_stream(step + kQPS < per_wave ? i_begin + step + kQPS : i_begin + step, os_next, lse_next, xg_next);
     // sparse output and gate inputs of this step
     float osv[kCols];
     if constexpr (kES == 2) {
@@ -363,9 +365,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
       }
     }
 
-    // the next step's streamed inputs
-    load_stream(step + kQPS < per_wave ? i_begin + step + kQPS : i_begin + step, os_next, lse_next, xg_next);
-
     float a0 = 0.0f, a1 = 0.0f;
     if (gate_fast) {
 #pragma unroll
@@ -401,6 +400,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
       o_lr[k] = num[k] * rz;
       yv[k] = __builtin_fmaf(ws, osv[k], g_lr * o_lr[k]);
     }
+    // The next step's streamed inputs and codes are waited for here, before
+    // this step's store: the vector memory counter retires in issue order,
+    // so a wait for them after the store would also wait for the store.
+    asm volatile("" : "+v"(yv[0]) : "v"(os_next), "v"(xg_next), "v"(lse_next) : "memory");
+#pragma unroll
+    for (int k = 0; k < kCW; ++k) asm volatile("" : "+v"(yv[0]) : "v"(cw[k]) : "memory");
     const uint32_t yo = static_cast<uint32_t>(i) * kRowBytes + vbase;
     if constexpr (kES == 2) {
       __builtin_amdgcn_raw_buffer_store_b128(
