@@ -19,6 +19,10 @@ LIB_PATH = os.path.join(_PKG, "libelsaa.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE = 0, -1, -2, -3, -4
 DTYPE_F32, DTYPE_BF16 = 0, 1
+ABI_VERSION = 2
+# elsaa_variant_t: the operator, the ablation with alpha fixed to one, and the
+# two single-branch models
+VARIANTS = {"full": 0, "no_alpha": 1, "race_only": 2, "sparse_only": 3}
 
 # Every symbol include/elsaa.h declares.
 EXPORTS = ("elsaa_validate", "elsaa_workspace_bytes", "elsaa_forward", "elsaa_status_str",
@@ -39,7 +43,7 @@ class ElsaaParams(ctypes.Structure):
         ("d", ctypes.c_int32), ("d_gate", ctypes.c_int32),
         ("sort_bits", ctypes.c_int32), ("chunk", ctypes.c_int32),
         ("race_tables", ctypes.c_int32), ("race_bits", ctypes.c_int32),
-        ("lambda_", ctypes.c_float), ("dtype", ctypes.c_int),
+        ("lambda_", ctypes.c_float), ("dtype", ctypes.c_int), ("variant", ctypes.c_int),
         ("gate_w", ctypes.c_void_p), ("gate_b", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p), ("aux", ctypes.POINTER(ElsaaAux)),
@@ -93,13 +97,14 @@ def last_error() -> str:
 
 
 def make_params(B, H, N, d, d_gate, *, sort_bits, chunk, race_tables, race_bits, lam,
-                dtype=DTYPE_BF16, gate_w_ptr=0, gate_b_ptr=0, workspace_ptr=0,
+                dtype=DTYPE_BF16, variant=0, gate_w_ptr=0, gate_b_ptr=0, workspace_ptr=0,
                 workspace_bytes=0, stream_ptr=0, aux=None, stage_events=None) -> ElsaaParams:
     p = ElsaaParams()
     p.B, p.H, p.N, p.d, p.d_gate = B, H, N, d, d_gate
     p.sort_bits, p.chunk, p.race_tables, p.race_bits = sort_bits, chunk, race_tables, race_bits
     p.lambda_ = lam
     p.dtype = dtype
+    p.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     p.gate_w, p.gate_b = gate_w_ptr or None, gate_b_ptr or None
     p.workspace, p.workspace_bytes = workspace_ptr or None, workspace_bytes
     p.stream = stream_ptr or None
@@ -136,7 +141,7 @@ class Forward:
     """
 
     def __init__(self, *, B, H, N, d, d_gate=64, sort_bits, chunk, race_tables, race_bits,
-                 lam=1.0, dtype="bf16", device=None, aux=False):
+                 lam=1.0, dtype="bf16", variant="full", device=None, aux=False):
         import torch
         self.torch = torch
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
@@ -144,7 +149,7 @@ class Forward:
         self.dtype_code = DTYPE_BF16 if dtype == "bf16" else DTYPE_F32
         self.shape = dict(B=B, H=H, N=N, d=d, d_gate=d_gate)
         self.cfg = dict(sort_bits=sort_bits, chunk=chunk, race_tables=race_tables,
-                        race_bits=race_bits, lam=float(lam))
+                        race_bits=race_bits, lam=float(lam), variant=variant)
         probe = make_params(B, H, N, d, d_gate, dtype=self.dtype_code, gate_w_ptr=1, gate_b_ptr=1,
                             **self.cfg)
         st = validate(probe)
@@ -217,13 +222,13 @@ class Forward:
 
 
 def forward(q, k, v, x_gate, hyperplanes, gate_w, gate_b, *, sort_bits, chunk, race_tables,
-            race_bits, lam=1.0, aux=False):
+            race_bits, lam=1.0, variant="full", aux=False):
     """One-shot forward pass (allocates workspace and output)."""
     import torch
     B, H, N, d = q.shape
     dtype = "bf16" if q.dtype == torch.bfloat16 else "fp32"
     f = Forward(B=B, H=H, N=N, d=d, d_gate=x_gate.shape[-1], sort_bits=sort_bits, chunk=chunk,
                 race_tables=race_tables, race_bits=race_bits, lam=lam, dtype=dtype,
-                device=q.device, aux=aux)
+                variant=variant, device=q.device, aux=aux)
     out = f(q, k, v, x_gate, hyperplanes, gate_w, gate_b)
     return (out, f.aux) if aux else out

@@ -8,6 +8,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -61,6 +62,8 @@ int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
     return fail(ELSAA_ERR_INVALID_ARG, "lambda must be finite and >= 0");
   if (p->dtype != ELSAA_DTYPE_F32 && p->dtype != ELSAA_DTYPE_BF16)
     return fail(ELSAA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(p->dtype));
+  if (p->variant < ELSAA_VARIANT_FULL || p->variant > ELSAA_VARIANT_SPARSE_ONLY)
+    return fail(ELSAA_ERR_INVALID_ARG, "unknown variant %d", static_cast<int>(p->variant));
   if (!p->gate_w || !p->gate_b) return fail(ELSAA_ERR_INVALID_ARG, "gate_w / gate_b is NULL");
   // limits of this implementation
   if (p->d != 64 && p->d != 128) return fail(ELSAA_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", p->d);
@@ -76,6 +79,15 @@ int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
   if (p->N > (1 << 24)) return fail(ELSAA_ERR_UNSUPPORTED, "N must be <= 2^24 (got %d)", p->N);
   const long long BH = static_cast<long long>(p->B) * p->H;
   if (BH > 32767) return fail(ELSAA_ERR_UNSUPPORTED, "B * H must be <= 32767 (got %lld)", BH);
+  // The kernels address one head's rows (and one batch's gate inputs) through
+  // 32-bit byte offsets and buffer resources with 32-bit sizes.
+  const long long es = p->dtype == ELSAA_DTYPE_BF16 ? 2 : 4;
+  const long long head_bytes = static_cast<long long>(p->N) * p->d * es;
+  const long long gate_bytes = static_cast<long long>(p->N) * p->d_gate * es;
+  if (head_bytes >= (1ll << 31) || gate_bytes >= (1ll << 31))
+    return fail(ELSAA_ERR_UNSUPPORTED,
+                "per-(b, h) tensors must be below 2^31 bytes (N * d * elem = %lld, N * d_gate * elem = %lld)",
+                head_bytes, gate_bytes);
 
   g->B = p->B; g->H = p->H; g->N = p->N; g->D = p->d; g->DG = p->d_gate;
   g->ns = p->sort_bits; g->w = p->chunk; g->L = p->race_tables; g->P = p->race_bits;
@@ -87,8 +99,12 @@ int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
   g->rcb = p->race_bits <= 8 ? 1 : 2;
   g->sort_tiles = (p->N + elsaa::kSortTile - 1) / elsaa::kSortTile;
   g->bf16 = p->dtype == ELSAA_DTYPE_BF16;
-  g->lambda = p->lambda;
+  g->lambda = p->variant == ELSAA_VARIANT_NO_ALPHA ? 0.0f : p->lambda;
   g->cus = 256;
+  g->variant = static_cast<int>(p->variant);
+  g->run_sparse = p->variant != ELSAA_VARIANT_RACE_ONLY;
+  g->run_race = p->variant != ELSAA_VARIANT_SPARSE_ONLY;
+  g->identity = p->sort_bits == 0;
   return ELSAA_OK;
 }
 
@@ -120,6 +136,21 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   return off;
 }
 
+__global__ void fill_zero_bytes(uint8_t *__restrict__ p, long long n) {
+  const long long i = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) * 16;
+  if (i + 16 <= n) {
+    *reinterpret_cast<elsaa::u32x4 *>(p + i) = (elsaa::u32x4){0u, 0u, 0u, 0u};
+  } else {
+    for (long long j = i; j < n; ++j) p[j] = 0;
+  }
+}
+
+// perm[s][r] = r: the stable order of one bucket (sort_bits = 0).
+__global__ void identity_perm(int32_t *__restrict__ perm, long long n, int N) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) perm[i] = static_cast<int32_t>(i % N);
+}
+
 __global__ void widen_bf16(const uint16_t *__restrict__ src, float *__restrict__ dst, long long n) {
   const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
   if (i < n) dst[i] = elsaa::bf16_bits_to_f32(src[i]);
@@ -133,27 +164,46 @@ __global__ void codes_to_row_major(const CT *__restrict__ src, CT *__restrict__ 
 }
 
 hipError_t copy_aux(const elsaa::Geometry &g, const elsaa::Buffers &buf, const elsaa_aux_t *aux,
-                    hipStream_t s) {
+                    const void *out, hipStream_t s) {
   const size_t rows = static_cast<size_t>(g.rows);
   const size_t es = g.bf16 ? 2 : 4;
+  const bool sp = g.run_sparse, rc = g.run_race;
+  const bool sorted = sp && !g.identity;  // a sort ran: codes and permutations are in the workspace
   struct Item { void *dst; const void *src; size_t bytes; };
   const Item items[] = {
-      {aux->sort_code_q, buf.scode, rows * 2},
-      {aux->sort_code_k, buf.scode + rows, rows * 2},
-      {aux->race_code_q, buf.rcode, rows * g.L * g.rcb},
-      {aux->perm_q, buf.perm, rows * 4},
-      {aux->perm_k, buf.perm + rows, rows * 4},
-      {aux->race_sum, g.bf16 ? nullptr : buf.tsum, static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * 4},
-      {aux->race_cnt, buf.tcnt, static_cast<size_t>(g.BH) * g.L * g.nb_race * 4},
-      {aux->o_sparse, buf.o_s, rows * g.D * es},
-      {aux->lse_s, buf.lse, rows * 4},
+      {sorted ? aux->sort_code_q : nullptr, buf.scode, rows * 2},
+      {sorted ? aux->sort_code_k : nullptr, buf.scode + rows, rows * 2},
+      {rc ? aux->race_code_q : nullptr, buf.rcode, rows * g.L * g.rcb},
+      {sorted ? aux->perm_q : nullptr, buf.perm, rows * 4},
+      {sorted ? aux->perm_k : nullptr, buf.perm + rows, rows * 4},
+      {rc ? aux->race_sum : nullptr, g.bf16 ? nullptr : buf.tsum,
+       static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * 4},
+      {rc ? aux->race_cnt : nullptr, buf.tcnt, static_cast<size_t>(g.BH) * g.L * g.nb_race * 4},
+      // SPARSE_ONLY writes o_s as the output itself
+      {sp ? aux->o_sparse : nullptr, rc ? buf.o_s : out, rows * g.D * es},
+      {sp ? aux->lse_s : nullptr, buf.lse, rows * 4},
   };
   for (const Item &it : items) {
     if (!it.dst || !it.src) continue;
     const hipError_t e = hipMemcpyAsync(it.dst, it.src, it.bytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
-  if (aux->race_code_k) {
+  if (sp && g.identity) {  // one bucket: zero codes, identity permutations
+    const long long n = g.rows;
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+    for (uint16_t *c : {aux->sort_code_q, aux->sort_code_k}) {
+      if (!c) continue;
+      const hipError_t e = elsaa::launch_fill_zero(c, rows * 2, s);
+      if (e != hipSuccess) return e;
+    }
+    for (int32_t *pm : {aux->perm_q, aux->perm_k}) {
+      if (!pm) continue;
+      hipLaunchKernelGGL(identity_perm, grid, dim3(256), 0, s, pm, n, g.N);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (rc && aux->race_code_k) {
     const long long n = g.rows * g.L;
     const void *src = static_cast<const char *>(buf.rcode) + rows * g.L * g.rcb;
     if (g.rcb == 1)
@@ -166,7 +216,7 @@ hipError_t copy_aux(const elsaa::Geometry &g, const elsaa::Buffers &buf, const e
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (g.bf16 && aux->race_sum) {  // bfloat16 tables widen to the binary32 aux layout
+  if (rc && g.bf16 && aux->race_sum) {  // bfloat16 tables widen to the binary32 aux layout
     const long long n = static_cast<long long>(g.BH) * g.L * g.nb_race * g.D;
     hipLaunchKernelGGL(widen_bf16, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
                        static_cast<const uint16_t *>(buf.tsum), aux->race_sum, n);
@@ -175,7 +225,28 @@ hipError_t copy_aux(const elsaa::Geometry &g, const elsaa::Buffers &buf, const e
   return hipSuccess;
 }
 
+// ELSAA_DEBUG (read once): synchronise and check after every stage.
+bool debug_mode() {
+  static const bool on = [] {
+    const char *v = getenv("ELSAA_DEBUG");
+    return v != nullptr && atoi(v) != 0;
+  }();
+  return on;
+}
+
 }  // namespace
+
+namespace elsaa {
+
+hipError_t launch_fill_zero(void *p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const long long pieces = static_cast<long long>((n + 15) / 16);
+  hipLaunchKernelGGL(fill_zero_bytes, dim3(static_cast<unsigned>((pieces + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<uint8_t *>(p), static_cast<long long>(n));
+  return hipGetLastError();
+}
+
+}  // namespace elsaa
 
 extern "C" {
 
@@ -241,28 +312,56 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
   if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
 
   // stage_events[2i] / [2i+1] bracket stage i (hash, sort, RACE build, chunk
-  // attention, fusion)
+  // attention, fusion); a stage a variant skips is an empty interval
   void *const *ev = params->stage_events;
   auto mark = [&](int i) -> hipError_t {
     return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
   };
+  const bool dbg = debug_mode();
+  const char *stage = "";
+  auto run = [&](const char *name, auto &&launch) {
+    if (e != hipSuccess) return;
+    stage = name;
+    e = launch();
+    if (e == hipSuccess && dbg) e = hipStreamSynchronize(s);
+    if (e == hipSuccess && dbg) e = hipGetLastError();
+  };
+  // Planes of the stages that run: RACE_ONLY skips the sort planes, and
+  // SPARSE_ONLY hashes only them (no RACE codes are made).
+  elsaa::Geometry gh = g;
+  const void *planes = hyperplanes;
+  if (!g.run_sparse) {
+    gh.ns = 0;
+    gh.R = g.L * g.P;
+    if (planes) planes = static_cast<const char *>(planes) + static_cast<size_t>(g.ns) * g.D * (g.bf16 ? 2 : 4);
+  } else if (!g.run_race) {
+    gh.L = 1;
+    gh.P = 0;
+    gh.rcb = 1;
+    gh.R = g.ns;
+  }
+  const bool need_hash = g.run_race || !g.identity;
   e = mark(0);
-  if (e == hipSuccess) e = elsaa::launch_hash(g, q, k, hyperplanes, buf, s);
+  if (need_hash) run("hash", [&] { return elsaa::launch_hash(gh, q, k, planes, buf, s); });
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = mark(4);
-  if (e == hipSuccess) e = elsaa::launch_race_build(g, v, buf, s);
+  if (g.run_race) run("RACE build", [&] { return elsaa::launch_race_build(g, v, buf, s); });
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = elsaa::launch_sort(g, buf, s);
+  if (g.run_sparse && !g.identity) run("sort", [&] { return elsaa::launch_sort(g, buf, s); });
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = mark(6);
-  if (e == hipSuccess) e = elsaa::launch_chunk_attention(g, q, k, v, buf, s);
+  if (g.run_sparse)
+    run("chunk attention",
+        [&] { return elsaa::launch_chunk_attention(g, q, k, v, buf, g.run_race ? buf.o_s : out, s); });
   if (e == hipSuccess) e = mark(7);
   if (e == hipSuccess) e = mark(8);
-  if (e == hipSuccess) e = elsaa::launch_fuse(g, x_gate, params->gate_w, params->gate_b, buf, params->aux, out, s);
+  if (g.run_race)
+    run("fusion",
+        [&] { return elsaa::launch_fuse(g, x_gate, params->gate_w, params->gate_b, buf, params->aux, out, s); });
   if (e == hipSuccess) e = mark(9);
-  if (e == hipSuccess && params->aux) e = copy_aux(g, buf, params->aux, s);
-  if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
+  if (params->aux) run("aux outputs", [&] { return copy_aux(g, buf, params->aux, out, s); });
+  if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error in stage '%s': %s", stage, hipGetErrorString(e));
   g_last_error[0] = '\0';
   return ELSAA_OK;
 }

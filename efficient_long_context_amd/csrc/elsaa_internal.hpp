@@ -28,6 +28,10 @@ struct Geometry {
   bool bf16;
   float lambda;
   int cus;       // compute units of the device (set at launch; 256 otherwise)
+  int variant;   // elsaa_variant_t
+  bool run_sparse;  // the Sort-LSH branch runs (not RACE_ONLY)
+  bool run_race;    // the RACE branch runs (not SPARSE_ONLY)
+  bool identity;    // sort_bits == 0: the stable order is the original one, no sort
 };
 
 // Device buffers carved out of the caller's workspace.
@@ -72,11 +76,15 @@ __host__ __device__ __forceinline__ int race_parts(int N) { return (N + kGatherP
 constexpr int kSortTile = 2048;         // elements per sort tile (4 waves x 8 rounds x 64)
 
 // Launchers (each enqueues on `stream`, returns hipError_t of the launch).
+// Zero bytes [p, p + n) (p 16-byte aligned) with a fill kernel: no
+// hipMemsetAsync, so a caller may capture the forward pass into a graph.
+hipError_t launch_fill_zero(void *p, size_t n, hipStream_t stream);
 hipError_t launch_hash(const Geometry &g, const void *q, const void *k, const void *planes,
                        const Buffers &buf, hipStream_t stream);
 hipError_t launch_sort(const Geometry &g, const Buffers &buf, hipStream_t stream);
+// o_s goes to `o_s` (buf.o_s, or the output itself for SPARSE_ONLY).
 hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *k,
-                                  const void *v, const Buffers &buf, hipStream_t stream);
+                                  const void *v, const Buffers &buf, void *o_s, hipStream_t stream);
 hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
                              hipStream_t stream);
 hipError_t launch_fuse(const Geometry &g, const void *x_gate, const float *gate_w,

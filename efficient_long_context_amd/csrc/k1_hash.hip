@@ -490,7 +490,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
       if (valid && g == 0) {
-        scode[out_row] = static_cast<uint16_t>(byte0 & ((1u << ns) - 1u));
+        if (ns > 0) scode[out_row] = static_cast<uint16_t>(byte0 & ((1u << ns) - 1u));
         // a projection binary64 could not decide: the exact pass redoes the row
         flags[out_row] = ((undecided_mask >> r16) & 0x0001000100010001ull) ? 1 : 0;
       }
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
     };
     if (valid) {
       if (g == 0) {
-        scode[out_row] = static_cast<uint16_t>(words[0] & ((1u << ns) - 1u));  // ns <= 12
+        if (ns > 0) scode[out_row] = static_cast<uint16_t>(words[0] & ((1u << ns) - 1u));  // ns <= 12
         flags[out_row] = ((undecided_mask >> r16) & 0x0001000100010001ull) ? 1 : 0;
       }
       for (int l = g; l < L; l += 4) {
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_fixup(
         const unsigned long long mm = m[wd >> 1];
         return (wd & 1) ? static_cast<uint32_t>(mm >> 32) : static_cast<uint32_t>(mm);
       };
-      if (lane == 0) scode[r] = static_cast<uint16_t>(bit_field(get, 0, ns));
+      if (lane == 0 && ns > 0) scode[r] = static_cast<uint16_t>(bit_field(get, 0, ns));
       for (int l = lane; l < L; l += 64) {
         const uint32_t c = bit_field(get, ns + l * P, P);
         const long long ci = race_code_index(r >= rows ? 1 : 0, r >= rows ? r - rows : r, l, rows, L);
@@ -691,7 +691,6 @@ __global__ __launch_bounds__(256) void elsaa_k1_hash_f32(
       code = 0;
     }
   }
-  if (ns == 0) scode[out_row] = 0;
   if (P == 0) {
     for (int l = 0; l < L; ++l) {
       const long long ci = race_code_index(tensor, row, l, rows, L);
@@ -739,6 +738,9 @@ void dispatch_npt(int npt, const Geometry &g, const void *q, const void *k, cons
 
 hipError_t launch_hash(const Geometry &g, const void *q, const void *k, const void *planes,
                        const Buffers &buf, hipStream_t stream) {
+  // No planes (sort_bits = race_bits = 0): every RACE code is zero, and with
+  // one sort bucket nothing reads sort codes.  The planes pointer may be NULL.
+  if (g.R == 0) return launch_fill_zero(buf.rcode, 2 * static_cast<size_t>(g.rows) * g.L * g.rcb, stream);
   if (g.bf16) {
     const int npt = g.R > 0 ? (g.R + 15) / 16 : 1;  // R <= 256: at most 16 plane tiles
     if (g.D == 64) dispatch_npt<64>(npt, g, q, k, planes, buf, stream);

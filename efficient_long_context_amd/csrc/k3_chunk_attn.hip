@@ -16,16 +16,31 @@
 // (padded rows), V transposed so the PV operand reads contiguous keys -- and
 // the next block's rows are loaded into registers while the current one is
 // used.  S^T = K Q^T and O^T = V^T P^T run on 16x16x32 bf16 MFMA with fp32
-// accumulation; the softmax is online in the exp2 domain (v_exp_f32 directly:
-// every argument is <= 0), P is rounded to bf16 for the PV product and the row
-// sum is taken from the fp32 P.  Workgroups of neighbouring tiles (which share
-// key blocks) are mapped to the same XCD.
+// accumulation; the softmax is online in the exp2 domain (v_exp_f32 directly)
+// with a lazily moved reference point, so an exponent argument can reach +8
+// (see attend_stage); P is rounded to bf16 for the PV product and the row sum
+// is the sum of those bf16 weights (an MFMA of an all-ones operand with P).
+// Workgroups of neighbouring tiles (which share key blocks) are mapped to the
+// same XCD.  With one sort bucket (sort_bits = 0) the sorted order is the
+// original one: the kIdent instances index tokens directly and read no
+// permutation.
 #include "elsaa_internal.hpp"
 
 namespace elsaa {
 namespace {
 
 constexpr int kKBlock = 64;
+
+// Original index of sorted rank r of the segment starting at row `seg`: the
+// permutation's entry, or r itself when the order is the identity.
+template <bool kIdent>
+__device__ __forceinline__ int sorted_index(const int32_t *__restrict__ perm, long long seg, int r) {
+  if constexpr (kIdent) {
+    return r;
+  } else {
+    return perm[seg + r];
+  }
+}
 
 
 
@@ -189,7 +204,7 @@ __device__ __forceinline__ void attend_blocks(const uint16_t *const (&Kb)[NBLK],
   }
 }
 
-template <int D, int QT, int NB>
+template <int D, int QT, int NB, bool kIdent>
 __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N, int w,
@@ -217,10 +232,9 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
   const int lo = c > 0 ? (c - 1) * w : 0;
   const int hi = (c + 1) * w;
   const long long seg = bh * N;
-  const int32_t *pk = perm_k + seg;
 
   // Q^T operand: lane holds query r16 of this wave, d-slice g*8 .. +7 of each 32.
-  const int qidx = perm_q[seg + r0 + wave * 16 + r16];
+  const int qidx = sorted_index<kIdent>(perm_q, seg, r0 + wave * 16 + r16);
   const uint16_t *qrow = q + (seg + qidx) * D;
   bf16x8 bq[1][D / 32];
 #pragma unroll
@@ -250,14 +264,14 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
     for (int p = 0; p < kKPer; ++p) {
       int j = (tid + p * kThreads) / (D / 8);
       j = j < nkeys ? j : nkeys - 1;  // clamped: rows past the stage are reloads, not used
-      kj[p] = pk[s0 + j];
+      kj[p] = sorted_index<kIdent>(perm_k, seg, s0 + j);
     }
 #pragma unroll
     for (int p = 0; p < kVPer; ++p) {
       int jp = (tid + p * kThreads) % (kKeys / 2);
       jp = 2 * jp + 1 < nkeys ? jp : nkeys / 2 - 1;
-      v0[p] = pk[s0 + 2 * jp];
-      v1[p] = pk[s0 + 2 * jp + 1];
+      v0[p] = sorted_index<kIdent>(perm_k, seg, s0 + 2 * jp);
+      v1[p] = sorted_index<kIdent>(perm_k, seg, s0 + 2 * jp + 1);
     }
     u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer];
 #pragma unroll
@@ -320,7 +334,7 @@ __global__ __launch_bounds__(QT * 4) void elsaa_k3_chunk_attn_bf16(
 // key indices.  One barrier per job separates the two; it orders LDS only, so
 // loads stay in flight across it.  Consumers also load the next tile's query
 // rows one tile ahead.
-template <int D, int NB>
+template <int D, int NB, bool kIdent>
 __global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_pc(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N, int w,
@@ -367,20 +381,20 @@ __global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_pc(
     int kj[kKPer], v0[kVPer], v1[kVPer];  // key indices of the next job to load
     u16x8 kreg[kKPer], vreg0[kVPer], vreg1[kVPer];
     auto load_idx = [&](const Job &j) {
-      const int32_t *pk = perm_k + (j.tile / tiles_per_seg) * N;
+      const long long pseg = (j.tile / tiles_per_seg) * N;
       const int nkeys = j.hi - j.s0 < kKeys ? j.hi - j.s0 : kKeys;
 #pragma unroll
       for (int p = 0; p < kKPer; ++p) {
         int r = (ptid + p * kPThreads) / (D / 8);
         r = r < nkeys ? r : nkeys - 1;  // rows past the stage are reloads, never used
-        kj[p] = pk[j.s0 + r];
+        kj[p] = sorted_index<kIdent>(perm_k, pseg, j.s0 + r);
       }
 #pragma unroll
       for (int p = 0; p < kVPer; ++p) {
         int jp = (ptid + p * kPThreads) % (kKeys / 2);
         jp = 2 * jp + 1 < nkeys ? jp : nkeys / 2 - 1;
-        v0[p] = pk[j.s0 + 2 * jp];
-        v1[p] = pk[j.s0 + 2 * jp + 1];
+        v0[p] = sorted_index<kIdent>(perm_k, pseg, j.s0 + 2 * jp);
+        v1[p] = sorted_index<kIdent>(perm_k, pseg, j.s0 + 2 * jp + 1);
       }
     };
     auto load_rows = [&](const Job &j) {
@@ -444,7 +458,8 @@ __global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_pc(
   // query rows: group qg's query of this lane, d-slice g*8 .. +7 of each 32
   auto q_index = [&](long long t, int qg) -> int {
     const long long tt = t < t_end ? t : t_end - 1;
-    return perm_q[(tt / tiles_per_seg) * N + (tt % tiles_per_seg) * QT + (wave * QG + qg) * 16 + r16];
+    return sorted_index<kIdent>(perm_q, (tt / tiles_per_seg) * N,
+                                static_cast<int>(tt % tiles_per_seg) * QT + (wave * QG + qg) * 16 + r16);
   };
   auto load_q = [&](long long t, int qi, bf16x8 (&dst)[D / 32]) {
     const long long tt = t < t_end ? t : t_end - 1;
@@ -528,6 +543,7 @@ __global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_pc(
 // index slots.  Waves 0-7 compute 16 queries each; they load their query rows
 // for the next tile while computing the current one.  One LDS-only barrier
 // per tile.
+template <bool kIdent>
 __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N,
@@ -553,8 +569,8 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
   if (t_begin >= t_end) return;  // whole workgroup
   auto chunk_of = [&](long long t) { return static_cast<int>(t % tiles_per_seg); };
   auto seg_of = [&](long long t) { return (t / tiles_per_seg) * N; };
-  // piece of a row at a 32-bit byte offset from its segment's first row (a
-  // segment is at most 2^18 rows of 128 bytes): a uniform base plus one
+  // piece of a row at a 32-bit byte offset from its segment's first row (the
+  // host keeps a segment's rows below 2^31 bytes): a uniform base plus one
   // offset register per load
   auto piece = [](const uint16_t *base, int row, int ch) {
     const uint32_t off = static_cast<uint32_t>(row) * (D * 2) + static_cast<uint32_t>(ch) * 16;
@@ -576,13 +592,13 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
     // key indices of chunk c and query indices of tile t (whose chunk is c)
     auto load_idx = [&](Idx &ix, long long t, int c, bool with_q) {
       const long long seg = seg_of(t);
-      const int32_t *pk = perm_k + seg + c * W;
 #pragma unroll
-      for (int p = 0; p < kKPer; ++p) ix.kj[p] = pk[(ptid + p * kPThreads) / (D / 8)];
+      for (int p = 0; p < kKPer; ++p) ix.kj[p] = sorted_index<kIdent>(perm_k, seg, c * W + (ptid + p * kPThreads) / (D / 8));
       static_assert(kPThreads % (W / 2) == 0, "every V piece of a thread is one key pair");
-      ix.v0 = pk[2 * (ptid % (W / 2))];
-      ix.v1 = pk[2 * (ptid % (W / 2)) + 1];
-      if (with_q) ix.qj = perm_q[seg + c * W + ptid % W];  // threads from W on: a repeat, not stored
+      ix.v0 = sorted_index<kIdent>(perm_k, seg, c * W + 2 * (ptid % (W / 2)));
+      ix.v1 = sorted_index<kIdent>(perm_k, seg, c * W + 2 * (ptid % (W / 2)) + 1);
+      // threads from W on: a repeat, not stored
+      if (with_q) ix.qj = sorted_index<kIdent>(perm_q, seg, c * W + ptid % W);
     };
     auto load_rows = [&](Rows &r, const Idx &ix, long long t) {
       const long long seg = seg_of(t);
@@ -754,13 +770,13 @@ __global__ __launch_bounds__(128) void elsaa_k3_chunk_attn_f32(
   const int c = rank / w;
   const int lo = c > 0 ? (c - 1) * w : 0;
   const int hi = (c + 1) * w;
-  const int qidx = perm_q[seg + rank];
+  const int qidx = perm_q ? perm_q[seg + rank] : rank;  // no permutation: the identity
   const float *qr = q + (seg + qidx) * D;
   float acc[D];
   for (int e = 0; e < D; ++e) acc[e] = 0.0f;
   float m = -INFINITY, l = 0.0f;
   for (int t = lo; t < hi; ++t) {
-    const int kidx = perm_k[seg + t];
+    const int kidx = perm_k ? perm_k[seg + t] : t;
     const float *kr = k + (seg + kidx) * D;
     float dot = 0.0f;
     for (int e = 0; e < D; ++e) dot = __builtin_fmaf(qr[e], kr[e], dot);
@@ -784,26 +800,27 @@ constexpr size_t attn_lds_bytes(int D, int NB) {
   return (static_cast<size_t>(NB) * kKBlock * (D + 8) + static_cast<size_t>(D) * (NB * kKBlock + 4)) * 2;
 }
 
-template <int D, int QT, int NB>
+template <int D, int QT, int NB, bool kIdent>
 hipError_t launch_bf16(const Geometry &g, const void *q, const void *k, const void *v,
-                       const Buffers &buf, float scale_log2, hipStream_t stream) {
+                       const int32_t *pq, const int32_t *pk, void *o_s, float *lse, float scale_log2,
+                       hipStream_t stream) {
   const int tiles_per_seg = g.N / QT;
   const long long n_tiles = static_cast<long long>(tiles_per_seg) * g.BH;
   const long long grid = (n_tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
-  hipLaunchKernelGGL((elsaa_k3_chunk_attn_bf16<D, QT, NB>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((elsaa_k3_chunk_attn_bf16<D, QT, NB, kIdent>), dim3(static_cast<unsigned>(grid)),
                      dim3(QT * 4), attn_lds_bytes(D, NB), stream, static_cast<const uint16_t *>(q),
-                     static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), buf.perm,
-                     buf.perm + g.rows, g.N, g.w, tiles_per_seg, static_cast<int>(n_tiles),
-                     scale_log2, static_cast<uint16_t *>(buf.o_s), buf.lse);
+                     static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), pq, pk, g.N, g.w,
+                     tiles_per_seg, static_cast<int>(n_tiles), scale_log2, static_cast<uint16_t *>(o_s), lse);
   return hipGetLastError();
 }
 
 // LDS bytes of the pipelined kernel: two stage buffers.
 constexpr size_t attn_pc_lds_bytes(int D, int NB) { return 2 * attn_lds_bytes(D, NB); }
 
-template <int D, int NB>
+template <int D, int NB, bool kIdent>
 hipError_t launch_bf16_pc(const Geometry &g, const void *q, const void *k, const void *v,
-                          const Buffers &buf, float scale_log2, hipStream_t stream) {
+                          const int32_t *pq, const int32_t *pk, void *o_s, float *lse, float scale_log2,
+                          hipStream_t stream) {
   const int tiles_per_seg = g.N / 128;
   const long long n_tiles = static_cast<long long>(tiles_per_seg) * g.BH;
   // one workgroup per compute unit (two stage buffers fill its LDS), a
@@ -811,59 +828,66 @@ hipError_t launch_bf16_pc(const Geometry &g, const void *q, const void *k, const
   long long wgs = (g.cus + kXcdCount - 1) / kXcdCount * kXcdCount;
   if (wgs > n_tiles) wgs = (n_tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
   const long long tiles_per_wg = (n_tiles + wgs - 1) / wgs;
-  hipLaunchKernelGGL((elsaa_k3_chunk_attn_pc<D, NB>), dim3(static_cast<unsigned>(wgs)), dim3(512),
+  hipLaunchKernelGGL((elsaa_k3_chunk_attn_pc<D, NB, kIdent>), dim3(static_cast<unsigned>(wgs)), dim3(512),
                      attn_pc_lds_bytes(D, NB), stream, static_cast<const uint16_t *>(q),
-                     static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), buf.perm,
-                     buf.perm + g.rows, g.N, g.w, tiles_per_seg, n_tiles, tiles_per_wg, scale_log2,
-                     static_cast<uint16_t *>(buf.o_s), buf.lse);
+                     static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), pq, pk, g.N, g.w,
+                     tiles_per_seg, n_tiles, tiles_per_wg, scale_log2, static_cast<uint16_t *>(o_s), lse);
   return hipGetLastError();
 }
 
+template <bool kIdent>
 hipError_t launch_bf16_slide(const Geometry &g, const void *q, const void *k, const void *v,
-                             const Buffers &buf, float scale_log2, hipStream_t stream) {
+                             const int32_t *pq, const int32_t *pk, void *o_s, float *lse, float scale_log2,
+                             hipStream_t stream) {
   const int tiles_per_seg = g.N / 128;
   const long long n_tiles = static_cast<long long>(tiles_per_seg) * g.BH;
   long long wgs = (g.cus + kXcdCount - 1) / kXcdCount * kXcdCount;
   if (wgs > n_tiles) wgs = (n_tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
   const long long tiles_per_wg = (n_tiles + wgs - 1) / wgs;
-  hipLaunchKernelGGL(elsaa_k3_chunk_attn_slide, dim3(static_cast<unsigned>(wgs)), dim3(768),
-                     attn_slide_lds_bytes(), stream,
-                     static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                     static_cast<const uint16_t *>(v), buf.perm, buf.perm + g.rows, g.N, tiles_per_seg,
-                     n_tiles, tiles_per_wg, scale_log2, static_cast<uint16_t *>(buf.o_s), buf.lse);
+  hipLaunchKernelGGL((elsaa_k3_chunk_attn_slide<kIdent>), dim3(static_cast<unsigned>(wgs)), dim3(768),
+                     attn_slide_lds_bytes(), stream, static_cast<const uint16_t *>(q),
+                     static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), pq, pk, g.N,
+                     tiles_per_seg, n_tiles, tiles_per_wg, scale_log2, static_cast<uint16_t *>(o_s), lse);
   return hipGetLastError();
+}
+
+template <bool kIdent>
+hipError_t launch_bf16_any(const Geometry &g, const void *q, const void *k, const void *v, const int32_t *pq,
+                           const int32_t *pk, void *o_s, float *lse, float scale_log2, hipStream_t stream) {
+  // 128-query tiles when w allows; key stages of 4 blocks (d = 64: the whole
+  // 256-key window of w = 128) or 2, keeping LDS <= 72 KB (two workgroups
+  // per CU)
+  const bool wide = g.w % 128 == 0;
+  if (g.D == 64 && g.w == 128) return launch_bf16_slide<kIdent>(g, q, k, v, pq, pk, o_s, lse, scale_log2, stream);
+  if (g.D == 64)
+    return wide ? launch_bf16_pc<64, 4, kIdent>(g, q, k, v, pq, pk, o_s, lse, scale_log2, stream)
+                : launch_bf16<64, 64, 2, kIdent>(g, q, k, v, pq, pk, o_s, lse, scale_log2, stream);
+  return wide ? launch_bf16_pc<128, 2, kIdent>(g, q, k, v, pq, pk, o_s, lse, scale_log2, stream)
+              : launch_bf16<128, 64, 2, kIdent>(g, q, k, v, pq, pk, o_s, lse, scale_log2, stream);
 }
 
 }  // namespace
 
 hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *k, const void *v,
-                                  const Buffers &buf, hipStream_t stream) {
+                                  const Buffers &buf, void *o_s, hipStream_t stream) {
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(g.D));
-  const int32_t *pq = buf.perm;
-  const int32_t *pk = buf.perm + g.rows;
-  if (g.bf16) {
-    // 128-query tiles when w allows; key stages of 4 blocks (d = 64: the whole
-    // 256-key window of w = 128) or 2, keeping LDS <= 72 KB (two workgroups
-    // per CU)
-    const bool wide = g.w % 128 == 0;
-    if (g.D == 64 && g.w == 128) return launch_bf16_slide(g, q, k, v, buf, scale_log2, stream);
-    if (g.D == 64)
-      return wide ? launch_bf16_pc<64, 4>(g, q, k, v, buf, scale_log2, stream)
-                  : launch_bf16<64, 64, 2>(g, q, k, v, buf, scale_log2, stream);
-    return wide ? launch_bf16_pc<128, 2>(g, q, k, v, buf, scale_log2, stream)
-                : launch_bf16<128, 64, 2>(g, q, k, v, buf, scale_log2, stream);
-  }
+  // one sort bucket: no permutation is read (the identity order)
+  const int32_t *pq = g.identity ? nullptr : buf.perm;
+  const int32_t *pk = g.identity ? nullptr : buf.perm + g.rows;
+  if (g.bf16)
+    return g.identity ? launch_bf16_any<true>(g, q, k, v, pq, pk, o_s, buf.lse, scale_log2, stream)
+                      : launch_bf16_any<false>(g, q, k, v, pq, pk, o_s, buf.lse, scale_log2, stream);
   const dim3 grid((g.N + 127) / 128, g.BH);
   if (g.D == 64)
     hipLaunchKernelGGL(elsaa_k3_chunk_attn_f32<64>, grid, dim3(128), 0, stream,
                        static_cast<const float *>(q), static_cast<const float *>(k),
                        static_cast<const float *>(v), pq, pk, g.N, g.w, scale_log2,
-                       static_cast<float *>(buf.o_s), buf.lse);
+                       static_cast<float *>(o_s), buf.lse);
   else
     hipLaunchKernelGGL(elsaa_k3_chunk_attn_f32<128>, grid, dim3(128), 0, stream,
                        static_cast<const float *>(q), static_cast<const float *>(k),
                        static_cast<const float *>(v), pq, pk, g.N, g.w, scale_log2,
-                       static_cast<float *>(buf.o_s), buf.lse);
+                       static_cast<float *>(o_s), buf.lse);
   return hipGetLastError();
 }
 

@@ -15,6 +15,9 @@
 // still be mis-scaled" and "The ablation isolates the actual contribution":
 // the multiplier acts on the sparse branch only, the gates are independent.)
 //
+// The RACE-only variant (race_only != 0) outputs y = o_lr: the sparse output,
+// its LSE and the gates are neither read nor computed.
+//
 // Two layouts.  L in {8, 16} (the wide path): 16-byte lane pieces, so a load
 // instruction gathers 8 table rows of bfloat16 d = 64; a workgroup serves a
 // run of queries of one (b, h) with that (b, h)'s bucket counts staged in LDS
@@ -47,7 +50,8 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
     const VT *__restrict__ o_s, const float *__restrict__ lse, const CT *__restrict__ qcodes,
     const VT *__restrict__ tsum, const float *__restrict__ tcnt, const VT *__restrict__ x_gate,
     const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int L,
-    int P, int DG, float lambda, long long total, long long qpw, VT *__restrict__ out, AuxOut aux) {
+    int P, int DG, float lambda, int race_only, long long total, long long qpw, VT *__restrict__ out,
+    AuxOut aux) {
   constexpr int kLPQ = D / 4;      // lanes per query, 4 value columns each
   constexpr int kQPS = 64 / kLPQ;  // queries per wave step
   const int lane = threadIdx.x & 63;
@@ -74,9 +78,12 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
     const VT *ts = tsum + bh * L * nb * static_cast<long long>(D) + sub * 4;
     const float *tc = tcnt + bh * L * nb;
 
-    float osv[4];
-    Elem<VT>::load4(o_s + qi * D + sub * 4, osv);
-    const float lse_i = lse[qi];
+    float osv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float lse_i = 0.0f;
+    if (!race_only) {
+      Elem<VT>::load4(o_s + qi * D + sub * 4, osv);
+      lse_i = lse[qi];
+    }
     const VT *xg = x_gate + (b * N + i) * DG;
     const float *w0 = gate_w + static_cast<long long>(h) * DG;
     const float *w1 = gate_w + static_cast<long long>(H + h) * DG;
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
     }
 
     float a0 = 0.0f, a1 = 0.0f;
-    for (int e = sub; e < DG; e += kLPQ) {
+    for (int e = sub; e < DG && !race_only; e += kLPQ) {
       const float x = Elem<VT>::load(xg + e);
       a0 = __builtin_fmaf(x, w0[e], a0);
       a1 = __builtin_fmaf(x, w1[e], a1);
@@ -125,18 +132,21 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
     const float mass_lr = lambda * z_lr;
     const float alpha = mass_lr > 0.0f ? __builtin_amdgcn_rcpf(1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
 
-    const float ws = g_s * alpha;
+    const float ws = race_only ? 0.0f : g_s * alpha;
+    const float wl = race_only ? 1.0f : g_lr;
     if (valid) {
       float yv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) yv[e] = __builtin_fmaf(ws, osv[e], g_lr * o_lr[e]);
+      for (int e = 0; e < 4; ++e) yv[e] = __builtin_fmaf(ws, osv[e], wl * o_lr[e]);
       Elem<VT>::store4(out + qi * D + sub * 4, yv);
       if (aux.o_lr) *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * 4) = o_lr;
       if (sub == 0) {
         if (aux.z_lr) aux.z_lr[qi] = z_lr;
-        if (aux.alpha) aux.alpha[qi] = alpha;
-        if (aux.g_s) aux.g_s[qi] = g_s;
-        if (aux.g_lr) aux.g_lr[qi] = g_lr;
+        if (!race_only) {
+          if (aux.alpha) aux.alpha[qi] = alpha;
+          if (aux.g_s) aux.g_s[qi] = g_s;
+          if (aux.g_lr) aux.g_lr[qi] = g_lr;
+        }
       }
     }
     i0 += kQPS;
@@ -196,7 +206,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     const VT *__restrict__ o_s, const float *__restrict__ lse, const CT *__restrict__ qcodes,
     const VT *__restrict__ tsum, const float *__restrict__ tcnt, const VT *__restrict__ x_gate,
     const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int P,
-    int DG, float lambda, int R, long long units, VT *__restrict__ out, AuxOut aux) {
+    int DG, float lambda, int race_only, int R, long long units, VT *__restrict__ out, AuxOut aux) {
   constexpr int kES = static_cast<int>(sizeof(VT));
   constexpr int kCols = 16 / kES;         // value columns per lane
   constexpr int kLPQ = D / kCols;         // lanes per query
@@ -271,6 +281,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   // the streamed inputs of a step (sparse output, its LSE, gate inputs) are
   // requested one step ahead, so their HBM latency overlaps the table gathers
   auto load_stream = [&](int i0, u32x4 &os_raw, float &lse_v, u32x4 &xg_raw) {
+    if (race_only) return;  // y = o_lr: no sparse output, LSE or gate inputs
     const uint32_t ii = static_cast<uint32_t>(i0 + lane / kLPQ);
     os_raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(os_rs, ii * kRowBytes + vbase, 0, 0));
     lse_v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lse_rs, ii * 4u, 0, 0));
@@ -366,7 +377,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     }
 
     float a0 = 0.0f, a1 = 0.0f;
-    if (gate_fast) {
+    if (race_only) {
+    } else if (gate_fast) {
 #pragma unroll
       for (int e = 0; e < kGE; ++e) {
         a0 = __builtin_fmaf(xv[e], gw_lds[0][sub * kGE + e], a0);
@@ -392,13 +404,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     const float rz = z > 0.0f ? __builtin_amdgcn_rcpf(z) : 0.0f;  // (num / L) / (z / L); 0 where z = 0
     const float mass_lr = lambda * z_lr;
     const float alpha = mass_lr > 0.0f ? __builtin_amdgcn_rcpf(1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
-    const float ws = g_s * alpha;
+    const float ws = race_only ? 0.0f : g_s * alpha;
+    const float wl = race_only ? 1.0f : g_lr;
 
     float o_lr[kCols], yv[kCols];
 #pragma unroll
     for (int k = 0; k < kCols; ++k) {
       o_lr[k] = num[k] * rz;
-      yv[k] = __builtin_fmaf(ws, osv[k], g_lr * o_lr[k]);
+      yv[k] = __builtin_fmaf(ws, osv[k], wl * o_lr[k]);
     }
     // The next step's streamed inputs and codes are waited for here, before
     // this step's store: the vector memory counter retires in issue order,
@@ -425,9 +438,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     }
     if (sub == 0) {
       if (aux.z_lr) aux.z_lr[qi] = z_lr;
-      if (aux.alpha) aux.alpha[qi] = alpha;
-      if (aux.g_s) aux.g_s[qi] = g_s;
-      if (aux.g_lr) aux.g_lr[qi] = g_lr;
+      if (!race_only) {
+        if (aux.alpha) aux.alpha[qi] = alpha;
+        if (aux.g_s) aux.g_s[qi] = g_s;
+        if (aux.g_lr) aux.g_lr[qi] = g_lr;
+      }
     }
   }
 }
@@ -447,8 +462,8 @@ void launch_wide(const Geometry &g, const void *x_gate, const float *gate_w, con
   hipLaunchKernelGGL((elsaa_k5_fuse_wide<D, VT, CT, LC>), dim3(static_cast<unsigned>(grid)), dim3(256), lds,
                      stream, static_cast<const VT *>(buf.o_s), buf.lse,
                      static_cast<const CT *>(buf.rcode), static_cast<const VT *>(buf.tsum), buf.tcnt,
-                     static_cast<const VT *>(x_gate), gate_w, gate_b, g.H, g.N, g.P, g.DG, g.lambda, R,
-                     units, static_cast<VT *>(out), aux);
+                     static_cast<const VT *>(x_gate), gate_w, gate_b, g.H, g.N, g.P, g.DG, g.lambda,
+                     g.run_sparse ? 0 : 1, R, units, static_cast<VT *>(out), aux);
 }
 
 template <int D, typename VT, typename CT>
@@ -464,7 +479,7 @@ void launch_any(const Geometry &g, const void *x_gate, const float *gate_w, cons
                      stream, static_cast<const VT *>(buf.o_s), buf.lse,
                      static_cast<const CT *>(buf.rcode), static_cast<const VT *>(buf.tsum), buf.tcnt,
                      static_cast<const VT *>(x_gate), gate_w, gate_b, g.H, g.N, g.L, g.P, g.DG,
-                     g.lambda, total, qpw, static_cast<VT *>(out), aux);
+                     g.lambda, g.run_sparse ? 0 : 1, total, qpw, static_cast<VT *>(out), aux);
 }
 
 template <int D, typename VT>

@@ -37,6 +37,12 @@
  *   - Calls that share a workspace must not overlap; calls with distinct
  *     workspaces may run concurrently on different streams.
  *   - NaN or Inf inputs propagate into the outputs; they are not trapped.
+ *   - With the environment variable ELSAA_DEBUG set to a nonzero integer when
+ *     the library is first called, elsaa_forward synchronises the stream after
+ *     every stage and reports the first stage whose kernels failed
+ *     (ELSAA_ERR_DEVICE, the stage named in elsaa_last_error()).  For
+ *     debugging only: the calls then block, and must not be captured into a
+ *     HIP graph.
  */
 #ifndef ELSAA_H
 #define ELSAA_H
@@ -48,12 +54,29 @@
 extern "C" {
 #endif
 
-#define ELSAA_ABI_VERSION 1
+#define ELSAA_ABI_VERSION 2
 
 typedef enum {
   ELSAA_DTYPE_F32 = 0,  /* IEEE binary32                                     */
   ELSAA_DTYPE_BF16 = 1  /* bfloat16 (8-bit exponent, 7 stored fraction bits) */
 } elsaa_dtype_t;
+
+/* Which output the call produces.  The full operator and its three
+ * single-mechanism relatives that the pages compare it with ("Two Efficient
+ * Attentions, One Denominator Problem", sections "The ablation isolates the
+ * actual contribution", "Workload structure matters more than a single
+ * leaderboard" and "Length extrapolation is the strongest robustness
+ * signal"): the ablation with the sparse multiplier fixed to one, a model
+ * with the RACE branch alone and one with the sparse (Sort-LSH) branch alone.
+ * A branch-only variant runs only the stages its branch needs. */
+typedef enum {
+  ELSAA_VARIANT_FULL = 0,        /* y = g_s alpha o_s + g_lr o_lr                   */
+  ELSAA_VARIANT_NO_ALPHA = 1,    /* y = g_s o_s + g_lr o_lr (alpha fixed to 1)      */
+  ELSAA_VARIANT_RACE_ONLY = 2,   /* y = o_lr: hash (RACE planes), RACE build and
+                                    gather only; no sort, no chunk attention       */
+  ELSAA_VARIANT_SPARSE_ONLY = 3  /* y = o_s: hash (sort planes), sort and chunk
+                                    attention only; no RACE stages, no gates      */
+} elsaa_variant_t;
 
 enum {
   ELSAA_OK = 0,
@@ -66,7 +89,11 @@ enum {
 
 /* Optional per-stage outputs, for tests and diagnostics.  Every member may be
  * NULL (not written).  Each non-NULL member is a device buffer of the stated
- * shape; writing them costs extra HBM traffic. */
+ * shape; writing them costs extra HBM traffic.  A branch-only variant leaves
+ * the members of the stages it skips unwritten (RACE_ONLY: sort codes,
+ * permutations, o_sparse, lse_s, alpha, g_s, g_lr; SPARSE_ONLY: RACE codes,
+ * tables, z_lr, alpha, g_s, g_lr, o_lowrank).  With sort_bits = 0 the
+ * permutations are the identity and the sort codes zero. */
 typedef struct {
   uint16_t *sort_code_q;  /* [B][H][N]    Sort-LSH code of each query           */
   uint16_t *sort_code_k;  /* [B][H][N]    Sort-LSH code of each key             */
@@ -90,10 +117,16 @@ typedef struct {
 /* Problem description.  Limits of this implementation (outside them the call
  * returns ELSAA_ERR_UNSUPPORTED):
  *   d in {64, 128};  1 <= d_gate <= 512;
- *   0 <= sort_bits <= 12;  0 <= race_bits <= 12;  1 <= race_tables <= 64;
+ *   0 <= sort_bits <= 12 (the sort keeps 2^sort_bits counters per wave in
+ *   LDS);  0 <= race_bits <= 12;  1 <= race_tables <= 64;
  *   sort_bits + race_tables * race_bits <= 256 hyperplanes;
  *   race_tables * 2^race_bits <= 16384;
- *   chunk is a multiple of 64 and divides N;  1 <= N <= 2^24. */
+ *   chunk is a multiple of 64 (the attention kernels step over keys in
+ *   blocks of 64) and divides N;  1 <= N <= 2^24;  B * H <= 32767;
+ *   every per-(b, h) extent in bytes -- N * d * elem (q, k, v, out), N *
+ *   d_gate * elem (x_gate of one b) -- is below 2^31 (the kernels address a
+ *   head's rows with 32-bit offsets); for bfloat16 and d = 128 this is
+ *   N < 2^23, for binary32 and d = 128 N < 2^22. */
 typedef struct {
   int32_t B, H, N, d, d_gate;
   int32_t sort_bits;   /* n_s: bits of the Sort-LSH code (0 = one bucket)        */
@@ -102,6 +135,7 @@ typedef struct {
   int32_t race_bits;   /* P: bits per RACE code (0 = one bucket per table)       */
   float lambda;        /* >= 0 and finite; 0 fixes the sparse multiplier to one */
   elsaa_dtype_t dtype; /* of q, k, v, x_gate, hyperplanes and out                */
+  elsaa_variant_t variant; /* ELSAA_VARIANT_FULL for the operator itself         */
   const float *gate_w; /* device [2][H][d_gate]: [0] sparse gate, [1] low-rank   */
   const float *gate_b; /* device [2][H]                                           */
   void *workspace;     /* device scratch, >= elsaa_workspace_bytes(params) bytes */
@@ -127,15 +161,22 @@ size_t elsaa_workspace_bytes(const elsaa_params_t *p);
 /* The forward pass.
  *   q, k, v     [B][H][N][d]      dtype
  *   x_gate      [B][N][d_gate]    dtype; one gate input per token, shared by heads
+ *               (not read by the branch-only variants)
  *   hyperplanes [sort_bits + L*P][d] dtype; rows 0..sort_bits-1 are the Sort-LSH
  *               planes (row t gives code bit t, least significant first), then
  *               table l's P planes at rows sort_bits + l*P + t.  Shared by all
- *               (b, h); used for queries and keys alike.
+ *               (b, h); used for queries and keys alike.  May be NULL when
+ *               sort_bits + L*P = 0.
  *   out         [B][H][N][d]      dtype, in original token order.
  * Hash bit semantics: bit = 1 iff the exact dot product of the stored vector
  * with the plane is > 0 (exact zero gives 0), independent of summation order.
  * Softmax scale 1/sqrt(d).  Chunk c (sorted ranks [c w, (c+1) w)) attends
- * sorted key ranks [max(0, (c-1) w), (c+1) w).  Z_lr and the low-rank numerator
+ * sorted key ranks [max(0, (c-1) w), (c+1) w).  With sort_bits = 0 every
+ * token shares one bucket, the stable order is the original one and the
+ * sparse branch is local-window attention over consecutive tokens (the
+ * local selection named beside LSH in the arxivlens summary's first
+ * paragraph); the sort stage is then skipped and the kernels index tokens
+ * directly.  Z_lr and the low-rank numerator
  * are means over the L tables; o_lr = 0 and alpha = 1 where Z_lr = 0.
  * Returns ELSAA_OK once every kernel is enqueued. */
 int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gate,

@@ -215,13 +215,30 @@ class OracleResult:
     seconds: float
 
 
+VARIANTS = ("full", "no_alpha", "race_only", "sparse_only")
+
+
 def forward(q, k, v, x_gate, hyperplanes, gate_w, gate_b, *, sort_bits: int,
-            chunk: int, race_tables_n: int, race_bits: int, lam: float) -> OracleResult:
+            chunk: int, race_tables_n: int, race_bits: int, lam: float,
+            variant: str = "full") -> OracleResult:
     """The whole forward pass on binary64 copies of the stored inputs.
 
     q, k, v: [B, H, N, d]; x_gate: [B, N, dg]; hyperplanes: [sort_bits + L*P, d]
     (sort planes first, then table l's P planes); gate_w [2, H, dg]; gate_b [2, H].
+
+    variant selects the output ("Two Efficient Attentions, One Denominator
+    Problem", sections "The ablation isolates the actual contribution" and
+    "Workload structure matters more than a single leaderboard"):
+      full         y = g_s alpha o_s + g_lr o_lr
+      no_alpha     the ablation that fixes the sparse multiplier to one, all
+                   else unchanged: y = g_s o_s + g_lr o_lr
+      race_only    the RACE model alone: y = o_lr
+      sparse_only  the sparse (Sort-LSH) model alone: y = o_s
+    Every intermediate is computed for every variant (this is a checker, not a
+    fast path); alpha is 1 wherever the variant has no multiplier.
     """
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
     t0 = time.perf_counter()
     q = _f64(q); k = _f64(k); v = _f64(v); planes = _f64(hyperplanes)
     B, H, N, d = q.shape
@@ -237,6 +254,13 @@ def forward(q, k, v, x_gate, hyperplanes, gate_w, gate_b, *, sort_bits: int,
     sums, counts = race_tables(v, rk, P)
     o_lr, z_lr = race_query(rq, sums, counts, P)
     g_s, g_lr = gates(x_gate, gate_w, gate_b, H)
-    alpha, y = fuse(o_s, lse, o_lr, z_lr, g_s, g_lr, lam)
+    if variant == "full":
+        alpha, y = fuse(o_s, lse, o_lr, z_lr, g_s, g_lr, lam)
+    elif variant == "no_alpha":  # lambda = 0 gives alpha = 1 in the fusion
+        alpha, y = fuse(o_s, lse, o_lr, z_lr, g_s, g_lr, 0.0)
+    elif variant == "race_only":
+        alpha, y = np.ones(z_lr.shape), o_lr.copy()
+    else:
+        alpha, y = np.ones(lse.shape), o_s.copy()
     return OracleResult(cq, ck, rq, rk, pq, pk, o_s, lse, sums, counts, o_lr, z_lr,
                         g_s, g_lr, alpha, y, pairs, time.perf_counter() - t0)

@@ -24,7 +24,7 @@ def to_device(inp: workloads.Inputs, device):
                 gate_b=torch.from_numpy(inp.gate_b).to(device))
 
 
-def run_gpu(inp: workloads.Inputs, lam=None, device="cuda:0"):
+def run_gpu(inp: workloads.Inputs, lam=None, device="cuda:0", variant="full"):
     import torch
 
     import efficient_long_context_amd as elsaa
@@ -33,7 +33,8 @@ def run_gpu(inp: workloads.Inputs, lam=None, device="cuda:0"):
     x = to_device(inp, dev)
     f = elsaa.Forward(B=wl.B, H=wl.H, N=wl.N, d=wl.d, d_gate=wl.d_gate, sort_bits=wl.sort_bits,
                       chunk=wl.chunk, race_tables=wl.race_tables, race_bits=wl.race_bits,
-                      lam=wl.lam if lam is None else lam, dtype=wl.dtype, device=dev, aux=True)
+                      lam=wl.lam if lam is None else lam, dtype=wl.dtype, variant=variant,
+                      device=dev, aux=True)
     out = f(x["q"], x["k"], x["v"], x["x_gate"], x["hyperplanes"], x["gate_w"], x["gate_b"])
     torch.cuda.synchronize()
     res = {"y": out.float().cpu().numpy().astype(np.float64)}
@@ -52,13 +53,13 @@ def run_gpu(inp: workloads.Inputs, lam=None, device="cuda:0"):
     return res
 
 
-def run_oracle(inp: workloads.Inputs, lam=None):
+def run_oracle(inp: workloads.Inputs, lam=None, variant="full"):
     import oracle
     wl = inp.wl
     return oracle.forward(inp.q, inp.k, inp.v, inp.x_gate, inp.hyperplanes, inp.gate_w,
                           inp.gate_b, sort_bits=wl.sort_bits, chunk=wl.chunk,
                           race_tables_n=wl.race_tables, race_bits=wl.race_bits,
-                          lam=wl.lam if lam is None else lam)
+                          lam=wl.lam if lam is None else lam, variant=variant)
 
 
 def rel_err(got, ref) -> float:
@@ -94,4 +95,28 @@ def compare_all(g: dict, r, dtype: str, label: str = "") -> dict:
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"{label}: over tolerance {tol}: {bad}"
     assert (g["alpha"] >= 0).all() and (g["alpha"] <= 1).all()
+    return errs
+
+
+def compare_variant(g: dict, r, dtype: str, variant: str, label: str = "") -> dict:
+    """As compare_all, restricted to the outputs the variant produces: the
+    branch-only variants leave the skipped branch's per-stage outputs
+    unwritten."""
+    if variant in ("full", "no_alpha"):
+        errs = compare_all(g, r, dtype, label)
+        if variant == "no_alpha":
+            assert (g["alpha"] == 1.0).all(), label + " alpha"
+        return errs
+    tol = TOL[dtype]
+    if variant == "race_only":
+        exact = ("race_code_q", "race_code_k", "race_cnt")
+        close = {"race_sum": r.race_sum, "z_lr": r.z_lr, "o_lowrank": r.o_lr, "y": r.y}
+    else:
+        exact = ("sort_code_q", "sort_code_k", "perm_q", "perm_k")
+        close = {"o_sparse": r.o_s, "lse_s": r.lse, "y": r.y}
+    for key in exact:
+        np.testing.assert_array_equal(g[key], getattr(r, key), err_msg=f"{label} {key}")
+    errs = {key: rel_err(g[key], ref) for key, ref in close.items()}
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{label}: over tolerance {tol}: {bad}"
     return errs

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(elsaa.EXPORTS)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.elsaa_abi_version() == 1
+    assert lib.elsaa_abi_version() == elsaa.ABI_VERSION == 2
 
 
 def test_status_strings():
@@ -74,12 +74,44 @@ def test_valid_params_and_workspace_size():
     (dict(race_tables=32, race_bits=10), elsaa.ERR_UNSUPPORTED),  # 32 * 1024 > 16384
     (dict(chunk=96, N=96 * 300), elsaa.ERR_UNSUPPORTED),
     (dict(d_gate=1024), elsaa.ERR_UNSUPPORTED),
+    (dict(variant=4), elsaa.ERR_INVALID_ARG),
+    (dict(variant=-1), elsaa.ERR_INVALID_ARG),
+    # per-(b, h) byte extents at 2^31 and beyond: the kernels' 32-bit offsets
+    (dict(B=1, H=1, d=128, N=1 << 24), elsaa.ERR_UNSUPPORTED),                    # bf16, 2^32 B
+    (dict(B=1, H=1, d=128, N=1 << 23), elsaa.ERR_UNSUPPORTED),                    # bf16, 2^31 B
+    (dict(B=1, H=1, d=128, N=1 << 22, dtype=elsaa.DTYPE_F32), elsaa.ERR_UNSUPPORTED),  # fp32 d=128
+    (dict(B=1, H=1, d=64, N=1 << 23, dtype=elsaa.DTYPE_F32), elsaa.ERR_UNSUPPORTED),   # fp32 d=64
+    (dict(B=1, H=1, d_gate=512, N=1 << 20, dtype=elsaa.DTYPE_F32), elsaa.ERR_UNSUPPORTED),  # x_gate
 ])
 def test_invalid_params_rejected(over, status):
     p = params(**over)
     assert elsaa.validate(p) == status
     assert elsaa.workspace_bytes(p) == 0
     assert elsaa.last_error() != ""
+
+
+@pytest.mark.parametrize("over", [
+    dict(B=1, H=1, d=128, N=(1 << 23) - 128),                       # bf16 d=128 just below 2^31 B
+    dict(B=1, H=1, d=128, N=(1 << 22) - 128, dtype=elsaa.DTYPE_F32),
+    dict(B=1, H=1, d=64, N=(1 << 23) - 128, dtype=elsaa.DTYPE_F32),
+    dict(sort_bits=0, race_bits=0),                                   # no hyperplanes at all
+    dict(variant=1), dict(variant=2), dict(variant=3),
+])
+def test_valid_edge_params(over):
+    p = params(**over)
+    assert elsaa.validate(p) == elsaa.OK, elsaa.last_error()
+    assert elsaa.workspace_bytes(p) > 0
+
+
+def test_forward_accepts_null_planes_without_planes():
+    """sort_bits = race_bits = 0: no hyperplane rows, so a NULL pointer passes the
+    pointer checks (the call then stops at the missing workspace, before any launch)."""
+    lib = elsaa.lib()
+    fake = ctypes.c_void_p(0x10000)
+    p = params(sort_bits=0, race_bits=0)
+    assert lib.elsaa_forward(fake, fake, fake, fake, None, ctypes.byref(p), fake) == elsaa.ERR_WORKSPACE
+    p = params()
+    assert lib.elsaa_forward(fake, fake, fake, fake, None, ctypes.byref(p), fake) == elsaa.ERR_INVALID_ARG
 
 
 def test_forward_rejects_before_launch():
@@ -118,7 +150,9 @@ def test_forward_rejects_misaligned_pointers():
 
 
 def test_struct_layout_matches_header():
-    # elsaa_params_t: 9 int32, float, enum, then 8-byte aligned pointers
+    # elsaa_params_t: 9 int32, float, two enums (dtype, variant), then 8-byte
+    # aligned pointers
     assert ctypes.sizeof(elsaa.ElsaaParams) == 48 + 8 * 2 + 8 + 8 + 8 + 8 + 8
+    assert elsaa.ElsaaParams.variant.offset == 44
     assert elsaa.ElsaaParams.gate_w.offset == 48
     assert ctypes.sizeof(elsaa.ElsaaAux) == 15 * 8

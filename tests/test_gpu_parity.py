@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_common import compare_all, run_gpu, run_oracle
+from gpu_common import compare_all, compare_variant, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,21 @@ CASES = {
     # 4096 buckets with 16K codes a segment (the tiled sort: the counters and
     # the codes do not fit one workgroup)
     "bf16-sort12-N16k": ("small-bf16", dict(B=1, H=1, N=16384, sort_bits=12)),
+    # one sort bucket: local-window attention in original order, no sort and no
+    # permutation reads, through each attention kernel (sliding-window d = 64
+    # w = 128, producer/consumer d = 128, 64-query tiles, fp32)
+    "bf16-ns0-slide": ("text32k-bf16", dict(B=1, H=2, N=4096, sort_bits=0)),
+    "bf16-ns0-d128-w256": ("needle256k-bf16", dict(H=2, N=4096, sort_bits=0)),
+    "bf16-ns0-w64": ("small-bf16", dict(B=1, H=2, N=2048, sort_bits=0)),
+    "fp32-ns0": ("tiny-fp32", dict(sort_bits=0)),
+    # no hyperplanes at all (sort_bits = race_bits = 0)
+    "bf16-no-planes": ("small-bf16", dict(B=1, H=2, N=2048, sort_bits=0, race_bits=0)),
+    "fp32-no-planes": ("tiny-fp32", dict(sort_bits=0, race_bits=0)),
+    # gate inputs of other widths: the wide fusion's general gate loop and the
+    # any-L fusion with d_gate != 64
+    "bf16-dgate48-L16": ("text32k-bf16", dict(B=1, H=2, N=4096, d_gate=48)),
+    "bf16-dgate100-L3": ("small-bf16", dict(B=1, H=2, N=2048, race_tables=3, d_gate=100)),
+    "fp32-dgate100-L8": ("tiny-fp32", dict(race_tables=8, d_gate=100)),
 }
 
 
@@ -56,6 +71,28 @@ def test_parity(case):
     r = run_oracle(inp)
     errs = compare_all(g, r, wl.dtype, case)
     print(f"[parity] {case}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+
+
+VARIANT_CASES = {
+    "tiny-fp32": ("tiny-fp32", {}),
+    "text32k-1head": ("text32k-bf16", dict(B=1, H=2, N=4096)),
+    "needle-d128": ("needle256k-bf16", dict(H=2, N=4096)),
+    "small-L3": ("small-bf16", dict(B=1, H=2, N=2048, race_tables=3, race_bits=5)),
+}
+
+
+@pytest.mark.parametrize("variant", ["no_alpha", "race_only", "sparse_only"])
+@pytest.mark.parametrize("case", list(VARIANT_CASES))
+def test_variant_parity(case, variant):
+    """The ablation and the two single-branch models against the oracle's."""
+    name, over = VARIANT_CASES[case]
+    wl = workloads.workload(name, **over)
+    inp = workloads.generate(wl, seed=13)
+    print(f"[variant] {case} {variant}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} {wl.dtype}", flush=True)
+    g = run_gpu(inp, variant=variant)
+    r = run_oracle(inp, variant=variant)
+    errs = compare_variant(g, r, wl.dtype, variant, f"{case} {variant}")
+    print(f"[variant] {case} {variant}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
 
 
 def test_exact_attention_special_case():

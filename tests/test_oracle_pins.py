@@ -315,6 +315,70 @@ def test_alpha_large_lse_no_overflow(oracle_lib):
     assert np.isfinite(y).all()
 
 
+# --------------------------------------------------------------- variants ----
+# The three relatives of the operator that the pages compare it with ("Two
+# Efficient Attentions, One Denominator Problem", sections "The ablation
+# isolates the actual contribution" and "Workload structure matters more than
+# a single leaderboard"), pinned where they reduce to textbook quantities:
+# with one sort bucket and one chunk the sparse branch is dense softmax
+# attention, with P = 0 every table has one bucket holding every key, and
+# zero gate weights give gates of exactly one half.
+
+def _closed_form_inputs(N=128):
+    inp = small_inputs("fp32", N=N, chunk=N, sort_bits=0, P=0, L=3)
+    inp.gate_w[...] = 0.0
+    inp.gate_b[...] = 0.0
+    return inp
+
+
+def _dense_attention(inp):
+    q = inp.q.astype(np.float64); k = inp.k.astype(np.float64); v = inp.v.astype(np.float64)
+    s = q @ np.swapaxes(k, -1, -2) / np.sqrt(q.shape[-1])
+    m = s.max(axis=-1, keepdims=True)
+    p = np.exp(s - m)
+    return (p @ v) / p.sum(axis=-1, keepdims=True)
+
+
+def test_variant_sparse_only_is_dense_attention_at_one_bucket_one_chunk(oracle_lib):
+    inp = _closed_form_inputs()
+    r = run_oracle(oracle_lib, inp, variant="sparse_only")
+    np.testing.assert_allclose(r.y, _dense_attention(inp), rtol=0, atol=1e-12)
+
+
+def test_variant_race_only_is_mean_value_at_zero_bits(oracle_lib):
+    """P = 0: each table's single bucket holds every key, so o_lr is the mean of v."""
+    inp = _closed_form_inputs()
+    r = run_oracle(oracle_lib, inp, variant="race_only")
+    mean_v = inp.v.astype(np.float64).mean(axis=-2, keepdims=True)
+    np.testing.assert_allclose(r.y, np.broadcast_to(mean_v, r.y.shape), rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(r.z_lr, np.full(r.z_lr.shape, float(inp.wl.N)))
+
+
+def test_variant_no_alpha_is_half_sum_at_zero_gates(oracle_lib):
+    """alpha fixed to one and g = 1/2: y = (dense attention + mean of v) / 2."""
+    inp = _closed_form_inputs()
+    r = run_oracle(oracle_lib, inp, variant="no_alpha")
+    assert (r.alpha == 1.0).all() and (r.g_s == 0.5).all() and (r.g_lr == 0.5).all()
+    mean_v = inp.v.astype(np.float64).mean(axis=-2, keepdims=True)
+    np.testing.assert_allclose(r.y, 0.5 * (_dense_attention(inp) + mean_v), rtol=0, atol=1e-12)
+
+
+def test_variant_full_differs_from_no_alpha_only_by_alpha(oracle_lib):
+    """With lambda > 0 the full operator's alpha lies strictly inside (0, 1) here,
+    and the output is that multiple of the sparse term plus the same low-rank term."""
+    inp = _closed_form_inputs()
+    full = run_oracle(oracle_lib, inp, variant="full")
+    assert ((full.alpha > 0) & (full.alpha < 1)).all()
+    mean_v = inp.v.astype(np.float64).mean(axis=-2, keepdims=True)
+    y = 0.5 * full.alpha[..., None] * _dense_attention(inp) + 0.5 * mean_v
+    np.testing.assert_allclose(full.y, y, rtol=0, atol=1e-12)
+
+
+def test_unknown_variant_rejected(oracle_lib):
+    with pytest.raises(ValueError):
+        run_oracle(oracle_lib, _closed_form_inputs(64), variant="bogus")
+
+
 # -------------------------------------------------------- page-level facts ----
 
 def test_interaction_reduction_matches_pages_order_of_magnitude(oracle_lib):
