@@ -25,8 +25,9 @@ ABI_VERSION = 2
 VARIANTS = {"full": 0, "no_alpha": 1, "race_only": 2, "sparse_only": 3}
 
 # Every symbol include/elsaa.h declares.
-EXPORTS = ("elsaa_validate", "elsaa_workspace_bytes", "elsaa_forward", "elsaa_status_str",
-           "elsaa_last_error", "elsaa_abi_version")
+EXPORTS = ("elsaa_validate", "elsaa_workspace_bytes", "elsaa_forward", "elsaa_forward_noalloc",
+           "elsaa_status_str", "elsaa_last_error", "elsaa_abi_version")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ELSAA_NOALLOC_SCRATCH_BYTES
 
 AUX_FIELDS = ("sort_code_q", "sort_code_k", "race_code_q", "race_code_k", "perm_q", "perm_k",
               "race_sum", "race_cnt", "o_sparse", "lse_s", "z_lr", "alpha", "g_s", "g_lr",
@@ -80,6 +81,8 @@ def lib():
         L.elsaa_workspace_bytes.restype = ctypes.c_size_t
         L.elsaa_forward.argtypes = [ctypes.c_void_p] * 5 + [ctypes.POINTER(ElsaaParams), ctypes.c_void_p]
         L.elsaa_forward.restype = ctypes.c_int
+        L.elsaa_forward_noalloc.argtypes = L.elsaa_forward.argtypes
+        L.elsaa_forward_noalloc.restype = ctypes.c_int
         L.elsaa_status_str.argtypes = [ctypes.c_int]
         L.elsaa_status_str.restype = ctypes.c_char_p
         L.elsaa_last_error.restype = ctypes.c_char_p

@@ -15,6 +15,14 @@
 
 #include "elsaa_internal.hpp"
 
+// Scratch of elsaa_forward_noalloc: a fixed array in device memory, one copy
+// per device (allocated when the code object is loaded on it, held until the
+// process ends), shared by every call on that device.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in): the
+// device address of each device's copy comes from hipGetSymbolAddress, taken
+// once per device with that device current (device_scratch below).
+static __device__ __align__(256) char scratch[ELSAA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -234,6 +242,31 @@ bool debug_mode() {
   return on;
 }
 
+bool misaligned(const void *ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
+
+int check_pointers(const elsaa::Geometry &g, const void *q, const void *k, const void *v, const void *x_gate,
+                   const void *hyperplanes, const elsaa_params_t *params, const void *out);
+int enqueue_forward(elsaa::Geometry &g, const void *q, const void *k, const void *v, const void *x_gate,
+                    const void *hyperplanes, const elsaa_params_t *params, void *out, char *ws);
+
+constexpr size_t kNoAllocScratchBytes = ELSAA_NOALLOC_SCRATCH_BYTES;
+std::mutex g_scratch_mu;
+char *g_scratch[kMaxDevices] = {nullptr};
+
+hipError_t device_scratch(int device, char **ptr) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[device]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[device] = static_cast<char *>(p);
+  }
+  *ptr = g_scratch[device];
+  return hipSuccess;
+}
+
 }  // namespace
 
 namespace elsaa {
@@ -279,11 +312,51 @@ size_t elsaa_workspace_bytes(const elsaa_params_t *p) {
 int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gate,
                   const void *hyperplanes, const elsaa_params_t *params, void *out) {
   elsaa::Geometry g;
-  const int st = make_geometry(params, &g);
+  int st = make_geometry(params, &g);
+  if (st == ELSAA_OK) st = check_pointers(g, q, k, v, x_gate, hyperplanes, params, out);
   if (st != ELSAA_OK) return st;
+  const size_t need = carve(g, nullptr, nullptr);
+  if (!params->workspace || params->workspace_bytes < need)
+    return fail(ELSAA_ERR_WORKSPACE, "workspace of %zu bytes required (given %zu%s)", need,
+                params->workspace_bytes, params->workspace ? "" : ", NULL");
+  if (misaligned(params->workspace, 256))
+    return fail(ELSAA_ERR_WORKSPACE, "the workspace must be 256-byte aligned");
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e == hipSuccess) e = device_cus(device, &g.cus);
+  if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
+  return enqueue_forward(g, q, k, v, x_gate, hyperplanes, params, out, static_cast<char *>(params->workspace));
+}
+
+int elsaa_forward_noalloc(const void *q, const void *k, const void *v, const void *x_gate,
+                          const void *hyperplanes, const elsaa_params_t *params, void *out) {
+  elsaa::Geometry g;
+  int st = make_geometry(params, &g);
+  if (st == ELSAA_OK) st = check_pointers(g, q, k, v, x_gate, hyperplanes, params, out);
+  if (st != ELSAA_OK) return st;
+  const size_t need = carve(g, nullptr, nullptr);
+  if (need > kNoAllocScratchBytes)
+    return fail(ELSAA_ERR_WORKSPACE,
+                "elsaa_forward_noalloc: the problem needs %zu bytes of scratch, above the fixed %zu "
+                "(ELSAA_NOALLOC_SCRATCH_BYTES); use elsaa_forward with a workspace",
+                need, kNoAllocScratchBytes);
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e == hipSuccess) e = device_cus(device, &g.cus);
+  char *scratch_ptr = nullptr;
+  if (e == hipSuccess) e = device_scratch(device, &scratch_ptr);
+  if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
+  return enqueue_forward(g, q, k, v, x_gate, hyperplanes, params, out, scratch_ptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_pointers(const elsaa::Geometry &g, const void *q, const void *k, const void *v, const void *x_gate,
+                   const void *hyperplanes, const elsaa_params_t *params, const void *out) {
   if (!q || !k || !v || !x_gate || !out || (!hyperplanes && g.R > 0))
     return fail(ELSAA_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  auto misaligned = [](const void *ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; };
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(x_gate, 16) ||
       misaligned(hyperplanes, 16) || misaligned(out, 16))
     return fail(ELSAA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
@@ -296,20 +369,17 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
     for (const void *ptr : ptrs)
       if (misaligned(ptr, 16)) return fail(ELSAA_ERR_INVALID_ARG, "aux output pointers must be 16-byte aligned");
   }
-  const size_t need = carve(g, nullptr, nullptr);
-  if (!params->workspace || params->workspace_bytes < need)
-    return fail(ELSAA_ERR_WORKSPACE, "workspace of %zu bytes required (given %zu%s)", need,
-                params->workspace_bytes, params->workspace ? "" : ", NULL");
-  if (misaligned(params->workspace, 256))
-    return fail(ELSAA_ERR_WORKSPACE, "the workspace must be 256-byte aligned");
-  elsaa::Buffers buf;
-  carve(g, static_cast<char *>(params->workspace), &buf);
-  hipStream_t s = static_cast<hipStream_t>(params->stream);
+  return ELSAA_OK;
+}
 
-  int device = 0;
-  hipError_t e = hipGetDevice(&device);
-  if (e == hipSuccess) e = device_cus(device, &g.cus);
-  if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
+// Enqueues every stage on params->stream with the scratch buffers carved out
+// of `ws` (at least carve(g) bytes, 256-byte aligned).
+int enqueue_forward(elsaa::Geometry &g, const void *q, const void *k, const void *v, const void *x_gate,
+                    const void *hyperplanes, const elsaa_params_t *params, void *out, char *ws) {
+  elsaa::Buffers buf;
+  carve(g, ws, &buf);
+  hipStream_t s = static_cast<hipStream_t>(params->stream);
+  hipError_t e = hipSuccess;
 
   // stage_events[2i] / [2i+1] bracket stage i (hash, sort, RACE build, chunk
   // attention, fusion); a stage a variant skips is an empty interval
@@ -366,4 +436,4 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
   return ELSAA_OK;
 }
 
-}  // extern "C"
+}  // namespace

@@ -182,6 +182,24 @@ size_t elsaa_workspace_bytes(const elsaa_params_t *p);
 int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gate,
                   const void *hyperplanes, const elsaa_params_t *params, void *out);
 
+/* Bytes of the fixed device scratch elsaa_forward_noalloc uses (64 MiB). */
+#define ELSAA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward pass as elsaa_forward, with the same arguments, outputs and errors,
+ * except that params->workspace and params->workspace_bytes are ignored.  Its
+ * scratch is a fixed array of ELSAA_NOALLOC_SCRATCH_BYTES in device memory,
+ * one per device, which the library holds from its load until the process
+ * ends; the call itself allocates nothing.  A problem whose
+ * elsaa_workspace_bytes() exceeds ELSAA_NOALLOC_SCRATCH_BYTES is rejected with
+ * ELSAA_ERR_WORKSPACE before any device call.  Every call on a device shares
+ * that device's array and no kernel relies on its previous contents: calls on
+ * one device that overlap in time (concurrent streams, or host threads) race
+ * on it and must be serialised by the caller. */
+int elsaa_forward_noalloc(const void *q, const void *k, const void *v, const void *x_gate,
+                          const void *hyperplanes, const elsaa_params_t *params, void *out);
+
 /* Static name of a status code ("ELSAA_OK", ...). */
 const char *elsaa_status_str(int status);
 

@@ -132,6 +132,23 @@ def test_forward_rejects_before_launch():
     assert lib.elsaa_forward(fake, fake, fake, fake, fake, None, fake) == elsaa.ERR_INVALID_ARG
 
 
+def test_noalloc_rejects_problems_above_its_scratch_before_any_device_call():
+    """elsaa_forward_noalloc ignores the workspace fields and rejects a problem
+    whose scratch exceeds its fixed array on the host, before touching the
+    device (there is none here)."""
+    lib = elsaa.lib()
+    fake = ctypes.c_void_p(0x10000)
+    p = params()  # the 32K-token text shape: far above 64 MiB of scratch
+    assert elsaa.workspace_bytes(p) > elsaa.NOALLOC_SCRATCH_BYTES
+    assert lib.elsaa_forward_noalloc(fake, fake, fake, fake, fake, ctypes.byref(p), fake) == elsaa.ERR_WORKSPACE
+    assert "noalloc" in elsaa.last_error()
+    p = params(N=1000)
+    assert lib.elsaa_forward_noalloc(fake, fake, fake, fake, fake, ctypes.byref(p), fake) == elsaa.ERR_INVALID_ARG
+    p = params(B=1, H=1, N=4096)
+    assert elsaa.workspace_bytes(p) <= elsaa.NOALLOC_SCRATCH_BYTES
+    assert lib.elsaa_forward_noalloc(None, fake, fake, fake, fake, ctypes.byref(p), fake) == elsaa.ERR_INVALID_ARG
+
+
 def test_forward_rejects_misaligned_pointers():
     lib = elsaa.lib()
     fake = ctypes.c_void_p(0x10000)
