@@ -49,7 +49,10 @@ class ElsaaParams(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p), ("aux", ctypes.POINTER(ElsaaAux)),
         ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+        ("options", ctypes.c_uint32),
     ]
+
+OPT_FUSED_EPILOGUE = 1  # ELSAA_OPT_FUSED_EPILOGUE
 
 STAGES = ("hash", "sort", "race_build", "chunk_attention", "fuse")
 
@@ -100,7 +103,7 @@ def last_error() -> str:
 
 
 def make_params(B, H, N, d, d_gate, *, sort_bits, chunk, race_tables, race_bits, lam,
-                dtype=DTYPE_BF16, variant=0, gate_w_ptr=0, gate_b_ptr=0, workspace_ptr=0,
+                dtype=DTYPE_BF16, variant=0, options=0, gate_w_ptr=0, gate_b_ptr=0, workspace_ptr=0,
                 workspace_bytes=0, stream_ptr=0, aux=None, stage_events=None) -> ElsaaParams:
     p = ElsaaParams()
     p.B, p.H, p.N, p.d, p.d_gate = B, H, N, d, d_gate
@@ -108,6 +111,7 @@ def make_params(B, H, N, d, d_gate, *, sort_bits, chunk, race_tables, race_bits,
     p.lambda_ = lam
     p.dtype = dtype
     p.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    p.options = int(options)
     p.gate_w, p.gate_b = gate_w_ptr or None, gate_b_ptr or None
     p.workspace, p.workspace_bytes = workspace_ptr or None, workspace_bytes
     p.stream = stream_ptr or None
@@ -144,7 +148,7 @@ class Forward:
     """
 
     def __init__(self, *, B, H, N, d, d_gate=64, sort_bits, chunk, race_tables, race_bits,
-                 lam=1.0, dtype="bf16", variant="full", device=None, aux=False):
+                 lam=1.0, dtype="bf16", variant="full", options=0, device=None, aux=False):
         import torch
         self.torch = torch
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
@@ -152,7 +156,7 @@ class Forward:
         self.dtype_code = DTYPE_BF16 if dtype == "bf16" else DTYPE_F32
         self.shape = dict(B=B, H=H, N=N, d=d, d_gate=d_gate)
         self.cfg = dict(sort_bits=sort_bits, chunk=chunk, race_tables=race_tables,
-                        race_bits=race_bits, lam=float(lam), variant=variant)
+                        race_bits=race_bits, lam=float(lam), variant=variant, options=int(options))
         probe = make_params(B, H, N, d, d_gate, dtype=self.dtype_code, gate_w_ptr=1, gate_b_ptr=1,
                             **self.cfg)
         st = validate(probe)

@@ -113,6 +113,10 @@ int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
   g->run_sparse = p->variant != ELSAA_VARIANT_RACE_ONLY;
   g->run_race = p->variant != ELSAA_VARIANT_SPARSE_ONLY;
   g->identity = p->sort_bits == 0;
+  if (p->options & ~static_cast<uint32_t>(ELSAA_OPT_FUSED_EPILOGUE))
+    return fail(ELSAA_ERR_INVALID_ARG, "unknown option bits 0x%x", p->options);
+  g->fused = false;
+  g->fused = (p->options & ELSAA_OPT_FUSED_EPILOGUE) != 0 && elsaa::attention_fusable(*g);
   return ELSAA_OK;
 }
 
@@ -138,8 +142,10 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   t.rpart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (elsaa::race_parts(g.N) + 1) * 8));
   t.tsum = take(static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * es);
   t.tcnt = reinterpret_cast<float *>(take(static_cast<size_t>(g.BH) * g.L * g.nb_race * 4));
-  t.o_s = take(rows * g.D * es);
-  t.lse = reinterpret_cast<float *>(take(rows * 4));
+  // the sparse output and its LSE round-trip through memory unless the fusion
+  // runs in the attention's epilogue
+  t.o_s = g.fused ? nullptr : take(rows * g.D * es);
+  t.lse = g.fused ? nullptr : reinterpret_cast<float *>(take(rows * 4));
   if (b) *b = t;
   return off;
 }
@@ -187,9 +193,10 @@ hipError_t copy_aux(const elsaa::Geometry &g, const elsaa::Buffers &buf, const e
       {rc ? aux->race_sum : nullptr, g.bf16 ? nullptr : buf.tsum,
        static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * 4},
       {rc ? aux->race_cnt : nullptr, buf.tcnt, static_cast<size_t>(g.BH) * g.L * g.nb_race * 4},
-      // SPARSE_ONLY writes o_s as the output itself
-      {sp ? aux->o_sparse : nullptr, rc ? buf.o_s : out, rows * g.D * es},
-      {sp ? aux->lse_s : nullptr, buf.lse, rows * 4},
+      // SPARSE_ONLY writes o_s as the output itself; the fused attention
+      // writes these two aux outputs itself
+      {sp && !g.fused ? aux->o_sparse : nullptr, rc ? buf.o_s : out, rows * g.D * es},
+      {sp && !g.fused ? aux->lse_s : nullptr, buf.lse, rows * 4},
   };
   for (const Item &it : items) {
     if (!it.dst || !it.src) continue;
@@ -421,12 +428,17 @@ int enqueue_forward(elsaa::Geometry &g, const void *q, const void *k, const void
   if (g.run_sparse && !g.identity) run("sort", [&] { return elsaa::launch_sort(g, buf, s); });
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = mark(6);
-  if (g.run_sparse)
+  if (g.fused)
+    run("chunk attention + fusion", [&] {
+      return elsaa::launch_attention_fused(g, q, k, v, x_gate, params->gate_w, params->gate_b, buf, params->aux,
+                                           out, s);
+    });
+  else if (g.run_sparse)
     run("chunk attention",
         [&] { return elsaa::launch_chunk_attention(g, q, k, v, buf, g.run_race ? buf.o_s : out, s); });
   if (e == hipSuccess) e = mark(7);
   if (e == hipSuccess) e = mark(8);
-  if (g.run_race)
+  if (g.run_race && !g.fused)
     run("fusion",
         [&] { return elsaa::launch_fuse(g, x_gate, params->gate_w, params->gate_b, buf, params->aux, out, s); });
   if (e == hipSuccess) e = mark(9);

@@ -32,6 +32,7 @@ struct Geometry {
   bool run_sparse;  // the Sort-LSH branch runs (not RACE_ONLY)
   bool run_race;    // the RACE branch runs (not SPARSE_ONLY)
   bool identity;    // sort_bits == 0: the stable order is the original one, no sort
+  bool fused;       // the fusion runs in the chunk attention's epilogue (no o_s, LSE buffers)
 };
 
 // Device buffers carved out of the caller's workspace.
@@ -87,6 +88,13 @@ hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *
                                   const void *v, const Buffers &buf, void *o_s, hipStream_t stream);
 hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
                              hipStream_t stream);
+// Chunk attention with the RACE gather, gates and fusion in its epilogue, for
+// the shapes attention_fusable() accepts: writes y to `out` (and the aux
+// outputs of both stages that are requested), never o_s or its LSE.
+bool attention_fusable(const Geometry &g);
+hipError_t launch_attention_fused(const Geometry &g, const void *q, const void *k, const void *v,
+                                  const void *x_gate, const float *gate_w, const float *gate_b,
+                                  const Buffers &buf, const elsaa_aux_t *aux, void *out, hipStream_t stream);
 hipError_t launch_fuse(const Geometry &g, const void *x_gate, const float *gate_w,
                        const float *gate_b, const Buffers &buf, const elsaa_aux_t *aux,
                        void *out, hipStream_t stream);

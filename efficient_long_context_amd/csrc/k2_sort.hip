@@ -62,38 +62,70 @@ __global__ __launch_bounds__(256) void elsaa_k2_sort_hist(const uint16_t *__rest
   for (int b = threadIdx.x; b < nb; b += 256) out[static_cast<long long>(b) * T + tile] = h[b];
 }
 
-// In-place exclusive scan of M counts per segment; one 1024-thread block each.
-__global__ __launch_bounds__(1024) void elsaa_k2_sort_scan(uint32_t *__restrict__ hist,
-                                                           long long M) {
-  __shared__ uint32_t part[1024];
+// In-place exclusive scan of the M = nb * T counts of each segment, one
+// 1024-thread block per segment, in chunks of 1024 * kScanPer counts: each
+// thread owns kScanPer consecutive counts of a chunk, requested at once as
+// 16-byte pieces (so the chunk's loads are all in flight together), then a
+// block scan of the per-thread sums and a running carry across chunks.
+constexpr int kScanPer = 64;
+__global__ __launch_bounds__(1024) void elsaa_k2_sort_scan(uint32_t *__restrict__ hist, long long M) {
+  __shared__ uint32_t part[16];
   uint32_t *p = hist + static_cast<long long>(blockIdx.x) * M;
-  const int tid = threadIdx.x;
-  const long long per = (M + 1023) / 1024;
-  const long long lo = tid * per;
-  const long long hi = lo + per < M ? lo + per : M;
-  uint32_t sum = 0;
-  for (long long i = lo; i < hi; ++i) sum += p[i];
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
-    const uint32_t add = tid >= off ? part[tid - off] : 0u;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t carry = 0;
+  for (long long c0 = 0; c0 < M; c0 += 1024ll * kScanPer) {
+    const long long lo = c0 + static_cast<long long>(tid) * kScanPer;
+    uint32_t v[kScanPer];
+    // 16-byte pieces when M is a multiple of 4 (every segment's counts then
+    // start 16-byte aligned); otherwise, and past the end, element by element
+    if (lo + kScanPer <= M && (M & 3) == 0) {
+#pragma unroll
+      for (int e = 0; e < kScanPer; e += 4) {
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(p + lo + e);
+        v[e] = x[0]; v[e + 1] = x[1]; v[e + 2] = x[2]; v[e + 3] = x[3];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kScanPer; ++e) v[e] = lo + e < M ? p[lo + e] : 0u;
+    }
+    uint32_t sum = 0;
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e) sum += v[e];
+    uint32_t run = block_exclusive_scan(sum, part, lane, wave);
+    if (tid == 1023) part[0] = run + sum;  // the chunk's total (after the scan's reads of part)
+    run += carry;
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e) {
+      const uint32_t c = v[e];
+      v[e] = run;
+      run += c;
+    }
+    if (lo + kScanPer <= M && (M & 3) == 0) {
+#pragma unroll
+      for (int e = 0; e < kScanPer; e += 4)
+        *reinterpret_cast<u32x4 *>(p + lo + e) = u32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < kScanPer; ++e)
+        if (lo + e < M) p[lo + e] = v[e];
+    }
     __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  uint32_t run = part[tid] - sum;  // exclusive prefix of this thread's run
-  for (long long i = lo; i < hi; ++i) {
-    const uint32_t c = p[i];
-    p[i] = run;
-    run += c;
+    carry += part[0];
+    __syncthreads();  // part is reused by the next chunk's scan
   }
 }
 
+// Per tile: the first sorted rank of each (bucket, tile) is staged in LDS
+// with the waves' running counters; each wave then ranks its 8 rounds of 64
+// codes in order.  Every lane of a group of equal codes reads the group's
+// counter (one address, a broadcast) and writes back the same advanced value,
+// adding its rank inside the group; a wave's LDS accesses are carried out in
+// issue order, so the next round's read sees the update without a wait.
 __global__ __launch_bounds__(256) void elsaa_k2_sort_scatter(const uint16_t *__restrict__ codes,
                                                              int N, int ns, int nb, int T,
                                                              const uint32_t *__restrict__ offs,
                                                              int32_t *__restrict__ perm) {
-  extern __shared__ uint32_t cnt[];  // [kWaves][nb]
+  extern __shared__ uint32_t cnt[];  // [kWaves][nb] running sorted positions
   const int tile = blockIdx.x;
   const long long s = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -103,15 +135,20 @@ __global__ __launch_bounds__(256) void elsaa_k2_sort_scatter(const uint16_t *__r
   const int wbase = tile * kSortTile + wave * (kSortTile / kWaves);
   uint32_t *wc = cnt + wave * nb;
 
-  for (int b = tid; b < kWaves * nb; b += 256) cnt[b] = 0;
-  __syncthreads();
+  uint32_t code[kRounds];
+#pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int i = wbase + r * 64 + lane;
-    if (i < N) atomicAdd(&wc[c[i]], 1u);
+    code[r] = i < N ? c[i] : 0xffffffffu;
   }
+  for (int b = tid; b < kWaves * nb; b += 256) cnt[b] = 0;
   __syncthreads();
-  for (int b = tid; b < nb; b += 256) {  // counts of earlier waves in this tile
-    uint32_t run = 0;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+    if (code[r] != 0xffffffffu) atomicAdd(&wc[code[r]], 1u);
+  __syncthreads();
+  for (int b = tid; b < nb; b += 256) {  // the bucket's first rank in this tile, then earlier waves
+    uint32_t run = o[static_cast<long long>(b) * T + tile];
     for (int w = 0; w < kWaves; ++w) {
       const uint32_t t = cnt[w * nb + b];
       cnt[w * nb + b] = run;
@@ -121,27 +158,16 @@ __global__ __launch_bounds__(256) void elsaa_k2_sort_scatter(const uint16_t *__r
   __syncthreads();
 
   const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
   for (int r = 0; r < kRounds; ++r) {
-    const int i = wbase + r * 64 + lane;
-    const bool valid = i < N;
-    const uint32_t code = valid ? c[i] : 0u;
-    const unsigned long long mask = same_code_lanes(code, valid, ns);
-    const int rank = __popcll(mask & lt);
-    const int leader = __ffsll(static_cast<long long>(mask)) - 1;
-    uint32_t before = 0;
-    if (valid && lane == leader) {
-      before = wc[code];
-      wc[code] = before + static_cast<uint32_t>(__popcll(mask));
-    }
-    before = __shfl(before, leader < 0 ? 0 : leader);
+    const bool valid = code[r] != 0xffffffffu;
+    const uint32_t cv = valid ? code[r] : 0u;
+    const unsigned long long same = same_code_lanes(cv, valid, ns);
+    const uint32_t before = wc[cv];
     if (valid) {
-      const uint32_t dest = o[static_cast<long long>(code) * T + tile] + before + rank;
-      pm[dest] = i;
+      wc[cv] = before + static_cast<uint32_t>(__popcll(same));
+      pm[before + static_cast<uint32_t>(__popcll(same & lt))] = wbase + r * 64 + lane;
     }
-    // the leader's counter update must land before the next round reads it
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 

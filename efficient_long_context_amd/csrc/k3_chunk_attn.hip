@@ -24,6 +24,8 @@
 // same XCD.  With one sort bucket (sort_bits = 0) the sorted order is the
 // original one: the kIdent instances index tokens directly and read no
 // permutation.
+#include <type_traits>
+
 #include "elsaa_internal.hpp"
 
 namespace elsaa {
@@ -543,12 +545,189 @@ __global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_pc(
 // index slots.  Waves 0-7 compute 16 queries each; they load their query rows
 // for the next tile while computing the current one.  One LDS-only barrier
 // per tile.
-template <bool kIdent>
+//
+// Fused epilogue (kFuseL = L in {8, 16}): instead of writing o_s and its LSE,
+// each computing wave finishes its 16 queries with the RACE gather, the gates
+// and the fusion of the forward pass (the same arithmetic as the separate
+// fusion kernel): it requests the queries' L table codes with their query
+// rows, then gathers the L bucket rows (bfloat16, two 16-byte pieces a lane)
+// and counts, the gate inputs, and writes y.  The transposed V rows are
+// staged in a permuted row order so that a lane's O^T results are the 16
+// consecutive columns g*16 .. g*16+15 of its query: table rows, gate inputs
+// and y are then read and written as whole 16-byte pieces.  The sparse
+// output never goes to memory (except as an optional aux output).
+struct FuseArgs {
+  const uint8_t *qcodes;   // [BH*N][L] query RACE codes (P <= 8)
+  const uint16_t *tsum;    // [BH][L][2^P][64] bucket sums, bfloat16
+  const float *tcnt;       // [BH][L][2^P] bucket counts
+  const uint16_t *x_gate;  // [B][N][64]
+  const float *gate_w;     // [2][H][64]
+  const float *gate_b;     // [2][H]
+  int H, P;
+  float lambda;
+  uint16_t *out;           // [BH][N][64]
+  // optional aux outputs (NULL: not written)
+  uint16_t *o_s;
+  float *lse, *z_lr, *alpha, *g_s, *g_lr, *o_lr;
+};
+
+// The fused epilogue of one computing wave's 16 queries (d = 64): lane
+// (g, r16) holds columns g*16 + dt*4 + i of query r16's unnormalised sparse
+// output in o[dt][i] (1/l_tot = inv), its LSE, and the query's L codes in cw.
+//   Z_lr = (1/L) sum_l count_l[c_l],  num = (1/L) sum_l sum_l[c_l][:],
+//   o_lr = num / Z_lr (0 where Z_lr = 0),  g = sigmoid(<x_gate, W> + b),
+//   alpha = 1 / (1 + exp(log(lambda Z_lr) - lse)) (1 where lambda Z_lr = 0),
+//   y = g_s alpha o_s + g_lr o_lr
+// ("ELSAA: Efficient Low-Rank and Sparse Attention Approximation for Training
+// Transformers", first paragraph; "Two Efficient Attentions, One Denominator
+// Problem", section "Two efficient branches can still be mis-scaled").  The
+// table rows are requested four tables at a time, two sets in flight.  The
+// next tile's query rows (qnext) are waited for before the stores: the vector
+// memory counter retires in issue order.
+template <int L>
+__device__ __forceinline__ void fused_epilogue(const FuseArgs &fz, const f32x4 (&o)[4], float inv, float lse_v,
+                                               const uint32_t (&cw)[L / 4], long long bh, int qidx, int N,
+                                               int g, const float *gw_lds, const u16x8 (&qnext)[2]) {
+  constexpr int D = 64;
+  // o_s rounded to bfloat16 (as the separate fusion reads it), packed: the
+  // registers of the fp32 values are free for the table rows
+  uint32_t os[8];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    os[2 * dt] = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+    os[2 * dt + 1] = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+  }
+  constexpr int kBatches = L / 4;
+  static_assert(kBatches == 2 || kBatches == 4, "8 or 16 tables");
+  const int nb = 1 << fz.P;
+  const int h = static_cast<int>(bh % fz.H);
+  const long long b = bh / fz.H;
+  const __amdgpu_buffer_rsrc_t ts_rs =
+      make_rsrc(fz.tsum + bh * L * nb * D, static_cast<uint32_t>(L * nb * D * 2));
+  const __amdgpu_buffer_rsrc_t tc_rs = make_rsrc(fz.tcnt + bh * L * nb, static_cast<uint32_t>(L * nb * 4));
+  const __amdgpu_buffer_rsrc_t xg_rs = make_rsrc(fz.x_gate + b * N * 64, static_cast<uint32_t>(N) * 128u);
+  const uint32_t lane_off = static_cast<uint32_t>(g) * 32u;  // columns g*16 .. +15, bfloat16
+  auto code_of = [&](int l) -> uint32_t { return (cw[l >> 2] >> (8 * (l & 3))) & 0xffu; };
+  auto issue = [&](int batch, u32x4 (&dst)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int l = batch * 4 + j;
+      const uint32_t off = code_of(l) * static_cast<uint32_t>(D * 2) + lane_off;
+      const int soff = l * nb * D * 2;
+      dst[2 * j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, off, soff, 0));
+      dst[2 * j + 1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, off + 16, soff, 0));
+    }
+  };
+  // gate inputs of the query (columns g*16 .. +15) and the counts of tables
+  // g, g + 4, ... (lane group g's byte of every code word)
+  u32x4 xg0, xg1;
+  float cnt[kBatches];
+  auto issue_gate_and_counts = [&]() {
+    const uint32_t xo = static_cast<uint32_t>(qidx) * 128u + lane_off;
+    xg0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xg_rs, xo, 0, 0));
+    xg1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xg_rs, xo + 16, 0, 0));
+#pragma unroll
+    for (int r = 0; r < kBatches; ++r) {
+      const uint32_t c = (cw[r] >> (8 * g)) & 0xffu;  // code of table 4 r + g
+      cnt[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          tc_rs, (static_cast<uint32_t>((4 * r + g) * nb) + c) * 4u, 0, 0));
+    }
+  };
+  const Bf16Adder adder;
+  float num[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) num[j] = 0.0f;
+  auto accumulate = [&](const u32x4 (&src)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = src[2 * j + half][e];
+          num[8 * half + 2 * e] = adder.lo(num[8 * half + 2 * e], w);
+          num[8 * half + 2 * e + 1] = adder.hi(num[8 * half + 2 * e + 1], w);
+        }
+  };
+  // two batches (8 tables) in flight; the gate inputs and counts follow the
+  // first two (three batches in flight spill at 16 tables, and measured slower)
+  u32x4 ta[8], tb[8];
+  issue(0, ta);
+  issue(1, tb);
+  issue_gate_and_counts();
+#pragma unroll
+  for (int bt = 0; bt < kBatches; bt += 2) {
+    accumulate(ta);
+    if (bt + 2 < kBatches) issue(bt + 2, ta);
+    accumulate(tb);
+    if (bt + 3 < kBatches) issue(bt + 3, tb);
+  }
+  // gate logits: this lane's 16 products, then the query's four lanes
+  float a0 = 0.0f, a1 = 0.0f, z = 0.0f;
+  const float *w0 = gw_lds + h * 64 + g * 16;
+  const float *w1 = gw_lds + (fz.H + h) * 64 + g * 16;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t word = e < 4 ? xg0[e] : xg1[e - 4];
+    const float x0 = __uint_as_float(word << 16), x1 = __uint_as_float(word & 0xffff0000u);
+    a0 = __builtin_fmaf(x0, w0[2 * e], a0);
+    a0 = __builtin_fmaf(x1, w0[2 * e + 1], a0);
+    a1 = __builtin_fmaf(x0, w1[2 * e], a1);
+    a1 = __builtin_fmaf(x1, w1[2 * e + 1], a1);
+  }
+#pragma unroll
+  for (int r = 0; r < kBatches; ++r) z += cnt[r];
+  a0 = sum_over_lane_groups<16>(a0);
+  a1 = sum_over_lane_groups<16>(a1);
+  z = sum_over_lane_groups<16>(z);
+  const float g_s = __builtin_amdgcn_rcpf(1.0f + __expf(-(a0 + fz.gate_b[h])));
+  const float g_lr = __builtin_amdgcn_rcpf(1.0f + __expf(-(a1 + fz.gate_b[fz.H + h])));
+  const float z_lr = z * (1.0f / static_cast<float>(L));
+  const float rz = z > 0.0f ? __builtin_amdgcn_rcpf(z) : 0.0f;  // (num / L) / (z / L); 0 where z = 0
+  const float mass_lr = fz.lambda * z_lr;
+  const float alpha = mass_lr > 0.0f ? __builtin_amdgcn_rcpf(1.0f + __expf(__logf(mass_lr) - lse_v)) : 1.0f;
+  const float cs = g_s * alpha, cl = g_lr * rz;
+  float y[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    y[2 * j] = __builtin_fmaf(cs, __uint_as_float(os[j] << 16), cl * num[2 * j]);
+    y[2 * j + 1] = __builtin_fmaf(cs, __uint_as_float(os[j] & 0xffff0000u), cl * num[2 * j + 1]);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) asm volatile("" : "+v"(y[0]) : "v"(qnext[kk]) : "memory");
+  const long long row = bh * N + qidx;
+  uint16_t *yrow = fz.out + row * D + g * 16;
+  *reinterpret_cast<u32x4 *>(yrow) = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                           pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+  *reinterpret_cast<u32x4 *>(yrow + 8) = u32x4{pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]),
+                                               pack_bf16x2(y[12], y[13]), pack_bf16x2(y[14], y[15])};
+  if (fz.o_s) {
+    uint16_t *orow = fz.o_s + row * D + g * 16;
+    *reinterpret_cast<u32x4 *>(orow) = u32x4{os[0], os[1], os[2], os[3]};
+    *reinterpret_cast<u32x4 *>(orow + 8) = u32x4{os[4], os[5], os[6], os[7]};
+  }
+  if (fz.o_lr) {
+    float *lrow = fz.o_lr + row * D + g * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<f32x4 *>(lrow + 4 * j) =
+          f32x4{num[4 * j] * rz, num[4 * j + 1] * rz, num[4 * j + 2] * rz, num[4 * j + 3] * rz};
+  }
+  if (g == 0) {
+    if (fz.lse) fz.lse[row] = lse_v;
+    if (fz.z_lr) fz.z_lr[row] = z_lr;
+    if (fz.alpha) fz.alpha[row] = alpha;
+    if (fz.g_s) fz.g_s[row] = g_s;
+    if (fz.g_lr) fz.g_lr[row] = g_lr;
+  }
+}
+
+template <bool kIdent, int kFuseL>
 __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N,
     int tiles_per_seg, long long n_tiles, long long tiles_per_wg, float scale_log2,
-    uint16_t *__restrict__ o_s, float *__restrict__ lse) {
+    uint16_t *__restrict__ o_s, float *__restrict__ lse, FuseArgs fz) {
   constexpr int D = 64, W = 128;
   constexpr int kConsumerWaves = 8;
   constexpr int kPThreads = 256;
@@ -561,12 +740,19 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
   constexpr int kVPer = kVPairs / kPThreads;   // 2
   extern __shared__ __align__(16) uint16_t smem[];
   int32_t *qidx_lds = reinterpret_cast<int32_t *>(smem + 3 * kSlotElems);  // [4][W], tile m in m % 4
+  float *gw_lds = reinterpret_cast<float *>(qidx_lds + 4 * W);  // fused: gate weights [2][H][64]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long t_begin = xcd_logical_block(blockIdx.x, gridDim.x) * tiles_per_wg;
   const long long t_end = t_begin + tiles_per_wg < n_tiles ? t_begin + tiles_per_wg : n_tiles;
   if (t_begin >= t_end) return;  // whole workgroup
+  if constexpr (kFuseL > 0) {  // visible to the computing waves after the first barrier
+    for (int i = tid; i < 2 * fz.H * 64; i += 768) gw_lds[i] = fz.gate_w[i];
+  }
+  // V^T row of column c: the O^T tile dt holds columns g*16 + dt*4 + i in its
+  // rows 4 g + i, so that lane group g's results are columns g*16 .. +15
+  auto vt_row = [](int c) { return ((c >> 2) & 3) * 16 + (c >> 4) * 4 + (c & 3); };
   auto chunk_of = [&](long long t) { return static_cast<int>(t % tiles_per_seg); };
   auto seg_of = [&](long long t) { return (t / tiles_per_seg) * N; };
   // piece of a row at a 32-bit byte offset from its segment's first row (the
@@ -626,7 +812,7 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t word = static_cast<uint32_t>(r.v0[p][e]) | (static_cast<uint32_t>(r.v1[p][e]) << 16);
-          *reinterpret_cast<uint32_t *>(Vt + (ch * 8 + e) * kVRow + 2 * jp) = word;
+          *reinterpret_cast<uint32_t *>(Vt + vt_row(ch * 8 + e) * kVRow + 2 * jp) = word;
         }
       }
     };
@@ -716,6 +902,25 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) bq[kk] = __builtin_bit_cast(bf16x8, qnext[kk]);
     const int qidx = qidx_next;
+    const long long bh = t / tiles_per_seg;
+    // fused: the query's L table codes, in flight during the attention (a
+    // query's codes are contiguous: kFuseL bytes)
+    uint32_t cw[kFuseL > 0 ? kFuseL / 4 : 1];
+    if constexpr (kFuseL > 0) {
+      const __amdgpu_buffer_rsrc_t qc_rs =
+          make_rsrc(fz.qcodes + bh * N * kFuseL, static_cast<uint32_t>(N) * kFuseL);
+      const uint32_t off = static_cast<uint32_t>(qidx) * kFuseL;
+      if constexpr (kFuseL == 16) {
+        const u32x4 w4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qc_rs, off, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cw[e] = w4[e];
+      } else {
+        static_assert(kFuseL == 8, "8 or 16 tables");
+        const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(qc_rs, off, 0, 0);
+        cw[0] = w2[0];
+        cw[1] = w2[1];
+      }
+    }
     {  // the next tile's query rows, in flight during this tile
       const bool more = t + 1 < t_end;
       qidx_next = more ? qidx_lds[((m_idx + 1) & 3) * W + qrow] : qidx;
@@ -739,23 +944,30 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
     const long long seg = seg_of(t);
     const float l_tot = l_acc[0];
     float inv = 1.0f / l_tot;
+    const float lse_v = (m + log2f(l_tot)) * 0.69314718055994530942f;
+    // lane group g holds columns g*16 + dt*4 + i of its query in o[dt][i]
+    if constexpr (kFuseL == 0) {
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) asm volatile("" : "+v"(inv) : "v"(qnext[kk]) : "memory");
-    uint16_t *orow = o_s + (seg + qidx) * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const uint2 outv = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
-                          pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
-      *reinterpret_cast<uint2 *>(orow + dt * 16 + g * 4) = outv;
+      for (int kk = 0; kk < D / 32; ++kk) asm volatile("" : "+v"(inv) : "v"(qnext[kk]) : "memory");
+      uint16_t *orow = o_s + (seg + qidx) * D + g * 16;
+      *reinterpret_cast<u32x4 *>(orow) =
+          u32x4{pack_bf16x2(o[0][0] * inv, o[0][1] * inv), pack_bf16x2(o[0][2] * inv, o[0][3] * inv),
+                pack_bf16x2(o[1][0] * inv, o[1][1] * inv), pack_bf16x2(o[1][2] * inv, o[1][3] * inv)};
+      *reinterpret_cast<u32x4 *>(orow + 8) =
+          u32x4{pack_bf16x2(o[2][0] * inv, o[2][1] * inv), pack_bf16x2(o[2][2] * inv, o[2][3] * inv),
+                pack_bf16x2(o[3][0] * inv, o[3][1] * inv), pack_bf16x2(o[3][2] * inv, o[3][3] * inv)};
+      if (g == 0) lse[seg + qidx] = lse_v;
+    } else {
+      fused_epilogue<kFuseL>(fz, o, inv, lse_v, cw, bh, qidx, N, g, gw_lds, qnext);
     }
-    if (g == 0) lse[seg + qidx] = (m + log2f(l_tot)) * 0.69314718055994530942f;
   }
 }
 
-// LDS bytes of the sliding-window kernel: three chunk slots and four
-// query-index slots.
-constexpr size_t attn_slide_lds_bytes() {
-  return 3 * (static_cast<size_t>(128) * (64 + 8) + static_cast<size_t>(64) * (128 + 4)) * 2 + 4 * 128 * 4;
+// LDS bytes of the sliding-window kernel: three chunk slots, four
+// query-index slots and, fused, the gate weights of every head.
+constexpr size_t attn_slide_lds_bytes(int fused_heads) {
+  return 3 * (static_cast<size_t>(128) * (64 + 8) + static_cast<size_t>(64) * (128 + 4)) * 2 + 4 * 128 * 4 +
+         static_cast<size_t>(fused_heads) * 2 * 64 * 4;
 }
 
 // fp32 inputs: one thread per sorted query, binary32 arithmetic throughout.
@@ -835,19 +1047,19 @@ hipError_t launch_bf16_pc(const Geometry &g, const void *q, const void *k, const
   return hipGetLastError();
 }
 
-template <bool kIdent>
+template <bool kIdent, int kFuseL>
 hipError_t launch_bf16_slide(const Geometry &g, const void *q, const void *k, const void *v,
                              const int32_t *pq, const int32_t *pk, void *o_s, float *lse, float scale_log2,
-                             hipStream_t stream) {
+                             const FuseArgs &fz, hipStream_t stream) {
   const int tiles_per_seg = g.N / 128;
   const long long n_tiles = static_cast<long long>(tiles_per_seg) * g.BH;
   long long wgs = (g.cus + kXcdCount - 1) / kXcdCount * kXcdCount;
   if (wgs > n_tiles) wgs = (n_tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
   const long long tiles_per_wg = (n_tiles + wgs - 1) / wgs;
-  hipLaunchKernelGGL((elsaa_k3_chunk_attn_slide<kIdent>), dim3(static_cast<unsigned>(wgs)), dim3(768),
-                     attn_slide_lds_bytes(), stream, static_cast<const uint16_t *>(q),
+  hipLaunchKernelGGL((elsaa_k3_chunk_attn_slide<kIdent, kFuseL>), dim3(static_cast<unsigned>(wgs)), dim3(768),
+                     attn_slide_lds_bytes(kFuseL > 0 ? g.H : 0), stream, static_cast<const uint16_t *>(q),
                      static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), pq, pk, g.N,
-                     tiles_per_seg, n_tiles, tiles_per_wg, scale_log2, static_cast<uint16_t *>(o_s), lse);
+                     tiles_per_seg, n_tiles, tiles_per_wg, scale_log2, static_cast<uint16_t *>(o_s), lse, fz);
   return hipGetLastError();
 }
 
@@ -858,7 +1070,8 @@ hipError_t launch_bf16_any(const Geometry &g, const void *q, const void *k, cons
   // 256-key window of w = 128) or 2, keeping LDS <= 72 KB (two workgroups
   // per CU)
   const bool wide = g.w % 128 == 0;
-  if (g.D == 64 && g.w == 128) return launch_bf16_slide<kIdent>(g, q, k, v, pq, pk, o_s, lse, scale_log2, stream);
+  if (g.D == 64 && g.w == 128)
+    return launch_bf16_slide<kIdent, 0>(g, q, k, v, pq, pk, o_s, lse, scale_log2, FuseArgs{}, stream);
   if (g.D == 64)
     return wide ? launch_bf16_pc<64, 4, kIdent>(g, q, k, v, pq, pk, o_s, lse, scale_log2, stream)
                 : launch_bf16<64, 64, 2, kIdent>(g, q, k, v, pq, pk, o_s, lse, scale_log2, stream);
@@ -889,6 +1102,52 @@ hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *
                        static_cast<const float *>(v), pq, pk, g.N, g.w, scale_log2,
                        static_cast<float *>(o_s), buf.lse);
   return hipGetLastError();
+}
+
+bool attention_fusable(const Geometry &g) {
+  // the sliding-window kernel's shape (bfloat16, d = 64, w = 128), 8 or 16
+  // tables of byte codes, gate inputs of width 64, both branches, and the
+  // gate weights of every head in LDS
+  return g.bf16 && g.D == 64 && g.w == 128 && (g.L == 8 || g.L == 16) && g.P <= 8 && g.DG == 64 &&
+         g.run_sparse && g.run_race && g.H <= 64;
+}
+
+hipError_t launch_attention_fused(const Geometry &g, const void *q, const void *k, const void *v,
+                                  const void *x_gate, const float *gate_w, const float *gate_b,
+                                  const Buffers &buf, const elsaa_aux_t *aux, void *out, hipStream_t stream) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(g.D));
+  const int32_t *pq = g.identity ? nullptr : buf.perm;
+  const int32_t *pk = g.identity ? nullptr : buf.perm + g.rows;
+  FuseArgs fz{};
+  fz.qcodes = static_cast<const uint8_t *>(buf.rcode);
+  fz.tsum = static_cast<const uint16_t *>(buf.tsum);
+  fz.tcnt = buf.tcnt;
+  fz.x_gate = static_cast<const uint16_t *>(x_gate);
+  fz.gate_w = gate_w;
+  fz.gate_b = gate_b;
+  fz.H = g.H;
+  fz.P = g.P;
+  fz.lambda = g.lambda;
+  fz.out = static_cast<uint16_t *>(out);
+  if (aux) {
+    fz.o_s = static_cast<uint16_t *>(aux->o_sparse);
+    fz.lse = aux->lse_s;
+    fz.z_lr = aux->z_lr;
+    fz.alpha = aux->alpha;
+    fz.g_s = aux->g_s;
+    fz.g_lr = aux->g_lr;
+    fz.o_lr = aux->o_lowrank;
+  }
+  auto go = [&](auto ident, auto fl) {
+    return launch_bf16_slide<decltype(ident)::value, decltype(fl)::value>(g, q, k, v, pq, pk, nullptr, nullptr,
+                                                                          scale_log2, fz, stream);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using L8 = std::integral_constant<int, 8>;
+  using L16 = std::integral_constant<int, 16>;
+  if (g.identity) return g.L == 16 ? go(T{}, L16{}) : go(T{}, L8{});
+  return g.L == 16 ? go(F{}, L16{}) : go(F{}, L8{});
 }
 
 }  // namespace elsaa

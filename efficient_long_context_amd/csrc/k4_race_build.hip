@@ -269,7 +269,7 @@ template <typename VT, int D, typename PT>
 __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
     const VT *__restrict__ v, const PT *__restrict__ rperm, const int32_t *__restrict__ rstart,
     const int32_t *__restrict__ rpart, int N, int L, int P, int parts, long long waves_total,
-    VT *__restrict__ tsum) {
+    int xcd_local, VT *__restrict__ tsum) {
   using PC = Piece<VT, D>;
   constexpr int kCols = PC::kCols, kLPR = PC::kLanesPerRow;
   constexpr int kRPI = PC::kRowsPerLoad;
@@ -279,7 +279,12 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   const int nb = 1 << P;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const long long u = xcd_logical_block(blockIdx.x, gridDim.x) * kGatherWaves + wave;
+  // xcd_local: consecutive workgroups (one (b, h) after another) on one XCD,
+  // whose L2 then holds that (b, h)'s value rows; otherwise workgroups in
+  // dispatch order, so every XCD works on the same (b, h) at once and its
+  // value rows (too many for one L2) stay in the last-level cache
+  const long long wg = xcd_local ? xcd_logical_block(blockIdx.x, gridDim.x) : static_cast<long long>(blockIdx.x);
+  const long long u = wg * kGatherWaves + wave;
   if (u >= waves_total) return;  // whole wave; the kernel has no barriers
   uint32_t *stage = stage_all[wave];
   const int prt = static_cast<int>(u % parts);
@@ -423,9 +428,12 @@ hipError_t launch_race_build_pt(const Geometry &g, const void *v, const Buffers 
   auto gather = [&](auto vt, auto dc) {
     using VT = decltype(vt);
     constexpr int D = decltype(dc)::value;
+    // one (b, h)'s value rows fit an XCD's 4 MB L2 at most a few times over:
+    // keep its gathers on one XCD; beyond that spread each (b, h) over all
+    const int xcd_local = static_cast<long long>(g.N) * D * sizeof(VT) <= (4ll << 20) ? 1 : 0;
     hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT>), grid, dim3(kGatherWaves * 64), 0, stream,
                        static_cast<const VT *>(v), rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts,
-                       waves_total, static_cast<VT *>(buf.tsum));
+                       waves_total, xcd_local, static_cast<VT *>(buf.tsum));
   };
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;

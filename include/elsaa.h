@@ -148,7 +148,20 @@ typedef struct {
                         attention, 4 gather/gates/fusion) on params->stream,
                         so elapsed(2i, 2i+1) times stage i.  The caller
                         creates and owns the events.                             */
+  uint32_t options;    /* bit set of ELSAA_OPT_* (0 = defaults)                   */
 } elsaa_params_t;
+
+/* elsaa_params_t.options bits. */
+enum {
+  /* Run the RACE gather, gates and fusion in the epilogue of the chunk
+   * attention, so the sparse output and its LSE never go to memory (the
+   * workspace holds neither).  Applies to bfloat16, d = 64, chunk = 128, 8 or
+   * 16 tables of P <= 8 bits, d_gate = 64, H <= 64 and ELSAA_VARIANT_FULL or
+   * NO_ALPHA; elsewhere it is ignored.  Off by default: on MI355X its per-tile
+   * table gathers run after the tile's attention instead of beside it, and the
+   * two separate kernels are faster (see the design notes). */
+  ELSAA_OPT_FUSED_EPILOGUE = 1u << 0
+};
 
 /* Host-only check of every field of *p except the device pointers' targets.
  * Returns ELSAA_OK or a negative status; never touches the device. */

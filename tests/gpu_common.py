@@ -24,7 +24,7 @@ def to_device(inp: workloads.Inputs, device):
                 gate_b=torch.from_numpy(inp.gate_b).to(device))
 
 
-def run_gpu(inp: workloads.Inputs, lam=None, device="cuda:0", variant="full"):
+def run_gpu(inp: workloads.Inputs, lam=None, device="cuda:0", variant="full", options=0):
     import torch
 
     import efficient_long_context_amd as elsaa
@@ -34,7 +34,7 @@ def run_gpu(inp: workloads.Inputs, lam=None, device="cuda:0", variant="full"):
     f = elsaa.Forward(B=wl.B, H=wl.H, N=wl.N, d=wl.d, d_gate=wl.d_gate, sort_bits=wl.sort_bits,
                       chunk=wl.chunk, race_tables=wl.race_tables, race_bits=wl.race_bits,
                       lam=wl.lam if lam is None else lam, dtype=wl.dtype, variant=variant,
-                      device=dev, aux=True)
+                      options=options, device=dev, aux=True)
     out = f(x["q"], x["k"], x["v"], x["x_gate"], x["hyperplanes"], x["gate_w"], x["gate_b"])
     torch.cuda.synchronize()
     res = {"y": out.float().cpu().numpy().astype(np.float64)}

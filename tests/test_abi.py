@@ -50,9 +50,17 @@ def test_valid_params_and_workspace_size():
     assert elsaa.validate(p) == elsaa.OK
     ws = elsaa.workspace_bytes(p)
     rows = 2 * 12 * 32768
-    # codes + perms + tables (bf16 sums, binary32 counts) + o_s + lse at least
+    # codes + perms + tables (bf16 sums, binary32 counts) at least
     tables = 24 * 16 * 256 * (64 * 2 + 4)
-    assert ws >= 2 * rows * 2 + 2 * rows * 16 + 2 * rows * 4 + tables + rows * 64 * 2 + rows * 4
+    base = 2 * rows * 2 + 2 * rows * 16 + 2 * rows * 4 + tables
+    # the separate fusion kernel reads o_s and its LSE back; with the fused
+    # epilogue neither goes to memory
+    assert ws >= base + rows * 64 * 2 + rows * 4
+    fused = elsaa.workspace_bytes(params(options=elsaa.OPT_FUSED_EPILOGUE))
+    assert base <= fused < base + rows * 64 * 2
+    # where the fused epilogue does not apply (12 tables) the option is ignored
+    assert (elsaa.workspace_bytes(params(race_tables=12, options=elsaa.OPT_FUSED_EPILOGUE))
+            == elsaa.workspace_bytes(params(race_tables=12)))
     assert ws < 400 * 2 ** 20
 
 
@@ -76,6 +84,7 @@ def test_valid_params_and_workspace_size():
     (dict(d_gate=1024), elsaa.ERR_UNSUPPORTED),
     (dict(variant=4), elsaa.ERR_INVALID_ARG),
     (dict(variant=-1), elsaa.ERR_INVALID_ARG),
+    (dict(options=2), elsaa.ERR_INVALID_ARG),
     # per-(b, h) byte extents at 2^31 and beyond: the kernels' 32-bit offsets
     (dict(B=1, H=1, d=128, N=1 << 24), elsaa.ERR_UNSUPPORTED),                    # bf16, 2^32 B
     (dict(B=1, H=1, d=128, N=1 << 23), elsaa.ERR_UNSUPPORTED),                    # bf16, 2^31 B
@@ -169,7 +178,8 @@ def test_forward_rejects_misaligned_pointers():
 def test_struct_layout_matches_header():
     # elsaa_params_t: 9 int32, float, two enums (dtype, variant), then 8-byte
     # aligned pointers
-    assert ctypes.sizeof(elsaa.ElsaaParams) == 48 + 8 * 2 + 8 + 8 + 8 + 8 + 8
+    assert ctypes.sizeof(elsaa.ElsaaParams) == 48 + 8 * 2 + 8 + 8 + 8 + 8 + 8 + 8
     assert elsaa.ElsaaParams.variant.offset == 44
     assert elsaa.ElsaaParams.gate_w.offset == 48
+    assert elsaa.ElsaaParams.options.offset == 48 + 8 * 7
     assert ctypes.sizeof(elsaa.ElsaaAux) == 15 * 8

@@ -95,6 +95,30 @@ def test_variant_parity(case, variant):
     print(f"[variant] {case} {variant}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
 
 
+FUSED_CASES = {
+    "text32k-L16": ("text32k-bf16", dict(B=1, H=2, N=4096), "full"),
+    "vision16k-L8": ("vision16k-bf16", dict(B=1, H=2), "full"),
+    "text32k-ns0": ("text32k-bf16", dict(B=1, H=2, N=4096, sort_bits=0), "full"),
+    "text32k-no-alpha": ("text32k-bf16", dict(B=2, H=3, N=2048), "no_alpha"),
+    "text32k-lambda0.25": ("text32k-bf16", dict(B=1, H=2, N=2048, lam=0.25), "full"),
+}
+
+
+@pytest.mark.parametrize("case", list(FUSED_CASES))
+def test_fused_epilogue_parity(case):
+    """The chunk attention with the RACE gather, gates and fusion in its
+    epilogue (ELSAA_OPT_FUSED_EPILOGUE) against the oracle."""
+    import efficient_long_context_amd as elsaa
+    name, over, variant = FUSED_CASES[case]
+    wl = workloads.workload(name, **over)
+    inp = workloads.generate(wl, seed=19)
+    print(f"[fused] {case}: B={wl.B} H={wl.H} N={wl.N}", flush=True)
+    g = run_gpu(inp, variant=variant, options=elsaa.OPT_FUSED_EPILOGUE)
+    r = run_oracle(inp, variant=variant)
+    errs = compare_variant(g, r, wl.dtype, variant, f"fused {case}")
+    print(f"[fused] {case}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+
+
 def test_exact_attention_special_case():
     """sort_bits = 0 and chunk = N: the sparse branch is dense softmax attention."""
     wl = workloads.workload("small-bf16", B=1, H=2, N=1024, chunk=1024, sort_bits=0)
