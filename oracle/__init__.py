@@ -66,6 +66,8 @@ def _load():
         lib.oracle_race_query.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P]
         lib.oracle_gates.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
         lib.oracle_fuse.argtypes = [P, P, P, P, P, P, f64, i64, i32, P, P]
+        lib.oracle_backward.argtypes = [P] * 17 + [i32] * 8 + [f64, i32] + [P] * 7
+        lib.oracle_backward.restype = i32
         _lib = lib
     return _lib
 
@@ -264,3 +266,45 @@ def forward(q, k, v, x_gate, hyperplanes, gate_w, gate_b, *, sort_bits: int,
         alpha, y = np.ones(lse.shape), o_s.copy()
     return OracleResult(cq, ck, rq, rk, pq, pk, o_s, lse, sums, counts, o_lr, z_lr,
                         g_s, g_lr, alpha, y, pairs, time.perf_counter() - t0)
+
+
+# --------------------------------------------------------------- backward ----
+
+@dataclass
+class OracleGrads:
+    dq: np.ndarray
+    dk: np.ndarray
+    dv: np.ndarray
+    dx_gate: np.ndarray
+    dgate_w: np.ndarray
+    dgate_b: np.ndarray
+    dlambda: float
+    fwd: OracleResult
+
+
+def backward(q, k, v, x_gate, hyperplanes, gate_w, gate_b, dy, *, sort_bits: int, chunk: int,
+             race_tables_n: int, race_bits: int, lam: float, variant: str = "full") -> OracleGrads:
+    """Gradients of sum(y * dy) with respect to q, k, v, x_gate, W_g, b_g and lambda,
+    for the forward pass above on the same inputs (its intermediates are recomputed
+    by running it).  Hash codes, permutations and counts are constants."""
+    fwd = forward(q, k, v, x_gate, hyperplanes, gate_w, gate_b, sort_bits=sort_bits, chunk=chunk,
+                  race_tables_n=race_tables_n, race_bits=race_bits, lam=lam, variant=variant)
+    q = _f64(q); k = _f64(k); v = _f64(v); x_gate = _f64(x_gate); gate_w = _f64(gate_w)
+    dy = _f64(dy)
+    B, H, N, d = q.shape
+    dg = x_gate.shape[-1]
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+               dx_gate=np.zeros_like(x_gate), dgate_w=np.zeros((2, H, dg)), dgate_b=np.zeros((2, H)))
+    dl = ctypes.c_double(0.0)
+    i32 = lambda a: np.ascontiguousarray(a, dtype=np.int32)
+    keep = [i32(fwd.perm_q), i32(fwd.perm_k), i32(fwd.race_code_q), i32(fwd.race_code_k),
+            _f64(fwd.o_s), _f64(fwd.lse), _f64(fwd.o_lr), _f64(fwd.z_lr), _f64(fwd.g_s),
+            _f64(fwd.g_lr), _f64(fwd.alpha)]
+    st = _load().oracle_backward(
+        _p(q), _p(k), _p(v), _p(x_gate), _p(gate_w), *[_p(a) for a in keep], _p(dy),
+        B, H, N, d, dg, chunk, race_tables_n, race_bits, float(lam), VARIANTS.index(variant),
+        _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dx_gate"]), _p(out["dgate_w"]),
+        _p(out["dgate_b"]), ctypes.byref(dl))
+    if st != 0:
+        raise MemoryError("oracle_backward: allocation failed")
+    return OracleGrads(dlambda=dl.value, fwd=fwd, **out)

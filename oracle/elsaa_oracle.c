@@ -319,3 +319,169 @@ void oracle_fuse(const double *o_s, const double *lse, const double *o_lr,
                                g_lr[idx] * o_lr[(size_t)idx * d + e];
   }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Backward pass: the exact gradient of the forward output above, for          */
+/* training ("ELSAA: Efficient Low-Rank and Sparse Attention Approximation for */
+/* Training Transformers", first paragraph: a framework for training, with a   */
+/* learnable lambda; "ELSAA combines sparsity and low-rank methods to reduce   */
+/* transformer attention complexity": it acts on the attention computation at */
+/* run time, so gradients flow through it).  Given dL/dy, it returns dL/dq,    */
+/* dL/dk, dL/dv, dL/dx_gate, dL/dW_g, dL/db_g and dL/dlambda.  Hash codes,     */
+/* permutations and bucket counts are piecewise constant in the inputs and     */
+/* carry no gradient.  Derivation, per query i (original index):               */
+/*   y = c_s o_s + c_lr o_lr with (c_s, c_lr) = (g_s alpha, g_lr) for the full */
+/*   operator, (g_s, g_lr) with alpha fixed to one, (0, 1) RACE only, (1, 0)   */
+/*   sparse only;                                                              */
+/*   alpha = Z_s / (Z_s + lambda Z_lr), Z_s = exp(lse):                        */
+/*     d alpha / d lse = alpha (1 - alpha),                                    */
+/*     d alpha / d lambda = -alpha^2 Z_lr / Z_s;                               */
+/*   sparse branch: p_ij = exp(s_ij - lse_i) over the window, o_s = sum p v,   */
+/*     lse = log sum exp s:  with do = dL/do_s and D_i = do_i . o_s,i,         */
+/*     ds_ij = p_ij (do_i . v_j - D_i + dL/dlse_i), s_ij = q_i . k_j / sqrt d; */
+/*   low-rank branch: o_lr = num / Z_lr, num = (1/L) sum_l T_l[c_l(q)], Z_lr   */
+/*     constant: dT_l[b] = (1/L) sum over queries in bucket b of do_lr / Z_lr, */
+/*     and dv_j = sum_l dT_l[c_l(k_j)] (T_l[b] sums the values of its keys);   */
+/*   gates: g = sigmoid(a), da = dg g (1 - g), a = <x_gate, W> + b.            */
+/* Arrays are [B][H][n][...] (x_gate [B][n][dg], W_g [2][H][dg], b_g [2][H]);  */
+/* perms [B H][n], RACE codes [B H][n][L].  The outputs are overwritten.       */
+/* ------------------------------------------------------------------------- */
+int oracle_backward(const double *q, const double *k, const double *v, const double *x_gate,
+                    const double *gate_w, const int32_t *perm_q, const int32_t *perm_k,
+                    const int32_t *rq, const int32_t *rk, const double *o_s, const double *lse,
+                    const double *o_lr, const double *z_lr, const double *g_s, const double *g_lr,
+                    const double *alpha, const double *dy, int B, int H, int n, int d, int dg,
+                    int w, int L, int P, double lambda, int variant, double *dq, double *dk,
+                    double *dv, double *dx_gate, double *dgate_w, double *dgate_b,
+                    double *dlambda) {
+  const long segs = (long)B * H;
+  const long rows = segs * n;
+  const long nb = 1L << P;
+  const double scale = 1.0 / sqrt((double)d);
+  double *da_s = (double *)calloc((size_t)rows, sizeof(double));
+  double *da_lr = (double *)calloc((size_t)rows, sizeof(double));
+  double *dlam_seg = (double *)calloc((size_t)segs, sizeof(double));
+  int fail = (!da_s || !da_lr || !dlam_seg);
+  long s;
+  if (!fail) {
+#pragma omp parallel for schedule(dynamic) reduction(| : fail)
+    for (s = 0; s < segs; ++s) {
+      const size_t base = (size_t)s * n;
+      double *do_s = (double *)malloc(sizeof(double) * (size_t)n * d);
+      double *dlse = (double *)malloc(sizeof(double) * (size_t)n);
+      double *dT = (double *)calloc((size_t)L * nb * d, sizeof(double));
+      if (!do_s || !dlse || !dT) {
+        free(do_s); free(dlse); free(dT);
+        fail = 1;
+        continue;
+      }
+      for (size_t e = base * d; e < (base + n) * d; ++e) dq[e] = dk[e] = dv[e] = 0.0;
+      double dlam = 0.0;
+      /* 1. the fusion, per query */
+      for (int i = 0; i < n; ++i) {
+        const size_t r = base + i;
+        const double *dyi = dy + r * d, *osi = o_s + r * d, *olri = o_lr + r * d;
+        double dy_os = 0.0, dy_olr = 0.0;
+        for (int e = 0; e < d; ++e) {
+          dy_os += dyi[e] * osi[e];
+          dy_olr += dyi[e] * olri[e];
+        }
+        double c_s, c_lr;
+        dlse[i] = 0.0;
+        if (variant == 0) {  /* full operator */
+          c_s = g_s[r] * alpha[r];
+          c_lr = g_lr[r];
+          const double dalpha = g_s[r] * dy_os;
+          dlse[i] = dalpha * alpha[r] * (1.0 - alpha[r]);
+          if (z_lr[r] > 0.0) dlam += dalpha * (-alpha[r] * alpha[r] * exp(log(z_lr[r]) - lse[r]));
+          da_s[r] = alpha[r] * dy_os * g_s[r] * (1.0 - g_s[r]);
+          da_lr[r] = dy_olr * g_lr[r] * (1.0 - g_lr[r]);
+        } else if (variant == 1) {  /* alpha fixed to one */
+          c_s = g_s[r];
+          c_lr = g_lr[r];
+          da_s[r] = dy_os * g_s[r] * (1.0 - g_s[r]);
+          da_lr[r] = dy_olr * g_lr[r] * (1.0 - g_lr[r]);
+        } else if (variant == 2) {  /* RACE only */
+          c_s = 0.0;
+          c_lr = 1.0;
+        } else {  /* sparse only */
+          c_s = 1.0;
+          c_lr = 0.0;
+        }
+        for (int e = 0; e < d; ++e) do_s[(size_t)i * d + e] = c_s * dyi[e];
+        /* low-rank branch: scatter do_lr / (L Z_lr) into the query's buckets */
+        if (c_lr != 0.0 && z_lr[r] > 0.0) {
+          for (int l = 0; l < L; ++l) {
+            double *t = dT + ((size_t)l * nb + rq[r * L + l]) * d;
+            for (int e = 0; e < d; ++e) t[e] += c_lr * dyi[e] / ((double)L * z_lr[r]);
+          }
+        }
+      }
+      dlam_seg[s] = dlam;
+      /* 2. sparse branch: every (query, key) pair of every window */
+      for (int rank = 0; rank < n; ++rank) {
+        const int c = rank / w;
+        const int lo = c > 0 ? (c - 1) * w : 0;
+        const int hi = (c + 1) * w;
+        const int i = perm_q[base + rank];
+        const double *qi = q + (base + i) * d, *doi = do_s + (size_t)i * d, *osi = o_s + (base + i) * d;
+        double D = 0.0;
+        for (int e = 0; e < d; ++e) D += doi[e] * osi[e];
+        for (int t = lo; t < hi; ++t) {
+          const int j = perm_k[base + t];
+          const double *kj = k + (base + j) * d, *vj = v + (base + j) * d;
+          double sij = 0.0, dp = 0.0;
+          for (int e = 0; e < d; ++e) {
+            sij += qi[e] * kj[e];
+            dp += doi[e] * vj[e];
+          }
+          const double p = exp(sij * scale - lse[base + i]);
+          const double ds = p * (dp - D + dlse[i]);
+          for (int e = 0; e < d; ++e) {
+            dq[(base + i) * d + e] += ds * kj[e] * scale;
+            dk[(base + j) * d + e] += ds * qi[e] * scale;
+            dv[(base + j) * d + e] += p * doi[e];
+          }
+        }
+      }
+      /* 3. low-rank branch: each key collects its buckets' gradients */
+      for (int j = 0; j < n; ++j) {
+        for (int l = 0; l < L; ++l) {
+          const double *t = dT + ((size_t)l * nb + rk[(base + j) * L + l]) * d;
+          for (int e = 0; e < d; ++e) dv[(base + j) * d + e] += t[e];
+        }
+      }
+      free(do_s); free(dlse); free(dT);
+    }
+  }
+  if (fail) {
+    free(da_s); free(da_lr); free(dlam_seg);
+    return -1;
+  }
+  /* 4. gates: dW_g, db_g over every (batch, token); dx_gate over the heads */
+  for (long e = 0; e < 2L * H * dg; ++e) dgate_w[e] = 0.0;
+  for (long e = 0; e < 2L * H; ++e) dgate_b[e] = 0.0;
+  for (long e = 0; e < (long)B * n * dg; ++e) dx_gate[e] = 0.0;
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h)
+      for (int i = 0; i < n; ++i) {
+        const size_t r = ((size_t)b * H + h) * n + i;
+        const double *x = x_gate + ((size_t)b * n + i) * dg;
+        double *dx = dx_gate + ((size_t)b * n + i) * dg;
+        const double *w0 = gate_w + (size_t)h * dg, *w1 = gate_w + ((size_t)H + h) * dg;
+        double *dw0 = dgate_w + (size_t)h * dg, *dw1 = dgate_w + ((size_t)H + h) * dg;
+        for (int e = 0; e < dg; ++e) {
+          dw0[e] += da_s[r] * x[e];
+          dw1[e] += da_lr[r] * x[e];
+          dx[e] += da_s[r] * w0[e] + da_lr[r] * w1[e];
+        }
+        dgate_b[h] += da_s[r];
+        dgate_b[H + h] += da_lr[r];
+      }
+  double dl = 0.0;
+  for (s = 0; s < segs; ++s) dl += dlam_seg[s];
+  *dlambda = variant == 0 ? dl : 0.0;
+  (void)lambda;
+  free(da_s); free(da_lr); free(dlam_seg);
+  return 0;
+}
