@@ -26,7 +26,8 @@ VARIANTS = {"full": 0, "no_alpha": 1, "race_only": 2, "sparse_only": 3}
 
 # Every symbol include/elsaa.h declares.
 EXPORTS = ("elsaa_validate", "elsaa_workspace_bytes", "elsaa_forward", "elsaa_forward_noalloc",
-           "elsaa_status_str", "elsaa_last_error", "elsaa_abi_version")
+           "elsaa_backward_workspace_bytes", "elsaa_backward", "elsaa_status_str", "elsaa_last_error",
+           "elsaa_abi_version")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ELSAA_NOALLOC_SCRATCH_BYTES
 
 AUX_FIELDS = ("sort_code_q", "sort_code_k", "race_code_q", "race_code_k", "perm_q", "perm_k",
@@ -86,6 +87,11 @@ def lib():
         L.elsaa_forward.restype = ctypes.c_int
         L.elsaa_forward_noalloc.argtypes = L.elsaa_forward.argtypes
         L.elsaa_forward_noalloc.restype = ctypes.c_int
+        L.elsaa_backward_workspace_bytes.argtypes = [ctypes.POINTER(ElsaaParams)]
+        L.elsaa_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.elsaa_backward.argtypes = ([ctypes.c_void_p] * 6 + [ctypes.POINTER(ElsaaParams), ctypes.c_void_p,
+                                     ctypes.c_size_t] + [ctypes.c_void_p] * 7)
+        L.elsaa_backward.restype = ctypes.c_int
         L.elsaa_status_str.argtypes = [ctypes.c_int]
         L.elsaa_status_str.restype = ctypes.c_char_p
         L.elsaa_last_error.restype = ctypes.c_char_p
@@ -226,6 +232,51 @@ class Forward:
         if st != OK:
             raise ElsaaError(st, last_error())
         return self.out
+
+
+class Backward:
+    """Backward pass of a Forward object's last call (its workspace holds that
+    call's results).  Owns the backward scratch and the gradient tensors;
+    calling it enqueues elsaa_backward on torch's current stream and returns
+    (dq, dk, dv, dx_gate, dgate_w, dgate_b, dlambda) as tensors."""
+
+    def __init__(self, fwd: "Forward"):
+        torch = fwd.torch
+        self.fwd = fwd
+        B, H, N, d, dg = (fwd.shape[x] for x in ("B", "H", "N", "d", "d_gate"))
+        probe = make_params(B, H, N, d, dg, dtype=fwd.dtype_code, gate_w_ptr=1, gate_b_ptr=1, **fwd.cfg)
+        self.ws_bytes = lib().elsaa_backward_workspace_bytes(ctypes.byref(probe))
+        if self.ws_bytes == 0:
+            raise ElsaaError(ERR_UNSUPPORTED, last_error())
+        dev, dt = fwd.device, fwd.tdtype
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.dq = torch.empty((B, H, N, d), dtype=dt, device=dev)
+        self.dk = torch.empty_like(self.dq)
+        self.dv = torch.empty_like(self.dq)
+        self.dx_gate = torch.empty((B, N, dg), dtype=dt, device=dev)
+        self.dgate_w = torch.empty((2, H, dg), dtype=torch.float32, device=dev)
+        self.dgate_b = torch.empty((2, H), dtype=torch.float32, device=dev)
+        self.dlambda = torch.empty((1,), dtype=torch.float32, device=dev)
+
+    def __call__(self, q, k, v, x_gate, gate_w, gate_b, dy, stream=None):
+        f = self.fwd
+        torch = f.torch
+        B, H, N, d, dg = (f.shape[x] for x in ("B", "H", "N", "d", "d_gate"))
+        _check_tensor("dy", dy, (B, H, N, d), f.tdtype, f.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(f.device)
+        p = make_params(B, H, N, d, dg, dtype=f.dtype_code, gate_w_ptr=gate_w.data_ptr(),
+                        gate_b_ptr=gate_b.data_ptr(), workspace_ptr=f.workspace.data_ptr(),
+                        workspace_bytes=f.ws_bytes, stream_ptr=stream.cuda_stream, **f.cfg)
+        st = lib().elsaa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), x_gate.data_ptr(),
+                                  f.out.data_ptr(), dy.data_ptr(), ctypes.byref(p),
+                                  self.workspace.data_ptr(), self.ws_bytes, self.dq.data_ptr(),
+                                  self.dk.data_ptr(), self.dv.data_ptr(), self.dx_gate.data_ptr(),
+                                  self.dgate_w.data_ptr(), self.dgate_b.data_ptr(),
+                                  self.dlambda.data_ptr())
+        if st != OK:
+            raise ElsaaError(st, last_error())
+        return (self.dq, self.dk, self.dv, self.dx_gate, self.dgate_w, self.dgate_b, self.dlambda)
 
 
 def forward(q, k, v, x_gate, hyperplanes, gate_w, gate_b, *, sort_bits, chunk, race_tables,

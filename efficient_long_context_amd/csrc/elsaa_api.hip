@@ -150,6 +150,50 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   return off;
 }
 
+// Backward scratch layout; with base == nullptr only the size is computed.
+size_t carve_bwd(const elsaa::Geometry &g, char *base, elsaa::BackwardBuffers *b) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char * {
+    char *ptr = base ? base + off : nullptr;
+    off += align256(bytes);
+    return ptr;
+  };
+  const size_t rows = static_cast<size_t>(g.rows);
+  const size_t es = g.bf16 ? 2 : 4;
+  const size_t tab = static_cast<size_t>(g.BH) * g.L * g.nb_race;
+  elsaa::BackwardBuffers t;
+  t.do_s = take(rows * g.D * es);
+  t.delta = reinterpret_cast<float *>(take(rows * 4));
+  t.dcon = reinterpret_cast<float *>(take(rows * g.D * 4));
+  t.da_s = reinterpret_cast<float *>(take(rows * 4));
+  t.da_lr = reinterpret_cast<float *>(take(rows * 4));
+  t.dlam = reinterpret_cast<float *>(take(rows * 4));
+  t.dv_acc = reinterpret_cast<float *>(take(rows * g.D * 4));
+  t.qcode_t = take(rows * g.L * g.rcb);
+  t.qrperm = take(static_cast<size_t>(g.BH) * g.L * g.N * 4);
+  t.qrstart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
+  t.qrpart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (elsaa::race_parts(g.N) + 1) * 8));
+  t.dT = reinterpret_cast<float *>(take(tab * g.D * 4));
+  t.qtcnt = reinterpret_cast<float *>(take(tab * 4));
+  t.gate_part = reinterpret_cast<float *>(take(static_cast<size_t>(g.H) * elsaa::kGateBlocks * (2 * g.DG + 3) * 4));
+  t.flag = reinterpret_cast<uint32_t *>(take(4));
+  if (b) *b = t;
+  return off;
+}
+
+// Limits the backward adds to the forward's.
+int backward_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
+  const int st = make_geometry(p, g);
+  if (st != ELSAA_OK) return st;
+  if (g->fused)
+    return fail(ELSAA_ERR_UNSUPPORTED,
+                "the backward needs the forward's o_s and LSE: run the forward without ELSAA_OPT_FUSED_EPILOGUE");
+  if (static_cast<long long>(g->N) * g->D * 4 >= (1ll << 31))
+    return fail(ELSAA_ERR_UNSUPPORTED, "the backward needs N * d * 4 < 2^31 (got %lld)",
+                static_cast<long long>(g->N) * g->D * 4);
+  return ELSAA_OK;
+}
+
 __global__ void fill_zero_bytes(uint8_t *__restrict__ p, long long n) {
   const long long i = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) * 16;
   if (i + 16 <= n) {
@@ -333,6 +377,56 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
   if (e == hipSuccess) e = device_cus(device, &g.cus);
   if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
   return enqueue_forward(g, q, k, v, x_gate, hyperplanes, params, out, static_cast<char *>(params->workspace));
+}
+
+size_t elsaa_backward_workspace_bytes(const elsaa_params_t *p) {
+  elsaa::Geometry g;
+  if (backward_geometry(p, &g) != ELSAA_OK) return 0;
+  return carve_bwd(g, nullptr, nullptr);
+}
+
+int elsaa_backward(const void *q, const void *k, const void *v, const void *x_gate, const void *y,
+                   const void *dy, const elsaa_params_t *params, void *bwd_workspace,
+                   size_t bwd_workspace_bytes, void *dq, void *dk, void *dv, void *dx_gate,
+                   float *dgate_w, float *dgate_b, float *dlambda) {
+  elsaa::Geometry g;
+  int st = backward_geometry(params, &g);
+  if (st != ELSAA_OK) return st;
+  if (!q || !k || !v || !x_gate || !dy || !dq || !dk || !dv || !dx_gate || !dgate_w || !dgate_b || !dlambda ||
+      (!y && g.variant == ELSAA_VARIANT_SPARSE_ONLY))
+    return fail(ELSAA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  for (const void *ptr : {q, k, v, x_gate, y, dy, static_cast<const void *>(dq), static_cast<const void *>(dk),
+                          static_cast<const void *>(dv), static_cast<const void *>(dx_gate)})
+    if (misaligned(ptr, 16)) return fail(ELSAA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (misaligned(params->gate_w, 4) || misaligned(params->gate_b, 4) || misaligned(dgate_w, 4) ||
+      misaligned(dgate_b, 4) || misaligned(dlambda, 4))
+    return fail(ELSAA_ERR_INVALID_ARG, "gate parameters and their gradients must be 4-byte aligned");
+  const size_t need_fwd = carve(g, nullptr, nullptr);
+  if (!params->workspace || params->workspace_bytes < need_fwd || misaligned(params->workspace, 256))
+    return fail(ELSAA_ERR_WORKSPACE, "params->workspace must be the forward call's workspace (%zu bytes, 256-byte "
+                "aligned)", need_fwd);
+  const size_t need = carve_bwd(g, nullptr, nullptr);
+  if (!bwd_workspace || bwd_workspace_bytes < need)
+    return fail(ELSAA_ERR_WORKSPACE, "backward workspace of %zu bytes required (given %zu%s)", need,
+                bwd_workspace_bytes, bwd_workspace ? "" : ", NULL");
+  if (misaligned(bwd_workspace, 256)) return fail(ELSAA_ERR_WORKSPACE, "the backward workspace must be 256-byte aligned");
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e == hipSuccess) e = device_cus(device, &g.cus);
+  if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
+  elsaa::Buffers fb;
+  carve(g, static_cast<char *>(params->workspace), &fb);
+  elsaa::BackwardBuffers bb;
+  carve_bwd(g, static_cast<char *>(bwd_workspace), &bb);
+  elsaa::BackwardInputs in{q, k, v, x_gate, y, dy, params->gate_w, params->gate_b, params->lambda};
+  elsaa::BackwardOutputs out{dq, dk, dv, dx_gate, dgate_w, dgate_b, dlambda};
+  hipStream_t s = static_cast<hipStream_t>(params->stream);
+  e = elsaa::launch_backward(g, in, fb, bb, out, s);
+  if (e == hipSuccess && debug_mode()) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && debug_mode()) e = hipGetLastError();
+  if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error in the backward pass: %s", hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return ELSAA_OK;
 }
 
 int elsaa_forward_noalloc(const void *q, const void *k, const void *v, const void *x_gate,

@@ -88,6 +88,52 @@ hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *
                                   const void *v, const Buffers &buf, void *o_s, hipStream_t stream);
 hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
                              hipStream_t stream);
+// The RACE build over any codes and rows: per table, the counts of codes[l][row]
+// and the per-bucket sums of the rows (the forward sums values by key code;
+// the backward sums query gradients by query code).
+struct RaceBuildIO {
+  const void *codes;  // [L][BH*N] codes, uint8 if P <= 8 else uint16
+  const void *values; // [BH][N][D] rows
+  bool values_f32;    // rows and sums are binary32 (else the problem's dtype)
+  void *rperm;        // [BH][L][N] sorted indices (uint16 when N <= 65536, else int32)
+  int32_t *rstart;    // [BH][L][2^P + 1]
+  int32_t *rpart;     // [BH][L][parts + 1][2]
+  void *tsum;         // [BH][L][2^P][D] sums
+  float *tcnt;        // [BH][L][2^P] counts
+  uint32_t *flag;     // a word the rank kernel clears
+};
+hipError_t launch_race_build_io(const Geometry &g, const RaceBuildIO &io, hipStream_t stream);
+
+// Backward pass (k6_backward.hip).  The forward's workspace (Buffers) still
+// holds that call's codes, permutations, tables, o_s and LSE.
+struct BackwardInputs {
+  const void *q, *k, *v, *x_gate, *y, *dy;
+  const float *gate_w, *gate_b;
+  float lambda;  // the caller's lambda (the variant decides whether alpha uses it)
+};
+struct BackwardBuffers {
+  void *do_s;        // [BH][N][D] dtype
+  float *delta;      // [BH][N]
+  float *dcon;       // [BH][N][D] binary32
+  float *da_s, *da_lr, *dlam;  // [BH][N]
+  float *dv_acc;     // [BH][N][D] binary32, the sparse part of dv
+  void *qcode_t;     // [L][BH*N] query codes, table-major
+  void *qrperm;      // [BH][L][N]
+  int32_t *qrstart;  // [BH][L][2^P + 1]
+  int32_t *qrpart;   // [BH][L][parts + 1][2]
+  float *dT;         // [BH][L][2^P][D]
+  float *qtcnt;      // [BH][L][2^P]
+  float *gate_part;  // [H][64][2 d_gate + 3]
+  uint32_t *flag;
+};
+// Token blocks of the backward's gate-gradient partial sums (reduced in order).
+constexpr int kGateBlocks = 64;
+struct BackwardOutputs {
+  void *dq, *dk, *dv, *dx_gate;
+  float *dgate_w, *dgate_b, *dlambda;
+};
+hipError_t launch_backward(const Geometry &g, const BackwardInputs &in, const Buffers &fb,
+                           const BackwardBuffers &bb, const BackwardOutputs &out, hipStream_t stream);
 // Chunk attention with the RACE gather, gates and fusion in its epilogue, for
 // the shapes attention_fusable() accepts: writes y to `out` (and the aux
 // outputs of both stages that are requested), never o_s or its LSE.

@@ -394,10 +394,9 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
 namespace {
 
 template <typename PT>
-hipError_t launch_race_build_pt(const Geometry &g, const void *v, const Buffers &buf, hipStream_t stream) {
+hipError_t launch_race_build_pt(const Geometry &g, const RaceBuildIO &io, hipStream_t stream) {
   const int nb = g.nb_race;
-  const void *rk = static_cast<const char *>(buf.rcode) + static_cast<size_t>(g.rows) * g.L * g.rcb;
-  PT *rperm = reinterpret_cast<PT *>(buf.rperm);
+  PT *rperm = reinterpret_cast<PT *>(io.rperm);
   const long long units = static_cast<long long>(g.BH) * g.L;
   int waves = 16384 / nb;  // LDS counters: waves * nb * 4 bytes <= 64 KB
   waves = waves < 1 ? 1 : (waves > 16 ? 16 : waves);
@@ -412,12 +411,12 @@ hipError_t launch_race_build_pt(const Geometry &g, const void *v, const Buffers 
   const size_t rlds = rank_lds(waves, staged);
   if (g.rcb == 1)
     hipLaunchKernelGGL((elsaa_k4_race_rank<uint8_t, PT>), dim3(static_cast<unsigned>(units)), dim3(waves * 64),
-                       rlds, stream, static_cast<const uint8_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0,
-                       race_parts(g.N), rperm, buf.rstart, buf.rpart, buf.tcnt, flagged_any(buf.flags, g.rows));
+                       rlds, stream, static_cast<const uint8_t *>(io.codes), g.N, g.L, g.P, g.rows, staged ? 1 : 0,
+                       race_parts(g.N), rperm, io.rstart, io.rpart, io.tcnt, io.flag);
   else
     hipLaunchKernelGGL((elsaa_k4_race_rank<uint16_t, PT>), dim3(static_cast<unsigned>(units)), dim3(waves * 64),
-                       rlds, stream, static_cast<const uint16_t *>(rk), g.N, g.L, g.P, g.rows, staged ? 1 : 0,
-                       race_parts(g.N), rperm, buf.rstart, buf.rpart, buf.tcnt, flagged_any(buf.flags, g.rows));
+                       rlds, stream, static_cast<const uint16_t *>(io.codes), g.N, g.L, g.P, g.rows, staged ? 1 : 0,
+                       race_parts(g.N), rperm, io.rstart, io.rpart, io.tcnt, io.flag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -432,12 +431,12 @@ hipError_t launch_race_build_pt(const Geometry &g, const void *v, const Buffers 
     // keep its gathers on one XCD; beyond that spread each (b, h) over all
     const int xcd_local = static_cast<long long>(g.N) * D * sizeof(VT) <= (4ll << 20) ? 1 : 0;
     hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT>), grid, dim3(kGatherWaves * 64), 0, stream,
-                       static_cast<const VT *>(v), rperm, buf.rstart, buf.rpart, g.N, g.L, g.P, parts,
-                       waves_total, xcd_local, static_cast<VT *>(buf.tsum));
+                       static_cast<const VT *>(io.values), rperm, io.rstart, io.rpart, g.N, g.L, g.P, parts,
+                       waves_total, xcd_local, static_cast<VT *>(io.tsum));
   };
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;
-  if (g.bf16) {
+  if (g.bf16 && !io.values_f32) {
     if (g.D == 64) gather(uint16_t{}, D64{});
     else gather(uint16_t{}, D128{});
   } else {
@@ -449,11 +448,25 @@ hipError_t launch_race_build_pt(const Geometry &g, const void *v, const Buffers 
 
 }  // namespace
 
+hipError_t launch_race_build_io(const Geometry &g, const RaceBuildIO &io, hipStream_t stream) {
+  // 16-bit key indices whenever they fit
+  return g.N <= 65536 ? launch_race_build_pt<uint16_t>(g, io, stream)
+                      : launch_race_build_pt<int32_t>(g, io, stream);
+}
+
 hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &buf,
                              hipStream_t stream) {
-  // 16-bit key indices whenever they fit (the workspace holds 32-bit ones)
-  return g.N <= 65536 ? launch_race_build_pt<uint16_t>(g, v, buf, stream)
-                      : launch_race_build_pt<int32_t>(g, v, buf, stream);
+  RaceBuildIO io;
+  io.codes = static_cast<const char *>(buf.rcode) + static_cast<size_t>(g.rows) * g.L * g.rcb;
+  io.values = v;
+  io.values_f32 = false;
+  io.rperm = buf.rperm;
+  io.rstart = buf.rstart;
+  io.rpart = buf.rpart;
+  io.tsum = buf.tsum;
+  io.tcnt = buf.tcnt;
+  io.flag = flagged_any(buf.flags, g.rows);  // the fix-up has run: cleared for the next call
+  return launch_race_build_io(g, io, stream);
 }
 
 }  // namespace elsaa

@@ -213,6 +213,36 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
 int elsaa_forward_noalloc(const void *q, const void *k, const void *v, const void *x_gate,
                           const void *hyperplanes, const elsaa_params_t *params, void *out);
 
+/* Host-only: scratch bytes elsaa_backward needs for *p, beyond the forward's
+ * workspace (0 if *p is invalid or outside the backward's limits;
+ * elsaa_validate and elsaa_last_error say why). */
+size_t elsaa_backward_workspace_bytes(const elsaa_params_t *p);
+
+/* The backward pass, for training ("ELSAA: Efficient Low-Rank and Sparse
+ * Attention Approximation for Training Transformers", first paragraph: a
+ * training framework with a learnable lambda): given dy = dL/dy for the output
+ * y of the elsaa_forward call made with the same inputs and *params, writes
+ *   dq, dk, dv  [B][H][N][d]     dtype   dL/dq, dL/dk, dL/dv
+ *   dx_gate     [B][N][d_gate]   dtype   dL/dx_gate
+ *   dgate_w     [2][H][d_gate]   binary32, dgate_b [2][H] binary32, and
+ *   *dlambda    one binary32 (dL/dlambda; 0 unless the variant is FULL).
+ * Hash codes, permutations and bucket counts are constants (piecewise constant
+ * in the inputs); the sparse branch recomputes its probabilities from the
+ * stored LSE.  params->workspace must still hold that forward call's results
+ * (nothing may run on it in between) and the forward must not have used
+ * ELSAA_OPT_FUSED_EPILOGUE (which keeps o_s and the LSE out of memory):
+ * otherwise ELSAA_ERR_UNSUPPORTED.  y is the forward's output (read only by
+ * ELSAA_VARIANT_SPARSE_ONLY, whose o_s it is).  bwd_workspace is caller-owned
+ * device scratch of at least elsaa_backward_workspace_bytes(params) bytes,
+ * 256-byte aligned.  Additional limit: N * d * 4 < 2^31 (binary32 gradient
+ * rows).  Every gradient is written (zeros where a variant has none); the
+ * summation orders are fixed, so results repeat bit for bit.  Asynchronous on
+ * params->stream like the forward; validation as in elsaa_forward. */
+int elsaa_backward(const void *q, const void *k, const void *v, const void *x_gate, const void *y,
+                   const void *dy, const elsaa_params_t *params, void *bwd_workspace,
+                   size_t bwd_workspace_bytes, void *dq, void *dk, void *dv, void *dx_gate,
+                   float *dgate_w, float *dgate_b, float *dlambda);
+
 /* Static name of a status code ("ELSAA_OK", ...). */
 const char *elsaa_status_str(int status);
 
