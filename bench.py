@@ -5,17 +5,24 @@
 A step is one whole forward pass (hash, sort, RACE build, chunk attention,
 gather/gates/fusion) over one batch of seeded synthetic input already resident
 in HBM.  W untimed steps, then K steps timed between two device
-synchronisations (no instrumentation inside), then K more steps with the
-library's stage events for the per-stage split.  Prints ONE JSON line:
+synchronisations (no instrumentation inside: ms_per_step and value), then K
+steps each bracketed by its own pair of events (median and spread), then K
+steps with the library's stage events for the per-stage split.  Prints ONE
+JSON line:
   value        tokens/s (B*N per step) of the whole job
   roofline     the dominant kernel (largest share of the step): algorithmic
-               bytes (or flops) per launch over its mean duration, measured with
-               HIP events recorded around it on the stream it runs on
-  stages       the same figures for every stage
+               bytes (or flops) per launch over its median duration, measured
+               with HIP events recorded around it on the stream it runs on
+  stages       the same figures for every stage, with % of HBM / MFMA peak and
+               % attainable (max(bytes / BW, flops / peak) / t), against the
+               published peaks and against the peaks measured on this GPU
+  peaks_measured  a 1 GiB device copy (HBM) and a bf16 8192^3 matmul (MFMA)
+  backward     the same timing for the backward pass (elsaa_backward)
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload on
-               this host's cores (whole-job tokens/s extrapolated from the sample)
+               this host's cores (whole-job tokens/s extrapolated from the
+               sample), plus a one-thread figure on the small workloads
   parity       GPU vs oracle on the sampled heads
-  secondary    the same step timing for the second headline workload
+  secondary    the same step timing for the other headline workloads
 Multi-GPU runs are not supported: every stage is independent per (batch, head),
 and this build measures one GPU.
 """
@@ -76,6 +83,25 @@ def stage_model(wl: workloads.Workload) -> dict:
         "fuse": dict(bytes=th * (L * c + d * s + 4 + d * s) + wl.B * wl.H * T + wl.B * N * wl.d_gate * s,
                      flops=th * (L * d + 4 * wl.d_gate + 8 * d), mfma=False),
     }
+
+
+def backward_model(wl: workloads.Workload) -> dict:
+    """Algorithmic HBM bytes and MFMA flops of the backward pass, per call.
+
+    Reads q, k, v, dy, o_s (d s each), LSE, the query's and key's L codes and
+    the gate inputs once per token-head, the tables once per (b, h); writes
+    dq, dk, dv (d s each) and dx_gate.  Flops: the sparse branch's five
+    products per (query, key) pair (S, dP, dQ, dK, dV: 2 d each), plus the
+    RACE transposes (L d adds per query and per key)."""
+    s = 2 if wl.dtype == "bf16" else 4
+    c = 1 if wl.race_bits <= 8 else 2
+    d, L, P, N = wl.d, wl.race_tables, wl.race_bits, wl.N
+    th = wl.B * wl.H * N
+    T = L * (1 << P) * (d * s + 4)
+    pairs = wl.B * wl.H * (N * 2 * wl.chunk - wl.chunk * wl.chunk)
+    rd = th * (5 * d * s + 4 + 2 * L * c) + wl.B * wl.H * T + wl.B * N * wl.d_gate * s
+    wr = th * 3 * d * s + wl.B * N * wl.d_gate * s
+    return dict(bytes=rd + wr, flops=10 * d * pairs + 2 * th * L * d, mfma=wl.dtype == "bf16")
 
 
 def source_sha(stage: str) -> str:
@@ -196,15 +222,72 @@ class HipEvents:
             self.hip.hipEventDestroy(h)
 
 
+def stage_figures(model: dict, ms: float, peaks: dict) -> dict:
+    """Per-stage figures for one stage model entry at `ms` per launch: GB/s and
+    TFLOP/s achieved, fractions of the published HBM / MFMA peaks, and the
+    fraction of the attainable time max(bytes / BW, flops / peak) against the
+    published and the measured peaks."""
+    t = ms * 1e-3
+    gbs = model["bytes"] / t / 1e9
+    tfl = model["flops"] / t / 1e12
+    peak_fl = BF16_PEAK_TFLOPS if model["mfma"] else FP32_PEAK_TFLOPS
+    attain = max(model["bytes"] / (HBM_PEAK_GBS * 1e9), model["flops"] / (peak_fl * 1e12))
+    out = {"ms": round(ms, 5), "alg_bytes": model["bytes"], "alg_flops": model["flops"],
+           "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "TFLOP_s": round(tfl, 2), "flop_frac": round(tfl / peak_fl, 4),
+           "attainable_frac": round(attain / t, 4)}
+    if peaks:
+        mpk = peaks["mfma_TFLOP_s"] if model["mfma"] else FP32_PEAK_TFLOPS
+        attain_m = max(model["bytes"] / (peaks["copy_GB_s"] * 1e9), model["flops"] / (mpk * 1e12))
+        out["attainable_frac_measured_peaks"] = round(attain_m / t, 4)
+    return out
+
+
+def measure_peaks(torch, dev) -> dict:
+    """Achievable peaks on this GPU: a 1 GiB device-to-device copy (2 GiB of
+    HBM traffic per copy) and a bf16 8192 x 8192 x 8192 matmul (hipBLASLt)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma = 2 * 8192 ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return {"copy_GB_s": round(copy_gbs, 1), "mfma_TFLOP_s": round(mfma, 1),
+            "copy_frac_of_published": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "mfma_frac_of_published": round(mfma / BF16_PEAK_TFLOPS, 4),
+            "how": "1 GiB device-to-device copy x10 (2 GiB of traffic each); bf16 8192^3 torch.matmul x10"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="text32k-bf16", choices=list(workloads.WORKLOADS))
-    ap.add_argument("--also", default="vision16k-bf16",
-                    help="second workload timed the same way ('none' to skip)")
+    ap.add_argument("--also", default="vision16k-bf16,needle256k-bf16",
+                    help="comma-separated workloads timed the same way ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="(b, h) heads the oracle runs on (0 = enough for ~10 s)")
     ap.add_argument("--seed", type=int, default=0)
@@ -240,8 +323,12 @@ def main(argv=None):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    peaks = {} if args.no_peaks else measure_peaks(torch, dev)
 
-    def time_workload(name: str, steps: int, warmup: int):
+    def event_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def time_workload(name: str, steps: int, warmup: int, backward: bool):
         wl = workloads.WORKLOADS[name]
         t0 = time.perf_counter()
         inp = workloads.generate(wl, seed=args.seed)
@@ -254,41 +341,67 @@ def main(argv=None):
         for _ in range(warmup):
             f(*call)
         torch.cuda.synchronize()
-        # the timed steps run without stage events; a second pass with the
-        # library's stage events (the same number of steps) splits the time
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # K steps between two synchronisations, no instrumentation inside
+        start, stop = event_pair()
         torch.cuda.synchronize()
         start.record()
-        for i in range(steps):
+        for _ in range(steps):
             f(*call)
         stop.record()
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(stop)
+        # K steps, each between its own pair of events (median and spread)
+        pairs = [event_pair() for _ in range(steps)]
+        for a, b in pairs:
+            a.record()
+            f(*call)
+            b.record()
+        torch.cuda.synchronize()
+        per_step = np.array([a.elapsed_time(b) for a, b in pairs])
+        # K steps with the library's stage events (a begin, end pair per stage)
         stage_ev = [ev.create(2 * len(elsaa.STAGES)) for _ in range(steps)]
         for i in range(steps):
             f(*call, stage_events=stage_ev[i])
         torch.cuda.synchronize()
-        stage_ms = {st: float(np.mean([ev.elapsed_ms(e[2 * j], e[2 * j + 1]) for e in stage_ev]))
+        stage_ms = {st: float(np.median([ev.elapsed_ms(e[2 * j], e[2 * j + 1]) for e in stage_ev]))
                     for j, st in enumerate(elsaa.STAGES)}
         for e in stage_ev:
             ev.destroy(e)
         out = f.out.float().cpu().numpy()
-        return wl, inp, f, total_ms / steps, stage_ms, out, gen_s
+        res = dict(wl=wl, inp=inp, ms_step=total_ms / steps, median_ms=float(np.median(per_step)),
+                   p10_ms=float(np.percentile(per_step, 10)), p90_ms=float(np.percentile(per_step, 90)),
+                   stage_ms=stage_ms, out=out, gen_s=gen_s)
+        if backward:
+            bwd = elsaa.Backward(f)
+            rng = np.random.default_rng(args.seed + 1)
+            dy = torch.from_numpy(rng.standard_normal((wl.B, wl.H, wl.N, wl.d)).astype(np.float32)).to(dev)
+            dy = dy.to(f.tdtype)
+            bargs = (x["q"], x["k"], x["v"], x["x_gate"], x["gate_w"], x["gate_b"], dy)
+            for _ in range(max(2, warmup // 2)):
+                f(*call)
+                bwd(*bargs)
+            torch.cuda.synchronize()
+            bpairs = [event_pair() for _ in range(steps)]
+            for a, b in bpairs:
+                f(*call)  # the backward reads this call's results
+                a.record()
+                bwd(*bargs)
+                b.record()
+            torch.cuda.synchronize()
+            res["backward_ms"] = float(np.median([a.elapsed_time(b) for a, b in bpairs]))
+        del x, f
+        torch.cuda.empty_cache()
+        return res
 
-    wl, inp, f, ms_step, stage_ms, out, gen_s = time_workload(args.workload, args.steps, args.warmup)
+    main_res = time_workload(args.workload, args.steps, args.warmup, backward=not args.no_backward)
+    wl, inp, out = main_res["wl"], main_res["inp"], main_res["out"]
+    ms_step = main_res["ms_step"]
     tokens = wl.B * wl.N
     value = tokens / (ms_step * 1e-3)
 
     model = stage_model(wl)
-    stages = {}
-    for st, ms in stage_ms.items():
-        m = model[st]
-        gbs = m["bytes"] / (ms * 1e-3) / 1e9
-        tfl = m["flops"] / (ms * 1e-3) / 1e12
-        peak_fl = BF16_PEAK_TFLOPS if m["mfma"] else FP32_PEAK_TFLOPS
-        stages[st] = {"ms": round(ms, 5), "alg_bytes": m["bytes"], "alg_flops": m["flops"],
-                      "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                      "TFLOP_s": round(tfl, 2), "flop_frac": round(tfl / peak_fl, 4)}
+    stage_ms = main_res["stage_ms"]
+    stages = {st: stage_figures(model[st], ms, peaks) for st, ms in stage_ms.items()}
     dom = max(stage_ms, key=stage_ms.get)
     m = model[dom]
     ms = stage_ms[dom]
@@ -304,6 +417,7 @@ def main(argv=None):
     roof["traffic"] = measured_traffic(dom, wl.name)
     roof["kernel"] = dom
     roof["ms_per_launch"] = round(ms, 5)
+    roof["timing"] = f"median over {args.steps} launches of the stage's begin/end events"
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -314,15 +428,34 @@ def main(argv=None):
                    "sort_bits": wl.sort_bits, "chunk": wl.chunk, "race_tables": wl.race_tables,
                    "race_bits": wl.race_bits, "lambda": wl.lam, "parallelism": "single GPU"},
         "head_tokens_per_s": round(value * wl.H, 1),
+        "step_ms": {"median": round(main_res["median_ms"], 5), "p10": round(main_res["p10_ms"], 5),
+                    "p90": round(main_res["p90_ms"], 5), "n": args.steps},
         "roofline": roof,
         "stages": stages,
     }
+    if peaks:
+        result["peaks_measured"] = peaks
+    if "backward_ms" in main_res:
+        bm = backward_model(wl)
+        bms = main_res["backward_ms"]
+        result["backward"] = dict(stage_figures(bm, bms, peaks), tokens_per_s=round(tokens / (bms * 1e-3), 1),
+                                  timing=f"median over {args.steps} calls of elsaa_backward, each after a "
+                                         f"forward call")
 
-    if args.also and args.also != "none" and args.also != args.workload:
-        wl2, _, _, ms2, st2, _, _ = time_workload(args.also, args.steps, args.warmup)
-        result["secondary"] = {"workload": wl2.name, "value": round(wl2.B * wl2.N / (ms2 * 1e-3), 1),
-                               "unit": "tokens/s", "ms_per_step": round(ms2, 5),
-                               "stages_ms": {k: round(v, 5) for k, v in st2.items()}}
+    secondary = []
+    for name in (args.also.split(",") if args.also and args.also != "none" else []):
+        if name == args.workload:
+            continue
+        r2 = time_workload(name, args.steps, args.warmup, backward=False)
+        wl2 = r2["wl"]
+        m2 = stage_model(wl2)
+        secondary.append({"workload": wl2.name, "value": round(wl2.B * wl2.N / (r2["ms_step"] * 1e-3), 1),
+                          "unit": "tokens/s", "ms_per_step": round(r2["ms_step"], 5),
+                          "median_ms": round(r2["median_ms"], 5),
+                          "stages": {st: stage_figures(m2[st], v, peaks) for st, v in r2["stage_ms"].items()}})
+        del r2
+    if secondary:
+        result["secondary"] = secondary
 
     if not args.no_cpu_baseline:
         import oracle
@@ -333,7 +466,6 @@ def main(argv=None):
         t_used = 0.0
         done = 0
         errs = []
-        exact = True
         for (b, h) in bh_all:
             if done >= heads and (args.cpu_heads or t_used >= 10.0):
                 break
@@ -355,6 +487,19 @@ def main(argv=None):
                       f"{t_used:.1f} s of oracle time; whole-job tokens/s extrapolated "
                       f"from the mean time per (batch, head)",
         }
+        # one thread, whole small workloads
+        one = {}
+        oracle.set_num_threads(1)
+        for name in ("tiny-fp32", "small-bf16"):
+            w1 = workloads.WORKLOADS[name]
+            i1 = workloads.generate(w1, seed=args.seed)
+            r1 = oracle.forward(i1.q, i1.k, i1.v, i1.x_gate, i1.hyperplanes, i1.gate_w, i1.gate_b,
+                                sort_bits=w1.sort_bits, chunk=w1.chunk, race_tables_n=w1.race_tables,
+                                race_bits=w1.race_bits, lam=w1.lam)
+            one[name] = {"seconds": round(r1.seconds, 3),
+                         "tokens_per_s": round(w1.B * w1.N / r1.seconds, 1)}
+        oracle.set_num_threads(threads)
+        result["cpu_baseline"]["one_thread"] = one
         result["parity"] = {"heads_checked": done, "max_rel_err_y": max(errs),
                             "tolerance": 2e-2 if wl.dtype == "bf16" else 1e-4}
 
