@@ -372,6 +372,10 @@ def main(argv=None):
                    p10_ms=float(np.percentile(per_step, 10)), p90_ms=float(np.percentile(per_step, 90)),
                    stage_ms=stage_ms, out=out, gen_s=gen_s)
         if backward:
+            # training: the forward keeps what the backward reads (o_lr, counts, gates)
+            f = elsaa.Forward(B=wl.B, H=wl.H, N=wl.N, d=wl.d, d_gate=wl.d_gate, sort_bits=wl.sort_bits,
+                              chunk=wl.chunk, race_tables=wl.race_tables, race_bits=wl.race_bits,
+                              lam=wl.lam, dtype=wl.dtype, options=elsaa.OPT_SAVE_FOR_BACKWARD, device=dev)
             bwd = elsaa.Backward(f)
             rng = np.random.default_rng(args.seed + 1)
             dy = torch.from_numpy(rng.standard_normal((wl.B, wl.H, wl.N, wl.d)).astype(np.float32)).to(dev)
@@ -382,13 +386,17 @@ def main(argv=None):
                 bwd(*bargs)
             torch.cuda.synchronize()
             bpairs = [event_pair() for _ in range(steps)]
-            for a, b in bpairs:
+            fpairs = [event_pair() for _ in range(steps)]
+            for (a, b), (c, d) in zip(bpairs, fpairs):
+                c.record()
                 f(*call)  # the backward reads this call's results
+                d.record()
                 a.record()
                 bwd(*bargs)
                 b.record()
             torch.cuda.synchronize()
             res["backward_ms"] = float(np.median([a.elapsed_time(b) for a, b in bpairs]))
+            res["forward_saving_ms"] = float(np.median([c.elapsed_time(d) for c, d in fpairs]))
         del x, f
         torch.cuda.empty_cache()
         return res
@@ -439,8 +447,9 @@ def main(argv=None):
         bm = backward_model(wl)
         bms = main_res["backward_ms"]
         result["backward"] = dict(stage_figures(bm, bms, peaks), tokens_per_s=round(tokens / (bms * 1e-3), 1),
+                                  forward_with_saving_ms=round(main_res["forward_saving_ms"], 5),
                                   timing=f"median over {args.steps} calls of elsaa_backward, each after a "
-                                         f"forward call")
+                                         f"forward call that saves o_lr, counts and gates for it")
 
     secondary = []
     for name in (args.also.split(",") if args.also and args.also != "none" else []):

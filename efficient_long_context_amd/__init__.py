@@ -54,6 +54,7 @@ class ElsaaParams(ctypes.Structure):
     ]
 
 OPT_FUSED_EPILOGUE = 1  # ELSAA_OPT_FUSED_EPILOGUE
+OPT_SAVE_FOR_BACKWARD = 2  # ELSAA_OPT_SAVE_FOR_BACKWARD
 
 STAGES = ("hash", "sort", "race_build", "chunk_attention", "fuse")
 

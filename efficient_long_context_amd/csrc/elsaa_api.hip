@@ -113,10 +113,11 @@ int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
   g->run_sparse = p->variant != ELSAA_VARIANT_RACE_ONLY;
   g->run_race = p->variant != ELSAA_VARIANT_SPARSE_ONLY;
   g->identity = p->sort_bits == 0;
-  if (p->options & ~static_cast<uint32_t>(ELSAA_OPT_FUSED_EPILOGUE))
+  if (p->options & ~static_cast<uint32_t>(ELSAA_OPT_FUSED_EPILOGUE | ELSAA_OPT_SAVE_FOR_BACKWARD))
     return fail(ELSAA_ERR_INVALID_ARG, "unknown option bits 0x%x", p->options);
   g->fused = false;
-  g->fused = (p->options & ELSAA_OPT_FUSED_EPILOGUE) != 0 && elsaa::attention_fusable(*g);
+  g->save = (p->options & ELSAA_OPT_SAVE_FOR_BACKWARD) != 0 && g->run_race;
+  g->fused = (p->options & ELSAA_OPT_FUSED_EPILOGUE) != 0 && !g->save && elsaa::attention_fusable(*g);
   return ELSAA_OK;
 }
 
@@ -146,6 +147,10 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   // runs in the attention's epilogue
   t.o_s = g.fused ? nullptr : take(rows * g.D * es);
   t.lse = g.fused ? nullptr : reinterpret_cast<float *>(take(rows * 4));
+  t.sv_olr = g.save ? take(rows * g.D * es) : nullptr;
+  t.sv_z = g.save ? reinterpret_cast<float *>(take(rows * 4)) : nullptr;
+  t.sv_gs = g.save ? reinterpret_cast<float *>(take(rows * 4)) : nullptr;
+  t.sv_glr = g.save ? reinterpret_cast<float *>(take(rows * 4)) : nullptr;
   if (b) *b = t;
   return off;
 }
@@ -164,7 +169,7 @@ size_t carve_bwd(const elsaa::Geometry &g, char *base, elsaa::BackwardBuffers *b
   elsaa::BackwardBuffers t;
   t.do_s = take(rows * g.D * es);
   t.delta = reinterpret_cast<float *>(take(rows * 4));
-  t.dcon = reinterpret_cast<float *>(take(rows * g.D * 4));
+  t.dcon = take(rows * g.D * es);
   t.da_s = reinterpret_cast<float *>(take(rows * 4));
   t.da_lr = reinterpret_cast<float *>(take(rows * 4));
   t.dlam = reinterpret_cast<float *>(take(rows * 4));
@@ -173,7 +178,7 @@ size_t carve_bwd(const elsaa::Geometry &g, char *base, elsaa::BackwardBuffers *b
   t.qrperm = take(static_cast<size_t>(g.BH) * g.L * g.N * 4);
   t.qrstart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
   t.qrpart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (elsaa::race_parts(g.N) + 1) * 8));
-  t.dT = reinterpret_cast<float *>(take(tab * g.D * 4));
+  t.dT = take(tab * g.D * es);
   t.qtcnt = reinterpret_cast<float *>(take(tab * 4));
   t.gate_part = reinterpret_cast<float *>(take(static_cast<size_t>(g.H) * elsaa::kGateBlocks * (2 * g.DG + 3) * 4));
   t.flag = reinterpret_cast<uint32_t *>(take(4));
@@ -188,9 +193,6 @@ int backward_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
   if (g->fused)
     return fail(ELSAA_ERR_UNSUPPORTED,
                 "the backward needs the forward's o_s and LSE: run the forward without ELSAA_OPT_FUSED_EPILOGUE");
-  if (static_cast<long long>(g->N) * g->D * 4 >= (1ll << 31))
-    return fail(ELSAA_ERR_UNSUPPORTED, "the backward needs N * d * 4 < 2^31 (got %lld)",
-                static_cast<long long>(g->N) * g->D * 4);
   return ELSAA_OK;
 }
 

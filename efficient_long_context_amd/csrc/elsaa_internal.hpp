@@ -33,6 +33,7 @@ struct Geometry {
   bool run_race;    // the RACE branch runs (not SPARSE_ONLY)
   bool identity;    // sort_bits == 0: the stable order is the original one, no sort
   bool fused;       // the fusion runs in the chunk attention's epilogue (no o_s, LSE buffers)
+  bool save;        // the fusion keeps o_lr, z and the gates for the backward pass
 };
 
 // Device buffers carved out of the caller's workspace.
@@ -50,6 +51,9 @@ struct Buffers {
   float *tcnt;      // [BH][L][nb_race]
   void *o_s;        // [BH][N][D] in dtype
   float *lse;       // [BH][N]
+  // kept for the backward pass (ELSAA_OPT_SAVE_FOR_BACKWARD; else NULL):
+  void *sv_olr;     // [BH][N][D] o_lr in dtype
+  float *sv_z, *sv_gs, *sv_glr;  // [BH][N] raw count sum z = L Z_lr, g_s, g_lr
 };
 
 // The word after the exact-pass flags (2 rows bytes): the hash sets it when it flags
@@ -114,20 +118,20 @@ struct BackwardInputs {
 struct BackwardBuffers {
   void *do_s;        // [BH][N][D] dtype
   float *delta;      // [BH][N]
-  float *dcon;       // [BH][N][D] binary32
+  void *dcon;        // [BH][N][D] dtype
   float *da_s, *da_lr, *dlam;  // [BH][N]
   float *dv_acc;     // [BH][N][D] binary32, the sparse part of dv
   void *qcode_t;     // [L][BH*N] query codes, table-major
   void *qrperm;      // [BH][L][N]
   int32_t *qrstart;  // [BH][L][2^P + 1]
   int32_t *qrpart;   // [BH][L][parts + 1][2]
-  float *dT;         // [BH][L][2^P][D]
+  void *dT;          // [BH][L][2^P][D] dtype
   float *qtcnt;      // [BH][L][2^P]
   float *gate_part;  // [H][64][2 d_gate + 3]
   uint32_t *flag;
 };
 // Token blocks of the backward's gate-gradient partial sums (reduced in order).
-constexpr int kGateBlocks = 64;
+constexpr int kGateBlocks = 128;
 struct BackwardOutputs {
   void *dq, *dk, *dv, *dx_gate;
   float *dgate_w, *dgate_b, *dlambda;

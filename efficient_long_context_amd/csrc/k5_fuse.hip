@@ -40,6 +40,10 @@ constexpr long long kFuseWaves = ELSAA_FUSE_WAVES;
 
 struct AuxOut {
   float *z_lr, *alpha, *g_s, *g_lr, *o_lr;
+  // saved for the backward pass (NULL: not saved): o_lr in the value dtype,
+  // and per query the raw count sum z (= L Z_lr), g_s and g_lr
+  void *sv_olr;
+  float *sv_z, *sv_gs, *sv_glr;
 };
 
 // ------------------------------------------------------------- any-L path --
@@ -140,6 +144,15 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
       for (int e = 0; e < 4; ++e) yv[e] = __builtin_fmaf(ws, osv[e], wl * o_lr[e]);
       Elem<VT>::store4(out + qi * D + sub * 4, yv);
       if (aux.o_lr) *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * 4) = o_lr;
+      if (aux.sv_olr) {
+        const float lr4[4] = {o_lr[0], o_lr[1], o_lr[2], o_lr[3]};
+        Elem<VT>::store4(static_cast<VT *>(aux.sv_olr) + qi * D + sub * 4, lr4);
+      }
+      if (sub == 0 && aux.sv_z) {
+        aux.sv_z[qi] = z;
+        aux.sv_gs[qi] = g_s;
+        aux.sv_glr[qi] = g_lr;
+      }
       if (sub == 0) {
         if (aux.z_lr) aux.z_lr[qi] = z_lr;
         if (!race_only) {
@@ -436,6 +449,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
         *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * kCols + k) =
             f32x4{o_lr[k], o_lr[k + 1], o_lr[k + 2], o_lr[k + 3]};
     }
+    if (aux.sv_olr) {
+#pragma unroll
+      for (int k = 0; k < kCols; k += 4) Elem<VT>::store4(static_cast<VT *>(aux.sv_olr) + qi * D + sub * kCols + k, o_lr + k);
+    }
+    if (sub == 0 && aux.sv_z) {
+      aux.sv_z[qi] = z;
+      aux.sv_gs[qi] = g_s;
+      aux.sv_glr[qi] = g_lr;
+    }
     if (sub == 0) {
       if (aux.z_lr) aux.z_lr[qi] = z_lr;
       if (!race_only) {
@@ -502,8 +524,14 @@ hipError_t launch_d(const Geometry &g, const void *x_gate, const float *gate_w, 
 hipError_t launch_fuse(const Geometry &g, const void *x_gate, const float *gate_w,
                        const float *gate_b, const Buffers &buf, const elsaa_aux_t *aux,
                        void *out, hipStream_t stream) {
-  AuxOut a = {nullptr, nullptr, nullptr, nullptr, nullptr};
-  if (aux) a = {aux->z_lr, aux->alpha, aux->g_s, aux->g_lr, aux->o_lowrank};
+  AuxOut a = {nullptr, nullptr, nullptr, nullptr, nullptr, buf.sv_olr, buf.sv_z, buf.sv_gs, buf.sv_glr};
+  if (aux) {
+    a.z_lr = aux->z_lr;
+    a.alpha = aux->alpha;
+    a.g_s = aux->g_s;
+    a.g_lr = aux->g_lr;
+    a.o_lr = aux->o_lowrank;
+  }
   if (g.bf16)
     return g.D == 64 ? launch_d<64, uint16_t>(g, x_gate, gate_w, gate_b, buf, a, out, stream)
                      : launch_d<128, uint16_t>(g, x_gate, gate_w, gate_b, buf, a, out, stream);

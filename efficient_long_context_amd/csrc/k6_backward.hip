@@ -19,8 +19,9 @@
 //     and dv_j gains sum_l dT_l[c_l(k_j)];
 //   gates: da = dg g (1 - g), dW = sum da x_gate, db = sum da, dx_gate = sum_h da W.
 // Kernels (all deterministic: no atomics, fixed summation orders):
-//   prep     per query: recomputes z, o_lr, gates, alpha like the fusion, and
-//            writes do (dtype), delta, the RACE row c_lr dy / z (binary32),
+//   prep     per query: z, o_lr and the gates as the forward's fusion saved
+//            them (ELSAA_OPT_SAVE_FOR_BACKWARD) or recomputed like it, alpha, and
+//            writes do and the RACE row c_lr dy / z (both in dtype), delta,
 //            da_s, da_lr and the query's share of dL/dlambda;
 //   dq, dkv  the sparse branch: bfloat16 tiles of 64 sorted queries (keys) on
 //            MFMA (S^T = K Q^T, dP^T = V dO^T, dQ^T = K^T dS^T; and S = Q K^T,
@@ -80,11 +81,14 @@ struct PrepArgs {
   const void *x_gate;     // [B][N][DG] dtype
   const float *gate_w;    // [2][H][DG]
   const float *gate_b;    // [2][H]
+  // saved by the forward (ELSAA_OPT_SAVE_FOR_BACKWARD; else NULL)
+  const void *sv_olr;     // [BH][N][D] dtype
+  const float *sv_z, *sv_gs, *sv_glr;  // [BH][N]
   int H, N, L, P, DG, rcb, variant;
   float lambda;
   void *do_s;             // out [BH][N][D] dtype
   float *delta;           // out [BH][N]
-  float *dcon;            // out [BH][N][D]: c_lr dy / z (0 where z = 0)
+  void *dcon;             // out [BH][N][D] dtype: c_lr dy / z (0 where z = 0)
   float *da_s, *da_lr;    // out [BH][N]
   float *dlam;            // out [BH][N]: the query's share of dL/dlambda
 };
@@ -118,7 +122,10 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_prep(PrepArgs a, long long r
   float z = 0.0f, olr[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) olr[c] = 0.0f;
-  if (race) {
+  if (race && a.sv_olr) {
+    load_cols<VT, C>(static_cast<const VT *>(a.sv_olr) + r * D + sub * C, olr);
+    z = a.sv_z[r];
+  } else if (race) {
     for (int l = 0; l < a.L; ++l) {
       const uint32_t code = a.rcb == 1 ? static_cast<const uint8_t *>(a.qcodes)[r * a.L + l]
                                        : static_cast<const uint16_t *>(a.qcodes)[r * a.L + l];
@@ -134,7 +141,10 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_prep(PrepArgs a, long long r
     for (int c = 0; c < C; ++c) olr[c] *= rz;
   }
   float g_s = 1.0f, g_lr = 1.0f, alpha = 1.0f;
-  if (gated) {
+  if (gated && a.sv_gs) {
+    g_s = a.sv_gs[r];
+    g_lr = a.sv_glr[r];
+  } else if (gated) {
     float a0 = 0.0f, a1 = 0.0f;
     const VT *x = static_cast<const VT *>(a.x_gate) + (b * a.N + i) * a.DG;
     const float *w0 = a.gate_w + static_cast<long long>(h) * a.DG;
@@ -148,6 +158,8 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_prep(PrepArgs a, long long r
     a1 = sum16(a1);
     g_s = 1.0f / (1.0f + __expf(-(a0 + a.gate_b[h])));
     g_lr = 1.0f / (1.0f + __expf(-(a1 + a.gate_b[a.H + h])));
+  }
+  if (gated) {
     const float mass = a.lambda * z / static_cast<float>(a.L);
     if (a.variant == ELSAA_VARIANT_FULL && mass > 0.0f) alpha = 1.0f / (1.0f + __expf(__logf(mass) - lse_i));
   }
@@ -190,7 +202,7 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_prep(PrepArgs a, long long r
     float dc[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) dc[c] = sc * dy[c];
-    store_cols<float, C>(a.dcon + r * D + sub * C, dc);
+    store_cols<VT, C>(static_cast<VT *>(a.dcon) + r * D + sub * C, dc);
   }
   if (sub == 0) {
     a.da_s[r] = da_s;
@@ -515,7 +527,7 @@ __global__ void elsaa_k6_bwd_codes_t(const CT *__restrict__ src, CT *__restrict_
 // dv_j = (sparse part) + sum_l dT_l[c_l(k_j)]: 16 lanes per key, original order.
 template <typename VT, int D, typename CT>
 __global__ __launch_bounds__(256) void elsaa_k6_bwd_dv(const float *__restrict__ dv_acc, const CT *__restrict__ kcodes,
-                                                       const float *__restrict__ dT, long long rows, int N, int L,
+                                                       const VT *__restrict__ dT, long long rows, int N, int L,
                                                        int P, VT *__restrict__ dv) {
   constexpr int C = D / 16;
   const int sub = threadIdx.x & 15;
@@ -530,7 +542,7 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dv(const float *__restrict__
     for (int l = 0; l < L; ++l) {
       const long long t = (bh * L + l) * (1ll << P) + kcodes[static_cast<long long>(l) * rows + r];
       float row[C];
-      load_cols<float, C>(dT + t * D + sub * C, row);
+      load_cols<VT, C>(dT + t * D + sub * C, row);
 #pragma unroll
       for (int e = 0; e < C; ++e) acc[e] += row[e];
     }
@@ -560,56 +572,81 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dxgate(const float *__restri
 }
 
 // Partial sums over a block of tokens of head h: dW_g[0][h][:], dW_g[1][h][:],
-// db_g[0][h], db_g[1][h] and dL/dlambda, into part[h][blk][2 DG + 3].
+// db_g[0][h], db_g[1][h] and dL/dlambda, into part[h][blk][2 DG + 3].  Wave w
+// takes tokens t_lo + w, + 4, ... (its da values are wave-uniform loads), lanes
+// the gate columns; the four waves' sums are added in LDS in wave order.
 template <typename VT>
 __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_part(const float *__restrict__ da_s,
                                                               const float *__restrict__ da_lr,
                                                               const float *__restrict__ dlam, const VT *__restrict__ x,
                                                               int B, int H, int N, int DG, float *__restrict__ part) {
+  constexpr int kPer = 8;  // gate columns per lane: DG <= 512
+  __shared__ float red[4][2 * 512 + 3];
   const int h = blockIdx.x, blk = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const long long tokens = static_cast<long long>(B) * N;
   const long long per = (tokens + kGateBlocks - 1) / kGateBlocks;
   const long long t_lo = blk * per, t_hi = t_lo + per < tokens ? t_lo + per : tokens;
+  float w0[kPer], w1[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) w0[j] = w1[j] = 0.0f;
+  float b0 = 0.0f, b1 = 0.0f, lam = 0.0f;
+  for (long long t = t_lo + wave; t < t_hi; t += 4) {
+    const long long b = t / N;
+    const long long r = (b * H + h) * N + (t - b * N);
+    const float s0 = da_s[r], s1 = da_lr[r];
+    b0 += s0;
+    b1 += s1;
+    lam += dlam[r];
+    const VT *xr = x + t * DG;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane + 64 * j;
+      if (e < DG) {
+        const float xe = Elem<VT>::load(xr + e);
+        w0[j] = __builtin_fmaf(s0, xe, w0[j]);
+        w1[j] = __builtin_fmaf(s1, xe, w1[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + 64 * j;
+    if (e < DG) {
+      red[wave][e] = w0[j];
+      red[wave][DG + e] = w1[j];
+    }
+  }
+  if (lane == 0) {
+    red[wave][2 * DG] = b0;
+    red[wave][2 * DG + 1] = b1;
+    red[wave][2 * DG + 2] = lam;
+  }
+  __syncthreads();
   float *out = part + (static_cast<long long>(h) * kGateBlocks + blk) * (2 * DG + 3);
-  for (int e = threadIdx.x; e < DG; e += 256) {
-    float w0 = 0.0f, w1 = 0.0f;
-    for (long long t = t_lo; t < t_hi; ++t) {
-      const long long b = t / N;
-      const long long r = (b * H + h) * N + (t - b * N);
-      const float xe = Elem<VT>::load(x + t * DG + e);
-      w0 = __builtin_fmaf(da_s[r], xe, w0);
-      w1 = __builtin_fmaf(da_lr[r], xe, w1);
-    }
-    out[e] = w0;
-    out[DG + e] = w1;
-  }
-  if (threadIdx.x == 0) {
-    float b0 = 0.0f, b1 = 0.0f, lam = 0.0f;
-    for (long long t = t_lo; t < t_hi; ++t) {
-      const long long b = t / N;
-      const long long r = (b * H + h) * N + (t - b * N);
-      b0 += da_s[r];
-      b1 += da_lr[r];
-      lam += dlam[r];
-    }
-    out[2 * DG] = b0;
-    out[2 * DG + 1] = b1;
-    out[2 * DG + 2] = lam;
-  }
+  for (int e = threadIdx.x; e < 2 * DG + 3; e += 256) out[e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
 }
 
 // Block h < H: dW_g and db_g of head h; block H: dL/dlambda.  Partials are
-// added in block order.
+// added in block order (eight independent running sums, then combined).
 __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_reduce(const float *__restrict__ part, int H, int DG,
                                                                 int with_lambda, float *__restrict__ dgate_w,
                                                                 float *__restrict__ dgate_b, float *__restrict__ dlambda) {
   const int h = blockIdx.x;
   const int stride = 2 * DG + 3;
+  auto sum_blocks = [&](const float *p) {  // sum over kGateBlocks entries stride apart
+    float acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
+    for (int blk = 0; blk < kGateBlocks; blk += 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += p[static_cast<long long>(blk + u) * stride];
+    return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  };
   if (h < H) {
     const float *p = part + static_cast<long long>(h) * kGateBlocks * stride;
     for (int e = threadIdx.x; e < 2 * DG + 2; e += 256) {
-      float s = 0.0f;
-      for (int blk = 0; blk < kGateBlocks; ++blk) s += p[blk * stride + e];
+      const float s = sum_blocks(p + e);
       if (e < DG) dgate_w[static_cast<long long>(h) * DG + e] = s;
       else if (e < 2 * DG) dgate_w[static_cast<long long>(H + h) * DG + (e - DG)] = s;
       else if (e == 2 * DG) dgate_b[h] = s;
@@ -617,8 +654,7 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_reduce(const float *__r
     }
   } else if (threadIdx.x == 0) {
     float s = 0.0f;
-    for (int hh = 0; hh < H; ++hh)
-      for (int blk = 0; blk < kGateBlocks; ++blk) s += part[(static_cast<long long>(hh) * kGateBlocks + blk) * stride + 2 * DG + 2];
+    for (int hh = 0; hh < H; ++hh) s += sum_blocks(part + static_cast<long long>(hh) * kGateBlocks * stride + 2 * DG + 2);
     *dlambda = with_lambda ? s : 0.0f;
   }
 }
@@ -687,6 +723,10 @@ hipError_t launch_backward_t(const Geometry &g, const BackwardInputs &in, const 
   pa.x_gate = in.x_gate;
   pa.gate_w = in.gate_w;
   pa.gate_b = in.gate_b;
+  pa.sv_olr = fb.sv_olr;
+  pa.sv_z = fb.sv_z;
+  pa.sv_gs = fb.sv_gs;
+  pa.sv_glr = fb.sv_glr;
   pa.H = g.H; pa.N = g.N; pa.L = g.L; pa.P = g.P; pa.DG = g.DG; pa.rcb = g.rcb; pa.variant = g.variant;
   pa.lambda = in.lambda;
   pa.do_s = bb.do_s; pa.delta = bb.delta; pa.dcon = bb.dcon;
@@ -722,7 +762,7 @@ hipError_t launch_backward_t(const Geometry &g, const BackwardInputs &in, const 
     RaceBuildIO io;
     io.codes = bb.qcode_t;
     io.values = bb.dcon;
-    io.values_f32 = true;
+    io.values_f32 = false;  // rows and sums in dtype, accumulated in binary32
     io.rperm = bb.qrperm;
     io.rstart = bb.qrstart;
     io.rpart = bb.qrpart;
@@ -734,7 +774,7 @@ hipError_t launch_backward_t(const Geometry &g, const BackwardInputs &in, const 
   }
   {
     const float *dva = sparse ? bb.dv_acc : nullptr;
-    const float *dT = race ? bb.dT : nullptr;
+    const VT *dT = race ? static_cast<const VT *>(bb.dT) : nullptr;
     const void *kc = static_cast<const char *>(fb.rcode) + rows * g.L * g.rcb;  // key codes, table-major
     if (g.rcb == 1)
       hipLaunchKernelGGL((elsaa_k6_bwd_dv<VT, D, uint8_t>), dim3(blocks_for(g.rows * 16)), dim3(256), 0, stream, dva,

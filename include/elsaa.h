@@ -160,7 +160,14 @@ enum {
    * NO_ALPHA; elsewhere it is ignored.  Off by default: on MI355X its per-tile
    * table gathers run after the tile's attention instead of beside it, and the
    * two separate kernels are faster (see the design notes). */
-  ELSAA_OPT_FUSED_EPILOGUE = 1u << 0
+  ELSAA_OPT_FUSED_EPILOGUE = 1u << 0,
+  /* Training: the fusion also keeps, in the workspace, what the backward pass
+   * would otherwise recompute with a second gather of the L table rows per
+   * query: o_lr (in dtype) and per query the count sum, g_s and g_lr.  The
+   * workspace grows by B H N (d elem + 12) bytes (elsaa_workspace_bytes
+   * includes it); the forward writes that much more.  Takes precedence over
+   * ELSAA_OPT_FUSED_EPILOGUE, which the backward cannot use. */
+  ELSAA_OPT_SAVE_FOR_BACKWARD = 1u << 1
 };
 
 /* Host-only check of every field of *p except the device pointers' targets.
@@ -234,8 +241,7 @@ size_t elsaa_backward_workspace_bytes(const elsaa_params_t *p);
  * otherwise ELSAA_ERR_UNSUPPORTED.  y is the forward's output (read only by
  * ELSAA_VARIANT_SPARSE_ONLY, whose o_s it is).  bwd_workspace is caller-owned
  * device scratch of at least elsaa_backward_workspace_bytes(params) bytes,
- * 256-byte aligned.  Additional limit: N * d * 4 < 2^31 (binary32 gradient
- * rows).  Every gradient is written (zeros where a variant has none); the
+ * 256-byte aligned.  Every gradient is written (zeros where a variant has none); the
  * summation orders are fixed, so results repeat bit for bit.  Asynchronous on
  * params->stream like the forward; validation as in elsaa_forward. */
 int elsaa_backward(const void *q, const void *k, const void *v, const void *x_gate, const void *y,

@@ -58,6 +58,12 @@ def test_valid_params_and_workspace_size():
     assert ws >= base + rows * 64 * 2 + rows * 4
     fused = elsaa.workspace_bytes(params(options=elsaa.OPT_FUSED_EPILOGUE))
     assert base <= fused < base + rows * 64 * 2
+    # saving for the backward adds o_lr (dtype) and three floats per token-head,
+    # and excludes the fused epilogue
+    saved = elsaa.workspace_bytes(params(options=elsaa.OPT_SAVE_FOR_BACKWARD))
+    assert ws + rows * (64 * 2 + 12) <= saved <= ws + rows * (64 * 2 + 12) + 4 * 256
+    both = elsaa.workspace_bytes(params(options=elsaa.OPT_SAVE_FOR_BACKWARD | elsaa.OPT_FUSED_EPILOGUE))
+    assert both == saved
     # where the fused epilogue does not apply (12 tables) the option is ignored
     assert (elsaa.workspace_bytes(params(race_tables=12, options=elsaa.OPT_FUSED_EPILOGUE))
             == elsaa.workspace_bytes(params(race_tables=12)))
@@ -84,7 +90,7 @@ def test_valid_params_and_workspace_size():
     (dict(d_gate=1024), elsaa.ERR_UNSUPPORTED),
     (dict(variant=4), elsaa.ERR_INVALID_ARG),
     (dict(variant=-1), elsaa.ERR_INVALID_ARG),
-    (dict(options=2), elsaa.ERR_INVALID_ARG),
+    (dict(options=4), elsaa.ERR_INVALID_ARG),
     # per-(b, h) byte extents at 2^31 and beyond: the kernels' 32-bit offsets
     (dict(B=1, H=1, d=128, N=1 << 24), elsaa.ERR_UNSUPPORTED),                    # bf16, 2^32 B
     (dict(B=1, H=1, d=128, N=1 << 23), elsaa.ERR_UNSUPPORTED),                    # bf16, 2^31 B
@@ -139,6 +145,33 @@ def test_forward_rejects_before_launch():
     assert lib.elsaa_forward(fake, fake, fake, fake, fake, ctypes.byref(p), fake) == elsaa.ERR_WORKSPACE
     assert "workspace" in elsaa.last_error()
     assert lib.elsaa_forward(fake, fake, fake, fake, fake, None, fake) == elsaa.ERR_INVALID_ARG
+
+
+def test_backward_validation_before_any_device_call():
+    lib = elsaa.lib()
+    fake = ctypes.c_void_p(0x10000)
+    f32 = ctypes.c_void_p(0x30000)
+    p = params()
+    assert elsaa.lib().elsaa_backward_workspace_bytes(ctypes.byref(p)) > 0
+    # the fused epilogue keeps o_s and the LSE out of memory: no backward
+    pf = params(options=elsaa.OPT_FUSED_EPILOGUE)
+    assert lib.elsaa_backward_workspace_bytes(ctypes.byref(pf)) == 0
+    args = [fake] * 6 + [None, fake, 1 << 30] + [fake] * 4 + [f32] * 3
+    args[6] = ctypes.byref(pf)
+    assert lib.elsaa_backward(*args) == elsaa.ERR_UNSUPPORTED
+    # missing forward workspace, then missing backward workspace
+    args[6] = ctypes.byref(p)
+    assert lib.elsaa_backward(*args) == elsaa.ERR_WORKSPACE
+    need = elsaa.workspace_bytes(p)
+    pw = params(workspace_ptr=0x20000, workspace_bytes=need)
+    args[6] = ctypes.byref(pw)
+    args[7], args[8] = None, 0
+    assert lib.elsaa_backward(*args) == elsaa.ERR_WORKSPACE
+    assert "backward workspace" in elsaa.last_error()
+    # a NULL gradient pointer
+    args[7], args[8] = fake, 1 << 40
+    args[9] = None
+    assert lib.elsaa_backward(*args) == elsaa.ERR_INVALID_ARG
 
 
 def test_noalloc_rejects_problems_above_its_scratch_before_any_device_call():

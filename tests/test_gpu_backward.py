@@ -27,6 +27,10 @@ CASES = {
     "fp32-race-only": ("tiny-fp32", dict(H=2), "race_only"),
     "fp32-sparse-only": ("tiny-fp32", dict(H=2), "sparse_only"),
 }
+# the same with the forward keeping o_lr, the counts and the gates for the
+# backward (ELSAA_OPT_SAVE_FOR_BACKWARD)
+SAVED = ("tiny-fp32", "small-bf16-w64", "text32k-w128", "needle-d128-w256", "small-L3-dgate48",
+         "text32k-no-alpha", "text32k-race-only")
 
 
 def _dy(inp, seed):
@@ -38,7 +42,7 @@ def _dy(inp, seed):
     return d64.astype(np.float32), None
 
 
-def run_backward(inp, dy, dy_bits, variant, repeat=1):
+def run_backward(inp, dy, dy_bits, variant, repeat=1, options=0):
     import torch
 
     import efficient_long_context_amd as elsaa
@@ -47,7 +51,7 @@ def run_backward(inp, dy, dy_bits, variant, repeat=1):
     x = to_device(inp, dev)
     f = elsaa.Forward(B=wl.B, H=wl.H, N=wl.N, d=wl.d, d_gate=wl.d_gate, sort_bits=wl.sort_bits,
                       chunk=wl.chunk, race_tables=wl.race_tables, race_bits=wl.race_bits, lam=wl.lam,
-                      dtype=wl.dtype, variant=variant, device=dev)
+                      dtype=wl.dtype, variant=variant, options=options, device=dev)
     bwd = elsaa.Backward(f)
     if dy_bits is not None:
         dyt = torch.from_numpy(dy_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
@@ -62,16 +66,20 @@ def run_backward(inp, dy, dy_bits, variant, repeat=1):
     return outs
 
 
-@pytest.mark.parametrize("case", list(CASES))
+@pytest.mark.parametrize("case", list(CASES) + [c + "+saved" for c in SAVED])
 def test_backward_parity(case):
     import oracle
-    name, over, variant = CASES[case]
+
+    import efficient_long_context_amd as elsaa
+    base = case.replace("+saved", "")
+    options = elsaa.OPT_SAVE_FOR_BACKWARD if case.endswith("+saved") else 0
+    name, over, variant = CASES[base]
     wl = workloads.workload(name, **over)
     inp = workloads.generate(wl, seed=23)
     inp.gate_w *= 20.0  # gates away from one half
     dy, dy_bits = _dy(inp, 29)
     print(f"[backward] {case}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} {wl.dtype} {variant}", flush=True)
-    (got,) = run_backward(inp, dy, dy_bits, variant)
+    (got,) = run_backward(inp, dy, dy_bits, variant, options=options)
     ref = oracle.backward(inp.q, inp.k, inp.v, inp.x_gate, inp.hyperplanes, inp.gate_w, inp.gate_b, dy,
                           sort_bits=wl.sort_bits, chunk=wl.chunk, race_tables_n=wl.race_tables,
                           race_bits=wl.race_bits, lam=wl.lam, variant=variant)
@@ -85,9 +93,11 @@ def test_backward_parity(case):
 
 
 def test_backward_deterministic():
+    import efficient_long_context_amd as elsaa
     wl = workloads.workload("text32k-bf16", B=1, H=2, N=4096)
     inp = workloads.generate(wl, seed=31)
     dy, dy_bits = _dy(inp, 37)
-    a, b = run_backward(inp, dy, dy_bits, "full", repeat=2)
-    for x, y in zip(a, b):
-        np.testing.assert_array_equal(x, y)
+    for options in (0, elsaa.OPT_SAVE_FOR_BACKWARD):
+        a, b = run_backward(inp, dy, dy_bits, "full", repeat=2, options=options)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
