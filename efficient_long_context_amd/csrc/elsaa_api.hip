@@ -55,6 +55,17 @@ hipError_t device_cus(int device, int *cus) {
   return hipSuccess;
 }
 
+// The integer a C caller stored in an enum field.  A value outside the enum's
+// range is valid C but undefined to load as the C++ enum type, so the bits
+// are copied out instead.
+template <typename E>
+int enum_bits(const E &e) {
+  static_assert(sizeof(E) == sizeof(int), "enum fields are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof(v));
+  return v;
+}
+
 // Fills the geometry; returns ELSAA_OK or an error status with a message.
 int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
   if (!p) return fail(ELSAA_ERR_INVALID_ARG, "params is NULL");
@@ -68,10 +79,11 @@ int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
     return fail(ELSAA_ERR_INVALID_ARG, "sort_bits >= 0, race_bits >= 0, race_tables >= 1 required");
   if (!(p->lambda >= 0.0f) || !isfinite(p->lambda))
     return fail(ELSAA_ERR_INVALID_ARG, "lambda must be finite and >= 0");
-  if (p->dtype != ELSAA_DTYPE_F32 && p->dtype != ELSAA_DTYPE_BF16)
-    return fail(ELSAA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(p->dtype));
-  if (p->variant < ELSAA_VARIANT_FULL || p->variant > ELSAA_VARIANT_SPARSE_ONLY)
-    return fail(ELSAA_ERR_INVALID_ARG, "unknown variant %d", static_cast<int>(p->variant));
+  const int dtype = enum_bits(p->dtype), variant = enum_bits(p->variant);
+  if (dtype != ELSAA_DTYPE_F32 && dtype != ELSAA_DTYPE_BF16)
+    return fail(ELSAA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (variant < ELSAA_VARIANT_FULL || variant > ELSAA_VARIANT_SPARSE_ONLY)
+    return fail(ELSAA_ERR_INVALID_ARG, "unknown variant %d", variant);
   if (!p->gate_w || !p->gate_b) return fail(ELSAA_ERR_INVALID_ARG, "gate_w / gate_b is NULL");
   // limits of this implementation
   if (p->d != 64 && p->d != 128) return fail(ELSAA_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", p->d);
@@ -89,7 +101,7 @@ int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
   if (BH > 32767) return fail(ELSAA_ERR_UNSUPPORTED, "B * H must be <= 32767 (got %lld)", BH);
   // The kernels address one head's rows (and one batch's gate inputs) through
   // 32-bit byte offsets and buffer resources with 32-bit sizes.
-  const long long es = p->dtype == ELSAA_DTYPE_BF16 ? 2 : 4;
+  const long long es = dtype == ELSAA_DTYPE_BF16 ? 2 : 4;
   const long long head_bytes = static_cast<long long>(p->N) * p->d * es;
   const long long gate_bytes = static_cast<long long>(p->N) * p->d_gate * es;
   if (head_bytes >= (1ll << 31) || gate_bytes >= (1ll << 31))
@@ -106,12 +118,12 @@ int make_geometry(const elsaa_params_t *p, elsaa::Geometry *g) {
   g->nb_race = 1 << p->race_bits;
   g->rcb = p->race_bits <= 8 ? 1 : 2;
   g->sort_tiles = (p->N + elsaa::kSortTile - 1) / elsaa::kSortTile;
-  g->bf16 = p->dtype == ELSAA_DTYPE_BF16;
-  g->lambda = p->variant == ELSAA_VARIANT_NO_ALPHA ? 0.0f : p->lambda;
+  g->bf16 = dtype == ELSAA_DTYPE_BF16;
+  g->lambda = variant == ELSAA_VARIANT_NO_ALPHA ? 0.0f : p->lambda;
   g->cus = 256;
-  g->variant = static_cast<int>(p->variant);
-  g->run_sparse = p->variant != ELSAA_VARIANT_RACE_ONLY;
-  g->run_race = p->variant != ELSAA_VARIANT_SPARSE_ONLY;
+  g->variant = variant;
+  g->run_sparse = variant != ELSAA_VARIANT_RACE_ONLY;
+  g->run_race = variant != ELSAA_VARIANT_SPARSE_ONLY;
   g->identity = p->sort_bits == 0;
   if (p->options & ~static_cast<uint32_t>(ELSAA_OPT_FUSED_EPILOGUE | ELSAA_OPT_SAVE_FOR_BACKWARD))
     return fail(ELSAA_ERR_INVALID_ARG, "unknown option bits 0x%x", p->options);

@@ -212,35 +212,57 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_prep(PrepArgs a, long long r
 }
 
 // -------------------------------------------------- sparse branch, bf16 --
-// Stages 64 rows (sorted ranks [s0, s0 + 64) of the segment, through perm)
-// of two tensors row-major ([64][D + 8]) and the first one also transposed
-// ([D][64 + 4], key pairs packed in 32-bit words): all 256 threads, each a
-// (row pair, 8-column chunk).
-template <int D, bool kIdent>
-__device__ __forceinline__ void stage_pair(const uint16_t *__restrict__ x, const uint16_t *__restrict__ y,
-                                           const int32_t *__restrict__ perm, long long seg, int s0,
-                                           uint16_t *xs, uint16_t *ys, uint16_t *xt, int tid) {
-  constexpr int kRow = D + 8, kTRow = 64 + 4;
-  constexpr int kItems = 32 * (D / 8);  // (row pair, chunk)
+// Staging of 64 rows (sorted ranks [s0, s0 + 64) of the segment, through perm)
+// of two tensors x and y: row-major ([64][D + 8]) and, when kXT / kYT, also
+// transposed ([D][64 + 4], row pairs packed in 32-bit words).  Each of the 256
+// threads owns kPer (row pair, 8-column chunk) items.  The indices of a block
+// are requested two blocks ahead and its rows one block ahead (into
+// registers), so the loads overlap the previous block's products.
+template <int D, bool kIdent, bool kXT, bool kYT>
+struct Stager {
+  static constexpr int kRow = D + 8, kTRow = 64 + 4;
+  static constexpr int kPer = 32 * (D / 8) / 256;  // 1 (d = 64) or 2 (d = 128)
+  int j0[kPer], j1[kPer];
+  u16x8 x0[kPer], x1[kPer], y0[kPer], y1[kPer];
+  __device__ __forceinline__ void load_idx(const int32_t *__restrict__ perm, long long seg, int s0, int tid) {
 #pragma unroll
-  for (int it = tid; it < kItems; it += 256) {
-    const int jp = it % 32, ch = it / 32;
-    const int j0 = sorted_at<kIdent>(perm, seg, s0 + 2 * jp);
-    const int j1 = sorted_at<kIdent>(perm, seg, s0 + 2 * jp + 1);
-    const u16x8 x0 = *reinterpret_cast<const u16x8 *>(x + (seg + j0) * D + ch * 8);
-    const u16x8 x1 = *reinterpret_cast<const u16x8 *>(x + (seg + j1) * D + ch * 8);
-    const u16x8 y0 = *reinterpret_cast<const u16x8 *>(y + (seg + j0) * D + ch * 8);
-    const u16x8 y1 = *reinterpret_cast<const u16x8 *>(y + (seg + j1) * D + ch * 8);
-    *reinterpret_cast<u16x8 *>(xs + (2 * jp) * kRow + ch * 8) = x0;
-    *reinterpret_cast<u16x8 *>(xs + (2 * jp + 1) * kRow + ch * 8) = x1;
-    *reinterpret_cast<u16x8 *>(ys + (2 * jp) * kRow + ch * 8) = y0;
-    *reinterpret_cast<u16x8 *>(ys + (2 * jp + 1) * kRow + ch * 8) = y1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint32_t *>(xt + (ch * 8 + e) * kTRow + 2 * jp) =
-          static_cast<uint32_t>(x0[e]) | (static_cast<uint32_t>(x1[e]) << 16);
+    for (int p = 0; p < kPer; ++p) {
+      const int jp = (tid + 256 * p) % 32;
+      j0[p] = sorted_at<kIdent>(perm, seg, s0 + 2 * jp);
+      j1[p] = sorted_at<kIdent>(perm, seg, s0 + 2 * jp + 1);
+    }
   }
-}
+  __device__ __forceinline__ void load_rows(const uint16_t *__restrict__ x, const uint16_t *__restrict__ y,
+                                            long long seg, int tid) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int ch = (tid + 256 * p) / 32;
+      x0[p] = *reinterpret_cast<const u16x8 *>(x + (seg + j0[p]) * D + ch * 8);
+      x1[p] = *reinterpret_cast<const u16x8 *>(x + (seg + j1[p]) * D + ch * 8);
+      y0[p] = *reinterpret_cast<const u16x8 *>(y + (seg + j0[p]) * D + ch * 8);
+      y1[p] = *reinterpret_cast<const u16x8 *>(y + (seg + j1[p]) * D + ch * 8);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t *xs, uint16_t *ys, uint16_t *xt, uint16_t *yt, int tid) const {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int jp = (tid + 256 * p) % 32, ch = (tid + 256 * p) / 32;
+      *reinterpret_cast<u16x8 *>(xs + (2 * jp) * kRow + ch * 8) = x0[p];
+      *reinterpret_cast<u16x8 *>(xs + (2 * jp + 1) * kRow + ch * 8) = x1[p];
+      *reinterpret_cast<u16x8 *>(ys + (2 * jp) * kRow + ch * 8) = y0[p];
+      *reinterpret_cast<u16x8 *>(ys + (2 * jp + 1) * kRow + ch * 8) = y1[p];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (kXT)
+          *reinterpret_cast<uint32_t *>(xt + (ch * 8 + e) * kTRow + 2 * jp) =
+              static_cast<uint32_t>(x0[p][e]) | (static_cast<uint32_t>(x1[p][e]) << 16);
+        if constexpr (kYT)
+          *reinterpret_cast<uint32_t *>(yt + (ch * 8 + e) * kTRow + 2 * jp) =
+              static_cast<uint32_t>(y0[p][e]) | (static_cast<uint32_t>(y1[p][e]) << 16);
+      }
+    }
+  }
+};
 
 // 16-row tile products of a 64-row block held in LDS (rows row-major, kRow
 // elements) with the wave's 16 columns (b[kk], the d-slice g*8 .. +7 of each
@@ -316,9 +338,35 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dq_bf16(
   f32x4 acc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  Stager<D, kIdent, true, false> st;
+  st.load_idx(perm_k, seg, lo, tid);
+  st.load_rows(k, v, seg, tid);
+  int nxt[Stager<D, kIdent, true, false>::kPer][2];  // indices of the block after next
   for (int s0 = lo; s0 < hi; s0 += 64) {
     if (s0 != lo) __syncthreads();  // the previous block is consumed
-    stage_pair<D, kIdent>(k, v, perm_k, seg, s0, Ks, Vs, Kt, tid);
+    st.store(Ks, Vs, Kt, nullptr, tid);
+    // the next block's indices were requested during the previous block
+    if (s0 + 64 < hi) {
+      if (s0 != lo) {
+#pragma unroll
+        for (int p = 0; p < st.kPer; ++p) {
+          st.j0[p] = nxt[p][0];
+          st.j1[p] = nxt[p][1];
+        }
+      } else {
+        st.load_idx(perm_k, seg, s0 + 64, tid);
+      }
+      st.load_rows(k, v, seg, tid);
+      if (s0 + 128 < hi) {
+        Stager<D, kIdent, true, false> ix;
+        ix.load_idx(perm_k, seg, s0 + 128, tid);
+#pragma unroll
+        for (int p = 0; p < st.kPer; ++p) {
+          nxt[p][0] = ix.j0[p];
+          nxt[p][1] = ix.j1[p];
+        }
+      }
+    }
     __syncthreads();
     f32x4 s[4], dp[4];
     block_times_cols<D>(Ks, bq, s, g, r16);   // S^T: keys x the wave's queries
@@ -373,27 +421,47 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dkv_bf16(
     dkt[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     dvt[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   }
+  using St = Stager<D, kIdent, true, true>;
+  St st;
+  st.load_idx(perm_q, seg, lo, tid);
+  st.load_rows(q, do_s, seg, tid);
+  // the LSE and delta of the block's queries, one thread per query
+  int qi_next = tid < 64 ? sorted_at<kIdent>(perm_q, seg, lo + tid) : 0;
+  float lse_next = tid < 64 ? lse[seg + qi_next] * kLog2e : 0.0f;
+  float dlt_next = tid < 64 ? delta[seg + qi_next] : 0.0f;
+  int nxt[St::kPer][2];
   for (int s0 = lo; s0 < hi; s0 += 64) {
     if (s0 != lo) __syncthreads();
-    stage_pair<D, kIdent>(q, do_s, perm_q, seg, s0, Qs, Os, Qt, tid);
-    // dO transposed as well (the second tensor of the pair is not)
-    constexpr int kItems = 32 * (D / 8);
-#pragma unroll
-    for (int it = tid; it < kItems; it += 256) {
-      const int jp = it % 32, ch = it / 32;
-      const int j0 = sorted_at<kIdent>(perm_q, seg, s0 + 2 * jp);
-      const int j1 = sorted_at<kIdent>(perm_q, seg, s0 + 2 * jp + 1);
-      const u16x8 o0 = *reinterpret_cast<const u16x8 *>(do_s + (seg + j0) * D + ch * 8);
-      const u16x8 o1 = *reinterpret_cast<const u16x8 *>(do_s + (seg + j1) * D + ch * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint32_t *>(Ot + (ch * 8 + e) * kTRow + 2 * jp) =
-            static_cast<uint32_t>(o0[e]) | (static_cast<uint32_t>(o1[e]) << 16);
-    }
+    st.store(Qs, Os, Qt, Ot, tid);
     if (tid < 64) {
-      const int qi = sorted_at<kIdent>(perm_q, seg, s0 + tid);
-      lse_s[tid] = lse[seg + qi] * kLog2e;
-      dlt_s[tid] = delta[seg + qi];
+      lse_s[tid] = lse_next;
+      dlt_s[tid] = dlt_next;
+    }
+    if (s0 + 64 < hi) {
+      if (s0 != lo) {
+#pragma unroll
+        for (int p = 0; p < St::kPer; ++p) {
+          st.j0[p] = nxt[p][0];
+          st.j1[p] = nxt[p][1];
+        }
+      } else {
+        st.load_idx(perm_q, seg, s0 + 64, tid);
+      }
+      st.load_rows(q, do_s, seg, tid);
+      if (tid < 64) {
+        qi_next = sorted_at<kIdent>(perm_q, seg, s0 + 64 + tid);
+        lse_next = lse[seg + qi_next] * kLog2e;
+        dlt_next = delta[seg + qi_next];
+      }
+      if (s0 + 128 < hi) {
+        St ix;
+        ix.load_idx(perm_q, seg, s0 + 128, tid);
+#pragma unroll
+        for (int p = 0; p < St::kPer; ++p) {
+          nxt[p][0] = ix.j0[p];
+          nxt[p][1] = ix.j1[p];
+        }
+      }
     }
     __syncthreads();
     f32x4 s[4], dp[4];

@@ -29,17 +29,25 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "elsaa_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ELSAA_ORACLE_LIB names another build of the same source to load instead
+# (the sanitizer test builds one with AddressSanitizer and UBSan); it is used
+# as given and never rebuilt here.
+_LIB_OVERRIDE = os.environ.get("ELSAA_ORACLE_LIB")
+_LIB = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 _lib = None
+
+# gcc flags of the oracle: binary64 as written (no fast-math, no contraction)
+CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+          "-Wall", "-Wextra"]
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (binary64, no fast-math, no FMA contraction)."""
+    if _LIB_OVERRIDE:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
-               "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
-               _SRC, "-o", tmp, "-lm"]
+        cmd = ["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -48,7 +56,7 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _LIB_OVERRIDE and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
