@@ -21,7 +21,8 @@
 // (see attend_stage); P is rounded to bf16 for the PV product and the row sum
 // is the sum of those bf16 weights (an MFMA of an all-ones operand with P).
 // Workgroups of neighbouring tiles (which share key blocks) are mapped to the
-// same XCD.  With one sort bucket (sort_bits = 0) the sorted order is the
+// same XCD.  At d = 128 with w a multiple of 256, a workgroup takes 256
+// queries (eight waves of 32) and every wave also stages key blocks.  With one sort bucket (sort_bits = 0) the sorted order is the
 // original one: the kIdent instances index tokens directly and read no
 // permutation.
 #include <type_traits>
@@ -963,6 +964,125 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
   }
 }
 
+// d = 128, w a multiple of 256: one workgroup per 256 sorted queries (a
+// whole chunk when w = 256), eight waves of 32 queries (two groups of 16 that
+// share every K and V fragment read from LDS, so each fragment serves 32
+// queries: at d = 128 the LDS reads of 16-query fragments would outweigh the
+// matrix work).  No producer waves: all eight waves stage each block of 64
+// window keys (K row-major, V transposed) into one of two LDS buffers, the
+// next block's rows in flight in registers while the current block is
+// computed, with one LDS-only barrier per block.  Neighbouring tiles share a
+// chunk of keys and run on one XCD.
+template <bool kIdent>
+__global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_c256(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, int N, int w, int tiles_per_seg,
+    long long n_tiles, float scale_log2, uint16_t *__restrict__ o_s, float *__restrict__ lse) {
+  constexpr int D = 128, QT = 256, QG = 2;
+  constexpr int kKRow = D + 8, kVRow = kKBlock + 4;
+  constexpr int kBufElems = kKBlock * kKRow + D * kVRow;
+  constexpr int kKPer = kKBlock * (D / 8) / 512;        // 2 K pieces per thread
+  constexpr int kVPer = (kKBlock / 2) * (D / 8) / 512;  // 1 V (pair, chunk) per thread
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const long long tile = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (tile >= n_tiles) return;  // padding workgroup (whole group exits)
+  const long long seg = (tile / tiles_per_seg) * N;
+  const int r0 = static_cast<int>(tile % tiles_per_seg) * QT;
+  const int c = r0 / w;
+  const int lo = c > 0 ? (c - 1) * w : 0, hi = (c + 1) * w;
+  // staging: thread tid holds K pieces (row (tid + 512 p) / 16, chunk
+  // (tid + 512 p) % 16) and the V pair tid % 32, chunk tid / 32
+  int kj[kKPer], vj0[kVPer], vj1[kVPer];
+  u16x8 kr[kKPer], vr0[kVPer], vr1[kVPer];
+  auto load_idx = [&](int s0) {
+#pragma unroll
+    for (int p = 0; p < kKPer; ++p) kj[p] = sorted_index<kIdent>(perm_k, seg, s0 + (tid + 512 * p) / (D / 8));
+#pragma unroll
+    for (int p = 0; p < kVPer; ++p) {
+      const int jp = (tid + 512 * p) % (kKBlock / 2);
+      vj0[p] = sorted_index<kIdent>(perm_k, seg, s0 + 2 * jp);
+      vj1[p] = sorted_index<kIdent>(perm_k, seg, s0 + 2 * jp + 1);
+    }
+  };
+  auto load_rows = [&]() {
+#pragma unroll
+    for (int p = 0; p < kKPer; ++p)
+      kr[p] = *reinterpret_cast<const u16x8 *>(k + (seg + kj[p]) * D + ((tid + 512 * p) % (D / 8)) * 8);
+#pragma unroll
+    for (int p = 0; p < kVPer; ++p) {
+      const int ch = (tid + 512 * p) / (kKBlock / 2);
+      vr0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + vj0[p]) * D + ch * 8);
+      vr1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + vj1[p]) * D + ch * 8);
+    }
+  };
+  auto store_rows = [&](uint16_t *buf) {
+    uint16_t *Ks = buf, *Vt = buf + kKBlock * kKRow;
+#pragma unroll
+    for (int p = 0; p < kKPer; ++p) {
+      const int i = tid + 512 * p;
+      *reinterpret_cast<u16x8 *>(Ks + (i / (D / 8)) * kKRow + (i % (D / 8)) * 8) = kr[p];
+    }
+#pragma unroll
+    for (int p = 0; p < kVPer; ++p) {
+      const int i = tid + 512 * p;
+      const int jp = i % (kKBlock / 2), ch = i / (kKBlock / 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint32_t *>(Vt + (ch * 8 + e) * kVRow + 2 * jp) =
+            static_cast<uint32_t>(vr0[p][e]) | (static_cast<uint32_t>(vr1[p][e]) << 16);
+    }
+  };
+  // the wave's 32 queries: Q^T operands, lane holds d-slice g*8 .. +7 of each 32
+  int qidx[QG];
+  bf16x8 bq[QG][D / 32];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    qidx[qg] = sorted_index<kIdent>(perm_q, seg, r0 + wave * 32 + qg * 16 + r16);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      bq[qg][kk] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u16x8 *>(q + (seg + qidx[qg]) * D + kk * 32 + g * 8));
+  }
+  f32x4 o[QG][D / 16], l_acc[QG];
+  float m[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[qg][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    l_acc[qg] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    m[qg] = -INFINITY;
+  }
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, (u16x8)0x3f80);
+
+  load_idx(lo);
+  load_rows();
+  for (int s0 = lo, b = 0; s0 < hi; s0 += kKBlock, ++b) {
+    uint16_t *buf = smem + (b & 1) * kBufElems;
+    store_rows(buf);  // waits for this block's rows
+    if (s0 + kKBlock < hi) {  // the next block's rows, in flight during this block
+      load_idx(s0 + kKBlock);
+      load_rows();
+    }
+    lds_barrier();  // block b staged; every wave is past block b - 1
+    attend_stage<D, kKBlock, QG>(buf, buf + kKBlock * kKRow, kKBlock, bq, o, l_acc, m, scale_log2, ones, g, r16);
+  }
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const float l_tot = l_acc[qg][0];
+    const float inv = 1.0f / l_tot;
+    uint16_t *orow = o_s + (seg + qidx[qg]) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      *reinterpret_cast<uint2 *>(orow + dt * 16 + g * 4) =
+          make_uint2(pack_bf16x2(o[qg][dt][0] * inv, o[qg][dt][1] * inv),
+                     pack_bf16x2(o[qg][dt][2] * inv, o[qg][dt][3] * inv));
+    if (g == 0) lse[seg + qidx[qg]] = (m[qg] + log2f(l_tot)) * 0.69314718055994530942f;
+  }
+}
+
 // LDS bytes of the sliding-window kernel: three chunk slots, four
 // query-index slots and, fused, the gate weights of every head.
 constexpr size_t attn_slide_lds_bytes(int fused_heads) {
@@ -1064,8 +1184,24 @@ hipError_t launch_bf16_slide(const Geometry &g, const void *q, const void *k, co
 }
 
 template <bool kIdent>
+hipError_t launch_bf16_c256(const Geometry &g, const void *q, const void *k, const void *v, const int32_t *pq,
+                            const int32_t *pk, void *o_s, float *lse, float scale_log2, hipStream_t stream) {
+  const int tiles_per_seg = g.N / 256;
+  const long long n_tiles = static_cast<long long>(tiles_per_seg) * g.BH;
+  const long long grid = (n_tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
+  constexpr size_t kLds = 2 * (static_cast<size_t>(kKBlock) * (128 + 8) + static_cast<size_t>(128) * (kKBlock + 4)) * 2;
+  hipLaunchKernelGGL((elsaa_k3_chunk_attn_c256<kIdent>), dim3(static_cast<unsigned>(grid)), dim3(512), kLds, stream,
+                     static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                     static_cast<const uint16_t *>(v), pq, pk, g.N, g.w, tiles_per_seg, n_tiles, scale_log2,
+                     static_cast<uint16_t *>(o_s), lse);
+  return hipGetLastError();
+}
+
+template <bool kIdent>
 hipError_t launch_bf16_any(const Geometry &g, const void *q, const void *k, const void *v, const int32_t *pq,
                            const int32_t *pk, void *o_s, float *lse, float scale_log2, hipStream_t stream) {
+  if (g.D == 128 && g.w % 256 == 0)
+    return launch_bf16_c256<kIdent>(g, q, k, v, pq, pk, o_s, lse, scale_log2, stream);
   // 128-query tiles when w allows; key stages of 4 blocks (d = 64: the whole
   // 256-key window of w = 128) or 2, keeping LDS <= 72 KB (two workgroups
   // per CU)

@@ -34,6 +34,11 @@ CASES = {
     "bf16-P12-L4": ("small-bf16", dict(B=1, H=1, race_tables=4, race_bits=12)),
     "bf16-d128-w64": ("needle256k-bf16", dict(H=2, N=4096, chunk=64, sort_bits=7, race_tables=5, race_bits=9)),
     "bf16-w256": ("small-bf16", dict(B=2, H=2, N=4096, chunk=256)),
+    # d = 128 through each bf16 attention kernel: 256-query tiles (w a
+    # multiple of 256, two tiles a chunk at w = 512), producer/consumer
+    # (w = 128)
+    "bf16-d128-w512": ("needle256k-bf16", dict(H=2, N=4096, chunk=512)),
+    "bf16-d128-w128": ("needle256k-bf16", dict(H=2, N=4096, chunk=128)),
     # 8-bit codes on byte boundaries: an even number of plane tiles with no
     # sort code, and 12 tables (three code words a row)
     "bf16-bytecodes-ns0-L4": ("small-bf16", dict(B=1, H=2, sort_bits=0, race_tables=4, race_bits=8)),
@@ -45,7 +50,7 @@ CASES = {
     "bf16-sort12-N16k": ("small-bf16", dict(B=1, H=1, N=16384, sort_bits=12)),
     # one sort bucket: local-window attention in original order, no sort and no
     # permutation reads, through each attention kernel (sliding-window d = 64
-    # w = 128, producer/consumer d = 128, 64-query tiles, fp32)
+    # w = 128, 256-query tiles d = 128, 64-query tiles, fp32)
     "bf16-ns0-slide": ("text32k-bf16", dict(B=1, H=2, N=4096, sort_bits=0)),
     "bf16-ns0-d128-w256": ("needle256k-bf16", dict(H=2, N=4096, sort_bits=0)),
     "bf16-ns0-w64": ("small-bf16", dict(B=1, H=2, N=2048, sort_bits=0)),
