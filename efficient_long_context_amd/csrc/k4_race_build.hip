@@ -118,9 +118,12 @@ __device__ __forceinline__ int transposed_column(int m, int lane) {
 //           the buckets whose run starts in its part, stages their key
 //           indices in LDS and sums the value rows bucket by bucket: 16-byte
 //           lane pieces (8 rows of 64 bfloat16 columns per load), two batches
-//           of 8 loads in flight, a scalar test per load for the common case
-//           of a load inside one bucket, and at a bucket end a transposing
-//           lane reduction whose column sums are stored as the table row.
+//           of 4 loads in flight and none past the part's end (every load
+//           instruction costs the texture addresser the same ~20 cycles,
+//           whether its lanes are in range or not, and that unit bounds this
+//           kernel), a scalar test per load for the common case of a load
+//           inside one bucket, and at a bucket end a transposing lane
+//           reduction whose column sums are stored as the table row.
 //           Waves of one (b, h) are consecutive and so share an XCD's L2,
 //           which then holds the value rows its tables gather.
 //   The sorted key indices are 16-bit (PT = uint16_t) whenever N <= 65536,
@@ -262,8 +265,8 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
 }
 
 constexpr int kGatherWaves = 4;       // waves per gather workgroup
-constexpr int kGatherStage = 1024;    // key indices a wave stages in LDS at once
-constexpr int kGatherSlack = 256;     // staged entries read past the end by the look-ahead
+constexpr int kGatherStage = 512;     // key indices a wave stages in LDS at once
+constexpr int kGatherSlack = 128;     // staged entries read past the end by the last batch
 
 template <typename VT, int D, typename PT>
 __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
@@ -273,9 +276,15 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   using PC = Piece<VT, D>;
   constexpr int kCols = PC::kCols, kLPR = PC::kLanesPerRow;
   constexpr int kRPI = PC::kRowsPerLoad;
-  constexpr int kI = 8;              // load instructions per batch
+  constexpr int kI = 4;              // load instructions per batch
   constexpr int kBP = kI * kRPI;     // positions per batch
-  __shared__ uint32_t stage_all[kGatherWaves][kGatherStage + kGatherSlack];
+  // the stage holds key indices as stored (PT), from a 16-byte boundary of
+  // the permutation at or below the stage's first position
+  constexpr int kE = 16 / static_cast<int>(sizeof(PT));  // key indices per 16-byte piece
+  constexpr int kStageCap = kGatherStage + kE + kGatherSlack;
+  constexpr int kStageLoads = ((kGatherStage + 2 * kE - 2) / kE + 1 + 63) / 64;
+  static_assert(kBP + kE <= kGatherSlack, "a stage's last batch reads inside the stage");
+  __shared__ __align__(16) PT stage_all[kGatherWaves][kStageCap];
   const int nb = 1 << P;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -286,7 +295,7 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   const long long wg = xcd_local ? xcd_logical_block(blockIdx.x, gridDim.x) : static_cast<long long>(blockIdx.x);
   const long long u = wg * kGatherWaves + wave;
   if (u >= waves_total) return;  // whole wave; the kernel has no barriers
-  uint32_t *stage = stage_all[wave];
+  PT *stage = stage_all[wave];
   const int prt = static_cast<int>(u % parts);
   const long long unit = u / parts;  // (b, h) * L + table
   const long long bh = unit / L;
@@ -309,7 +318,10 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   const int my_off = lane / kLPR;   // this lane's row within a load
   const Bf16Adder adder;
   int b = b0;
-  int bend = __builtin_amdgcn_readfirstlane(rs[b0 + 1]);
+  // run end of bucket bk: a wave-uniform (scalar) load, waited on the scalar
+  // counter, so a bucket end does not wait for the value rows in flight
+  auto end_of = [&](int bk) -> int { return __builtin_amdgcn_readfirstlane(rs[bk + 1]); };
+  int bend = end_of(b0);
   float a[kCols];
 #pragma unroll
   for (int k = 0; k < kCols; ++k) a[k] = 0.0f;
@@ -334,21 +346,40 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   const uint32_t cbyte = static_cast<uint32_t>(cc) * 16u;
   for (int s0 = p_lo; s0 < p_hi; s0 += kGatherStage) {
     const int s1 = s0 + kGatherStage < p_hi ? s0 + kGatherStage : p_hi;
-    // stage the key indices of positions [s0, s1) (entries past s1 are stale:
-    // the look-ahead may load their rows, which are never added)
-    for (int i = lane; i < s1 - s0; i += 64) stage[i] = static_cast<uint32_t>(rp[s0 + i]);
+    // stage the key indices of positions [s0a, s1) in 16-byte pieces, every
+    // load issued before the first store (entries past s1 are stale and never
+    // used; N is a multiple of kE, so no piece crosses the end of the
+    // permutation)
+    const int s0a = s0 - s0 % kE;
+    {
+      u32x4 pcs[kStageLoads];
+#pragma unroll
+      for (int t = 0; t < kStageLoads; ++t) {
+        const int pos = s0a + (t * 64 + lane) * kE;
+        pcs[t] = (u32x4){0u, 0u, 0u, 0u};
+        if (pos < s1) pcs[t] = *reinterpret_cast<const u32x4 *>(rp + pos);
+      }
+#pragma unroll
+      for (int t = 0; t < kStageLoads; ++t) {
+        const int pos = s0a + (t * 64 + lane) * kE;
+        if (pos < s1) *reinterpret_cast<u32x4 *>(stage + (pos - s0a)) = pcs[t];
+      }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    // positions at or past s1 (in the stage's last batch) load from an offset
+    // past the buffer's end, which reads zero and fetches nothing
     auto load_batch = [&](int pbase, u32x4 (&r)[kI]) {
-      uint32_t jl[kI];
-      const uint32_t *lp = stage + (pbase - s0) + my_off;
+      uint32_t off[kI];
+      const PT *lp = stage + (pbase - s0a) + my_off;
 #pragma unroll
-      for (int i = 0; i < kI; ++i) jl[i] = lp[i * kRPI];
+      for (int i = 0; i < kI; ++i) off[i] = static_cast<uint32_t>(lp[i * kRPI]) * PC::kRowBytes + cbyte;
+#pragma unroll
+      for (int i = 0; i < kI; ++i) off[i] = pbase + i * kRPI + my_off < s1 ? off[i] : 0x80000000u;
 #pragma unroll
       for (int i = 0; i < kI; ++i)
-        r[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, jl[i] * PC::kRowBytes + cbyte, 0, 0));
+        r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off[i], 0, 0));
     };
     auto consume = [&](int pbase, const u32x4 (&r)[kI]) {
 #pragma unroll
@@ -364,7 +395,7 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
             if (cur == bend) {
               flush();
               ++b;
-              bend = b < b1 ? __builtin_amdgcn_readfirstlane(rs[b + 1]) : 0x7fffffff;
+              bend = b < b1 ? end_of(b) : 0x7fffffff;
             }
             const int stop = pe < bend ? pe : bend;
             if (my >= cur && my < stop) PC::add(r[i], a, adder);
@@ -373,13 +404,26 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
         }
       }
     };
+    // two batches in flight and none loaded past the stage's end: the loop
+    // runs while batches k, k + 1 and k + 2 all exist, and the last one or
+    // two batches are consumed after it (straight-line code, so every wait
+    // covers exactly the batch it precedes)
+    const int nbat = (s1 - s0 + kBP - 1) / kBP;
     u32x4 ra[kI], rb[kI];
     load_batch(s0, ra);
-    for (int pc = s0; pc < s1; pc += 2 * kBP) {
-      load_batch(pc + kBP, rb);
-      consume(pc, ra);
-      load_batch(pc + 2 * kBP, ra);
-      consume(pc + kBP, rb);
+    int k = 0;
+    for (; k + 2 < nbat; k += 2) {
+      load_batch(s0 + (k + 1) * kBP, rb);
+      consume(s0 + k * kBP, ra);
+      load_batch(s0 + (k + 2) * kBP, ra);
+      consume(s0 + (k + 1) * kBP, rb);
+    }
+    if (nbat - k == 2) {
+      load_batch(s0 + (k + 1) * kBP, rb);
+      consume(s0 + k * kBP, ra);
+      consume(s0 + (k + 1) * kBP, rb);
+    } else {
+      consume(s0 + k * kBP, ra);
     }
     // the stage may be overwritten only after every lane has read it
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
