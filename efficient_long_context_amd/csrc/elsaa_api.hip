@@ -148,7 +148,11 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   t.rcode = take(2 * rows * g.L * g.rcb);
   t.perm = reinterpret_cast<int32_t *>(take(2 * rows * 4));
   t.flags = reinterpret_cast<uint8_t *>(take(2 * rows + 4));  // + one word: any row flagged
-  t.hist = reinterpret_cast<uint32_t *>(take(2 * static_cast<size_t>(g.BH) * g.nb_sort * g.sort_tiles * 4));
+  // the sort's tile counts, and before them (the RACE build runs first) the
+  // tiled RACE rank's
+  const size_t sort_hist = 2 * static_cast<size_t>(g.BH) * g.nb_sort * g.sort_tiles * 4;
+  const size_t race_hist = elsaa::race_hist_bytes(g);
+  t.hist = reinterpret_cast<uint32_t *>(take(sort_hist > race_hist ? sort_hist : race_hist));
   // per-table key permutation and run starts of the RACE build
   t.rperm = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * g.N * 4));
   t.rstart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
@@ -188,6 +192,7 @@ size_t carve_bwd(const elsaa::Geometry &g, char *base, elsaa::BackwardBuffers *b
   t.dv_acc = reinterpret_cast<float *>(take(rows * g.D * 4));
   t.qcode_t = take(rows * g.L * g.rcb);
   t.qrperm = take(static_cast<size_t>(g.BH) * g.L * g.N * 4);
+  t.qhist = reinterpret_cast<uint32_t *>(take(elsaa::race_hist_bytes(g)));
   t.qrstart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
   t.qrpart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (elsaa::race_parts(g.N) + 1) * 8));
   t.dT = take(tab * g.D * es);

@@ -43,8 +43,9 @@ struct Buffers {
   int32_t *perm;    // [2][BH][N]
   uint8_t *flags;   // [2][BH][N]     rows whose codes need the exact pass,
                     // then one word: nonzero when any row may be flagged
-  uint32_t *hist;   // [2][BH][nb_sort][sort_tiles] -> exclusive offsets
-  int32_t *rperm;   // [BH][L][N]     keys of each table sorted by bucket
+  uint32_t *hist;   // [2][BH][nb_sort][sort_tiles] -> exclusive offsets; then
+                    // the RACE build's tiled rank counts (race_hist_bytes)
+  int32_t *rperm;   // [L][BH][N]     keys of each table sorted by bucket
   int32_t *rstart;  // [BH][L][nb_race + 1] run start of each bucket in rperm
   int32_t *rpart;   // [BH][L][parts + 1][2] per gather part: first owned bucket, its run start
   void *tsum;       // [BH][L][nb_race][D] bucket sums, stored in dtype
@@ -99,7 +100,8 @@ struct RaceBuildIO {
   const void *codes;  // [L][BH*N] codes, uint8 if P <= 8 else uint16
   const void *values; // [BH][N][D] rows
   bool values_f32;    // rows and sums are binary32 (else the problem's dtype)
-  void *rperm;        // [BH][L][N] sorted indices (uint16 when N <= 65536, else int32)
+  void *rperm;        // [L][BH][N] sorted indices (uint16 when N <= 65536, else int32)
+  uint32_t *hist;     // race_hist_bytes(g): tile counts of the tiled rank (unused when staged)
   int32_t *rstart;    // [BH][L][2^P + 1]
   int32_t *rpart;     // [BH][L][parts + 1][2]
   void *tsum;         // [BH][L][2^P][D] sums
@@ -107,6 +109,19 @@ struct RaceBuildIO {
   uint32_t *flag;     // a word the rank kernel clears
 };
 hipError_t launch_race_build_io(const Geometry &g, const RaceBuildIO &io, hipStream_t stream);
+// Scratch of the RACE build's tiled rank (0 when one workgroup per table
+// ranks in LDS): [L][BH][2^P][tiles] counts.
+size_t race_hist_bytes(const Geometry &g);
+// Tiled counting sort (k2_sort.hip) of S segments of N codes (code_bytes 1 or
+// 2, `bits` bits), segment s at codes + s N, into perm + s N (index_bytes 2
+// or 4): buckets in ascending order, each bucket's elements in an order that
+// is the same on every run (tiles in order; inside a tile, the LDS unit's
+// order of same-address atomics).  hist holds S 2^bits tiled_sort_tiles(N,
+// bits) words; it is left with the scanned counts: word (s, b, 0) of
+// [S][2^bits][tiles] is the first sorted position of bucket b.
+int tiled_sort_tiles(int N, int bits);
+hipError_t launch_tiled_sort(const void *codes, int code_bytes, int N, int bits, long long S,
+                             uint32_t *hist, void *perm, int index_bytes, hipStream_t stream);
 
 // Backward pass (k6_backward.hip).  The forward's workspace (Buffers) still
 // holds that call's codes, permutations, tables, o_s and LSE.
@@ -122,7 +137,8 @@ struct BackwardBuffers {
   float *da_s, *da_lr, *dlam;  // [BH][N]
   float *dv_acc;     // [BH][N][D] binary32, the sparse part of dv
   void *qcode_t;     // [L][BH*N] query codes, table-major
-  void *qrperm;      // [BH][L][N]
+  void *qrperm;      // [L][BH][N]
+  uint32_t *qhist;   // race_hist_bytes(g)
   int32_t *qrstart;  // [BH][L][2^P + 1]
   int32_t *qrpart;   // [BH][L][parts + 1][2]
   void *dT;          // [BH][L][2^P][D] dtype

@@ -18,7 +18,8 @@
 //   1. per-tile bucket histogram (LDS integer atomics), stored bucket-major;
 //   2. exclusive scan of the [bucket][tile] counts of each segment: the first
 //      sorted rank of every (bucket, tile);
-//   3. per tile, each wave ranks its 8 rounds of 64 codes in order.
+//   3. per tile, each wave ranks its 8 rounds of 64 codes in order into the
+//      tile's sorted order in LDS, and the tile writes it out in that order.
 // Integer-only, hence bit-exact and deterministic.
 #include "elsaa_internal.hpp"
 
@@ -26,7 +27,7 @@ namespace elsaa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRounds = kSortTile / (kWaves * 64);  // 8
+constexpr int kRounds = kSortTile / (kWaves * 64);  // 8 rounds of 64 codes a wave
 
 // Lanes of the wave that are valid and hold this lane's code (ns bits): one
 // ballot per code bit, each folded in as same &= ~(ballot ^ my_bit_as_mask),
@@ -43,23 +44,27 @@ __device__ __forceinline__ unsigned long long same_code_lanes(uint32_t code, boo
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
 
-__global__ __launch_bounds__(256) void elsaa_k2_sort_hist(const uint16_t *__restrict__ codes,
-                                                          int N, int nb, int T,
-                                                          uint32_t *__restrict__ hist) {
+// Tiles of kW waves x kRounds rounds of 64 codes: 4 waves (2048 codes) for
+// the Sort-LSH sort; the RACE build's tiled rank takes 16 (8192 codes) when
+// 16 waves' counters fit 64 KB of LDS.
+template <typename CT, int kW>
+__global__ __launch_bounds__(kW * 64) void elsaa_k2_sort_hist(const CT *__restrict__ codes, int N, int nb,
+                                                              int T, uint32_t *__restrict__ hist) {
+  constexpr int kTile = kW * kRounds * 64;
   extern __shared__ uint32_t h[];
   const int tile = blockIdx.x;
   const long long s = blockIdx.y;
-  for (int b = threadIdx.x; b < nb; b += 256) h[b] = 0;
+  for (int b = threadIdx.x; b < nb; b += kW * 64) h[b] = 0;
   __syncthreads();
-  const uint16_t *c = codes + s * N;
-  const int base = tile * kSortTile;
-  for (int e = threadIdx.x; e < kSortTile; e += 256) {
+  const CT *c = codes + s * N;
+  const int base = tile * kTile;
+  for (int e = threadIdx.x; e < kTile; e += kW * 64) {
     const int i = base + e;
     if (i < N) atomicAdd(&h[c[i]], 1u);
   }
   __syncthreads();
   uint32_t *out = hist + s * static_cast<long long>(nb) * T;
-  for (int b = threadIdx.x; b < nb; b += 256) out[static_cast<long long>(b) * T + tile] = h[b];
+  for (int b = threadIdx.x; b < nb; b += kW * 64) out[static_cast<long long>(b) * T + tile] = h[b];
 }
 
 // In-place exclusive scan of the M = nb * T counts of each segment, one
@@ -115,44 +120,75 @@ __global__ __launch_bounds__(1024) void elsaa_k2_sort_scan(uint32_t *__restrict_
   }
 }
 
-// Per tile: the first sorted rank of each (bucket, tile) is staged in LDS
-// with the waves' running counters; each wave then ranks its 8 rounds of 64
-// codes in order.  Every lane of a group of equal codes reads the group's
-// counter (one address, a broadcast) and writes back the same advanced value,
-// adding its rank inside the group; a wave's LDS accesses are carried out in
-// issue order, so the next round's read sees the update without a wait.
-__global__ __launch_bounds__(256) void elsaa_k2_sort_scatter(const uint16_t *__restrict__ codes,
-                                                             int N, int ns, int nb, int T,
-                                                             const uint32_t *__restrict__ offs,
-                                                             int32_t *__restrict__ perm) {
-  extern __shared__ uint32_t cnt[];  // [kWaves][nb] running sorted positions
+// Per tile: each wave ranks its 8 rounds of 64 codes in order into the
+// tile's own sorted order (the tile's codes by bucket, stable), staged in
+// LDS with each slot's position in the segment's order, then the tile writes
+// its slots in order: consecutive lanes write consecutive positions of a
+// bucket's run, instead of 64 scattered positions per store.  Every lane of a
+// group of equal codes reads the group's counter (one address, a broadcast)
+// and writes back the same advanced value, adding its rank inside the group;
+// a wave's LDS accesses are carried out in issue order, so the next round's
+// read sees the update without a wait.
+template <int kW>
+constexpr size_t scatter_lds_bytes(int nb) {
+  return (static_cast<size_t>(kW) * nb + 16 + nb + 2 * kW * kRounds * 64) * 4;
+}
+
+// kBallot: stable ranks from the ballots (the Sort-LSH sort, whose
+// permutation is part of the method); otherwise each element takes the next
+// slot of its (wave, bucket) counter from an LDS atomic that returns the old
+// value, one instruction a round instead of one ballot per code bit: a fixed
+// order run to run (the RACE build needs only a deterministic order of each
+// bucket's keys).
+template <typename CT, typename PT, int kW, bool kBallot>
+__global__ __launch_bounds__(kW * 64) void elsaa_k2_sort_scatter(const CT *__restrict__ codes, int N, int ns,
+                                                                 int nb, int T,
+                                                                 const uint32_t *__restrict__ offs,
+                                                                 PT *__restrict__ perm) {
+  constexpr int kTile = kW * kRounds * 64;
+  extern __shared__ uint32_t lds[];
+  uint32_t *cnt = lds;                  // [kW][nb] running tile-local sorted slots
+  uint32_t *part = cnt + kW * nb;       // [16] scan scratch
+  uint32_t *delta = part + 16;          // [nb] segment position minus tile slot, per bucket
+  uint32_t *spos = delta + nb;          // [kTile] segment position of each slot
+  uint32_t *sidx = spos + kTile;        // [kTile] element of each slot
   const int tile = blockIdx.x;
   const long long s = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint16_t *c = codes + s * N;
+  const CT *c = codes + s * N;
   const uint32_t *o = offs + s * static_cast<long long>(nb) * T;
-  int32_t *pm = perm + s * N;
-  const int wbase = tile * kSortTile + wave * (kSortTile / kWaves);
+  PT *pm = perm + s * N;
+  const int wbase = tile * kTile + wave * (kRounds * 64);
   uint32_t *wc = cnt + wave * nb;
 
   uint32_t code[kRounds];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int i = wbase + r * 64 + lane;
-    code[r] = i < N ? c[i] : 0xffffffffu;
+    code[r] = i < N ? static_cast<uint32_t>(c[i]) : 0xffffffffu;
   }
-  for (int b = tid; b < kWaves * nb; b += 256) cnt[b] = 0;
+  for (int b = tid; b < kW * nb; b += kW * 64) cnt[b] = 0;
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < kRounds; ++r)
     if (code[r] != 0xffffffffu) atomicAdd(&wc[code[r]], 1u);
   __syncthreads();
-  for (int b = tid; b < nb; b += 256) {  // the bucket's first rank in this tile, then earlier waves
-    uint32_t run = o[static_cast<long long>(b) * T + tile];
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t t = cnt[w * nb + b];
-      cnt[w * nb + b] = run;
-      run += t;
+  {  // tile-local bucket-major exclusive scan of the [bucket][wave] counts
+    constexpr int kThreads = kW * 64;
+    const int per = (nb + kThreads - 1) / kThreads;
+    const int b_lo = tid * per < nb ? tid * per : nb;
+    const int b_hi = b_lo + per < nb ? b_lo + per : nb;
+    uint32_t sum = 0;
+    for (int b = b_lo; b < b_hi; ++b)
+      for (int w = 0; w < kW; ++w) sum += cnt[w * nb + b];
+    uint32_t run = block_exclusive_scan(sum, part, lane, wave);
+    for (int b = b_lo; b < b_hi; ++b) {
+      delta[b] = o[static_cast<long long>(b) * T + tile] - run;  // modulo 2^32
+      for (int w = 0; w < kW; ++w) {
+        const uint32_t t = cnt[w * nb + b];
+        cnt[w * nb + b] = run;
+        run += t;
+      }
     }
   }
   __syncthreads();
@@ -162,13 +198,23 @@ __global__ __launch_bounds__(256) void elsaa_k2_sort_scatter(const uint16_t *__r
   for (int r = 0; r < kRounds; ++r) {
     const bool valid = code[r] != 0xffffffffu;
     const uint32_t cv = valid ? code[r] : 0u;
-    const unsigned long long same = same_code_lanes(cv, valid, ns);
-    const uint32_t before = wc[cv];
+    uint32_t slot;
+    if constexpr (kBallot) {
+      const unsigned long long same = same_code_lanes(cv, valid, ns);
+      const uint32_t before = wc[cv];
+      if (valid) wc[cv] = before + static_cast<uint32_t>(__popcll(same));
+      slot = before + static_cast<uint32_t>(__popcll(same & lt));
+    } else {
+      slot = valid ? atomicAdd(&wc[cv], 1u) : 0u;
+    }
     if (valid) {
-      wc[cv] = before + static_cast<uint32_t>(__popcll(same));
-      pm[before + static_cast<uint32_t>(__popcll(same & lt))] = wbase + r * 64 + lane;
+      sidx[slot] = static_cast<uint32_t>(wbase + r * 64 + lane);
+      spos[slot] = slot + delta[cv];
     }
   }
+  __syncthreads();
+  const int valid_slots = N - tile * kTile < kTile ? N - tile * kTile : kTile;
+  for (int i = tid; i < valid_slots; i += kW * 64) pm[spos[i]] = static_cast<PT>(sidx[i]);
 }
 
 // One workgroup per segment (see the file comment).  Each wave holds the
@@ -280,17 +326,63 @@ hipError_t launch_sort(const Geometry &g, const Buffers &buf, hipStream_t stream
     return hipGetLastError();
   }
   const int T = g.sort_tiles;
-  hipLaunchKernelGGL(elsaa_k2_sort_hist, dim3(T, S), dim3(256), g.nb_sort * 4, stream, buf.scode,
-                     g.N, g.nb_sort, T, buf.hist);
+  hipLaunchKernelGGL((elsaa_k2_sort_hist<uint16_t, kWaves>), dim3(T, S), dim3(kWaves * 64), g.nb_sort * 4, stream,
+                     buf.scode, g.N, g.nb_sort, T, buf.hist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(elsaa_k2_sort_scan, dim3(S), dim3(1024), 0, stream, buf.hist,
                      static_cast<long long>(g.nb_sort) * T);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(elsaa_k2_sort_scatter, dim3(T, S), dim3(256), kWaves * g.nb_sort * 4, stream,
-                     buf.scode, g.N, g.ns, g.nb_sort, T, buf.hist, buf.perm);
+  hipLaunchKernelGGL((elsaa_k2_sort_scatter<uint16_t, int32_t, kWaves, true>), dim3(T, S), dim3(kWaves * 64),
+                     scatter_lds_bytes<kWaves>(g.nb_sort), stream, buf.scode, g.N, g.ns, g.nb_sort, T, buf.hist,
+                     buf.perm);
   return hipGetLastError();
+}
+
+namespace {
+// Waves per tile of the tiled rank: 16 when their counters fit 64 KB of LDS.
+int tiled_waves(int bits) { return (1 << bits) <= 1024 ? 16 : kWaves; }
+
+template <typename CT, typename PT, int kW>
+hipError_t tiled_sort_t(const void *codes, int N, int bits, long long S, uint32_t *hist, void *perm,
+                        hipStream_t stream) {
+  const int nb = 1 << bits;
+  const int T = tiled_sort_tiles(N, bits);
+  hipLaunchKernelGGL((elsaa_k2_sort_hist<CT, kW>), dim3(T, static_cast<unsigned>(S)), dim3(kW * 64), nb * 4,
+                     stream, static_cast<const CT *>(codes), N, nb, T, hist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(elsaa_k2_sort_scan, dim3(static_cast<unsigned>(S)), dim3(1024), 0, stream, hist,
+                     static_cast<long long>(nb) * T);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((elsaa_k2_sort_scatter<CT, PT, kW, false>), dim3(T, static_cast<unsigned>(S)), dim3(kW * 64),
+                     scatter_lds_bytes<kW>(nb), stream, static_cast<const CT *>(codes), N, bits, nb, T, hist,
+                     static_cast<PT *>(perm));
+  return hipGetLastError();
+}
+
+template <typename CT, typename PT>
+hipError_t tiled_sort_w(const void *codes, int N, int bits, long long S, uint32_t *hist, void *perm,
+                        hipStream_t stream) {
+  return tiled_waves(bits) == 16 ? tiled_sort_t<CT, PT, 16>(codes, N, bits, S, hist, perm, stream)
+                                 : tiled_sort_t<CT, PT, kWaves>(codes, N, bits, S, hist, perm, stream);
+}
+}  // namespace
+
+int tiled_sort_tiles(int N, int bits) {
+  const int tile = tiled_waves(bits) * kRounds * 64;
+  return (N + tile - 1) / tile;
+}
+
+hipError_t launch_tiled_sort(const void *codes, int code_bytes, int N, int bits, long long S, uint32_t *hist,
+                             void *perm, int index_bytes, hipStream_t stream) {
+  if (code_bytes == 1)
+    return index_bytes == 2 ? tiled_sort_w<uint8_t, uint16_t>(codes, N, bits, S, hist, perm, stream)
+                            : tiled_sort_w<uint8_t, int32_t>(codes, N, bits, S, hist, perm, stream);
+  return index_bytes == 2 ? tiled_sort_w<uint16_t, uint16_t>(codes, N, bits, S, hist, perm, stream)
+                          : tiled_sort_w<uint16_t, int32_t>(codes, N, bits, S, hist, perm, stream);
 }
 
 }  // namespace elsaa

@@ -128,10 +128,26 @@ __device__ __forceinline__ int transposed_column(int m, int lane) {
 //           which then holds the value rows its tables gather.
 //   The sorted key indices are 16-bit (PT = uint16_t) whenever N <= 65536,
 //   halving the permutation's write here and its read in the gather.
-template <typename CT, typename PT>
+// Gather part p (positions from lo_p = N p / parts) owns the buckets whose
+// run starts in [lo_p, lo_{p+1}); its first one is the first bucket starting
+// at or after lo_p: bucket b + 1, at position `end`, for every lo_p in
+// (start, end] of a nonempty bucket b.  Entry 0 (bucket 0, position 0) and
+// entry `parts` (2^P, N) are written separately.
+__device__ __forceinline__ void part_entries(int b, uint32_t start, uint32_t end, int N, int parts,
+                                             int32_t *__restrict__ rp2) {
+  if (end <= start) return;
+  long long pp = static_cast<long long>(start) * parts / N;
+  while (pp < parts && static_cast<long long>(N) * pp / parts <= static_cast<long long>(start)) ++pp;
+  for (; pp < parts && static_cast<long long>(N) * pp / parts <= static_cast<long long>(end); ++pp) {
+    rp2[2 * pp] = b + 1;
+    rp2[2 * pp + 1] = static_cast<int32_t>(end);
+  }
+}
+
+template <typename CT>
 __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
-    const CT *__restrict__ kcodes, int N, int L, int P, long long rows, int staged, int parts,
-    PT *__restrict__ rperm, int32_t *__restrict__ rstart, int32_t *__restrict__ rpart,
+    const CT *__restrict__ kcodes, int N, int L, int BH, int P, long long rows, int parts,
+    uint16_t *__restrict__ rperm, int32_t *__restrict__ rstart, int32_t *__restrict__ rpart,
     float *__restrict__ tcnt, uint32_t *__restrict__ hash_flagged) {
   extern __shared__ uint32_t lds[];
   if (blockIdx.x == 0 && threadIdx.x == 0) *hash_flagged = 0u;  // the fix-up has run
@@ -139,7 +155,7 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
   const int W = static_cast<int>(blockDim.x >> 6);
   uint32_t *cnt = lds;           // [W][nb] counts, then running offsets
   uint32_t *part = lds + W * nb;  // [W] scan
-  // [N] when staged (N <= 65536), 16-byte aligned for the vector copy-out
+  // [N] (N <= 65536), 16-byte aligned for the vector copy-out
   uint16_t *lperm = reinterpret_cast<uint16_t *>(lds + (W * nb + W + 3) / 4 * 4);
   const long long unit = blockIdx.x;  // (b, h) * L + table
   const int tid = threadIdx.x, lane = tid & 63;
@@ -208,9 +224,6 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
       for (int w = 0; w < W; ++w) sum += cnt[w * nb + b];
     uint32_t run = block_exclusive_scan(sum, part, lane, wave);
     int32_t *rs = rstart + unit * (nb + 1);
-    // gather part p (positions from lo_p = N p / parts) owns the buckets whose
-    // run starts in [lo_p, lo_{p+1}); its first one is the first bucket starting
-    // at or after lo_p: bucket b + 1 when lo_p lies in (start_b, end_b]
     int32_t *rp2 = rpart + unit * (parts + 1) * 2;
     for (int b = b_lo; b < b_hi; ++b) {
       rs[b] = static_cast<int32_t>(run);
@@ -221,14 +234,7 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
         run += t;
       }
       tcnt[unit * nb + b] = static_cast<float>(run - r0);
-      if (run > r0) {
-        long long pp = static_cast<long long>(r0) * parts / N;
-        while (pp < parts && static_cast<long long>(N) * pp / parts <= static_cast<long long>(r0)) ++pp;
-        for (; pp < parts && static_cast<long long>(N) * pp / parts <= static_cast<long long>(run); ++pp) {
-          rp2[2 * pp] = b + 1;
-          rp2[2 * pp + 1] = static_cast<int32_t>(run);
-        }
-      }
+      part_entries(b, r0, run, N, parts, rp2);
     }
     if (tid == 0) {
       rs[nb] = N;
@@ -239,13 +245,11 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
     }
   }
   __syncthreads();
-  // sorted key indices: staged in LDS and written out in order (coalesced),
-  // or scattered straight to memory when N does not fit
-  PT *rp = rperm + unit * N;
+  // sorted key indices: staged in LDS and written out in order (coalesced)
+  uint16_t *rp = rperm + (static_cast<long long>(l) * BH + bh) * N;
   auto place = [&](uint32_t code, int j) {
     const uint32_t pos = atomicAdd(&wc[code], 1u);
-    if (staged) lperm[pos] = static_cast<uint16_t>(j);
-    else rp[pos] = static_cast<PT>(j);
+    lperm[pos] = static_cast<uint16_t>(j);
   };
   if (j_begin < j_end) for_batch(j_begin, first, place);
   for (int jb = j_begin + kBatch; jb < j_end; jb += kBatch) {
@@ -253,14 +257,42 @@ __global__ __launch_bounds__(1024) void elsaa_k4_race_rank(
     load_batch(jb, pc);
     for_batch(jb, pc, place);
   }
-  if (staged) {
-    __syncthreads();
-    if constexpr (sizeof(PT) == 2) {  // 8 indices a 16-byte piece (N is a multiple of 64)
-      for (int i = tid; i < N / 8; i += W * 64)
-        reinterpret_cast<u32x4 *>(rp)[i] = reinterpret_cast<const u32x4 *>(lperm)[i];
-    } else {
-      for (int i = tid; i < N; i += W * 64) rp[i] = static_cast<PT>(lperm[i]);
-    }
+  __syncthreads();
+  // 8 indices a 16-byte piece (N is a multiple of 64)
+  for (int i = tid; i < N / 8; i += W * 64)
+    reinterpret_cast<u32x4 *>(rp)[i] = reinterpret_cast<const u32x4 *>(lperm)[i];
+}
+
+// Run table of the tiled rank (segments too long for one workgroup's LDS):
+// the tiled sort has left the scanned [bucket][tile] counts of segment
+// (table l, (b, h)), whose tile-0 word of bucket b is that bucket's run start.
+// One workgroup per (b, h, table) writes the run starts, the counts and the
+// gather's part table.
+__global__ __launch_bounds__(256) void elsaa_k4_race_runs(const uint32_t *__restrict__ offs, int N, int L, int BH,
+                                                          int P, int T, int parts, int32_t *__restrict__ rstart,
+                                                          int32_t *__restrict__ rpart, float *__restrict__ tcnt,
+                                                          uint32_t *__restrict__ hash_flagged) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *hash_flagged = 0u;  // the fix-up has run
+  const int nb = 1 << P;
+  const long long unit = blockIdx.x;  // (b, h) * L + table
+  const long long bh = unit / L;
+  const int l = static_cast<int>(unit % L);
+  const uint32_t *o = offs + (static_cast<long long>(l) * BH + bh) * nb * T;
+  int32_t *rs = rstart + unit * (nb + 1);
+  int32_t *rp2 = rpart + unit * (parts + 1) * 2;
+  for (int b = threadIdx.x; b < nb; b += 256) {
+    const uint32_t start = o[static_cast<long long>(b) * T];
+    const uint32_t end = b + 1 < nb ? o[static_cast<long long>(b + 1) * T] : static_cast<uint32_t>(N);
+    rs[b] = static_cast<int32_t>(start);
+    tcnt[unit * nb + b] = static_cast<float>(end - start);
+    part_entries(b, start, end, N, parts, rp2);
+  }
+  if (threadIdx.x == 0) {
+    rs[nb] = N;
+    rp2[0] = 0;
+    rp2[1] = 0;
+    rp2[2 * parts] = nb;
+    rp2[2 * parts + 1] = N;
   }
 }
 
@@ -271,7 +303,7 @@ constexpr int kGatherSlack = 128;     // staged entries read past the end by the
 template <typename VT, int D, typename PT>
 __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
     const VT *__restrict__ v, const PT *__restrict__ rperm, const int32_t *__restrict__ rstart,
-    const int32_t *__restrict__ rpart, int N, int L, int P, int parts, long long waves_total,
+    const int32_t *__restrict__ rpart, int N, int L, int BH, int P, int parts, long long waves_total,
     int xcd_local, VT *__restrict__ tsum) {
   using PC = Piece<VT, D>;
   constexpr int kCols = PC::kCols, kLPR = PC::kLanesPerRow;
@@ -300,7 +332,7 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   const long long unit = u / parts;  // (b, h) * L + table
   const long long bh = unit / L;
   const int32_t *rs = rstart + unit * (nb + 1);
-  const PT *rp = rperm + unit * N;
+  const PT *rp = rperm + (static_cast<long long>(unit % L) * BH + bh) * N;
   VT *ts = tsum + unit * nb * static_cast<long long>(D);
 
   // owned buckets [b0, b1) and their positions [p_lo, p_hi), from the part
@@ -437,30 +469,49 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
 
 namespace {
 
+// One workgroup per (b, h, table) ranks the table's codes in LDS when its
+// counters and the segment's 16-bit permutation fit with two workgroups per
+// CU; returns its waves, or 0 for the tiled rank.
+int staged_rank_waves(const Geometry &g) {
+  if (g.N > 65536) return 0;
+  const int nb = g.nb_race;
+  int waves = 16384 / nb;  // LDS counters: waves * nb * 4 bytes <= 64 KB
+  waves = waves < 1 ? 1 : (waves > 16 ? 16 : waves);
+  constexpr size_t kRankLdsTwoPerCu = 78 * 1024;
+  auto rank_lds = [&](int w) {  // + 16: the staged indices start 16-byte aligned
+    return (static_cast<size_t>(w) * nb + w) * 4 + static_cast<size_t>(g.N) * 2 + 16;
+  };
+  while (waves > 4 && rank_lds(waves) > kRankLdsTwoPerCu) waves /= 2;
+  return rank_lds(waves) > kRankLdsTwoPerCu ? 0 : waves;
+}
+
 template <typename PT>
 hipError_t launch_race_build_pt(const Geometry &g, const RaceBuildIO &io, hipStream_t stream) {
   const int nb = g.nb_race;
   PT *rperm = reinterpret_cast<PT *>(io.rperm);
   const long long units = static_cast<long long>(g.BH) * g.L;
-  int waves = 16384 / nb;  // LDS counters: waves * nb * 4 bytes <= 64 KB
-  waves = waves < 1 ? 1 : (waves > 16 ? 16 : waves);
-  // stage the sorted indices in LDS when N fits, keeping two workgroups per CU
-  constexpr size_t kRankLdsTwoPerCu = 78 * 1024;
-  auto rank_lds = [&](int w, bool st) {  // + 16: the staged indices start 16-byte aligned
-    return (static_cast<size_t>(w) * nb + w) * 4 + (st ? static_cast<size_t>(g.N) * 2 + 16 : 0);
-  };
-  bool staged = g.N <= 65536;
-  while (staged && waves > 4 && rank_lds(waves, true) > kRankLdsTwoPerCu) waves /= 2;
-  if (rank_lds(waves, staged) > kRankLdsTwoPerCu) staged = false;
-  const size_t rlds = rank_lds(waves, staged);
-  if (g.rcb == 1)
-    hipLaunchKernelGGL((elsaa_k4_race_rank<uint8_t, PT>), dim3(static_cast<unsigned>(units)), dim3(waves * 64),
-                       rlds, stream, static_cast<const uint8_t *>(io.codes), g.N, g.L, g.P, g.rows, staged ? 1 : 0,
-                       race_parts(g.N), rperm, io.rstart, io.rpart, io.tcnt, io.flag);
-  else
-    hipLaunchKernelGGL((elsaa_k4_race_rank<uint16_t, PT>), dim3(static_cast<unsigned>(units)), dim3(waves * 64),
-                       rlds, stream, static_cast<const uint16_t *>(io.codes), g.N, g.L, g.P, g.rows, staged ? 1 : 0,
-                       race_parts(g.N), rperm, io.rstart, io.rpart, io.tcnt, io.flag);
+  const int waves = staged_rank_waves(g);
+  if (waves > 0) {
+    const size_t rlds = (static_cast<size_t>(waves) * nb + waves) * 4 + static_cast<size_t>(g.N) * 2 + 16;
+    uint16_t *rp16 = reinterpret_cast<uint16_t *>(io.rperm);
+    if (g.rcb == 1)
+      hipLaunchKernelGGL((elsaa_k4_race_rank<uint8_t>), dim3(static_cast<unsigned>(units)), dim3(waves * 64), rlds,
+                         stream, static_cast<const uint8_t *>(io.codes), g.N, g.L, g.BH, g.P, g.rows,
+                         race_parts(g.N), rp16, io.rstart, io.rpart, io.tcnt, io.flag);
+    else
+      hipLaunchKernelGGL((elsaa_k4_race_rank<uint16_t>), dim3(static_cast<unsigned>(units)), dim3(waves * 64), rlds,
+                         stream, static_cast<const uint16_t *>(io.codes), g.N, g.L, g.BH, g.P, g.rows,
+                         race_parts(g.N), rp16, io.rstart, io.rpart, io.tcnt, io.flag);
+  } else {
+    // tiled counting sort of the L * BH segments (table-major, as the codes
+    // are), then the run table from its scanned counts
+    hipError_t e = launch_tiled_sort(io.codes, g.rcb, g.N, g.P, units, io.hist, io.rperm,
+                                     static_cast<int>(sizeof(PT)), stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(elsaa_k4_race_runs, dim3(static_cast<unsigned>(units)), dim3(256), 0, stream, io.hist,
+                       g.N, g.L, g.BH, g.P, tiled_sort_tiles(g.N, g.P), race_parts(g.N), io.rstart, io.rpart,
+                       io.tcnt, io.flag);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -475,8 +526,8 @@ hipError_t launch_race_build_pt(const Geometry &g, const RaceBuildIO &io, hipStr
     // keep its gathers on one XCD; beyond that spread each (b, h) over all
     const int xcd_local = static_cast<long long>(g.N) * D * sizeof(VT) <= (4ll << 20) ? 1 : 0;
     hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT>), grid, dim3(kGatherWaves * 64), 0, stream,
-                       static_cast<const VT *>(io.values), rperm, io.rstart, io.rpart, g.N, g.L, g.P, parts,
-                       waves_total, xcd_local, static_cast<VT *>(io.tsum));
+                       static_cast<const VT *>(io.values), rperm, io.rstart, io.rpart, g.N, g.L, g.BH, g.P,
+                       parts, waves_total, xcd_local, static_cast<VT *>(io.tsum));
   };
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;
@@ -492,6 +543,11 @@ hipError_t launch_race_build_pt(const Geometry &g, const RaceBuildIO &io, hipStr
 
 }  // namespace
 
+size_t race_hist_bytes(const Geometry &g) {
+  if (staged_rank_waves(g) > 0) return 0;
+  return static_cast<size_t>(g.L) * g.BH * g.nb_race * tiled_sort_tiles(g.N, g.P) * 4;
+}
+
 hipError_t launch_race_build_io(const Geometry &g, const RaceBuildIO &io, hipStream_t stream) {
   // 16-bit key indices whenever they fit
   return g.N <= 65536 ? launch_race_build_pt<uint16_t>(g, io, stream)
@@ -505,6 +561,7 @@ hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &bu
   io.values = v;
   io.values_f32 = false;
   io.rperm = buf.rperm;
+  io.hist = buf.hist;  // shared with the sort, which runs after this stage
   io.rstart = buf.rstart;
   io.rpart = buf.rpart;
   io.tsum = buf.tsum;

@@ -832,6 +832,7 @@ hipError_t launch_backward_t(const Geometry &g, const BackwardInputs &in, const 
     io.values = bb.dcon;
     io.values_f32 = false;  // rows and sums in dtype, accumulated in binary32
     io.rperm = bb.qrperm;
+    io.hist = bb.qhist;
     io.rstart = bb.qrstart;
     io.rpart = bb.qrpart;
     io.tsum = bb.dT;

@@ -26,6 +26,9 @@ CASES = {
     "text32k-sparse-only": ("text32k-bf16", dict(B=1, H=2, N=4096), "sparse_only"),
     "fp32-race-only": ("tiny-fp32", dict(H=2), "race_only"),
     "fp32-sparse-only": ("tiny-fp32", dict(H=2), "sparse_only"),
+    # segments longer than 65536: 32-bit permutation indices and the tiled rank
+    # of the RACE transposes
+    "small-long-N": ("small-bf16", dict(B=1, H=1, N=65536 + 192, chunk=64), "full"),
 }
 # the same with the forward keeping o_lr, the counts and the gates for the
 # backward (ELSAA_OPT_SAVE_FOR_BACKWARD)

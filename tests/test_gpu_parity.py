@@ -48,6 +48,9 @@ CASES = {
     # 4096 buckets with 16K codes a segment (the tiled sort: the counters and
     # the codes do not fit one workgroup)
     "bf16-sort12-N16k": ("small-bf16", dict(B=1, H=1, N=16384, sort_bits=12)),
+    # the RACE build's tiled rank: 4096 buckets whose counters and 16-bit
+    # permutation do not fit one workgroup's LDS (16-bit indices, 4-wave tiles)
+    "bf16-race12-N8k": ("small-bf16", dict(B=1, H=2, N=8192, race_tables=2, race_bits=12)),
     # one sort bucket: local-window attention in original order, no sort and no
     # permutation reads, through each attention kernel (sliding-window d = 64
     # w = 128, 256-query tiles d = 128, 64-query tiles, fp32)
