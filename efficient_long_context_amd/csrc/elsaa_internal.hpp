@@ -76,7 +76,7 @@ __host__ __device__ __forceinline__ long long race_code_index(int tensor, long l
 
 // Positions of one table's sorted keys per RACE gather wave ("part"), before
 // rounding to whole buckets.
-constexpr int kGatherPos = 512;
+constexpr int kGatherPos = 256;
 __host__ __device__ __forceinline__ int race_parts(int N) { return (N + kGatherPos - 1) / kGatherPos; }
 
 constexpr int kSortTile = 2048;         // elements per sort tile (4 waves x 8 rounds x 64)
