@@ -177,9 +177,10 @@ __global__ __launch_bounds__(256) void elsaa_k5_fuse(
 // ---------------------------------------------------------------- wide path --
 // L in {8, 16}: 16-byte lane pieces (8 lanes per query for bfloat16 rows of 64
 // columns), so one load instruction gathers 8 table rows.  A workgroup serves
-// a run of R queries of one (b, h): the bucket counts of that (b, h) are staged
-// in LDS once (L 2^P <= 16384 words) and read there, the two gate weight rows
-// are loaded once, and each wave streams R/4 queries.
+// a run of R queries of one (b, h) (see launch_wide for R): the bucket counts
+// of that (b, h) are staged in LDS once (L 2^P <= 16384 words) and read
+// there, the two gate weight rows are loaded once, and the four waves take
+// the run's steps in turn.
 template <typename VT, int GE> struct GateIn;  // GE consecutive gate inputs of one lane
 // unpack: the lane's GE gate inputs from their raw words (loaded as 16, 8 or
 // 4 bytes into the leading words of a u32x4)
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     const VT *__restrict__ o_s, const float *__restrict__ lse, const CT *__restrict__ qcodes,
     const VT *__restrict__ tsum, const float *__restrict__ tcnt, const VT *__restrict__ x_gate,
     const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int P,
-    int DG, float lambda, int race_only, int R, long long units, VT *__restrict__ out, AuxOut aux) {
+    int DG, float lambda, int race_only, int R, int runs, long long units, VT *__restrict__ out, AuxOut aux) {
   constexpr int kES = static_cast<int>(sizeof(VT));
   constexpr int kCols = 16 / kES;         // value columns per lane
   constexpr int kLPQ = D / kCols;         // lanes per query
@@ -233,9 +234,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
 
   const long long unit = xcd_logical_block(blockIdx.x, gridDim.x);
   if (unit >= units) return;  // whole workgroup
-  const int runs = N / R;
   const long long bh = unit / runs;
   const int i_run = static_cast<int>(unit % runs) * R;
+  const int run_len = N - i_run < R ? N - i_run : R;  // the (b, h)'s last run may be shorter
   const int h = static_cast<int>(bh % H);
   const long long b = bh / H;
   const int nb = 1 << P;
@@ -260,8 +261,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   const Bf16Adder adder;
   __syncthreads();
 
-  const int per_wave = R / 4;
-  const int i_begin = i_run + wave * per_wave;
+  // the four waves take the run's steps in turn (a run is a multiple of 64
+  // queries, so of 4 kQPS)
+  const int my_steps = run_len / (4 * kQPS);
+  auto i_of = [&](int st) { return i_run + (wave + 4 * st) * kQPS; };
   // the streamed tensors of this (b, h) through buffer resources: a scalar
   // base and 32-bit lane offsets keep the per-lane addresses in one register
   const __amdgpu_buffer_rsrc_t qc_rs =
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     }
   };
   uint32_t cw[kCW];
-  load_codes(i_begin, cw);
+  load_codes(i_of(0), cw);
   // the streamed inputs of a step (sparse output, its LSE, gate inputs) are
   // requested one step ahead, so their HBM latency overlaps the table gathers
   auto load_stream = [&](int i0, u32x4 &os_raw, float &lse_v, u32x4 &xg_raw) {
@@ -312,10 +315,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   };
   u32x4 os_next = {0u, 0u, 0u, 0u}, xg_next = {0u, 0u, 0u, 0u};
   float lse_next = 0.0f;
-  load_stream(i_begin, os_next, lse_next, xg_next);
+  load_stream(i_of(0), os_next, lse_next, xg_next);
 
-  for (int step = 0; step < per_wave; step += kQPS) {
-    const int i = i_begin + step + lane / kLPQ;
+  for (int st = 0; st < my_steps; ++st) {
+    const int i = i_of(st) + lane / kLPQ;
+    const int i_next = st + 1 < my_steps ? i_of(st + 1) : i_of(st);
     const long long qi = bh * N + i;
     const u32x4 os_raw = os_next, xg_raw = xg_next;
     const float lse_i = lse_next;
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
       t[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, off, l * nb * kRowBytes, 0));
     }
     // the next step's streamed inputs
-    load_stream(step + kQPS < per_wave ? i_begin + step + kQPS : i_begin + step, os_next, lse_next, xg_next);
+    load_stream(i_next, os_next, lse_next, xg_next);
     // sparse output and gate inputs of this step
     float osv[kCols];
     if constexpr (kES == 2) {
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
       }
     }
     // next step's codes, in flight while this step finishes
-    load_codes(step + kQPS < per_wave ? i_begin + step + kQPS : i_begin + step, cw);
+    load_codes(i_next, cw);
 
     float num[kCols];
 #pragma unroll
@@ -473,19 +477,37 @@ template <int D, typename VT, typename CT, int LC>
 void launch_wide(const Geometry &g, const void *x_gate, const float *gate_w, const float *gate_b,
                  const Buffers &buf, const AuxOut &aux, void *out, hipStream_t stream) {
   constexpr int kQPS = 64 / (D / (16 / static_cast<int>(sizeof(VT))));
-  // queries per workgroup: the largest of 512, 256, 128, 64 that divides N and
-  // gives every wave whole steps (N is a multiple of 64)
-  int R = 512;
-  while (R > 64 && (g.N % R != 0)) R /= 2;
-  while (R / 4 < kQPS) R *= 2;  // not reached for d <= 128
-  const long long units = static_cast<long long>(g.BH) * (g.N / R);
-  const long long grid = (units + kXcdCount - 1) / kXcdCount * kXcdCount;
+  static_assert(64 % (4 * kQPS) == 0, "runs of 64 queries hold whole steps of every wave");
+  // Runs of R queries (a multiple of 64) of one (b, h).  While four
+  // workgroups fit a CU (128 VGPRs a lane, the staged counts small), runs of
+  // 512: many short workgroups overlap each other's start and end (runs sized
+  // to fill exactly one round measured 128 µs against 122 at text32k).  When
+  // the staged counts allow fewer (2^10 buckets: 64 KB), one round of
+  // workgroups, each staging its counts once (683 µs against 722 at
+  // needle256k); a (b, h)'s last run may then be shorter.
   const size_t lds = static_cast<size_t>(LC) * g.nb_race * 4;
+  int per_cu = static_cast<int>((160 * 1024) / (lds + 1024));
+  per_cu = per_cu < 1 ? 1 : (per_cu > 4 ? 4 : per_cu);
+  long long R = 512, runs;
+  if (per_cu == 4) {
+    while (R > 64 && (g.N % R != 0)) R /= 2;
+    runs = g.N / R;
+  } else {
+    const long long slots = static_cast<long long>(g.cus) * per_cu;
+    runs = slots / g.BH;  // runs per (b, h)
+    if (runs < 1) runs = 1;
+    R = (g.N + runs - 1) / runs;
+    R = (R + 63) / 64 * 64;
+    runs = (g.N + R - 1) / R;
+  }
+  const long long units = static_cast<long long>(g.BH) * runs;
+  const long long grid = (units + kXcdCount - 1) / kXcdCount * kXcdCount;
   hipLaunchKernelGGL((elsaa_k5_fuse_wide<D, VT, CT, LC>), dim3(static_cast<unsigned>(grid)), dim3(256), lds,
                      stream, static_cast<const VT *>(buf.o_s), buf.lse,
                      static_cast<const CT *>(buf.rcode), static_cast<const VT *>(buf.tsum), buf.tcnt,
                      static_cast<const VT *>(x_gate), gate_w, gate_b, g.H, g.N, g.P, g.DG, g.lambda,
-                     g.run_sparse ? 0 : 1, R, units, static_cast<VT *>(out), aux);
+                     g.run_sparse ? 0 : 1, static_cast<int>(R), static_cast<int>(runs), units,
+                     static_cast<VT *>(out), aux);
 }
 
 template <int D, typename VT, typename CT>
