@@ -33,6 +33,8 @@
 //            query rows gives dT; a per-key gather adds it to dv;
 //   gates    dx_gate per token; dW_g, db_g and dlambda as per-block partial
 //            sums reduced in a fixed order.
+#include <type_traits>
+
 #include "elsaa_internal.hpp"
 
 namespace elsaa {
@@ -618,6 +620,72 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dv(const float *__restrict__
   store_cols<VT, C>(dv + r * D + sub * C, acc);
 }
 
+// The same sum, gathered the way the forward's fusion gathers table rows: a
+// workgroup of four waves takes 64 consecutive keys of one (b, h), stages
+// their L codes per table in LDS (one 64-byte load per table), and each wave
+// step covers 64 / (lanes per row) keys with 16-byte lane pieces, its LC row
+// loads (LC = 8 or 16) issued together: one load instruction per table for
+// 8 keys of bfloat16 d = 64, where 16 lanes per key took four.
+template <typename VT, int D, typename CT, int LC>
+__global__ __launch_bounds__(256) void elsaa_k6_bwd_dv_wide(const float *__restrict__ dv_acc,
+                                                            const CT *__restrict__ kcodes, const VT *__restrict__ dT,
+                                                            long long rows, int N, int P, VT *__restrict__ dv) {
+  constexpr int kCols = 16 / static_cast<int>(sizeof(VT));  // columns per lane
+  constexpr int kLPR = D / kCols;                           // lanes per key
+  constexpr int kKPS = 64 / kLPR;                           // keys per wave step
+  __shared__ CT codes[LC][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long r0 = static_cast<long long>(blockIdx.x) * 64;  // N is a multiple of 64
+  const long long bh = r0 / N;
+  for (int i = tid; i < LC * 64; i += 256) codes[i >> 6][i & 63] = kcodes[static_cast<long long>(i >> 6) * rows + r0 + (i & 63)];
+  __syncthreads();
+  const int cc = lane % kLPR;
+  const long long nb = 1ll << P;
+  const VT *tb = dT ? dT + bh * LC * nb * D + cc * kCols : nullptr;
+#pragma unroll
+  for (int st = 0; st < 16 / kKPS; ++st) {
+    const int kk = wave * 16 + st * kKPS + lane / kLPR;  // key within the block
+    const long long r = r0 + kk;
+    float acc[kCols];
+#pragma unroll
+    for (int e = 0; e < kCols; ++e) acc[e] = 0.0f;
+    if (dv_acc) {
+#pragma unroll
+      for (int e = 0; e < kCols; e += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(dv_acc + r * D + cc * kCols + e);
+        acc[e] = x[0]; acc[e + 1] = x[1]; acc[e + 2] = x[2]; acc[e + 3] = x[3];
+      }
+    }
+    if (tb) {
+      u32x4 t[LC];
+#pragma unroll
+      for (int l = 0; l < LC; ++l)
+        t[l] = *reinterpret_cast<const u32x4 *>(tb + (l * nb + static_cast<long long>(codes[l][kk])) * D);
+#pragma unroll
+      for (int l = 0; l < LC; ++l) {
+        if constexpr (sizeof(VT) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += __uint_as_float(t[l][e] << 16);
+            acc[2 * e + 1] += __uint_as_float(t[l][e] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(t[l][e]);
+        }
+      }
+    }
+    if constexpr (sizeof(VT) == 2) {
+      *reinterpret_cast<u32x4 *>(dv + r * D + cc * kCols) =
+          u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                pack_bf16x2(acc[6], acc[7])};
+    } else {
+      *reinterpret_cast<f32x4 *>(dv + r * D + cc * kCols) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    }
+  }
+}
+
 // -------------------------------------------------------------- gates --
 // dx_gate[b][i][e] = sum_h da_s[b][h][i] W_g[0][h][e] + da_lr[b][h][i] W_g[1][h][e]
 template <typename VT>
@@ -631,7 +699,25 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dxgate(const float *__restri
   const long long b = t / N;
   const int i = static_cast<int>(t - b * N);
   float acc = 0.0f;
-  for (int h = 0; h < H; ++h) {
+  // four heads a round, their loads issued together
+  int h = 0;
+  for (; h + 4 <= H; h += 4) {
+    float a[4], c[4], w[4], v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long long r = (b * H + h + u) * N + i;
+      a[u] = da_s[r];
+      c[u] = da_lr[r];
+      w[u] = gate_w[static_cast<long long>(h + u) * DG + e];
+      v[u] = gate_w[static_cast<long long>(H + h + u) * DG + e];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc = __builtin_fmaf(a[u], w[u], acc);
+      acc = __builtin_fmaf(c[u], v[u], acc);
+    }
+  }
+  for (; h < H; ++h) {
     const long long r = (b * H + h) * N + i;
     acc = __builtin_fmaf(da_s[r], gate_w[static_cast<long long>(h) * DG + e], acc);
     acc = __builtin_fmaf(da_lr[r], gate_w[static_cast<long long>(H + h) * DG + e], acc);
@@ -659,21 +745,37 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_part(const float *__res
 #pragma unroll
   for (int j = 0; j < kPer; ++j) w0[j] = w1[j] = 0.0f;
   float b0 = 0.0f, b1 = 0.0f, lam = 0.0f;
-  for (long long t = t_lo + wave; t < t_hi; t += 4) {
-    const long long b = t / N;
-    const long long r = (b * H + h) * N + (t - b * N);
-    const float s0 = da_s[r], s1 = da_lr[r];
-    b0 += s0;
-    b1 += s1;
-    lam += dlam[r];
-    const VT *xr = x + t * DG;
+  // kU tokens a round, every load of the round issued before the first use
+  // (one token at a time left each wave a chain of dependent loads)
+  constexpr int kU = 8;
+  for (long long t0 = t_lo + wave; t0 < t_hi; t0 += 4 * kU) {
+    float s0[kU], s1[kU], sl[kU], xe[kU][kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = lane + 64 * j;
-      if (e < DG) {
-        const float xe = Elem<VT>::load(xr + e);
-        w0[j] = __builtin_fmaf(s0, xe, w0[j]);
-        w1[j] = __builtin_fmaf(s1, xe, w1[j]);
+    for (int u = 0; u < kU; ++u) {
+      const long long t = t0 + 4 * u;
+      const bool ok = t < t_hi;
+      const long long tc = ok ? t : t_lo;
+      const long long b = tc / N;
+      const long long r = (b * H + h) * N + (tc - b * N);
+      s0[u] = ok ? da_s[r] : 0.0f;
+      s1[u] = ok ? da_lr[r] : 0.0f;
+      sl[u] = ok ? dlam[r] : 0.0f;
+      const VT *xr = x + tc * DG;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int e = lane + 64 * j;
+        xe[u][j] = e < DG ? Elem<VT>::load(xr + e) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      b0 += s0[u];
+      b1 += s1[u];
+      lam += sl[u];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        w0[j] = __builtin_fmaf(s0[u], xe[u][j], w0[j]);
+        w1[j] = __builtin_fmaf(s1[u], xe[u][j], w1[j]);
       }
     }
   }
@@ -702,13 +804,20 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_reduce(const float *__r
                                                                 float *__restrict__ dgate_b, float *__restrict__ dlambda) {
   const int h = blockIdx.x;
   const int stride = 2 * DG + 3;
-  auto sum_blocks = [&](const float *p) {  // sum over kGateBlocks entries stride apart
+  // sum over kGateBlocks entries stride apart: eight running sums (entry
+  // blk goes to sum blk % 8), 32 entries requested at a time
+  auto sum_blocks = [&](const float *p) {
+    static_assert(kGateBlocks % 32 == 0, "whole rounds of 32 partial sums");
     float acc[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
-    for (int blk = 0; blk < kGateBlocks; blk += 8)
+    for (int blk = 0; blk < kGateBlocks; blk += 32) {
+      float v[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] += p[static_cast<long long>(blk + u) * stride];
+      for (int u = 0; u < 32; ++u) v[u] = p[static_cast<long long>(blk + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) acc[u % 8] += v[u];
+    }
     return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   };
   if (h < H) {
@@ -720,10 +829,21 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_reduce(const float *__r
       else if (e == 2 * DG) dgate_b[h] = s;
       else dgate_b[H + h] = s;
     }
-  } else if (threadIdx.x == 0) {
-    float s = 0.0f;
-    for (int hh = 0; hh < H; ++hh) s += sum_blocks(part + static_cast<long long>(hh) * kGateBlocks * stride + 2 * DG + 2);
-    *dlambda = with_lambda ? s : 0.0f;
+  } else {
+    // thread t adds the dL/dlambda shares of heads t, t + 256, ... (in that
+    // order), then thread 0 adds the threads' sums in thread order: head
+    // order whenever H <= 256
+    __shared__ float lam_t[256];
+    float own = 0.0f;
+    for (int hh = threadIdx.x; hh < H; hh += 256)
+      own += sum_blocks(part + static_cast<long long>(hh) * kGateBlocks * stride + 2 * DG + 2);
+    lam_t[threadIdx.x] = own;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float s = 0.0f;
+      for (int t = 0; t < (H < 256 ? H : 256); ++t) s += lam_t[t];
+      *dlambda = with_lambda ? s : 0.0f;
+    }
   }
 }
 
@@ -845,13 +965,31 @@ hipError_t launch_backward_t(const Geometry &g, const BackwardInputs &in, const 
     const float *dva = sparse ? bb.dv_acc : nullptr;
     const VT *dT = race ? static_cast<const VT *>(bb.dT) : nullptr;
     const void *kc = static_cast<const char *>(fb.rcode) + rows * g.L * g.rcb;  // key codes, table-major
-    if (g.rcb == 1)
+    const unsigned kblocks = static_cast<unsigned>(g.rows / 64);
+    auto wide = [&](auto ct, auto lc) {
+      using CT = decltype(ct);
+      constexpr int LC = decltype(lc)::value;
+      hipLaunchKernelGGL((elsaa_k6_bwd_dv_wide<VT, D, CT, LC>), dim3(kblocks), dim3(256), 0, stream, dva,
+                         static_cast<const CT *>(kc), dT, g.rows, g.N, g.P, static_cast<VT *>(out.dv));
+    };
+    using L8 = std::integral_constant<int, 8>;
+    using L16 = std::integral_constant<int, 16>;
+    if (g.L == 16 || g.L == 8) {
+      if (g.rcb == 1) {
+        if (g.L == 16) wide(uint8_t{}, L16{});
+        else wide(uint8_t{}, L8{});
+      } else {
+        if (g.L == 16) wide(uint16_t{}, L16{});
+        else wide(uint16_t{}, L8{});
+      }
+    } else if (g.rcb == 1) {
       hipLaunchKernelGGL((elsaa_k6_bwd_dv<VT, D, uint8_t>), dim3(blocks_for(g.rows * 16)), dim3(256), 0, stream, dva,
                          static_cast<const uint8_t *>(kc), dT, g.rows, g.N, g.L, g.P, static_cast<VT *>(out.dv));
-    else
+    } else {
       hipLaunchKernelGGL((elsaa_k6_bwd_dv<VT, D, uint16_t>), dim3(blocks_for(g.rows * 16)), dim3(256), 0, stream,
                          dva, static_cast<const uint16_t *>(kc), dT, g.rows, g.N, g.L, g.P,
                          static_cast<VT *>(out.dv));
+    }
     if (!check()) return e;
   }
   // 4. gates and lambda
