@@ -729,12 +729,11 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dxgate(const float *__restri
 // db_g[0][h], db_g[1][h] and dL/dlambda, into part[h][blk][2 DG + 3].  Wave w
 // takes tokens t_lo + w, + 4, ... (its da values are wave-uniform loads), lanes
 // the gate columns; the four waves' sums are added in LDS in wave order.
-template <typename VT>
+template <typename VT, int kPer>  // kPer >= DG / 64: gate columns per lane
 __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_part(const float *__restrict__ da_s,
                                                               const float *__restrict__ da_lr,
                                                               const float *__restrict__ dlam, const VT *__restrict__ x,
                                                               int B, int H, int N, int DG, float *__restrict__ part) {
-  constexpr int kPer = 8;  // gate columns per lane: DG <= 512
   __shared__ float red[4][2 * 512 + 3];
   const int h = blockIdx.x, blk = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -757,14 +756,18 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_part(const float *__res
       const long long tc = ok ? t : t_lo;
       const long long b = tc / N;
       const long long r = (b * H + h) * N + (tc - b * N);
-      s0[u] = ok ? da_s[r] : 0.0f;
-      s1[u] = ok ? da_lr[r] : 0.0f;
-      sl[u] = ok ? dlam[r] : 0.0f;
+      // loads at clamped addresses and selects (no branch around a load,
+      // which would wait for it at the branch's end)
+      const float a0 = da_s[r], a1 = da_lr[r], al = dlam[r];
+      s0[u] = ok ? a0 : 0.0f;
+      s1[u] = ok ? a1 : 0.0f;
+      sl[u] = ok ? al : 0.0f;
       const VT *xr = x + tc * DG;
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int e = lane + 64 * j;
-        xe[u][j] = e < DG ? Elem<VT>::load(xr + e) : 0.0f;
+        const float xv = Elem<VT>::load(xr + (e < DG ? e : DG - 1));
+        xe[u][j] = e < DG ? xv : 0.0f;
       }
     }
 #pragma unroll
@@ -998,8 +1001,15 @@ hipError_t launch_backward_t(const Geometry &g, const BackwardInputs &in, const 
     hipLaunchKernelGGL(elsaa_k6_bwd_dxgate<VT>, dim3(blocks_for(nx)), dim3(256), 0, stream, bb.da_s, bb.da_lr,
                        in.gate_w, g.B, g.H, g.N, g.DG, static_cast<VT *>(out.dx_gate));
     if (!check()) return e;
-    hipLaunchKernelGGL(elsaa_k6_bwd_gate_part<VT>, dim3(g.H, kGateBlocks), dim3(256), 0, stream, bb.da_s, bb.da_lr,
-                       bb.dlam, static_cast<const VT *>(in.x_gate), g.B, g.H, g.N, g.DG, bb.gate_part);
+    auto gate_part = [&](auto kp) {
+      constexpr int kPer = decltype(kp)::value;
+      hipLaunchKernelGGL((elsaa_k6_bwd_gate_part<VT, kPer>), dim3(g.H, kGateBlocks), dim3(256), 0, stream, bb.da_s,
+                         bb.da_lr, bb.dlam, static_cast<const VT *>(in.x_gate), g.B, g.H, g.N, g.DG, bb.gate_part);
+    };
+    if (g.DG <= 64) gate_part(std::integral_constant<int, 1>{});
+    else if (g.DG <= 128) gate_part(std::integral_constant<int, 2>{});
+    else if (g.DG <= 256) gate_part(std::integral_constant<int, 4>{});
+    else gate_part(std::integral_constant<int, 8>{});
     if (!check()) return e;
     hipLaunchKernelGGL(elsaa_k6_bwd_gate_reduce, dim3(g.H + 1), dim3(256), 0, stream, bb.gate_part, g.H, g.DG,
                        g.variant == ELSAA_VARIANT_FULL ? 1 : 0, out.dgate_w, out.dgate_b, out.dlambda);
