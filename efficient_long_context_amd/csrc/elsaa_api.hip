@@ -55,6 +55,36 @@ hipError_t device_cus(int device, int *cus) {
   return hipSuccess;
 }
 
+// A second stream per device, for the sort to overlap the RACE build (they
+// depend only on the hash; the sort keeps one workgroup per segment busy,
+// 2 B H of them, far fewer than the compute units).  Created once per device
+// at default priority; the fork and join events are reused, each call
+// recording and waiting on them under the device's mutex (a wait binds to the
+// event's latest record when it is enqueued).
+struct SideStream {
+  std::mutex mu;
+  bool ready = false;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+hipError_t side_stream(int device, SideStream **out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream &ss = g_side[device];
+  if (!ss.ready) {
+    hipError_t e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    ss.ready = true;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
 // The integer a C caller stored in an enum field.  A value outside the enum's
 // range is valid C but undefined to load as the C++ enum type, so the bits
 // are copied out instead.
@@ -317,7 +347,7 @@ bool misaligned(const void *ptr, uintptr_t a) { return (reinterpret_cast<uintptr
 int check_pointers(const elsaa::Geometry &g, const void *q, const void *k, const void *v, const void *x_gate,
                    const void *hyperplanes, const elsaa_params_t *params, const void *out);
 int enqueue_forward(elsaa::Geometry &g, const void *q, const void *k, const void *v, const void *x_gate,
-                    const void *hyperplanes, const elsaa_params_t *params, void *out, char *ws);
+                    const void *hyperplanes, const elsaa_params_t *params, void *out, char *ws, SideStream *side);
 
 constexpr size_t kNoAllocScratchBytes = ELSAA_NOALLOC_SCRATCH_BYTES;
 std::mutex g_scratch_mu;
@@ -395,7 +425,15 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
   hipError_t e = hipGetDevice(&device);
   if (e == hipSuccess) e = device_cus(device, &g.cus);
   if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
-  return enqueue_forward(g, q, k, v, x_gate, hyperplanes, params, out, static_cast<char *>(params->workspace));
+  // the sort overlaps the RACE build on the device's second stream when both
+  // run and the sort needs no scratch the RACE build also uses
+  SideStream *side = nullptr;
+  if (g.run_sparse && g.run_race && !g.identity && !g.fused && !elsaa::sort_is_tiled(g) && !debug_mode()) {
+    e = side_stream(device, &side);
+    if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
+  }
+  return enqueue_forward(g, q, k, v, x_gate, hyperplanes, params, out, static_cast<char *>(params->workspace),
+                         side);
 }
 
 size_t elsaa_backward_workspace_bytes(const elsaa_params_t *p) {
@@ -466,7 +504,7 @@ int elsaa_forward_noalloc(const void *q, const void *k, const void *v, const voi
   char *scratch_ptr = nullptr;
   if (e == hipSuccess) e = device_scratch(device, &scratch_ptr);
   if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
-  return enqueue_forward(g, q, k, v, x_gate, hyperplanes, params, out, scratch_ptr);
+  return enqueue_forward(g, q, k, v, x_gate, hyperplanes, params, out, scratch_ptr, nullptr);
 }
 
 }  // extern "C"
@@ -493,9 +531,11 @@ int check_pointers(const elsaa::Geometry &g, const void *q, const void *k, const
 }
 
 // Enqueues every stage on params->stream with the scratch buffers carved out
-// of `ws` (at least carve(g) bytes, 256-byte aligned).
+// of `ws` (at least carve(g) bytes, 256-byte aligned).  With `side`, the sort
+// runs on that stream between a fork after the hash and a join before the
+// chunk attention, overlapping the RACE build.
 int enqueue_forward(elsaa::Geometry &g, const void *q, const void *k, const void *v, const void *x_gate,
-                    const void *hyperplanes, const elsaa_params_t *params, void *out, char *ws) {
+                    const void *hyperplanes, const elsaa_params_t *params, void *out, char *ws, SideStream *side) {
   elsaa::Buffers buf;
   carve(g, ws, &buf);
   hipStream_t s = static_cast<hipStream_t>(params->stream);
@@ -504,9 +544,12 @@ int enqueue_forward(elsaa::Geometry &g, const void *q, const void *k, const void
   // stage_events[2i] / [2i+1] bracket stage i (hash, sort, RACE build, chunk
   // attention, fusion); a stage a variant skips is an empty interval
   void *const *ev = params->stage_events;
-  auto mark = [&](int i) -> hipError_t {
-    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+  auto mark_on = [&](int i, hipStream_t st) -> hipError_t {
+    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), st) : hipSuccess;
   };
+  auto mark = [&](int i) -> hipError_t { return mark_on(i, s); };
+  std::unique_lock<std::mutex> side_lock;
+  if (side) side_lock = std::unique_lock<std::mutex>(side->mu);
   const bool dbg = debug_mode();
   const char *stage = "";
   auto run = [&](const char *name, auto &&launch) {
@@ -534,12 +577,25 @@ int enqueue_forward(elsaa::Geometry &g, const void *q, const void *k, const void
   e = mark(0);
   if (need_hash) run("hash", [&] { return elsaa::launch_hash(gh, q, k, planes, buf, s); });
   if (e == hipSuccess) e = mark(1);
+  if (side) {  // fork: the sort on the side stream, after the hash
+    if (e == hipSuccess) e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+    if (e == hipSuccess) e = mark_on(2, side->stream);
+    run("sort", [&] { return elsaa::launch_sort(g, buf, side->stream); });
+    if (e == hipSuccess) e = mark_on(3, side->stream);
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
+  }
   if (e == hipSuccess) e = mark(4);
   if (g.run_race) run("RACE build", [&] { return elsaa::launch_race_build(g, v, buf, s); });
   if (e == hipSuccess) e = mark(5);
-  if (e == hipSuccess) e = mark(2);
-  if (g.run_sparse && !g.identity) run("sort", [&] { return elsaa::launch_sort(g, buf, s); });
-  if (e == hipSuccess) e = mark(3);
+  if (side) {  // join
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+  } else {
+    if (e == hipSuccess) e = mark(2);
+    if (g.run_sparse && !g.identity) run("sort", [&] { return elsaa::launch_sort(g, buf, s); });
+    if (e == hipSuccess) e = mark(3);
+  }
+  if (side_lock.owns_lock()) side_lock.unlock();
   if (e == hipSuccess) e = mark(6);
   if (g.fused)
     run("chunk attention + fusion", [&] {

@@ -88,6 +88,9 @@ hipError_t launch_fill_zero(void *p, size_t n, hipStream_t stream);
 hipError_t launch_hash(const Geometry &g, const void *q, const void *k, const void *planes,
                        const Buffers &buf, hipStream_t stream);
 hipError_t launch_sort(const Geometry &g, const Buffers &buf, hipStream_t stream);
+// The sort takes the tiled path, which uses Buffers::hist (shared with the
+// RACE build's tiled rank); otherwise one workgroup per segment, no scratch.
+bool sort_is_tiled(const Geometry &g);
 // o_s goes to `o_s` (buf.o_s, or the output itself for SPARSE_ONLY).
 hipError_t launch_chunk_attention(const Geometry &g, const void *q, const void *k,
                                   const void *v, const Buffers &buf, void *o_s, hipStream_t stream);

@@ -316,6 +316,11 @@ int segment_sort_waves(const Geometry &g, size_t *lds) {
 
 }  // namespace
 
+bool sort_is_tiled(const Geometry &g) {
+  size_t lds = 0;
+  return segment_sort_waves(g, &lds) == 0;
+}
+
 hipError_t launch_sort(const Geometry &g, const Buffers &buf, hipStream_t stream) {
   const int S = 2 * g.BH;
   size_t seg_lds = 0;
