@@ -25,9 +25,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-# Per-source extra flags.  The hash kernel reads every MFMA result with plain
-# VALU instructions; its accumulators are kept in VGPRs (no AGPR copies).
-EXTRA: dict = {"k1_hash.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The hash and the backward kernels read every MFMA
+# result with plain VALU instructions; their accumulators are kept in VGPRs
+# (no AGPR copies; the backward's dq kernel then fits four waves per SIMD).
+EXTRA: dict = {"k1_hash.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "k6_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
