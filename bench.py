@@ -149,15 +149,22 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
 
     def per_kernel(path, counter):
         sums, counts, calib = {}, {}, 0.0
-        for row in csv.DictReader(open(path)):
-            if row["Counter_Name"] != counter:
-                continue
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        race_rank = False  # inside a RACE build's tiled rank (the sort's kernels, before its run table)
+        for row in rows:
             name = row["Kernel_Name"]
             val = float(row["Counter_Value"]) * 1024.0
             if name.startswith("__amd_rocclr_copyBuffer"):
                 calib = max(calib, val)
                 continue
             short = name.replace("void ", "").replace("elsaa::(anonymous namespace)::", "").split("(")[0]
+            if short.startswith("elsaa_k1_hash_"):
+                race_rank = True  # a forward call: the RACE build follows the hash
+            elif short.startswith("elsaa_k4_race_"):
+                race_rank = False
+            elif short.startswith(("elsaa_k2_sort_hist", "elsaa_k2_sort_scan", "elsaa_k2_sort_scatter")) and race_rank:
+                short = "elsaa_k4_race_rank_tiles:" + short  # the RACE build's tiled rank
             sums[short] = sums.get(short, 0.0) + val
             counts[short] = counts.get(short, 0) + 1
         if calib <= 0.0:
