@@ -150,7 +150,7 @@ struct BackwardBuffers {
   uint32_t *flag;
 };
 // Token blocks of the backward's gate-gradient partial sums (reduced in order).
-constexpr int kGateBlocks = 128;
+constexpr int kGateBlocks = 256;
 struct BackwardOutputs {
   void *dq, *dk, *dv, *dx_gate;
   float *dgate_w, *dgate_b, *dlambda;

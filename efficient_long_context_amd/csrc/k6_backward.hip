@@ -800,6 +800,114 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_part(const float *__res
   for (int e = threadIdx.x; e < 2 * DG + 3; e += 256) out[e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
 }
 
+// The same partial sums with every head in one workgroup (d_gate <= 64,
+// H <= kMaxH): a token's gate-input row is read by four waves instead of once
+// per head.  Block blk stages the da_s, da_lr and dL/dlambda shares of its
+// tokens for every head in LDS (coalesced rows of each head); then its 16
+// waves split into four head groups of four: wave (group, quarter) takes the
+// group's heads and tokens t_lo + quarter, + 4, ... in order, lanes the gate
+// columns.  The quarters' sums of each head are added in LDS in quarter
+// order into part[h][blk][2 DG + 3], the layout gate_reduce reads.
+constexpr int kMaxH = 16;
+constexpr int kHeadGroups = 4;
+template <typename VT>
+__global__ __launch_bounds__(1024) void elsaa_k6_bwd_gate_part_heads(const float *__restrict__ da_s,
+                                                                     const float *__restrict__ da_lr,
+                                                                     const float *__restrict__ dlam,
+                                                                     const VT *__restrict__ x, int B, int H, int N,
+                                                                     int DG, float *__restrict__ part) {
+  constexpr int kHpg = kMaxH / kHeadGroups;  // heads a group holds at most
+  extern __shared__ float st[];  // [3][H][per] staged shares, then [4][H][2 DG + 3] quarter sums
+  const int blk = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave / 4, tq = wave % 4;
+  const int hpg = (H + kHeadGroups - 1) / kHeadGroups;
+  const long long tokens = static_cast<long long>(B) * N;
+  const int per = static_cast<int>((tokens + kGateBlocks - 1) / kGateBlocks);
+  const long long t_lo = static_cast<long long>(blk) * per;
+  const int n = static_cast<int>(t_lo + per < tokens ? per : (tokens > t_lo ? tokens - t_lo : 0));
+  // staging: row (a, h) holds array a's shares of head h for tokens t_lo ..
+  // t_lo + n - 1; kR rows a round, every load of the round issued before its
+  // stores (one row at a time left each thread a chain of dependent loads)
+  constexpr int kR = 12;
+  for (int r0 = 0; r0 < 3 * H; r0 += kR) {
+    for (int j = tid; j < n; j += 1024) {
+      const long long t = t_lo + j;
+      const long long b = t / N;
+      const long long i = t - b * N;
+      float v[kR];
+#pragma unroll
+      for (int u = 0; u < kR; ++u) {
+        const int row = r0 + u < 3 * H ? r0 + u : 3 * H - 1;
+        const int a = row / H, h = row - a * H;
+        const float *src = a == 0 ? da_s : (a == 1 ? da_lr : dlam);
+        v[u] = src[(b * H + h) * N + i];
+      }
+#pragma unroll
+      for (int u = 0; u < kR; ++u)
+        if (r0 + u < 3 * H) st[(r0 + u) * per + j] = v[u];
+    }
+  }
+  __syncthreads();
+  float w0[kHpg], w1[kHpg], b0[kHpg], b1[kHpg], lm[kHpg];
+#pragma unroll
+  for (int k = 0; k < kHpg; ++k) w0[k] = w1[k] = b0[k] = b1[k] = lm[k] = 0.0f;
+  const int e = lane < DG ? lane : DG - 1;  // clamped column (lanes past d_gate add zeros)
+  constexpr int kU = 8;                     // tokens a round, their rows requested together
+  for (int j0 = tq; j0 < n; j0 += 4 * kU) {
+    float xe[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + 4 * u < n ? j0 + 4 * u : n - 1;
+      const float xv = Elem<VT>::load(x + (t_lo + j) * DG + e);
+      xe[u] = lane < DG ? xv : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + 4 * u;
+      if (j < n) {
+#pragma unroll
+        for (int k = 0; k < kHpg; ++k) {
+          const int h = hg * hpg + k;
+          if (k < hpg && h < H) {
+            const float s0 = st[h * per + j], s1 = st[(H + h) * per + j];
+            w0[k] = __builtin_fmaf(s0, xe[u], w0[k]);
+            w1[k] = __builtin_fmaf(s1, xe[u], w1[k]);
+            b0[k] += s0;
+            b1[k] += s1;
+            lm[k] += st[(2 * H + h) * per + j];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();  // the staged shares are consumed: the LDS holds the quarter sums next
+  const int stride = 2 * DG + 3;
+  float *red = st + static_cast<long long>(tq) * H * stride;
+#pragma unroll
+  for (int k = 0; k < kHpg; ++k) {
+    const int h = hg * hpg + k;
+    if (k < hpg && h < H) {
+      if (lane < DG) {
+        red[h * stride + lane] = w0[k];
+        red[h * stride + DG + lane] = w1[k];
+      }
+      if (lane == 0) {
+        red[h * stride + 2 * DG] = b0[k];
+        red[h * stride + 2 * DG + 1] = b1[k];
+        red[h * stride + 2 * DG + 2] = lm[k];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < H * stride; i += 1024) {
+    const int h = i / stride, c = i - h * stride;
+    const long long hs = static_cast<long long>(H) * stride;
+    part[(static_cast<long long>(h) * kGateBlocks + blk) * stride + c] =
+        ((st[i] + st[hs + i]) + st[2 * hs + i]) + st[3 * hs + i];
+  }
+}
+
 // Block h < H: dW_g and db_g of head h; block H: dL/dlambda.  Partials are
 // added in block order (eight independent running sums, then combined).
 __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_reduce(const float *__restrict__ part, int H, int DG,
@@ -1006,7 +1114,13 @@ hipError_t launch_backward_t(const Geometry &g, const BackwardInputs &in, const 
       hipLaunchKernelGGL((elsaa_k6_bwd_gate_part<VT, kPer>), dim3(g.H, kGateBlocks), dim3(256), 0, stream, bb.da_s,
                          bb.da_lr, bb.dlam, static_cast<const VT *>(in.x_gate), g.B, g.H, g.N, g.DG, bb.gate_part);
     };
-    if (g.DG <= 64) gate_part(std::integral_constant<int, 1>{});
+    const long long per = (static_cast<long long>(g.B) * g.N + kGateBlocks - 1) / kGateBlocks;
+    const size_t heads_lds = static_cast<size_t>(
+        4 * (3 * g.H * per > 4ll * g.H * (2 * g.DG + 3) ? 3 * g.H * per : 4ll * g.H * (2 * g.DG + 3)));
+    if (g.DG <= 64 && g.H <= kMaxH && heads_lds <= 64 * 1024)
+      hipLaunchKernelGGL(elsaa_k6_bwd_gate_part_heads<VT>, dim3(kGateBlocks), dim3(1024), heads_lds, stream, bb.da_s,
+                         bb.da_lr, bb.dlam, static_cast<const VT *>(in.x_gate), g.B, g.H, g.N, g.DG, bb.gate_part);
+    else if (g.DG <= 64) gate_part(std::integral_constant<int, 1>{});
     else if (g.DG <= 128) gate_part(std::integral_constant<int, 2>{});
     else if (g.DG <= 256) gate_part(std::integral_constant<int, 4>{});
     else gate_part(std::integral_constant<int, 8>{});
