@@ -807,15 +807,17 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_gate_part(const float *__res
 // waves split into four head groups of four: wave (group, quarter) takes the
 // group's heads and tokens t_lo + quarter, + 4, ... in order, lanes the gate
 // columns.  The quarters' sums of each head are added in LDS in quarter
-// order into part[h][blk][2 DG + 3], the layout gate_reduce reads.
+// order into part[h][blk][2 DG + 3], the layout gate_reduce reads.  The
+// same kernel writes dx_gate from the staged shares.
 constexpr int kMaxH = 16;
 constexpr int kHeadGroups = 4;
 template <typename VT>
 __global__ __launch_bounds__(1024) void elsaa_k6_bwd_gate_part_heads(const float *__restrict__ da_s,
                                                                      const float *__restrict__ da_lr,
                                                                      const float *__restrict__ dlam,
-                                                                     const VT *__restrict__ x, int B, int H, int N,
-                                                                     int DG, float *__restrict__ part) {
+                                                                     const VT *__restrict__ x, const float *__restrict__ gate_w,
+                                                                     int B, int H, int N, int DG,
+                                                                     float *__restrict__ part, VT *__restrict__ dx) {
   constexpr int kHpg = kMaxH / kHeadGroups;  // heads a group holds at most
   extern __shared__ float st[];  // [3][H][per] staged shares, then [4][H][2 DG + 3] quarter sums
   const int blk = blockIdx.x;
@@ -849,10 +851,30 @@ __global__ __launch_bounds__(1024) void elsaa_k6_bwd_gate_part_heads(const float
     }
   }
   __syncthreads();
+  const int e = lane < DG ? lane : DG - 1;  // clamped column (lanes past d_gate add zeros)
+  {  // dx_gate of the block's tokens: wave w takes tokens w, w + 16, ...; the
+     // heads in order, as the per-token kernel adds them
+    float g0[kMaxH], g1[kMaxH];
+#pragma unroll
+    for (int h = 0; h < kMaxH; ++h) {
+      g0[h] = h < H ? gate_w[static_cast<long long>(h) * DG + e] : 0.0f;
+      g1[h] = h < H ? gate_w[static_cast<long long>(H + h) * DG + e] : 0.0f;
+    }
+    for (int j = wave; j < n; j += 16) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int h = 0; h < kMaxH; ++h) {
+        if (h < H) {
+          acc = __builtin_fmaf(st[h * per + j], g0[h], acc);
+          acc = __builtin_fmaf(st[(H + h) * per + j], g1[h], acc);
+        }
+      }
+      if (lane < DG) dx[(t_lo + j) * DG + lane] = Elem<VT>::store_val(acc);
+    }
+  }
   float w0[kHpg], w1[kHpg], b0[kHpg], b1[kHpg], lm[kHpg];
 #pragma unroll
   for (int k = 0; k < kHpg; ++k) w0[k] = w1[k] = b0[k] = b1[k] = lm[k] = 0.0f;
-  const int e = lane < DG ? lane : DG - 1;  // clamped column (lanes past d_gate add zeros)
   constexpr int kU = 8;                     // tokens a round, their rows requested together
   for (int j0 = tq; j0 < n; j0 += 4 * kU) {
     float xe[kU];
@@ -1106,24 +1128,28 @@ hipError_t launch_backward_t(const Geometry &g, const BackwardInputs &in, const 
   // 4. gates and lambda
   const long long nx = static_cast<long long>(g.B) * g.N * g.DG;
   if (gated) {
-    hipLaunchKernelGGL(elsaa_k6_bwd_dxgate<VT>, dim3(blocks_for(nx)), dim3(256), 0, stream, bb.da_s, bb.da_lr,
-                       in.gate_w, g.B, g.H, g.N, g.DG, static_cast<VT *>(out.dx_gate));
-    if (!check()) return e;
-    auto gate_part = [&](auto kp) {
-      constexpr int kPer = decltype(kp)::value;
-      hipLaunchKernelGGL((elsaa_k6_bwd_gate_part<VT, kPer>), dim3(g.H, kGateBlocks), dim3(256), 0, stream, bb.da_s,
-                         bb.da_lr, bb.dlam, static_cast<const VT *>(in.x_gate), g.B, g.H, g.N, g.DG, bb.gate_part);
-    };
     const long long per = (static_cast<long long>(g.B) * g.N + kGateBlocks - 1) / kGateBlocks;
     const size_t heads_lds = static_cast<size_t>(
         4 * (3 * g.H * per > 4ll * g.H * (2 * g.DG + 3) ? 3 * g.H * per : 4ll * g.H * (2 * g.DG + 3)));
-    if (g.DG <= 64 && g.H <= kMaxH && heads_lds <= 64 * 1024)
+    if (g.DG <= 64 && g.H <= kMaxH && heads_lds <= 64 * 1024) {
       hipLaunchKernelGGL(elsaa_k6_bwd_gate_part_heads<VT>, dim3(kGateBlocks), dim3(1024), heads_lds, stream, bb.da_s,
-                         bb.da_lr, bb.dlam, static_cast<const VT *>(in.x_gate), g.B, g.H, g.N, g.DG, bb.gate_part);
-    else if (g.DG <= 64) gate_part(std::integral_constant<int, 1>{});
-    else if (g.DG <= 128) gate_part(std::integral_constant<int, 2>{});
-    else if (g.DG <= 256) gate_part(std::integral_constant<int, 4>{});
-    else gate_part(std::integral_constant<int, 8>{});
+                         bb.da_lr, bb.dlam, static_cast<const VT *>(in.x_gate), in.gate_w, g.B, g.H, g.N, g.DG,
+                         bb.gate_part, static_cast<VT *>(out.dx_gate));
+    } else {
+      hipLaunchKernelGGL(elsaa_k6_bwd_dxgate<VT>, dim3(blocks_for(nx)), dim3(256), 0, stream, bb.da_s, bb.da_lr,
+                         in.gate_w, g.B, g.H, g.N, g.DG, static_cast<VT *>(out.dx_gate));
+      if (!check()) return e;
+      auto gate_part = [&](auto kp) {
+        constexpr int kPer = decltype(kp)::value;
+        hipLaunchKernelGGL((elsaa_k6_bwd_gate_part<VT, kPer>), dim3(g.H, kGateBlocks), dim3(256), 0, stream,
+                           bb.da_s, bb.da_lr, bb.dlam, static_cast<const VT *>(in.x_gate), g.B, g.H, g.N, g.DG,
+                           bb.gate_part);
+      };
+      if (g.DG <= 64) gate_part(std::integral_constant<int, 1>{});
+      else if (g.DG <= 128) gate_part(std::integral_constant<int, 2>{});
+      else if (g.DG <= 256) gate_part(std::integral_constant<int, 4>{});
+      else gate_part(std::integral_constant<int, 8>{});
+    }
     if (!check()) return e;
     hipLaunchKernelGGL(elsaa_k6_bwd_gate_reduce, dim3(g.H + 1), dim3(256), 0, stream, bb.gate_part, g.H, g.DG,
                        g.variant == ELSAA_VARIANT_FULL ? 1 : 0, out.dgate_w, out.dgate_b, out.dlambda);
