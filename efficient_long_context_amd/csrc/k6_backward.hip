@@ -220,16 +220,19 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_prep(PrepArgs a, long long r
 // threads owns kPer (row pair, 8-column chunk) items.  The indices of a block
 // are requested two blocks ahead and its rows one block ahead (into
 // registers), so the loads overlap the previous block's products.
-template <int D, bool kIdent, bool kXT, bool kYT>
+template <int D, bool kIdent, bool kXT, bool kYT, int kT = 256>
 struct Stager {
   static constexpr int kRow = D + 8, kTRow = 64 + 4;
-  static constexpr int kPer = 32 * (D / 8) / 256;  // 1 (d = 64) or 2 (d = 128)
+  static constexpr int kItems = 32 * (D / 8);              // (row pair, 8-column chunk) items
+  static constexpr int kPer = (kItems + kT - 1) / kT;      // items a thread stages
+  static constexpr bool kAll = kItems % kT == 0;           // every thread has kPer items
   int j0[kPer], j1[kPer];
   u16x8 x0[kPer], x1[kPer], y0[kPer], y1[kPer];
   __device__ __forceinline__ void load_idx(const int32_t *__restrict__ perm, long long seg, int s0, int tid) {
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
-      const int jp = (tid + 256 * p) % 32;
+      const int it = (tid + kT * p) % kItems;  // threads past the items repeat one (never stored)
+      const int jp = it % 32;
       j0[p] = sorted_at<kIdent>(perm, seg, s0 + 2 * jp);
       j1[p] = sorted_at<kIdent>(perm, seg, s0 + 2 * jp + 1);
     }
@@ -238,7 +241,7 @@ struct Stager {
                                             long long seg, int tid) {
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
-      const int ch = (tid + 256 * p) / 32;
+      const int ch = ((tid + kT * p) % kItems) / 32;
       x0[p] = *reinterpret_cast<const u16x8 *>(x + (seg + j0[p]) * D + ch * 8);
       x1[p] = *reinterpret_cast<const u16x8 *>(x + (seg + j1[p]) * D + ch * 8);
       y0[p] = *reinterpret_cast<const u16x8 *>(y + (seg + j0[p]) * D + ch * 8);
@@ -248,7 +251,8 @@ struct Stager {
   __device__ __forceinline__ void store(uint16_t *xs, uint16_t *ys, uint16_t *xt, uint16_t *yt, int tid) const {
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
-      const int jp = (tid + 256 * p) % 32, ch = (tid + 256 * p) / 32;
+      if (!kAll && tid + kT * p >= kItems) continue;
+      const int jp = (tid + kT * p) % 32, ch = (tid + kT * p) / 32;
       *reinterpret_cast<u16x8 *>(xs + (2 * jp) * kRow + ch * 8) = x0[p];
       *reinterpret_cast<u16x8 *>(xs + (2 * jp + 1) * kRow + ch * 8) = x1[p];
       *reinterpret_cast<u16x8 *>(ys + (2 * jp) * kRow + ch * 8) = y0[p];
@@ -310,10 +314,10 @@ __device__ __forceinline__ void transposed_times_weights(const uint16_t *xt, con
   }
 }
 
-// dq: one workgroup per 64 sorted queries (4 waves x 16), over the keys of
-// their window in blocks of 64.
-template <int D, bool kIdent>
-__global__ __launch_bounds__(256) void elsaa_k6_bwd_dq_bf16(
+// dq: one workgroup per QT sorted queries (QT / 16 waves of 16; QT divides
+// w), over the keys of their window in blocks of 64.
+template <int D, bool kIdent, int QT>
+__global__ __launch_bounds__(QT * 4) void elsaa_k6_bwd_dq_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, const uint16_t *__restrict__ do_s,
     const float *__restrict__ lse, const float *__restrict__ delta, int N, int w, int tiles_per_seg,
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dq_bf16(
   const int g = lane >> 4, r16 = lane & 15;
   const long long tile = blockIdx.x;
   const long long seg = (tile / tiles_per_seg) * N;
-  const int r0 = static_cast<int>(tile % tiles_per_seg) * 64;
+  const int r0 = static_cast<int>(tile % tiles_per_seg) * QT;
   const int c = r0 / w;
   const int lo = c > 0 ? (c - 1) * w : 0, hi = (c + 1) * w;
   const int qidx = sorted_at<kIdent>(perm_q, seg, r0 + wave * 16 + r16);
@@ -340,10 +344,11 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dq_bf16(
   f32x4 acc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  Stager<D, kIdent, true, false> st;
+  using St = Stager<D, kIdent, true, false, QT * 4>;
+  St st;
   st.load_idx(perm_k, seg, lo, tid);
   st.load_rows(k, v, seg, tid);
-  int nxt[Stager<D, kIdent, true, false>::kPer][2];  // indices of the block after next
+  int nxt[St::kPer][2];  // indices of the block after next
   for (int s0 = lo; s0 < hi; s0 += 64) {
     if (s0 != lo) __syncthreads();  // the previous block is consumed
     st.store(Ks, Vs, Kt, nullptr, tid);
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dq_bf16(
       }
       st.load_rows(k, v, seg, tid);
       if (s0 + 128 < hi) {
-        Stager<D, kIdent, true, false> ix;
+        St ix;
         ix.load_idx(perm_k, seg, s0 + 128, tid);
 #pragma unroll
         for (int p = 0; p < st.kPer; ++p) {
@@ -390,10 +395,11 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dq_bf16(
                    pack_bf16x2(acc[dt][2] * scale, acc[dt][3] * scale));
 }
 
-// dk, dv: one workgroup per 64 sorted keys (4 waves x 16) of chunk c, over the
-// sorted queries that attend them, [c w, min((c + 2) w, N)), in blocks of 64.
-template <int D, bool kIdent>
-__global__ __launch_bounds__(256) void elsaa_k6_bwd_dkv_bf16(
+// dk, dv: one workgroup per QT sorted keys (QT / 16 waves of 16; QT divides w)
+// of chunk c, over the sorted queries that attend them, [c w, min((c + 2) w,
+// N)), in blocks of 64.
+template <int D, bool kIdent, int QT>
+__global__ __launch_bounds__(QT * 4) void elsaa_k6_bwd_dkv_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ perm_q, const int32_t *__restrict__ perm_k, const uint16_t *__restrict__ do_s,
     const float *__restrict__ lse, const float *__restrict__ delta, int N, int w, int tiles_per_seg,
@@ -407,7 +413,7 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dkv_bf16(
   const int g = lane >> 4, r16 = lane & 15;
   const long long tile = blockIdx.x;
   const long long seg = (tile / tiles_per_seg) * N;
-  const int t0 = static_cast<int>(tile % tiles_per_seg) * 64;
+  const int t0 = static_cast<int>(tile % tiles_per_seg) * QT;
   const int c = t0 / w;
   const int lo = c * w, hi = (c + 2) * w < N ? (c + 2) * w : N;
   const int kidx = sorted_at<kIdent>(perm_k, seg, t0 + wave * 16 + r16);
@@ -423,7 +429,7 @@ __global__ __launch_bounds__(256) void elsaa_k6_bwd_dkv_bf16(
     dkt[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     dvt[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   }
-  using St = Stager<D, kIdent, true, true>;
+  using St = Stager<D, kIdent, true, true, QT * 4>;
   St st;
   st.load_idx(perm_q, seg, lo, tid);
   st.load_rows(q, do_s, seg, tid);
@@ -991,19 +997,26 @@ template <int D, bool kIdent>
 void launch_sparse_bf16(const Geometry &g, const void *q, const void *k, const void *v, const int32_t *pq,
                         const int32_t *pk, const BackwardBuffers &bb, const float *lse, void *dq, void *dk,
                         hipStream_t stream) {
-  const int tiles_per_seg = g.N / 64;
-  const unsigned tiles = static_cast<unsigned>(static_cast<long long>(tiles_per_seg) * g.BH);
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float scale_log2 = scale * kLog2e;
-  hipLaunchKernelGGL((elsaa_k6_bwd_dq_bf16<D, kIdent>), dim3(tiles), dim3(256), 0, stream,
-                     static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                     static_cast<const uint16_t *>(v), pq, pk, static_cast<const uint16_t *>(bb.do_s), lse, bb.delta,
-                     g.N, g.w, tiles_per_seg, scale_log2, scale, static_cast<uint16_t *>(dq));
   constexpr size_t kLds = (2 * 64 * (D + 8) + 2 * D * (64 + 4)) * 2 + 2 * 64 * 4;
-  hipLaunchKernelGGL((elsaa_k6_bwd_dkv_bf16<D, kIdent>), dim3(tiles), dim3(256), kLds, stream,
+  auto tiles = [&](int qt) { return static_cast<unsigned>(static_cast<long long>(g.N / qt) * g.BH); };
+  auto dq_launch = [&](auto qt) {
+    constexpr int QT = decltype(qt)::value;
+    hipLaunchKernelGGL((elsaa_k6_bwd_dq_bf16<D, kIdent, QT>), dim3(tiles(QT)), dim3(QT * 4), 0, stream,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                       static_cast<const uint16_t *>(v), pq, pk, static_cast<const uint16_t *>(bb.do_s), lse,
+                       bb.delta, g.N, g.w, g.N / QT, scale_log2, scale, static_cast<uint16_t *>(dq));
+  };
+  // dq: 128-query tiles when w allows at d = 64 (each staged key block serves
+  // twice the queries: 232 -> 210 us at text32k); dk, dv: 64-key tiles (128
+  // took 398 against 340 us: 157 VGPRs leave one 8-wave workgroup per CU)
+  if (D == 64 && g.w % 128 == 0) dq_launch(std::integral_constant<int, 128>{});
+  else dq_launch(std::integral_constant<int, 64>{});
+  hipLaunchKernelGGL((elsaa_k6_bwd_dkv_bf16<D, kIdent, 64>), dim3(tiles(64)), dim3(256), kLds, stream,
                      static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                     static_cast<const uint16_t *>(v), pq, pk, static_cast<const uint16_t *>(bb.do_s), lse, bb.delta,
-                     g.N, g.w, tiles_per_seg, scale_log2, scale, static_cast<uint16_t *>(dk), bb.dv_acc);
+                     static_cast<const uint16_t *>(v), pq, pk, static_cast<const uint16_t *>(bb.do_s), lse,
+                     bb.delta, g.N, g.w, g.N / 64, scale_log2, scale, static_cast<uint16_t *>(dk), bb.dv_acc);
 }
 
 template <int D>
