@@ -18,7 +18,7 @@
 // The RACE-only variant (race_only != 0) outputs y = o_lr: the sparse output,
 // its LSE and the gates are neither read nor computed.
 //
-// Two layouts.  L in {8, 16} (the wide path): 16-byte lane pieces, so a load
+// Three layouts.  L in {8, 16} (the wide path): 16-byte lane pieces, so a load
 // instruction gathers 8 table rows of bfloat16 d = 64; a workgroup serves a
 // run of queries of one (b, h) with that (b, h)'s bucket counts staged in LDS
 // and the gate weight rows in registers; a query's L codes arrive in one
@@ -26,7 +26,11 @@
 // other L: d/4 lanes per query, one code and one row load per table.  In both
 // the gate dot products are split over the query's lanes and reduced with xor
 // shuffles, and consecutive workgroups run on one XCD, so its L2 holds the
-// tables of the few (b, h) it serves.
+// tables of the few (b, h) it serves.  For bfloat16 d = 64 with 16 tables of
+// at most 256 buckets (the LDS path) a workgroup copies its (b, h)'s tables
+// into LDS one at a time and reads the query rows there.
+#include <type_traits>
+
 #include "elsaa_internal.hpp"
 
 namespace elsaa {
@@ -526,9 +530,264 @@ void launch_any(const Geometry &g, const void *x_gate, const float *gate_w, cons
                      g.lambda, g.run_sparse ? 0 : 1, total, qpw, static_cast<VT *>(out), aux);
 }
 
+// ----------------------------------------------------------------- LDS path --
+// bfloat16, d = 64, d_gate = 64, 2^P <= 256 and an even L: a workgroup of
+// eight waves serves a tile of 512 queries of one (b, h), and that (b, h)'s
+// tables pass through LDS one at a time (2^P rows of 128 B: 32 KB at P = 8)
+// with their counts, so a query's L table rows are LDS reads instead of
+// texture gathers from L2 (in the wide path those are 16 of the 21 vector
+// memory instructions of a step at L = 16, and the texture path bounds it).
+// Two LDS buffers: table l + 1 is copied from L2 straight into LDS (no
+// registers) while table l is read.  The tile's codes are staged once; each
+// wave keeps the sums of its 64 queries in registers over the passes, adding
+// the tables in order 0, 1, ..., L - 1 as the wide path does (the same fp32
+// sums); the sparse output, LSE and gate inputs are then streamed
+// kLdsFuseAhead steps ahead of the epilogue.  About 75 KB of LDS: two
+// workgroups share a CU.
+constexpr int kLdsFuseWaves = 8;
+constexpr int kLdsFuseSteps = 8;                                 // 8-query steps per wave
+constexpr int kLdsFuseTile = kLdsFuseWaves * kLdsFuseSteps * 8;  // queries per workgroup
+constexpr int kLdsFuseAhead = 2;                                 // steps of streamed inputs in flight
+
+// s_waitcnt vmcnt(0) with the other counters left free (gfx9 encoding)
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int LC>
+__global__ __launch_bounds__(kLdsFuseWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void elsaa_k5_fuse_lds(
+    const uint16_t *__restrict__ o_s, const float *__restrict__ lse, const uint8_t *__restrict__ qcodes,
+    const uint16_t *__restrict__ tsum, const float *__restrict__ tcnt, const uint16_t *__restrict__ x_gate,
+    const float *__restrict__ gate_w, const float *__restrict__ gate_b, int H, int N, int P, float lambda,
+    int race_only, int tiles, long long units, uint16_t *__restrict__ out, AuxOut aux) {
+  constexpr int D = 64, kRowBytes = 128, kCols = 8;
+  constexpr int kS = kLdsFuseSteps, kT = kLdsFuseWaves * 64, kA = kLdsFuseAhead;
+  static_assert(LC % 2 == 0 && kS % kA == 0, "whole buffer pairs and prefetch slots");
+  // two buffers of 2^P rows x 8 pieces and their counts, as separate arrays:
+  // a copy in flight into one then provably does not alias reads of the
+  // other, and the compiler's wait before those reads is not needed
+  __shared__ __align__(16) u32x4 tab0[256 * 8], tab1[256 * 8];
+  __shared__ __align__(16) float cnt0[256], cnt1[256];
+  __shared__ __align__(16) u32x4 code_lds[kLdsFuseTile * LC / 16];
+  __shared__ float gw_lds[2][64];
+
+  const long long unit = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (unit >= units) return;  // whole workgroup
+  const long long bh = unit / tiles;
+  const int i_tile = static_cast<int>(unit % tiles) * kLdsFuseTile;
+  const int run_len = N - i_tile < kLdsFuseTile ? N - i_tile : kLdsFuseTile;  // a multiple of 64
+  const int h = static_cast<int>(bh % H);
+  const long long b = bh / H;
+  const int nb = 1 << P;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = lane & 7, qs = lane >> 3;
+  const bool active = wave * 64 < run_len;  // wave-uniform
+
+  const u32x4 *tsrc = reinterpret_cast<const u32x4 *>(tsum + bh * LC * nb * static_cast<long long>(D));
+  const float *csrc = tcnt + bh * LC * nb;
+  // table l and its counts into LDS buffer `buf`: wave-instructions of 64
+  // lanes x 16 bytes (1 KB of consecutive rows; lane j's piece lands j * 16
+  // bytes past the instruction's LDS base), counts 64 lanes x 4 bytes
+  auto stage = [&](int l, u32x4 *tab, float *cnt) {
+    const u32x4 *src = tsrc + static_cast<long long>(l) * nb * 8;
+    const int np = nb * 8;
+    for (int c = wave; c * 64 < np; c += kLdsFuseWaves) {
+      const int piece = c * 64 + lane;
+      if (piece < np) __builtin_amdgcn_global_load_lds(src + piece, tab + c * 64, 16, 0, 0);
+    }
+    const float *cs = csrc + static_cast<long long>(l) * nb;
+    for (int c = wave; c * 64 < nb; c += kLdsFuseWaves) {
+      const int k = c * 64 + lane;
+      if (k < nb) __builtin_amdgcn_global_load_lds(cs + k, cnt + c * 64, 4, 0, 0);
+    }
+  };
+
+  // the tile's codes (L bytes a query; the tile starts on a 16-byte
+  // boundary since N and the tile are multiples of 64 queries)
+  {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(qcodes + (bh * N + i_tile) * LC);
+    const int n = run_len * LC / 16;
+    for (int k = tid; k < n; k += kT) code_lds[k] = src[k];
+  }
+  if (tid < 128) gw_lds[tid >> 6][tid & 63] = gate_w[static_cast<long long>((tid >> 6) * H + h) * 64 + (tid & 63)];
+  const float gb0 = gate_b[h], gb1 = gate_b[H + h];
+  stage(0, tab0, cnt0);
+
+  wait_vm_all();
+  __syncthreads();  // codes, gate weights, table 0
+
+  stage(1, tab1, cnt1);
+
+  float num[kS][kCols], z[kS];
+#pragma unroll
+  for (int s = 0; s < kS; ++s) {
+    z[s] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kCols; ++k) num[s][k] = 0.0f;
+  }
+  const Bf16Adder adder;
+
+  // table l from (tab, cnt); then, once every wave is past it, table l + 2
+  // into the same buffer
+  auto pass = [&](int l, const u32x4 *tab, const float *cnt, u32x4 *tab_w, float *cnt_w) {
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        const uint32_t c = reinterpret_cast<const uint8_t *>(code_lds)[(wave * 64 + s * 8 + qs) * LC + l];
+        const u32x4 r = tab[c * 8 + sub];
+        const float cn = cnt[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          num[s][2 * e] = adder.lo(num[s][2 * e], r[e]);
+          num[s][2 * e + 1] = adder.hi(num[s][2 * e + 1], r[e]);
+        }
+        z[s] += sub == 0 ? cn : 0.0f;  // one lane of the query counts
+        if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_vm_all();    // this thread's copies of table l + 1 have landed
+    __syncthreads();  // every wave has read this buffer and copied table l + 1
+    if (l + 2 < LC) stage(l + 2, tab_w, cnt_w);
+  };
+#pragma unroll 1
+  for (int l = 0; l < LC; l += 2) {
+    pass(l, tab0, cnt0, tab0, cnt0);
+    pass(l + 1, tab1, cnt1, tab1, cnt1);
+  }
+  if (!active) return;  // no barrier follows
+
+  const __amdgpu_buffer_rsrc_t os_rs =
+      make_rsrc(o_s + bh * N * static_cast<long long>(D), static_cast<uint32_t>(N) * kRowBytes);
+  const __amdgpu_buffer_rsrc_t lse_rs = make_rsrc(lse + bh * N, static_cast<uint32_t>(N) * 4u);
+  const __amdgpu_buffer_rsrc_t xg_rs = make_rsrc(x_gate + b * N * 64, static_cast<uint32_t>(N) * kRowBytes);
+  const __amdgpu_buffer_rsrc_t out_rs =
+      make_rsrc(out + bh * N * static_cast<long long>(D), static_cast<uint32_t>(N) * kRowBytes);
+  const uint32_t vbase = static_cast<uint32_t>(sub) * 16u;
+  auto q_of = [&](int s) { return i_tile + wave * 64 + s * 8 + qs; };
+  u32x4 os_in[kA], xg_in[kA];
+  float lse_in[kA];
+  auto load_stream = [&](int s, int slot) {
+    const uint32_t ii = static_cast<uint32_t>(q_of(s));
+    os_in[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(os_rs, ii * kRowBytes + vbase, 0, 0));
+    lse_in[slot] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lse_rs, ii * 4u, 0, 0));
+    xg_in[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xg_rs, ii * kRowBytes + vbase, 0, 0));
+  };
+#pragma unroll
+  for (int a = 0; a < kA; ++a) {
+    if (race_only) {  // y = o_lr: no sparse output, LSE or gate inputs
+      os_in[a] = xg_in[a] = u32x4{0u, 0u, 0u, 0u};
+      lse_in[a] = 0.0f;
+    } else {
+      load_stream(a, a);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kS; ++s) {
+    const int slot = s % kA;
+    const u32x4 os_raw = os_in[slot], xg_raw = xg_in[slot];
+    const float lse_i = lse_in[slot];
+    // the inputs kA steps ahead go out before this step's store, so waiting
+    // for them never waits for a store
+    if (s + kA < kS && !race_only) load_stream(s + kA, slot);
+    const int i = q_of(s);
+    const long long qi = bh * N + i;
+    float osv[kCols], xv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      osv[2 * e] = __uint_as_float(os_raw[e] << 16);
+      osv[2 * e + 1] = __uint_as_float(os_raw[e] & 0xffff0000u);
+    }
+    GateIn<uint16_t, 8>::unpack(xg_raw, xv);
+    float a0 = 0.0f, a1 = 0.0f, zz = z[s];
+    if (!race_only) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a0 = __builtin_fmaf(xv[e], gw_lds[0][sub * 8 + e], a0);
+        a1 = __builtin_fmaf(xv[e], gw_lds[1][sub * 8 + e], a1);
+      }
+    }
+#pragma unroll
+    for (int off = 4; off > 0; off >>= 1) {
+      a0 += __shfl_xor(a0, off);
+      a1 += __shfl_xor(a1, off);
+      zz += __shfl_xor(zz, off);
+    }
+    const float g_s = __builtin_amdgcn_rcpf(1.0f + __expf(-(a0 + gb0)));
+    const float g_lr = __builtin_amdgcn_rcpf(1.0f + __expf(-(a1 + gb1)));
+    const float z_lr = zz * (1.0f / static_cast<float>(LC));
+    const float rz = zz > 0.0f ? __builtin_amdgcn_rcpf(zz) : 0.0f;
+    const float mass_lr = lambda * z_lr;
+    const float alpha = mass_lr > 0.0f ? __builtin_amdgcn_rcpf(1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
+    const float ws = race_only ? 0.0f : g_s * alpha;
+    const float wl = race_only ? 1.0f : g_lr;
+    float o_lr[kCols], yv[kCols];
+#pragma unroll
+    for (int k = 0; k < kCols; ++k) {
+      o_lr[k] = num[s][k] * rz;
+      yv[k] = __builtin_fmaf(ws, osv[k], wl * o_lr[k]);
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
+              pack_bf16x2(yv[6], yv[7])},
+        out_rs, static_cast<uint32_t>(i) * kRowBytes + vbase, 0, 0);
+    if (aux.o_lr) {
+#pragma unroll
+      for (int k = 0; k < kCols; k += 4)
+        *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * kCols + k) =
+            f32x4{o_lr[k], o_lr[k + 1], o_lr[k + 2], o_lr[k + 3]};
+    }
+    if (aux.sv_olr) {
+#pragma unroll
+      for (int k = 0; k < kCols; k += 4)
+        Elem<uint16_t>::store4(static_cast<uint16_t *>(aux.sv_olr) + qi * D + sub * kCols + k, o_lr + k);
+    }
+    if (sub == 0 && aux.sv_z) {
+      aux.sv_z[qi] = zz;
+      aux.sv_gs[qi] = g_s;
+      aux.sv_glr[qi] = g_lr;
+    }
+    if (sub == 0) {
+      if (aux.z_lr) aux.z_lr[qi] = z_lr;
+      if (!race_only) {
+        if (aux.alpha) aux.alpha[qi] = alpha;
+        if (aux.g_s) aux.g_s[qi] = g_s;
+        if (aux.g_lr) aux.g_lr[qi] = g_lr;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one step at a time (the sums hold the registers)
+  }
+}
+
+template <int LC>
+void launch_lds(const Geometry &g, const void *x_gate, const float *gate_w, const float *gate_b,
+                const Buffers &buf, const AuxOut &aux, void *out, hipStream_t stream) {
+  const long long tiles = (g.N + kLdsFuseTile - 1) / kLdsFuseTile;
+  const long long units = static_cast<long long>(g.BH) * tiles;
+  const long long grid = (units + kXcdCount - 1) / kXcdCount * kXcdCount;
+  hipLaunchKernelGGL((elsaa_k5_fuse_lds<LC>), dim3(static_cast<unsigned>(grid)), dim3(kLdsFuseWaves * 64), 0,
+                     stream, static_cast<const uint16_t *>(buf.o_s), buf.lse,
+                     static_cast<const uint8_t *>(buf.rcode), static_cast<const uint16_t *>(buf.tsum), buf.tcnt,
+                     static_cast<const uint16_t *>(x_gate), gate_w, gate_b, g.H, g.N, g.P, g.lambda,
+                     g.run_sparse ? 0 : 1, static_cast<int>(tiles), units, static_cast<uint16_t *>(out), aux);
+}
+
+// the LDS path applies: bfloat16 d = 64 rows, one code byte (2^P <= 256 rows
+// a table), d_gate = 64, and 16 tables.  With 8 tables its table passes save
+// less than the epilogue loses by streaming its inputs only after them: the
+// step was slower (vision16k 0.436 against 0.431 ms median) and the wide path
+// is kept; at 16 tables the step gains (text32k 0.428 against 0.432 ms).
+bool fuse_lds_applies(const Geometry &g) {
+  return g.bf16 && g.D == 64 && g.rcb == 1 && g.nb_race <= 256 && g.DG == 64 && g.L == 16;
+}
+
 template <int D, typename VT>
 hipError_t launch_d(const Geometry &g, const void *x_gate, const float *gate_w, const float *gate_b,
                     const Buffers &buf, const AuxOut &aux, void *out, hipStream_t stream) {
+  if constexpr (D == 64 && std::is_same_v<VT, uint16_t>) {
+    if (fuse_lds_applies(g)) {
+      launch_lds<16>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
+      return hipGetLastError();
+    }
+  }
   if (g.rcb == 1) {
     if (g.L == 16) launch_wide<D, VT, uint8_t, 16>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);
     else if (g.L == 8) launch_wide<D, VT, uint8_t, 8>(g, x_gate, gate_w, gate_b, buf, aux, out, stream);

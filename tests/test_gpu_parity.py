@@ -66,6 +66,12 @@ CASES = {
     "bf16-dgate48-L16": ("text32k-bf16", dict(B=1, H=2, N=4096, d_gate=48)),
     "bf16-dgate100-L3": ("small-bf16", dict(B=1, H=2, N=2048, race_tables=3, d_gate=100)),
     "fp32-dgate100-L8": ("tiny-fp32", dict(race_tables=8, d_gate=100)),
+    # the fusion's LDS path (bfloat16 d = 64, 16 tables, d_gate = 64): 16
+    # buckets a table (copies narrower than a wave, counts fewer than 64
+    # lanes) with a last tile of 128 queries (six of its eight waves idle),
+    # and 2 buckets a table with a last tile of 64 queries
+    "bf16-L16-P4-tail": ("text32k-bf16", dict(B=1, H=2, N=4096 + 128, race_bits=4)),
+    "bf16-L16-P1-tail": ("text32k-bf16", dict(B=1, H=1, N=2048 + 64, chunk=64, race_bits=1)),
 }
 
 
