@@ -219,6 +219,68 @@ template <> struct GateIn<float, 2> {
   }
 };
 
+// One query's lane piece (kCols value columns) once its gate dot products
+// a0, a1 and its count sum z are reduced over the query's lanes and its L
+// table sums num are complete: the gates, Z_lr, alpha, o_lr and y.  Shared by
+// the wide and LDS paths (the same arithmetic, so the same results).
+// Reciprocals use v_rcp_f32 (1 ulp).
+template <int kCols> struct Piece16 {
+  float g_s, g_lr, z_lr, alpha;
+  float o_lr[kCols], y[kCols];
+};
+template <int kCols>
+__device__ __forceinline__ Piece16<kCols> fuse_piece(float a0, float a1, float z, const float *num, const float *osv,
+                                                     float lse_i, float gb0, float gb1, float lambda, float inv_l,
+                                                     int race_only) {
+  Piece16<kCols> f;
+  f.g_s = __builtin_amdgcn_rcpf(1.0f + __expf(-(a0 + gb0)));
+  f.g_lr = __builtin_amdgcn_rcpf(1.0f + __expf(-(a1 + gb1)));
+  f.z_lr = z * inv_l;
+  const float rz = z > 0.0f ? __builtin_amdgcn_rcpf(z) : 0.0f;  // (num / L) / (z / L); 0 where z = 0
+  const float mass_lr = lambda * f.z_lr;
+  f.alpha = mass_lr > 0.0f ? __builtin_amdgcn_rcpf(1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
+  const float ws = race_only ? 0.0f : f.g_s * f.alpha;
+  const float wl = race_only ? 1.0f : f.g_lr;
+#pragma unroll
+  for (int k = 0; k < kCols; ++k) {
+    f.o_lr[k] = num[k] * rz;
+    f.y[k] = __builtin_fmaf(ws, osv[k], wl * f.o_lr[k]);
+  }
+  return f;
+}
+
+// The requested per-stage outputs and the values saved for the backward of
+// one query's lane piece (columns sub * kCols ..; per-query values from the
+// query's first lane).
+template <int kCols, typename VT>
+__device__ __forceinline__ void store_piece_aux(const AuxOut &aux, long long qi, int D, int sub, float z,
+                                                const Piece16<kCols> &f, int race_only) {
+  if (aux.o_lr) {
+#pragma unroll
+    for (int k = 0; k < kCols; k += 4)
+      *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * kCols + k) =
+          f32x4{f.o_lr[k], f.o_lr[k + 1], f.o_lr[k + 2], f.o_lr[k + 3]};
+  }
+  if (aux.sv_olr) {
+#pragma unroll
+    for (int k = 0; k < kCols; k += 4)
+      Elem<VT>::store4(static_cast<VT *>(aux.sv_olr) + qi * D + sub * kCols + k, f.o_lr + k);
+  }
+  if (sub == 0 && aux.sv_z) {
+    aux.sv_z[qi] = z;
+    aux.sv_gs[qi] = f.g_s;
+    aux.sv_glr[qi] = f.g_lr;
+  }
+  if (sub == 0) {
+    if (aux.z_lr) aux.z_lr[qi] = f.z_lr;
+    if (!race_only) {
+      if (aux.alpha) aux.alpha[qi] = f.alpha;
+      if (aux.g_s) aux.g_s[qi] = f.g_s;
+      if (aux.g_lr) aux.g_lr[qi] = f.g_lr;
+    }
+  }
+}
+
 template <int D, typename VT, typename CT, int LC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void elsaa_k5_fuse_wide(
     const VT *__restrict__ o_s, const float *__restrict__ lse, const CT *__restrict__ qcodes,
@@ -418,22 +480,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
       a1 += __shfl_xor(a1, off);
       z += __shfl_xor(z, off);
     }
-    // reciprocals with v_rcp_f32 (1 ulp)
-    const float g_s = __builtin_amdgcn_rcpf(1.0f + __expf(-(a0 + gb0)));
-    const float g_lr = __builtin_amdgcn_rcpf(1.0f + __expf(-(a1 + gb1)));
-    const float z_lr = z * (1.0f / static_cast<float>(LC));
-    const float rz = z > 0.0f ? __builtin_amdgcn_rcpf(z) : 0.0f;  // (num / L) / (z / L); 0 where z = 0
-    const float mass_lr = lambda * z_lr;
-    const float alpha = mass_lr > 0.0f ? __builtin_amdgcn_rcpf(1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
-    const float ws = race_only ? 0.0f : g_s * alpha;
-    const float wl = race_only ? 1.0f : g_lr;
-
-    float o_lr[kCols], yv[kCols];
+    const Piece16<kCols> f =
+        fuse_piece<kCols>(a0, a1, z, num, osv, lse_i, gb0, gb1, lambda, 1.0f / static_cast<float>(LC), race_only);
+    float yv[kCols];
 #pragma unroll
-    for (int k = 0; k < kCols; ++k) {
-      o_lr[k] = num[k] * rz;
-      yv[k] = __builtin_fmaf(ws, osv[k], wl * o_lr[k]);
-    }
+    for (int k = 0; k < kCols; ++k) yv[k] = f.y[k];
     // The next step's streamed inputs and codes are waited for here, before
     // this step's store: the vector memory counter retires in issue order,
     // so a wait for them after the store would also wait for the store.
@@ -451,29 +502,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
           u32x4{__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]), __float_as_uint(yv[3])},
           out_rs, yo, 0, 0);
     }
-    if (aux.o_lr) {
-#pragma unroll
-      for (int k = 0; k < kCols; k += 4)
-        *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * kCols + k) =
-            f32x4{o_lr[k], o_lr[k + 1], o_lr[k + 2], o_lr[k + 3]};
-    }
-    if (aux.sv_olr) {
-#pragma unroll
-      for (int k = 0; k < kCols; k += 4) Elem<VT>::store4(static_cast<VT *>(aux.sv_olr) + qi * D + sub * kCols + k, o_lr + k);
-    }
-    if (sub == 0 && aux.sv_z) {
-      aux.sv_z[qi] = z;
-      aux.sv_gs[qi] = g_s;
-      aux.sv_glr[qi] = g_lr;
-    }
-    if (sub == 0) {
-      if (aux.z_lr) aux.z_lr[qi] = z_lr;
-      if (!race_only) {
-        if (aux.alpha) aux.alpha[qi] = alpha;
-        if (aux.g_s) aux.g_s[qi] = g_s;
-        if (aux.g_lr) aux.g_lr[qi] = g_lr;
-      }
-    }
+    store_piece_aux<kCols, VT>(aux, qi, D, sub, z, f, race_only);
   }
 }
 
@@ -711,48 +740,13 @@ __global__ __launch_bounds__(kLdsFuseWaves * 64) __attribute__((amdgpu_waves_per
       a1 += __shfl_xor(a1, off);
       zz += __shfl_xor(zz, off);
     }
-    const float g_s = __builtin_amdgcn_rcpf(1.0f + __expf(-(a0 + gb0)));
-    const float g_lr = __builtin_amdgcn_rcpf(1.0f + __expf(-(a1 + gb1)));
-    const float z_lr = zz * (1.0f / static_cast<float>(LC));
-    const float rz = zz > 0.0f ? __builtin_amdgcn_rcpf(zz) : 0.0f;
-    const float mass_lr = lambda * z_lr;
-    const float alpha = mass_lr > 0.0f ? __builtin_amdgcn_rcpf(1.0f + __expf(__logf(mass_lr) - lse_i)) : 1.0f;
-    const float ws = race_only ? 0.0f : g_s * alpha;
-    const float wl = race_only ? 1.0f : g_lr;
-    float o_lr[kCols], yv[kCols];
-#pragma unroll
-    for (int k = 0; k < kCols; ++k) {
-      o_lr[k] = num[s][k] * rz;
-      yv[k] = __builtin_fmaf(ws, osv[k], wl * o_lr[k]);
-    }
+    const Piece16<kCols> f = fuse_piece<kCols>(a0, a1, zz, num[s], osv, lse_i, gb0, gb1, lambda,
+                                               1.0f / static_cast<float>(LC), race_only);
     __builtin_amdgcn_raw_buffer_store_b128(
-        u32x4{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
-              pack_bf16x2(yv[6], yv[7])},
+        u32x4{pack_bf16x2(f.y[0], f.y[1]), pack_bf16x2(f.y[2], f.y[3]), pack_bf16x2(f.y[4], f.y[5]),
+              pack_bf16x2(f.y[6], f.y[7])},
         out_rs, static_cast<uint32_t>(i) * kRowBytes + vbase, 0, 0);
-    if (aux.o_lr) {
-#pragma unroll
-      for (int k = 0; k < kCols; k += 4)
-        *reinterpret_cast<f32x4 *>(aux.o_lr + qi * D + sub * kCols + k) =
-            f32x4{o_lr[k], o_lr[k + 1], o_lr[k + 2], o_lr[k + 3]};
-    }
-    if (aux.sv_olr) {
-#pragma unroll
-      for (int k = 0; k < kCols; k += 4)
-        Elem<uint16_t>::store4(static_cast<uint16_t *>(aux.sv_olr) + qi * D + sub * kCols + k, o_lr + k);
-    }
-    if (sub == 0 && aux.sv_z) {
-      aux.sv_z[qi] = zz;
-      aux.sv_gs[qi] = g_s;
-      aux.sv_glr[qi] = g_lr;
-    }
-    if (sub == 0) {
-      if (aux.z_lr) aux.z_lr[qi] = z_lr;
-      if (!race_only) {
-        if (aux.alpha) aux.alpha[qi] = alpha;
-        if (aux.g_s) aux.g_s[qi] = g_s;
-        if (aux.g_lr) aux.g_lr[qi] = g_lr;
-      }
-    }
+    store_piece_aux<kCols, uint16_t>(aux, qi, D, sub, zz, f, race_only);
     __builtin_amdgcn_sched_barrier(0);  // one step at a time (the sums hold the registers)
   }
 }
