@@ -24,7 +24,7 @@ JSON line:
   parity       GPU vs oracle on the sampled heads
   secondary    the same step timing for the other headline workloads
 Multi-GPU runs are not supported: every stage is independent per (batch, head),
-and this build measures one GPU.
+and the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
