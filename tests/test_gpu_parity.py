@@ -72,6 +72,11 @@ CASES = {
     # and 2 buckets a table with a last tile of 64 queries
     "bf16-L16-P4-tail": ("text32k-bf16", dict(B=1, H=2, N=4096 + 128, race_bits=4)),
     "bf16-L16-P1-tail": ("text32k-bf16", dict(B=1, H=1, N=2048 + 64, chunk=64, race_bits=1)),
+    # the wide fusion at d = 128 with one code byte, and in binary32 with
+    # d_gate = 64 (16 and 8 tables)
+    "bf16-d128-L16-P8": ("needle256k-bf16", dict(H=2, N=4096, race_bits=8)),
+    "fp32-L16": ("tiny-fp32", dict(race_tables=16)),
+    "fp32-L8-N2k": ("tiny-fp32", dict(N=2048, race_tables=8, race_bits=6)),
 }
 
 
