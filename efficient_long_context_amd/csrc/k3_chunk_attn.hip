@@ -971,8 +971,11 @@ __global__ __launch_bounds__(768) void elsaa_k3_chunk_attn_slide(
 // matrix work).  No producer waves: all eight waves stage each block of 64
 // window keys (K row-major, V transposed) into one of two LDS buffers, the
 // next block's rows in flight in registers while the current block is
-// computed, with one LDS-only barrier per block.  Neighbouring tiles share a
-// chunk of keys and run on one XCD.
+// computed, with one LDS-only barrier per block.  Key indices are requested a
+// block before their rows, so neither a permutation load nor a row load is
+// waited for in the block that issues it, and rows come through buffer loads
+// with 32-bit offsets from the segment's base (N * d * 2 < 2^32 bytes).
+// Neighbouring tiles share a chunk of keys and run on one XCD.
 template <bool kIdent>
 __global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_c256(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -993,29 +996,44 @@ __global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_c256(
   const int r0 = static_cast<int>(tile % tiles_per_seg) * QT;
   const int c = r0 / w;
   const int lo = c > 0 ? (c - 1) * w : 0, hi = (c + 1) * w;
+  // the segment's K and V rows and key permutation as buffers: 32-bit
+  // offsets, no 64-bit address arithmetic per gathered row
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + seg * D, static_cast<uint32_t>(N) * (D * 2));
+  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v + seg * D, static_cast<uint32_t>(N) * (D * 2));
+  const __amdgpu_buffer_rsrc_t pk_rs = make_rsrc(perm_k + seg, static_cast<uint32_t>(N) * 4u);
+  auto key_index = [&](int r) -> int {
+    if constexpr (kIdent) {
+      return r;
+    } else {
+      return __builtin_amdgcn_raw_buffer_load_b32(pk_rs, static_cast<uint32_t>(r) * 4u, 0, 0);
+    }
+  };
   // staging: thread tid holds K pieces (row (tid + 512 p) / 16, chunk
   // (tid + 512 p) % 16) and the V pair tid % 32, chunk tid / 32
   int kj[kKPer], vj0[kVPer], vj1[kVPer];
   u16x8 kr[kKPer], vr0[kVPer], vr1[kVPer];
   auto load_idx = [&](int s0) {
 #pragma unroll
-    for (int p = 0; p < kKPer; ++p) kj[p] = sorted_index<kIdent>(perm_k, seg, s0 + (tid + 512 * p) / (D / 8));
+    for (int p = 0; p < kKPer; ++p) kj[p] = key_index(s0 + (tid + 512 * p) / (D / 8));
 #pragma unroll
     for (int p = 0; p < kVPer; ++p) {
       const int jp = (tid + 512 * p) % (kKBlock / 2);
-      vj0[p] = sorted_index<kIdent>(perm_k, seg, s0 + 2 * jp);
-      vj1[p] = sorted_index<kIdent>(perm_k, seg, s0 + 2 * jp + 1);
+      vj0[p] = key_index(s0 + 2 * jp);
+      vj1[p] = key_index(s0 + 2 * jp + 1);
     }
+  };
+  auto row = [&](__amdgpu_buffer_rsrc_t rs, int j, int piece) -> u16x8 {
+    return __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rs, static_cast<uint32_t>(j) * (D * 2) + piece * 16, 0, 0));
   };
   auto load_rows = [&]() {
 #pragma unroll
-    for (int p = 0; p < kKPer; ++p)
-      kr[p] = *reinterpret_cast<const u16x8 *>(k + (seg + kj[p]) * D + ((tid + 512 * p) % (D / 8)) * 8);
+    for (int p = 0; p < kKPer; ++p) kr[p] = row(k_rs, kj[p], (tid + 512 * p) % (D / 8));
 #pragma unroll
     for (int p = 0; p < kVPer; ++p) {
       const int ch = (tid + 512 * p) / (kKBlock / 2);
-      vr0[p] = *reinterpret_cast<const u16x8 *>(v + (seg + vj0[p]) * D + ch * 8);
-      vr1[p] = *reinterpret_cast<const u16x8 *>(v + (seg + vj1[p]) * D + ch * 8);
+      vr0[p] = row(v_rs, vj0[p], ch);
+      vr1[p] = row(v_rs, vj1[p], ch);
     }
   };
   auto store_rows = [&](uint16_t *buf) {
@@ -1057,15 +1075,16 @@ __global__ __launch_bounds__(512) void elsaa_k3_chunk_attn_c256(
   }
   const bf16x8 ones = __builtin_bit_cast(bf16x8, (u16x8)0x3f80);
 
+  // rows are requested one block ahead, their indices two blocks ahead (the
+  // last request repeats the last block's indices and goes unused)
   load_idx(lo);
   load_rows();
+  load_idx(lo + kKBlock);
   for (int s0 = lo, b = 0; s0 < hi; s0 += kKBlock, ++b) {
     uint16_t *buf = smem + (b & 1) * kBufElems;
     store_rows(buf);  // waits for this block's rows
-    if (s0 + kKBlock < hi) {  // the next block's rows, in flight during this block
-      load_idx(s0 + kKBlock);
-      load_rows();
-    }
+    if (s0 + kKBlock < hi) load_rows();  // the next block's rows, in flight during this block
+    load_idx(s0 + 2 * kKBlock < hi ? s0 + 2 * kKBlock : hi - kKBlock);
     lds_barrier();  // block b staged; every wave is past block b - 1
     attend_stage<D, kKBlock, QG>(buf, buf + kKBlock * kKRow, kKBlock, bq, o, l_acc, m, scale_log2, ones, g, r16);
   }
@@ -1200,7 +1219,7 @@ hipError_t launch_bf16_c256(const Geometry &g, const void *q, const void *k, con
 template <bool kIdent>
 hipError_t launch_bf16_any(const Geometry &g, const void *q, const void *k, const void *v, const int32_t *pq,
                            const int32_t *pk, void *o_s, float *lse, float scale_log2, hipStream_t stream) {
-  if (g.D == 128 && g.w % 256 == 0)
+  if (g.D == 128 && g.w % 256 == 0 && g.N < (1 << 24))  // 32-bit buffer offsets
     return launch_bf16_c256<kIdent>(g, q, k, v, pq, pk, o_s, lse, scale_log2, stream);
   // 128-query tiles when w allows; key stages of 4 blocks (d = 64: the whole
   // 256-key window of w = 128) or 2, keeping LDS <= 72 KB (two workgroups
