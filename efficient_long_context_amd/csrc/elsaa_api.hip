@@ -180,15 +180,20 @@ size_t carve(const elsaa::Geometry &g, char *base, elsaa::Buffers *b) {
   t.flags = reinterpret_cast<uint8_t *>(take(2 * rows + 4));  // + one word: any row flagged
   // the sort's tile counts, and before them (the RACE build runs first) the
   // tiled RACE rank's
+  // (the RACE build ranks and gathers over (b, h, token block) heads)
+  const elsaa::Geometry gr = elsaa::race_block_geometry(g);
+  const size_t rblocks = static_cast<size_t>(elsaa::race_blocks(g));
   const size_t sort_hist = 2 * static_cast<size_t>(g.BH) * g.nb_sort * g.sort_tiles * 4;
-  const size_t race_hist = elsaa::race_hist_bytes(g);
+  const size_t race_hist = elsaa::race_hist_bytes(gr);
   t.hist = reinterpret_cast<uint32_t *>(take(sort_hist > race_hist ? sort_hist : race_hist));
   // per-table key permutation and run starts of the RACE build
   t.rperm = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * g.N * 4));
-  t.rstart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (g.nb_race + 1) * 4));
-  t.rpart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(g.BH) * g.L * (elsaa::race_parts(g.N) + 1) * 8));
+  t.rstart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(gr.BH) * g.L * (g.nb_race + 1) * 4));
+  t.rpart = reinterpret_cast<int32_t *>(take(static_cast<size_t>(gr.BH) * g.L * (elsaa::race_parts(gr.N) + 1) * 8));
   t.tsum = take(static_cast<size_t>(g.BH) * g.L * g.nb_race * g.D * es);
   t.tcnt = reinterpret_cast<float *>(take(static_cast<size_t>(g.BH) * g.L * g.nb_race * 4));
+  t.psum = rblocks > 1 ? reinterpret_cast<float *>(take(g.BH * rblocks * g.L * g.nb_race * g.D * 4)) : nullptr;
+  t.pcnt = rblocks > 1 ? reinterpret_cast<float *>(take(g.BH * rblocks * g.L * g.nb_race * 4)) : nullptr;
   // the sparse output and its LSE round-trip through memory unless the fusion
   // runs in the attention's epilogue
   t.o_s = g.fused ? nullptr : take(rows * g.D * es);

@@ -50,6 +50,8 @@ struct Buffers {
   int32_t *rpart;   // [BH][L][parts + 1][2] per gather part: first owned bucket, its run start
   void *tsum;       // [BH][L][nb_race][D] bucket sums, stored in dtype
   float *tcnt;      // [BH][L][nb_race]
+  float *psum;      // [BH][race_blocks][L][nb_race][D] partial tables (race_blocks > 1, else NULL)
+  float *pcnt;      // [BH][race_blocks][L][nb_race] partial counts
   void *o_s;        // [BH][N][D] in dtype
   float *lse;       // [BH][N]
   // kept for the backward pass (ELSAA_OPT_SAVE_FOR_BACKWARD; else NULL):
@@ -110,7 +112,21 @@ struct RaceBuildIO {
   void *tsum;         // [BH][L][2^P][D] sums
   float *tcnt;        // [BH][L][2^P] counts
   uint32_t *flag;     // a word the rank kernel clears
+  // token blocks (race_blocks): with blocks > 1 the tables are first built
+  // per (b, h, block of N / blocks consecutive keys) into binary32 partial
+  // tables, then summed over the blocks in block order into tsum and tcnt
+  int blocks = 1;
+  float *psum = nullptr;  // [BH][blocks][L][2^P][D]
+  float *pcnt = nullptr;  // [BH][blocks][L][2^P]
 };
+// Token blocks of the forward's RACE build: 1, or the power of two that cuts
+// a (b, h)'s value rows into blocks of at most 8 MB (which one XCD's L2 and
+// its share of the last-level cache serve to all L tables' passes) when the
+// rows are too many for one XCD and one workgroup's LDS rank.
+int race_blocks(const Geometry &g);
+// The geometry the RACE build's rank and gather run on: (b, h, block) as
+// B * H * blocks heads of N / blocks keys.
+Geometry race_block_geometry(const Geometry &g);
 hipError_t launch_race_build_io(const Geometry &g, const RaceBuildIO &io, hipStream_t stream);
 // Scratch of the RACE build's tiled rank (0 when one workgroup per table
 // ranks in LDS): [L][BH][2^P][tiles] counts.

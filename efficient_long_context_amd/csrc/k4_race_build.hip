@@ -300,11 +300,11 @@ constexpr int kGatherWaves = 4;       // waves per gather workgroup
 constexpr int kGatherStage = 512;     // key indices a wave stages in LDS at once
 constexpr int kGatherSlack = 128;     // staged entries read past the end by the last batch
 
-template <typename VT, int D, typename PT>
+template <typename VT, int D, typename PT, typename TS>
 __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
     const VT *__restrict__ v, const PT *__restrict__ rperm, const int32_t *__restrict__ rstart,
     const int32_t *__restrict__ rpart, int N, int L, int BH, int P, int parts, long long waves_total,
-    int xcd_local, VT *__restrict__ tsum) {
+    int xcd_local, TS *__restrict__ tsum) {
   using PC = Piece<VT, D>;
   constexpr int kCols = PC::kCols, kLPR = PC::kLanesPerRow;
   constexpr int kRPI = PC::kRowsPerLoad;
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   const long long bh = unit / L;
   const int32_t *rs = rstart + unit * (nb + 1);
   const PT *rp = rperm + (static_cast<long long>(unit % L) * BH + bh) * N;
-  VT *ts = tsum + unit * nb * static_cast<long long>(D);
+  TS *ts = tsum + unit * nb * static_cast<long long>(D);
 
   // owned buckets [b0, b1) and their positions [p_lo, p_hi), from the part
   // table the rank kernel wrote (the buckets whose run starts in this part's
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
 #pragma unroll
     for (int m = 0; m < kCols / kRPI; ++m)
       ts[b * static_cast<long long>(D) + cc * kCols + transposed_column<kCols, kLPR>(m, lane)] =
-          Elem<VT>::store_val(r[m]);
+          Elem<TS>::store_val(r[m]);
 #pragma unroll
     for (int k = 0; k < kCols; ++k) a[k] = 0.0f;
   };
@@ -464,6 +464,40 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   }
 }
 
+// Token-blocked build: the tables of (b, h) are the sums over its blocks,
+// taken in block order, of the blocks' binary32 partial tables.  Threads
+// below n4 sum four columns of one table row each; the next nc threads one
+// count each.
+template <typename VT>
+__global__ __launch_bounds__(256) void elsaa_k4_race_blocks_sum(const float *__restrict__ psum,
+                                                               const float *__restrict__ pcnt, int blocks,
+                                                               long long row_elems, long long cnt_elems,
+                                                               long long n4, long long nc, VT *__restrict__ tsum,
+                                                               float *__restrict__ tcnt) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n4) {
+    // row_elems = L 2^P D values per (b, h), a multiple of 4
+    const long long e = i * 4;
+    const long long bh = e / row_elems;
+    const float *p = psum + bh * blocks * row_elems + (e - bh * row_elems);
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < blocks; ++t) {
+      float x[4];
+      Elem<float>::load4(p + t * row_elems, x);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) a[m] += x[m];
+    }
+    Elem<VT>::store4(tsum + e, a);
+  } else if (i < n4 + nc) {
+    const long long e = i - n4;
+    const long long bh = e / cnt_elems;
+    const float *p = pcnt + bh * blocks * cnt_elems + (e - bh * cnt_elems);
+    float a = 0.0f;
+    for (int t = 0; t < blocks; ++t) a += p[t * cnt_elems];
+    tcnt[e] = a;
+  }
+}
+
 }  // namespace
 
 
@@ -522,10 +556,20 @@ hipError_t launch_race_build_pt(const Geometry &g, const RaceBuildIO &io, hipStr
   auto gather = [&](auto vt, auto dc) {
     using VT = decltype(vt);
     constexpr int D = decltype(dc)::value;
-    // one (b, h)'s value rows fit an XCD's 4 MB L2 at most a few times over:
-    // keep its gathers on one XCD; beyond that spread each (b, h) over all
-    const int xcd_local = static_cast<long long>(g.N) * D * sizeof(VT) <= (4ll << 20) ? 1 : 0;
-    hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT>), grid, dim3(kGatherWaves * 64), 0, stream,
+    // one (b, h)'s value rows fit within twice an XCD's 4 MB L2: keep its
+    // gathers on one XCD (gathers of 128-byte rows ran at the addresser's
+    // rate up to 8 MB of rows per XCD); beyond that spread each (b, h) over
+    // all XCDs, so its rows stay in the last-level cache
+    const int xcd_local = static_cast<long long>(g.N) * D * sizeof(VT) <= (8ll << 20) ? 1 : 0;
+    if constexpr (sizeof(VT) == 2) {
+      if (io.blocks > 1) {  // binary32 partial tables
+        hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT, float>), grid, dim3(kGatherWaves * 64), 0, stream,
+                           static_cast<const VT *>(io.values), rperm, io.rstart, io.rpart, g.N, g.L, g.BH, g.P,
+                           parts, waves_total, xcd_local, static_cast<float *>(io.tsum));
+        return;
+      }
+    }
+    hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT, VT>), grid, dim3(kGatherWaves * 64), 0, stream,
                        static_cast<const VT *>(io.values), rperm, io.rstart, io.rpart, g.N, g.L, g.BH, g.P,
                        parts, waves_total, xcd_local, static_cast<VT *>(io.tsum));
   };
@@ -548,7 +592,54 @@ size_t race_hist_bytes(const Geometry &g) {
   return static_cast<size_t>(g.L) * g.BH * g.nb_race * tiled_sort_tiles(g.N, g.P) * 4;
 }
 
+int race_blocks(const Geometry &g) {
+  constexpr long long kBlockBytes = 8ll << 20;
+  const long long es = g.bf16 ? 2 : 4;
+  const long long head = static_cast<long long>(g.N) * g.D * es;
+  if (staged_rank_waves(g) > 0 || head <= kBlockBytes) return 1;
+  int blocks = 2;
+  while (static_cast<long long>(g.N) / blocks * g.D * es > kBlockBytes) blocks *= 2;
+  // whole 64-key groups per block (the rank's 16-byte index pieces), and
+  // partial tables no larger than twice the rows they sum
+  const long long nblk = g.N / blocks;
+  if (g.N % (64ll * blocks) != 0) return 1;
+  if (static_cast<long long>(g.L) * g.nb_race * 4 > 2 * nblk * es) return 1;
+  return blocks;
+}
+
+Geometry race_block_geometry(const Geometry &g) {
+  const int blocks = race_blocks(g);
+  Geometry gb = g;
+  gb.BH = g.BH * blocks;
+  gb.N = g.N / blocks;
+  return gb;
+}
+
 hipError_t launch_race_build_io(const Geometry &g, const RaceBuildIO &io, hipStream_t stream) {
+  if (io.blocks > 1) {
+    // rank and gather over (b, h, block) heads into the partial tables, then
+    // their sums in block order
+    Geometry gb = g;
+    gb.BH = g.BH * io.blocks;
+    gb.N = g.N / io.blocks;
+    RaceBuildIO ib = io;
+    ib.tsum = io.psum;
+    ib.tcnt = io.pcnt;
+    hipError_t e = gb.N <= 65536 ? launch_race_build_pt<uint16_t>(gb, ib, stream)
+                                 : launch_race_build_pt<int32_t>(gb, ib, stream);
+    if (e != hipSuccess) return e;
+    const long long row_elems = static_cast<long long>(g.L) * g.nb_race * g.D;
+    const long long cnt_elems = static_cast<long long>(g.L) * g.nb_race;
+    const long long n4 = g.BH * row_elems / 4, nc = g.BH * cnt_elems;
+    const dim3 grid(static_cast<unsigned>((n4 + nc + 255) / 256));
+    if (g.bf16 && !io.values_f32)
+      hipLaunchKernelGGL((elsaa_k4_race_blocks_sum<uint16_t>), grid, dim3(256), 0, stream, io.psum, io.pcnt,
+                         io.blocks, row_elems, cnt_elems, n4, nc, static_cast<uint16_t *>(io.tsum), io.tcnt);
+    else
+      hipLaunchKernelGGL((elsaa_k4_race_blocks_sum<float>), grid, dim3(256), 0, stream, io.psum, io.pcnt,
+                         io.blocks, row_elems, cnt_elems, n4, nc, static_cast<float *>(io.tsum), io.tcnt);
+    return hipGetLastError();
+  }
   // 16-bit key indices whenever they fit
   return g.N <= 65536 ? launch_race_build_pt<uint16_t>(g, io, stream)
                       : launch_race_build_pt<int32_t>(g, io, stream);
@@ -567,6 +658,9 @@ hipError_t launch_race_build(const Geometry &g, const void *v, const Buffers &bu
   io.tsum = buf.tsum;
   io.tcnt = buf.tcnt;
   io.flag = flagged_any(buf.flags, g.rows);  // the fix-up has run: cleared for the next call
+  io.blocks = race_blocks(g);
+  io.psum = buf.psum;
+  io.pcnt = buf.pcnt;
   return launch_race_build_io(g, io, stream);
 }
 

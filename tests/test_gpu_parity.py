@@ -77,6 +77,12 @@ CASES = {
     "bf16-d128-L16-P8": ("needle256k-bf16", dict(H=2, N=4096, race_bits=8)),
     "fp32-L16": ("tiny-fp32", dict(race_tables=16)),
     "fp32-L8-N2k": ("tiny-fp32", dict(N=2048, race_tables=8, race_bits=6)),
+    # the token-blocked RACE build (a (b, h)'s value rows beyond 8 MB): two
+    # blocks of 32768 keys at d = 128 with 1024-bucket tables, two blocks of
+    # 65536 keys (the 16-bit index limit) at d = 64, four binary32 blocks
+    "bf16-race-blocks-d128": ("needle256k-bf16", dict(H=1, N=65536, chunk=64)),
+    "bf16-race-blocks-d64": ("text32k-bf16", dict(B=1, H=1, N=131072)),
+    "fp32-race-blocks": ("tiny-fp32", dict(N=131072, race_tables=8, race_bits=6)),
 }
 
 
