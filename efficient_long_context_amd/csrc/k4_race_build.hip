@@ -300,7 +300,11 @@ constexpr int kGatherWaves = 4;       // waves per gather workgroup
 constexpr int kGatherStage = 512;     // key indices a wave stages in LDS at once
 constexpr int kGatherSlack = 128;     // staged entries read past the end by the last batch
 
-template <typename VT, int D, typename PT, typename TS>
+// A wave sums D columns of rows of DS columns: with DS = 2 D the (b, h)'s
+// work is done in two column halves, each half's passes (all tables) reading
+// half of every row, so the rows the half's in-flight waves touch are half
+// as many bytes (at d = 128, 4 MB per 8 MB token block: one XCD's L2).
+template <typename VT, int D, typename PT, typename TS, int DS>
 __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
     const VT *__restrict__ v, const PT *__restrict__ rperm, const int32_t *__restrict__ rstart,
     const int32_t *__restrict__ rpart, int N, int L, int BH, int P, int parts, long long waves_total,
@@ -328,12 +332,16 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
   const long long u = wg * kGatherWaves + wave;
   if (u >= waves_total) return;  // whole wave; the kernel has no barriers
   PT *stage = stage_all[wave];
+  static_assert(DS == D || DS == 2 * D, "whole rows or column halves");
   const int prt = static_cast<int>(u % parts);
-  const long long unit = u / parts;  // (b, h) * L + table
-  const long long bh = unit / L;
+  // work order (b, h), column half, table, part
+  const long long rest = u / parts;
+  const int half = DS == D ? 0 : static_cast<int>((rest / L) % 2);
+  const long long bh = DS == D ? rest / L : rest / (2ll * L);
+  const long long unit = bh * L + rest % L;  // (b, h) * L + table
   const int32_t *rs = rstart + unit * (nb + 1);
   const PT *rp = rperm + (static_cast<long long>(unit % L) * BH + bh) * N;
-  TS *ts = tsum + unit * nb * static_cast<long long>(D);
+  TS *ts = tsum + unit * nb * static_cast<long long>(DS) + half * D;
 
   // owned buckets [b0, b1) and their positions [p_lo, p_hi), from the part
   // table the rank kernel wrote (the buckets whose run starts in this part's
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
     lane_group_transpose_sum<kCols, kLPR>(a, r, lane);
 #pragma unroll
     for (int m = 0; m < kCols / kRPI; ++m)
-      ts[b * static_cast<long long>(D) + cc * kCols + transposed_column<kCols, kLPR>(m, lane)] =
+      ts[b * static_cast<long long>(DS) + cc * kCols + transposed_column<kCols, kLPR>(m, lane)] =
           Elem<TS>::store_val(r[m]);
 #pragma unroll
     for (int k = 0; k < kCols; ++k) a[k] = 0.0f;
@@ -374,7 +382,8 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
     return;
   }
   const __amdgpu_buffer_rsrc_t vrs =
-      make_rsrc(v + bh * N * static_cast<long long>(D), static_cast<uint32_t>(N) * PC::kRowBytes);
+      make_rsrc(v + bh * N * static_cast<long long>(DS) + half * D,
+                static_cast<uint32_t>(N) * (PC::kRowBytes * (DS / D)) - half * PC::kRowBytes);
   const uint32_t cbyte = static_cast<uint32_t>(cc) * 16u;
   for (int s0 = p_lo; s0 < p_hi; s0 += kGatherStage) {
     const int s1 = s0 + kGatherStage < p_hi ? s0 + kGatherStage : p_hi;
@@ -406,7 +415,8 @@ __global__ __launch_bounds__(kGatherWaves * 64) void elsaa_k4_race_gather(
       uint32_t off[kI];
       const PT *lp = stage + (pbase - s0a) + my_off;
 #pragma unroll
-      for (int i = 0; i < kI; ++i) off[i] = static_cast<uint32_t>(lp[i * kRPI]) * PC::kRowBytes + cbyte;
+      for (int i = 0; i < kI; ++i)
+        off[i] = static_cast<uint32_t>(lp[i * kRPI]) * (PC::kRowBytes * (DS / D)) + cbyte;
 #pragma unroll
       for (int i = 0; i < kI; ++i) off[i] = pbase + i * kRPI + my_off < s1 ? off[i] : 0x80000000u;
 #pragma unroll
@@ -563,13 +573,22 @@ hipError_t launch_race_build_pt(const Geometry &g, const RaceBuildIO &io, hipStr
     const int xcd_local = static_cast<long long>(g.N) * D * sizeof(VT) <= (8ll << 20) ? 1 : 0;
     if constexpr (sizeof(VT) == 2) {
       if (io.blocks > 1) {  // binary32 partial tables
-        hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT, float>), grid, dim3(kGatherWaves * 64), 0, stream,
-                           static_cast<const VT *>(io.values), rperm, io.rstart, io.rpart, g.N, g.L, g.BH, g.P,
-                           parts, waves_total, xcd_local, static_cast<float *>(io.tsum));
+        if constexpr (D == 128) {  // in column halves
+          const long long wt = 2 * waves_total;
+          const long long wg2 = (wt + kGatherWaves - 1) / kGatherWaves;
+          const dim3 grid2(static_cast<unsigned>((wg2 + kXcdCount - 1) / kXcdCount * kXcdCount));
+          hipLaunchKernelGGL((elsaa_k4_race_gather<VT, 64, PT, float, 128>), grid2, dim3(kGatherWaves * 64), 0,
+                             stream, static_cast<const VT *>(io.values), rperm, io.rstart, io.rpart, g.N, g.L,
+                             g.BH, g.P, parts, wt, xcd_local, static_cast<float *>(io.tsum));
+        } else {
+          hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT, float, D>), grid, dim3(kGatherWaves * 64), 0,
+                             stream, static_cast<const VT *>(io.values), rperm, io.rstart, io.rpart, g.N, g.L,
+                             g.BH, g.P, parts, waves_total, xcd_local, static_cast<float *>(io.tsum));
+        }
         return;
       }
     }
-    hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT, VT>), grid, dim3(kGatherWaves * 64), 0, stream,
+    hipLaunchKernelGGL((elsaa_k4_race_gather<VT, D, PT, VT, D>), grid, dim3(kGatherWaves * 64), 0, stream,
                        static_cast<const VT *>(io.values), rperm, io.rstart, io.rpart, g.N, g.L, g.BH, g.P,
                        parts, waves_total, xcd_local, static_cast<VT *>(io.tsum));
   };
