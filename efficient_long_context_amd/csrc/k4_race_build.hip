@@ -515,18 +515,23 @@ namespace {
 
 // One workgroup per (b, h, table) ranks the table's codes in LDS when its
 // counters and the segment's 16-bit permutation fit with two workgroups per
-// CU; returns its waves, or 0 for the tiled rank.
+// CU, else with one (then with as many waves as fit, up to 16); returns its
+// waves, or 0 for the tiled rank.
 int staged_rank_waves(const Geometry &g) {
   if (g.N > 65536) return 0;
   const int nb = g.nb_race;
   int waves = 16384 / nb;  // LDS counters: waves * nb * 4 bytes <= 64 KB
   waves = waves < 1 ? 1 : (waves > 16 ? 16 : waves);
-  constexpr size_t kRankLdsTwoPerCu = 78 * 1024;
+  constexpr size_t kRankLdsTwoPerCu = 78 * 1024, kRankLdsOnePerCu = 150 * 1024;
   auto rank_lds = [&](int w) {  // + 16: the staged indices start 16-byte aligned
     return (static_cast<size_t>(w) * nb + w) * 4 + static_cast<size_t>(g.N) * 2 + 16;
   };
-  while (waves > 4 && rank_lds(waves) > kRankLdsTwoPerCu) waves /= 2;
-  return rank_lds(waves) > kRankLdsTwoPerCu ? 0 : waves;
+  int w2 = waves;
+  while (w2 > 4 && rank_lds(w2) > kRankLdsTwoPerCu) w2 /= 2;
+  if (rank_lds(w2) <= kRankLdsTwoPerCu) return w2;
+  int w1 = 16;
+  while (w1 > 4 && rank_lds(w1) > kRankLdsOnePerCu) w1 /= 2;
+  return rank_lds(w1) > kRankLdsOnePerCu ? 0 : w1;
 }
 
 template <typename PT>
@@ -615,7 +620,7 @@ int race_blocks(const Geometry &g) {
   constexpr long long kBlockBytes = 8ll << 20;
   const long long es = g.bf16 ? 2 : 4;
   const long long head = static_cast<long long>(g.N) * g.D * es;
-  if (staged_rank_waves(g) > 0 || head <= kBlockBytes) return 1;
+  if (head <= kBlockBytes) return 1;
   int blocks = 2;
   while (static_cast<long long>(g.N) / blocks * g.D * es > kBlockBytes) blocks *= 2;
   // whole 64-key groups per block (the rank's 16-byte index pieces), and
