@@ -281,7 +281,11 @@ __device__ __forceinline__ void store_piece_aux(const AuxOut &aux, long long qi,
   }
 }
 
-template <int D, typename VT, typename CT, int LC>
+// With DS = 2 D (rows of 128 bfloat16 columns) a workgroup serves its run
+// twice, once per column half: the table rows its waves gather at a time are
+// then half of every row (2 MB of a (b, h)'s 16 tables of 2^10 buckets), and
+// the workgroups of an XCD, which start together, keep to one half at a time.
+template <int D, typename VT, typename CT, int LC, int DS = D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void elsaa_k5_fuse_wide(
     const VT *__restrict__ o_s, const float *__restrict__ lse, const CT *__restrict__ qcodes,
     const VT *__restrict__ tsum, const float *__restrict__ tcnt, const VT *__restrict__ x_gate,
@@ -291,7 +295,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   constexpr int kCols = 16 / kES;         // value columns per lane
   constexpr int kLPQ = D / kCols;         // lanes per query
   constexpr int kQPS = 64 / kLPQ;         // queries per wave step
-  constexpr int kRowBytes = D * kES;
+  constexpr int kRowBytes = D * kES;      // bytes of a lane group's piece of a row
+  constexpr int kRowStride = DS * kES;    // bytes of a whole row
+  static_assert(DS == D || DS == 2 * D, "whole rows or column halves");
   constexpr int cb = static_cast<int>(sizeof(CT));
   constexpr int kCW = LC * cb / 4;        // 32-bit words of one query's codes
   constexpr int kGE = 64 / kLPQ;          // gate inputs per lane when d_gate = 64
@@ -321,8 +327,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   if (gate_fast && tid < 128)
     gw_lds[tid >> 6][tid & 63] = gate_w[static_cast<long long>((tid >> 6) * H + h) * DG + (tid & 63)];
   const float gb0 = gate_b[h], gb1 = gate_b[H + h];
-  const __amdgpu_buffer_rsrc_t ts_rs =
-      make_rsrc(tsum + bh * LC * nb * static_cast<long long>(D), static_cast<uint32_t>(LC * nb * kRowBytes));
   const uint32_t vbase = static_cast<uint32_t>(sub) * 16u;
   const Bf16Adder adder;
   __syncthreads();
@@ -335,175 +339,182 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   // base and 32-bit lane offsets keep the per-lane addresses in one register
   const __amdgpu_buffer_rsrc_t qc_rs =
       make_rsrc(qcodes + bh * N * LC, static_cast<uint32_t>(N) * LC * cb);
-  const __amdgpu_buffer_rsrc_t os_rs =
-      make_rsrc(o_s + bh * N * static_cast<long long>(D), static_cast<uint32_t>(N) * kRowBytes);
   const __amdgpu_buffer_rsrc_t lse_rs = make_rsrc(lse + bh * N, static_cast<uint32_t>(N) * 4u);
   const __amdgpu_buffer_rsrc_t xg_rs =
       make_rsrc(x_gate + b * N * DG, static_cast<uint32_t>(N) * DG * kES);
-  const __amdgpu_buffer_rsrc_t out_rs =
-      make_rsrc(out + bh * N * static_cast<long long>(D), static_cast<uint32_t>(N) * kRowBytes);
-  auto load_codes = [&](int i0, uint32_t (&w)[kCW]) {
-    const uint32_t off = static_cast<uint32_t>(i0 + lane / kLPQ) * (LC * cb);
-    if constexpr (kCW % 4 == 0) {
+  for (int half = 0; half < DS / D; ++half) {
+    // this half's columns of the tables, the sparse output and the output
+    const int col0 = half * D;
+    const uint32_t cut = static_cast<uint32_t>(col0 * kES);
+    const __amdgpu_buffer_rsrc_t ts_rs = make_rsrc(tsum + bh * LC * nb * static_cast<long long>(DS) + col0,
+                                                   static_cast<uint32_t>(LC * nb * kRowStride) - cut);
+    const __amdgpu_buffer_rsrc_t os_rs =
+        make_rsrc(o_s + bh * N * static_cast<long long>(DS) + col0, static_cast<uint32_t>(N) * kRowStride - cut);
+    const __amdgpu_buffer_rsrc_t out_rs =
+        make_rsrc(out + bh * N * static_cast<long long>(DS) + col0, static_cast<uint32_t>(N) * kRowStride - cut);
+    auto load_codes = [&](int i0, uint32_t (&w)[kCW]) {
+      const uint32_t off = static_cast<uint32_t>(i0 + lane / kLPQ) * (LC * cb);
+      if constexpr (kCW % 4 == 0) {
 #pragma unroll
-      for (int k = 0; k < kCW / 4; ++k) {
-        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qc_rs, off, 16 * k, 0));
+        for (int k = 0; k < kCW / 4; ++k) {
+          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qc_rs, off, 16 * k, 0));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[4 * k + e] = v[e];
-      }
-    } else {
-      static_assert(kCW == 2, "8 code bytes per query");
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(qc_rs, off, 0, 0);
-      w[0] = v[0];
-      w[1] = v[1];
-    }
-  };
-  uint32_t cw[kCW];
-  load_codes(i_of(0), cw);
-  // the streamed inputs of a step (sparse output, its LSE, gate inputs) are
-  // requested one step ahead, so their HBM latency overlaps the table gathers
-  auto load_stream = [&](int i0, u32x4 &os_raw, float &lse_v, u32x4 &xg_raw) {
-    if (race_only) return;  // y = o_lr: no sparse output, LSE or gate inputs
-    const uint32_t ii = static_cast<uint32_t>(i0 + lane / kLPQ);
-    os_raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(os_rs, ii * kRowBytes + vbase, 0, 0));
-    lse_v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lse_rs, ii * 4u, 0, 0));
-    if (gate_fast) {
-      const uint32_t xo = (ii * static_cast<uint32_t>(DG) + static_cast<uint32_t>(sub * kGE)) * kES;
-      if constexpr (kGE * kES == 16) {
-        xg_raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xg_rs, xo, 0, 0));
-      } else if constexpr (kGE * kES == 8) {
-        const auto t2 = __builtin_amdgcn_raw_buffer_load_b64(xg_rs, xo, 0, 0);
-        xg_raw = u32x4{t2[0], t2[1], 0u, 0u};
+          for (int e = 0; e < 4; ++e) w[4 * k + e] = v[e];
+        }
       } else {
-        xg_raw = u32x4{__builtin_amdgcn_raw_buffer_load_b32(xg_rs, xo, 0, 0), 0u, 0u, 0u};
+        static_assert(kCW == 2, "8 code bytes per query");
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(qc_rs, off, 0, 0);
+        w[0] = v[0];
+        w[1] = v[1];
       }
-    }
-  };
-  u32x4 os_next = {0u, 0u, 0u, 0u}, xg_next = {0u, 0u, 0u, 0u};
-  float lse_next = 0.0f;
-  load_stream(i_of(0), os_next, lse_next, xg_next);
-
-  for (int st = 0; st < my_steps; ++st) {
-    const int i = i_of(st) + lane / kLPQ;
-    const int i_next = st + 1 < my_steps ? i_of(st + 1) : i_of(st);
-    const long long qi = bh * N + i;
-    const u32x4 os_raw = os_next, xg_raw = xg_next;
-    const float lse_i = lse_next;
-
-    // table rows of the L buckets (offsets relative to table l, whose base
-    // goes in the scalar offset)
-    u32x4 t[LC];
-#pragma unroll
-    for (int l = 0; l < LC; ++l) {
-      const uint32_t word = cw[l * cb / 4];
-      const int byte = l * cb % 4;
-      uint32_t off;
-      if constexpr (kRowBytes == 256) {
-        const uint32_t sel = cb == 1 ? (0x0c0c0000u | ((4u + byte) << 8))
-                                     : (0x0c000000u | ((5u + byte) << 16) | ((4u + byte) << 8));
-        off = __builtin_amdgcn_perm(word, vbase, sel);
-      } else {
-        const uint32_t c = (word >> (byte * 8)) & (cb == 1 ? 0xffu : 0xffffu);
-        off = c * static_cast<uint32_t>(kRowBytes) + vbase;
-      }
-      t[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, off, l * nb * kRowBytes, 0));
-    }
-    // the next step's streamed inputs
-    load_stream(i_next, os_next, lse_next, xg_next);
-    // sparse output and gate inputs of this step
-    float osv[kCols];
-    if constexpr (kES == 2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        osv[2 * e] = __uint_as_float(os_raw[e] << 16);
-        osv[2 * e + 1] = __uint_as_float(os_raw[e] & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) osv[e] = __uint_as_float(os_raw[e]);
-    }
-    const VT *xg = x_gate + (b * N + i) * DG;
-    float xv[kGE];
-    if (gate_fast) GateIn<VT, kGE>::unpack(xg_raw, xv);
-
-    // counts from LDS: lane sub adds tables sub, sub + kLPQ, ...
-    float z = 0.0f;
-#pragma unroll
-    for (int r = 0; r < kCntPer; ++r) {
-      const int l = sub + r * kLPQ;
-      if (l < LC) {
-        const int widx = l * cb / 4;
-        uint32_t wsel = cw[0];
-#pragma unroll
-        for (int k = 1; k < kCW; ++k) wsel = widx == k ? cw[k] : wsel;
-        const uint32_t c = (wsel >> ((l * cb % 4) * 8)) & (cb == 1 ? 0xffu : 0xffffu);
-        z += cnt_lds[l * nb + c];
-      }
-    }
-    // next step's codes, in flight while this step finishes
-    load_codes(i_next, cw);
-
-    float num[kCols];
-#pragma unroll
-    for (int k = 0; k < kCols; ++k) num[k] = 0.0f;
-#pragma unroll
-    for (int l = 0; l < LC; ++l) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (kES == 2) {
-          num[2 * e] = adder.lo(num[2 * e], t[l][e]);
-          num[2 * e + 1] = adder.hi(num[2 * e + 1], t[l][e]);
+    };
+    uint32_t cw[kCW];
+    load_codes(i_of(0), cw);
+    // the streamed inputs of a step (sparse output, its LSE, gate inputs) are
+    // requested one step ahead, so their HBM latency overlaps the table gathers
+    auto load_stream = [&](int i0, u32x4 &os_raw, float &lse_v, u32x4 &xg_raw) {
+      if (race_only) return;  // y = o_lr: no sparse output, LSE or gate inputs
+      const uint32_t ii = static_cast<uint32_t>(i0 + lane / kLPQ);
+      os_raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(os_rs, ii * kRowStride + vbase, 0, 0));
+      lse_v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lse_rs, ii * 4u, 0, 0));
+      if (gate_fast) {
+        const uint32_t xo = (ii * static_cast<uint32_t>(DG) + static_cast<uint32_t>(sub * kGE)) * kES;
+        if constexpr (kGE * kES == 16) {
+          xg_raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xg_rs, xo, 0, 0));
+        } else if constexpr (kGE * kES == 8) {
+          const auto t2 = __builtin_amdgcn_raw_buffer_load_b64(xg_rs, xo, 0, 0);
+          xg_raw = u32x4{t2[0], t2[1], 0u, 0u};
         } else {
-          num[e] += __uint_as_float(t[l][e]);
+          xg_raw = u32x4{__builtin_amdgcn_raw_buffer_load_b32(xg_rs, xo, 0, 0), 0u, 0u, 0u};
         }
       }
-    }
+    };
+    u32x4 os_next = {0u, 0u, 0u, 0u}, xg_next = {0u, 0u, 0u, 0u};
+    float lse_next = 0.0f;
+    load_stream(i_of(0), os_next, lse_next, xg_next);
 
-    float a0 = 0.0f, a1 = 0.0f;
-    if (race_only) {
-    } else if (gate_fast) {
+    for (int st = 0; st < my_steps; ++st) {
+      const int i = i_of(st) + lane / kLPQ;
+      const int i_next = st + 1 < my_steps ? i_of(st + 1) : i_of(st);
+      const long long qi = bh * N + i;
+      const u32x4 os_raw = os_next, xg_raw = xg_next;
+      const float lse_i = lse_next;
+
+      // table rows of the L buckets (offsets relative to table l, whose base
+      // goes in the scalar offset)
+      u32x4 t[LC];
 #pragma unroll
-      for (int e = 0; e < kGE; ++e) {
-        a0 = __builtin_fmaf(xv[e], gw_lds[0][sub * kGE + e], a0);
-        a1 = __builtin_fmaf(xv[e], gw_lds[1][sub * kGE + e], a1);
+      for (int l = 0; l < LC; ++l) {
+        const uint32_t word = cw[l * cb / 4];
+        const int byte = l * cb % 4;
+        uint32_t off;
+        if constexpr (kRowStride == 256) {
+          const uint32_t sel = cb == 1 ? (0x0c0c0000u | ((4u + byte) << 8))
+                                       : (0x0c000000u | ((5u + byte) << 16) | ((4u + byte) << 8));
+          off = __builtin_amdgcn_perm(word, vbase, sel);
+        } else {
+          const uint32_t c = (word >> (byte * 8)) & (cb == 1 ? 0xffu : 0xffffu);
+          off = c * static_cast<uint32_t>(kRowStride) + vbase;
+        }
+        t[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ts_rs, off, l * nb * kRowStride, 0));
       }
-    } else {
-      for (int e = sub; e < DG; e += kLPQ) {
-        const float x = Elem<VT>::load(xg + e);
-        a0 = __builtin_fmaf(x, gate_w[static_cast<long long>(h) * DG + e], a0);
-        a1 = __builtin_fmaf(x, gate_w[static_cast<long long>(H + h) * DG + e], a1);
+      // the next step's streamed inputs
+      load_stream(i_next, os_next, lse_next, xg_next);
+      // sparse output and gate inputs of this step
+      float osv[kCols];
+      if constexpr (kES == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          osv[2 * e] = __uint_as_float(os_raw[e] << 16);
+          osv[2 * e + 1] = __uint_as_float(os_raw[e] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) osv[e] = __uint_as_float(os_raw[e]);
       }
-    }
+      const VT *xg = x_gate + (b * N + i) * DG;
+      float xv[kGE];
+      if (gate_fast) GateIn<VT, kGE>::unpack(xg_raw, xv);
+
+      // counts from LDS: lane sub adds tables sub, sub + kLPQ, ...
+      float z = 0.0f;
 #pragma unroll
-    for (int off = kLPQ / 2; off > 0; off >>= 1) {
-      a0 += __shfl_xor(a0, off);
-      a1 += __shfl_xor(a1, off);
-      z += __shfl_xor(z, off);
-    }
-    const Piece16<kCols> f =
-        fuse_piece<kCols>(a0, a1, z, num, osv, lse_i, gb0, gb1, lambda, 1.0f / static_cast<float>(LC), race_only);
-    float yv[kCols];
+      for (int r = 0; r < kCntPer; ++r) {
+        const int l = sub + r * kLPQ;
+        if (l < LC) {
+          const int widx = l * cb / 4;
+          uint32_t wsel = cw[0];
 #pragma unroll
-    for (int k = 0; k < kCols; ++k) yv[k] = f.y[k];
-    // The next step's streamed inputs and codes are waited for here, before
-    // this step's store: the vector memory counter retires in issue order,
-    // so a wait for them after the store would also wait for the store.
-    asm volatile("" : "+v"(yv[0]) : "v"(os_next), "v"(xg_next), "v"(lse_next) : "memory");
+          for (int k = 1; k < kCW; ++k) wsel = widx == k ? cw[k] : wsel;
+          const uint32_t c = (wsel >> ((l * cb % 4) * 8)) & (cb == 1 ? 0xffu : 0xffffu);
+          z += cnt_lds[l * nb + c];
+        }
+      }
+      // next step's codes, in flight while this step finishes
+      load_codes(i_next, cw);
+
+      float num[kCols];
 #pragma unroll
-    for (int k = 0; k < kCW; ++k) asm volatile("" : "+v"(yv[0]) : "v"(cw[k]) : "memory");
-    const uint32_t yo = static_cast<uint32_t>(i) * kRowBytes + vbase;
-    if constexpr (kES == 2) {
-      __builtin_amdgcn_raw_buffer_store_b128(
-          u32x4{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
-                pack_bf16x2(yv[6], yv[7])},
-          out_rs, yo, 0, 0);
-    } else {
-      __builtin_amdgcn_raw_buffer_store_b128(
-          u32x4{__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]), __float_as_uint(yv[3])},
-          out_rs, yo, 0, 0);
+      for (int k = 0; k < kCols; ++k) num[k] = 0.0f;
+#pragma unroll
+      for (int l = 0; l < LC; ++l) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (kES == 2) {
+            num[2 * e] = adder.lo(num[2 * e], t[l][e]);
+            num[2 * e + 1] = adder.hi(num[2 * e + 1], t[l][e]);
+          } else {
+            num[e] += __uint_as_float(t[l][e]);
+          }
+        }
+      }
+
+      float a0 = 0.0f, a1 = 0.0f;
+      if (race_only) {
+      } else if (gate_fast) {
+#pragma unroll
+        for (int e = 0; e < kGE; ++e) {
+          a0 = __builtin_fmaf(xv[e], gw_lds[0][sub * kGE + e], a0);
+          a1 = __builtin_fmaf(xv[e], gw_lds[1][sub * kGE + e], a1);
+        }
+      } else {
+        for (int e = sub; e < DG; e += kLPQ) {
+          const float x = Elem<VT>::load(xg + e);
+          a0 = __builtin_fmaf(x, gate_w[static_cast<long long>(h) * DG + e], a0);
+          a1 = __builtin_fmaf(x, gate_w[static_cast<long long>(H + h) * DG + e], a1);
+        }
+      }
+#pragma unroll
+      for (int off = kLPQ / 2; off > 0; off >>= 1) {
+        a0 += __shfl_xor(a0, off);
+        a1 += __shfl_xor(a1, off);
+        z += __shfl_xor(z, off);
+      }
+      const Piece16<kCols> f =
+          fuse_piece<kCols>(a0, a1, z, num, osv, lse_i, gb0, gb1, lambda, 1.0f / static_cast<float>(LC), race_only);
+      float yv[kCols];
+#pragma unroll
+      for (int k = 0; k < kCols; ++k) yv[k] = f.y[k];
+      // The next step's streamed inputs and codes are waited for here, before
+      // this step's store: the vector memory counter retires in issue order,
+      // so a wait for them after the store would also wait for the store.
+      asm volatile("" : "+v"(yv[0]) : "v"(os_next), "v"(xg_next), "v"(lse_next) : "memory");
+#pragma unroll
+      for (int k = 0; k < kCW; ++k) asm volatile("" : "+v"(yv[0]) : "v"(cw[k]) : "memory");
+      const uint32_t yo = static_cast<uint32_t>(i) * kRowStride + vbase;
+      if constexpr (kES == 2) {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
+                  pack_bf16x2(yv[6], yv[7])},
+            out_rs, yo, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]), __float_as_uint(yv[3])},
+            out_rs, yo, 0, 0);
+      }
+      store_piece_aux<kCols, VT>(aux, qi, DS, sub + half * kLPQ, z, f, race_only);
     }
-    store_piece_aux<kCols, VT>(aux, qi, D, sub, z, f, race_only);
-  }
+  }  // column halves
 }
 
 template <int D, typename VT, typename CT, int LC>
@@ -535,8 +546,10 @@ void launch_wide(const Geometry &g, const void *x_gate, const float *gate_w, con
   }
   const long long units = static_cast<long long>(g.BH) * runs;
   const long long grid = (units + kXcdCount - 1) / kXcdCount * kXcdCount;
-  hipLaunchKernelGGL((elsaa_k5_fuse_wide<D, VT, CT, LC>), dim3(static_cast<unsigned>(grid)), dim3(256), lds,
-                     stream, static_cast<const VT *>(buf.o_s), buf.lse,
+  // rows of 128 bfloat16 columns: in column halves
+  constexpr bool kHalves = D == 128 && sizeof(VT) == 2;
+  hipLaunchKernelGGL((elsaa_k5_fuse_wide<kHalves ? 64 : D, VT, CT, LC, D>), dim3(static_cast<unsigned>(grid)),
+                     dim3(256), lds, stream, static_cast<const VT *>(buf.o_s), buf.lse,
                      static_cast<const CT *>(buf.rcode), static_cast<const VT *>(buf.tsum), buf.tcnt,
                      static_cast<const VT *>(x_gate), gate_w, gate_b, g.H, g.N, g.P, g.DG, g.lambda,
                      g.run_sparse ? 0 : 1, static_cast<int>(R), static_cast<int>(runs), units,
