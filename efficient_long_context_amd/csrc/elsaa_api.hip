@@ -431,9 +431,12 @@ int elsaa_forward(const void *q, const void *k, const void *v, const void *x_gat
   if (e == hipSuccess) e = device_cus(device, &g.cus);
   if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
   // the sort overlaps the RACE build on the device's second stream when both
-  // run and the sort needs no scratch the RACE build also uses
+  // run and the sort needs no scratch the RACE build also uses (the tile
+  // counts, shared by the tiled sort and the tiled RACE rank)
   SideStream *side = nullptr;
-  if (g.run_sparse && g.run_race && !g.identity && !g.fused && !elsaa::sort_is_tiled(g) && !debug_mode()) {
+  const bool shared_hist =
+      elsaa::sort_is_tiled(g) && elsaa::race_hist_bytes(elsaa::race_block_geometry(g)) > 0;
+  if (g.run_sparse && g.run_race && !g.identity && !g.fused && !shared_hist && !debug_mode()) {
     e = side_stream(device, &side);
     if (e != hipSuccess) return fail(ELSAA_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
   }
