@@ -22,7 +22,8 @@ JSON line:
                this host's cores (whole-job tokens/s extrapolated from the
                sample), plus a one-thread figure on the small workloads
   parity       GPU vs oracle on the sampled heads
-  secondary    the same step timing for the other headline workloads
+  secondary    the same step timing, roofline, stages, CPU baseline and parity
+               for the other headline workloads
 Multi-GPU runs are not supported: every stage is independent per (batch, head),
 and the benchmark runs on one GPU.
 """
@@ -414,25 +415,69 @@ def main(argv=None):
     tokens = wl.B * wl.N
     value = tokens / (ms_step * 1e-3)
 
+    def roofline(wlx, stage_ms_x):
+        """The dominant stage's algorithmic rate against its bound's peak."""
+        mx = stage_model(wlx)
+        dom = max(stage_ms_x, key=stage_ms_x.get)
+        m = mx[dom]
+        ms = stage_ms_x[dom]
+        # bound: MFMA if the stage's arithmetic intensity exceeds the chip's ridge
+        ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if m["mfma"] and m["flops"] / m["bytes"] > ridge:
+            roof = {"bound": "mfma", "achieved": round(m["flops"] / (ms * 1e-3) / 1e12, 2),
+                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        else:
+            roof = {"bound": "hbm", "achieved": round(m["bytes"] / (ms * 1e-3) / 1e9, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+        roof["traffic"] = measured_traffic(dom, wlx.name)
+        roof["kernel"] = dom
+        roof["ms_per_launch"] = round(ms, 5)
+        roof["timing"] = f"median over {args.steps} launches of the stage's begin/end events"
+        return roof
+
+    def cpu_baseline(wlx, inpx, outx):
+        """The oracle on (batch, head) slices of the workload at full N, one
+        slice at least and then until about 10 s of oracle time (or
+        --cpu-heads slices); whole-job tokens/s extrapolated from the mean
+        time per slice, and the GPU output's error on those slices."""
+        import oracle
+        oracle.build(force=False)
+        threads = oracle.num_threads()
+        heads = args.cpu_heads or 1
+        bh_all = [(b, h) for b in range(wlx.B) for h in range(wlx.H)]
+        t_used = 0.0
+        done = 0
+        errs = []
+        for (b, h) in bh_all:
+            if done >= heads and (args.cpu_heads or t_used >= 10.0):
+                break
+            sl = lambda a: np.ascontiguousarray(a[b:b + 1, h:h + 1])
+            r = oracle.forward(sl(inpx.q), sl(inpx.k), sl(inpx.v), np.ascontiguousarray(inpx.x_gate[b:b + 1]),
+                               inpx.hyperplanes, np.ascontiguousarray(inpx.gate_w[:, h:h + 1]),
+                               np.ascontiguousarray(inpx.gate_b[:, h:h + 1]), sort_bits=wlx.sort_bits,
+                               chunk=wlx.chunk, race_tables_n=wlx.race_tables, race_bits=wlx.race_bits,
+                               lam=wlx.lam)
+            t_used += r.seconds
+            done += 1
+            y = outx[b, h]
+            errs.append(float(np.abs(y - r.y[0, 0]).max() / np.abs(r.y[0, 0]).max()))
+        per_head = t_used / done
+        cpu = {
+            "value": round(wlx.B * wlx.N / (per_head * len(bh_all)), 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {len(bh_all)} (batch, head) slices of {wlx.name} at full N={wlx.N}; "
+                      f"{t_used:.1f} s of oracle time; whole-job tokens/s extrapolated "
+                      f"from the mean time per (batch, head)",
+        }
+        parity = {"heads_checked": done, "max_rel_err_y": max(errs),
+                  "tolerance": 2e-2 if wlx.dtype == "bf16" else 1e-4}
+        return cpu, parity
+
     model = stage_model(wl)
     stage_ms = main_res["stage_ms"]
     stages = {st: stage_figures(model[st], ms, peaks) for st, ms in stage_ms.items()}
-    dom = max(stage_ms, key=stage_ms.get)
-    m = model[dom]
-    ms = stage_ms[dom]
-    # bound: MFMA if the stage's arithmetic intensity exceeds the chip's ridge
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if m["mfma"] and m["flops"] / m["bytes"] > ridge:
-        roof = {"bound": "mfma", "achieved": round(m["flops"] / (ms * 1e-3) / 1e12, 2),
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(m["bytes"] / (ms * 1e-3) / 1e9, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dom, wl.name)
-    roof["kernel"] = dom
-    roof["ms_per_launch"] = round(ms, 5)
-    roof["timing"] = f"median over {args.steps} launches of the stage's begin/end events"
+    roof = roofline(wl, stage_ms)
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -465,44 +510,21 @@ def main(argv=None):
         r2 = time_workload(name, args.steps, args.warmup, backward=False)
         wl2 = r2["wl"]
         m2 = stage_model(wl2)
-        secondary.append({"workload": wl2.name, "value": round(wl2.B * wl2.N / (r2["ms_step"] * 1e-3), 1),
-                          "unit": "tokens/s", "ms_per_step": round(r2["ms_step"], 5),
-                          "median_ms": round(r2["median_ms"], 5),
-                          "stages": {st: stage_figures(m2[st], v, peaks) for st, v in r2["stage_ms"].items()}})
+        sec = {"workload": wl2.name, "value": round(wl2.B * wl2.N / (r2["ms_step"] * 1e-3), 1),
+               "unit": "tokens/s", "ms_per_step": round(r2["ms_step"], 5),
+               "median_ms": round(r2["median_ms"], 5), "roofline": roofline(wl2, r2["stage_ms"]),
+               "stages": {st: stage_figures(m2[st], v, peaks) for st, v in r2["stage_ms"].items()}}
+        if not args.no_cpu_baseline:
+            sec["cpu_baseline"], sec["parity"] = cpu_baseline(wl2, r2["inp"], r2["out"])
+        secondary.append(sec)
         del r2
     if secondary:
         result["secondary"] = secondary
 
     if not args.no_cpu_baseline:
         import oracle
-        oracle.build(force=False)
-        threads = oracle.num_threads()
-        heads = args.cpu_heads or 1
-        bh_all = [(b, h) for b in range(wl.B) for h in range(wl.H)]
-        t_used = 0.0
-        done = 0
-        errs = []
-        for (b, h) in bh_all:
-            if done >= heads and (args.cpu_heads or t_used >= 10.0):
-                break
-            sl = lambda a: np.ascontiguousarray(a[b:b + 1, h:h + 1])
-            r = oracle.forward(sl(inp.q), sl(inp.k), sl(inp.v), np.ascontiguousarray(inp.x_gate[b:b + 1]),
-                               inp.hyperplanes, np.ascontiguousarray(inp.gate_w[:, h:h + 1]),
-                               np.ascontiguousarray(inp.gate_b[:, h:h + 1]), sort_bits=wl.sort_bits,
-                               chunk=wl.chunk, race_tables_n=wl.race_tables, race_bits=wl.race_bits,
-                               lam=wl.lam)
-            t_used += r.seconds
-            done += 1
-            y = out[b, h]
-            errs.append(float(np.abs(y - r.y[0, 0]).max() / np.abs(r.y[0, 0]).max()))
-        per_head = t_used / done
-        cpu_value = tokens / (per_head * len(bh_all))
-        result["cpu_baseline"] = {
-            "value": round(cpu_value, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {len(bh_all)} (batch, head) slices of {wl.name} at full N={wl.N}; "
-                      f"{t_used:.1f} s of oracle time; whole-job tokens/s extrapolated "
-                      f"from the mean time per (batch, head)",
-        }
+        result["cpu_baseline"], parity = cpu_baseline(wl, inp, out)
+        threads = result["cpu_baseline"]["cores"]
         # one thread, whole small workloads
         one = {}
         oracle.set_num_threads(1)
@@ -516,8 +538,7 @@ def main(argv=None):
                          "tokens_per_s": round(w1.B * w1.N / r1.seconds, 1)}
         oracle.set_num_threads(threads)
         result["cpu_baseline"]["one_thread"] = one
-        result["parity"] = {"heads_checked": done, "max_rel_err_y": max(errs),
-                            "tolerance": 2e-2 if wl.dtype == "bf16" else 1e-4}
+        result["parity"] = parity
 
     print(json.dumps(result))
     return 0
