@@ -29,11 +29,17 @@ CASES = {
     # segments longer than 65536: 32-bit permutation indices and the tiled rank
     # of the RACE transposes
     "small-long-N": ("small-bf16", dict(B=1, H=1, N=65536 + 192, chunk=64), "full"),
+    # a forward in two token blocks (d = 128, 16 MB of value rows a head) and
+    # a backward whose query-side ranks need one workgroup a CU (2^10 buckets,
+    # 65536 16-bit indices), on the RACE branch those two change.  (The full
+    # model at this size puts d gate_b, a two-element sum over 65536 tokens,
+    # at 2.1e-2 of its maximum with and without token blocks.)
+    "needle-race-blocks": ("needle256k-bf16", dict(H=1, N=65536, chunk=64), "race_only"),
 }
 # the same with the forward keeping o_lr, the counts and the gates for the
 # backward (ELSAA_OPT_SAVE_FOR_BACKWARD)
 SAVED = ("tiny-fp32", "small-bf16-w64", "text32k-w128", "needle-d128-w256", "small-L3-dgate48",
-         "text32k-no-alpha", "text32k-race-only")
+         "text32k-no-alpha", "text32k-race-only", "needle-race-blocks")
 
 
 def _dy(inp, seed):

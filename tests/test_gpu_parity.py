@@ -172,12 +172,17 @@ def test_lambda_zero_ablation():
     compare_all(g, r, wl.dtype, "lambda0")
 
 
-def test_deterministic():
-    wl = workloads.workload("text32k-bf16", B=1, H=2, N=8192)
+@pytest.mark.parametrize("name,over", [
+    ("text32k-bf16", dict(B=1, H=2, N=8192)),
+    # the token-blocked RACE build: partial tables summed in block order
+    ("needle256k-bf16", dict(H=1, N=65536, chunk=64)),
+])
+def test_deterministic(name, over):
+    wl = workloads.workload(name, **over)
     inp = workloads.generate(wl, seed=7)
     a = run_gpu(inp)
     b = run_gpu(inp)
-    for key in ("y", "race_sum", "o_sparse", "lse_s", "perm_q", "perm_k"):
+    for key in ("y", "race_sum", "race_cnt", "o_sparse", "lse_s", "perm_q", "perm_k"):
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
 
 
