@@ -53,6 +53,8 @@ def _run(inp, noalloc: bool):
     (("text32k-bf16", dict(B=1, H=2, N=8192)), ("text32k-bf16", dict(B=1, H=1, N=2048))),
     (("needle256k-bf16", dict(H=2, N=8192)), ("small-bf16", dict(B=1, H=2, N=1024))),
     (("tiny-fp32", dict(H=2)), ("tiny-fp32", dict(N=512, chunk=64))),
+    # a RACE build in two token blocks (46 MB of scratch), then one block
+    (("needle256k-bf16", dict(H=1, N=65536, chunk=64)), ("needle256k-bf16", dict(H=1, N=4096))),
 ])
 def test_noalloc_matches_workspace_entry_point(first, second):
     for name, over in (first, second):
