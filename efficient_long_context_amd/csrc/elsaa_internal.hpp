@@ -119,10 +119,11 @@ struct RaceBuildIO {
   float *psum = nullptr;  // [BH][blocks][L][2^P][D]
   float *pcnt = nullptr;  // [BH][blocks][L][2^P]
 };
-// Token blocks of the forward's RACE build: 1, or the power of two that cuts
-// a (b, h)'s value rows into blocks of at most 8 MB (which one XCD's L2 and
-// its share of the last-level cache serve to all L tables' passes) when the
-// rows are too many for one XCD and one workgroup's LDS rank.
+// Token blocks of the forward's RACE build: 1, or, when a (b, h)'s value rows
+// exceed 8 MB, the power of two that cuts them into blocks of at most 8 MB
+// (which one XCD's L2 and its share of the last-level cache serve to all L
+// tables' passes); 1 again when the blocks would not hold whole 64-key groups
+// or their partial tables would exceed twice the rows they sum.
 int race_blocks(const Geometry &g);
 // The geometry the RACE build's rank and gather run on: (b, h, block) as
 // B * H * blocks heads of N / blocks keys.
