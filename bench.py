@@ -152,22 +152,28 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
         sums, counts, calib = {}, {}, 0.0
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-        race_rank = False  # inside a RACE build's tiled rank (the sort's kernels, before its run table)
+        named = []
         for row in rows:
             name = row["Kernel_Name"]
             val = float(row["Counter_Value"]) * 1024.0
             if name.startswith("__amd_rocclr_copyBuffer"):
                 calib = max(calib, val)
                 continue
-            short = name.replace("void ", "").replace("elsaa::(anonymous namespace)::", "").split("(")[0]
-            if short.startswith("elsaa_k1_hash_"):
-                race_rank = True  # a forward call: the RACE build follows the hash
-            elif short.startswith("elsaa_k4_race_"):
-                race_rank = False
-            elif short.startswith(("elsaa_k2_sort_hist", "elsaa_k2_sort_scan", "elsaa_k2_sort_scatter")) and race_rank:
-                short = "elsaa_k4_race_rank_tiles:" + short  # the RACE build's tiled rank
-            sums[short] = sums.get(short, 0.0) + val
-            counts[short] = counts.get(short, 0) + 1
+            named.append((name.replace("void ", "").replace("elsaa::(anonymous namespace)::", "").split("(")[0], val))
+        # A forward call starts at its hash kernel.  The tiled sort's kernels
+        # belong to the RACE build's tiled rank when they come before that
+        # call's run-table kernel (elsaa_k4_race_runs), which only the tiled
+        # rank launches; otherwise they are the Sort-LSH sort's.
+        starts = [i for i, (k, _) in enumerate(named) if k.startswith("elsaa_k1_hash_bf16")] + [len(named)]
+        tiled_sort = ("elsaa_k2_sort_hist", "elsaa_k2_sort_scan", "elsaa_k2_sort_scatter")
+        for c in range(len(starts) - 1):
+            call = named[starts[c]:starts[c + 1]]
+            runs_at = next((i for i, (k, _) in enumerate(call) if k.startswith("elsaa_k4_race_runs")), -1)
+            for i, (short, val) in enumerate(call):
+                if short.startswith(tiled_sort) and i < runs_at:
+                    short = "elsaa_k4_race_rank_tiles:" + short  # the RACE build's tiled rank
+                sums[short] = sums.get(short, 0.0) + val
+                counts[short] = counts.get(short, 0) + 1
         if calib <= 0.0:
             raise SystemExit(f"{path}: no calibration copy found (run with --copy-calibration)")
         scale = CALIB_BYTES / calib
