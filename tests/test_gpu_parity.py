@@ -83,6 +83,10 @@ CASES = {
     "bf16-race-blocks-d128": ("needle256k-bf16", dict(H=1, N=65536, chunk=64)),
     "bf16-race-blocks-d64": ("text32k-bf16", dict(B=1, H=1, N=131072)),
     "fp32-race-blocks": ("tiny-fp32", dict(N=131072, race_tables=8, race_bits=6)),
+    # two blocks of 65536 keys with 2^12-bucket tables: the blocks take the
+    # tiled rank (counters and indices beyond one workgroup's LDS), whose tile
+    # counts the Sort-LSH tiled sort then reuses
+    "bf16-race-blocks-P12": ("small-bf16", dict(B=1, H=1, N=131072, race_tables=4, race_bits=12)),
 }
 
 
