@@ -107,6 +107,8 @@ VARIANT_CASES = {
     "text32k-1head": ("text32k-bf16", dict(B=1, H=2, N=4096)),
     "needle-d128": ("needle256k-bf16", dict(H=2, N=4096)),
     "small-L3": ("small-bf16", dict(B=1, H=2, N=2048, race_tables=3, race_bits=5)),
+    # a RACE build in two token blocks
+    "needle-race-blocks": ("needle256k-bf16", dict(H=1, N=65536, chunk=64)),
 }
 
 
